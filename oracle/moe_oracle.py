@@ -1,0 +1,356 @@
+"""Plain, slow CPU reference of one GPU's mixture-of-experts layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The GPU library never calls it, and
+it shares no code with the GPU path: it imports nothing but NumPy.
+
+What it computes (all in float64 from the stored-precision inputs, rounding
+only where the layer stores a tensor):
+
+* gate routing - a linear router with a bias, top-k selection with the lowest
+  expert index winning ties, gate weights renormalised over the chosen k
+  (PopFetcher notes, §2.1.2 "MoE architecture": each token goes to one or more
+  experts by top-k selection; A Survey on Mixture of Experts, §5 System
+  Design, first paragraph: gate routing is the first step of expert
+  parallelism);
+* an optional per-expert capacity limit (GShard-style capacity, cited in the
+  survey's §5 first paragraph and in the PopFetcher notes §2.2); slots beyond
+  an expert's capacity are dropped;
+* input encode - gathering each expert's tokens into one contiguous block in a
+  stable order (survey §5, first paragraph);
+* the expert network FC -> ReLU -> FC with two weight matrices and no biases
+  (PopFetcher notes §2.1.1, and §5.1: matrices H x aH and aH x H, 4H^2
+  parameters);
+* output decode - restoring token order and summing the k expert outputs
+  weighted by the gate (survey §5, first paragraph);
+* per-expert popularity counts over a sliding window of iterations
+  (PopFetcher notes §3.1 routing-information collector and §4.2, Eq. 1,
+  whose body is missing from the page: the window sum of per-expert counts
+  is the reading taken here);
+* the backward pass of all of the above (the notes' §5.2.1 counts one GEMM
+  forward and two backward per expert layer: gradient w.r.t. input and
+  w.r.t. parameters).
+
+Readings of points the pages leave open (each is listed in the design notes):
+selection on the fp32 logits, ties to the lowest index, weights = softmax over
+the k selected logits; capacity C = ceil(cf*T*k/E) clamped to [1, T] (T when
+dropless); slots claim capacity in slot order t*k+j; kept weights are not
+renormalised after drops; ReLU'(0) = 0 with the mask taken from the stored h;
+the k expert outputs are summed in j order.
+
+Pins: every function here is checked in ``tests/test_oracle.py`` against
+brute force, library special cases, closed forms and finite differences.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+F64 = np.float64
+F32 = np.float32
+
+
+# --------------------------------------------------------------------------
+# storage precision
+# --------------------------------------------------------------------------
+def _to_bf16(a: np.ndarray) -> np.ndarray:
+    """Round to the nearest bf16 value (ties to even) via float32.
+
+    float64 -> float32 rounds to nearest even first; the second rounding can
+    differ from a direct float64 -> bf16 rounding only when the float32 value
+    lands exactly half-way between two bf16 values, i.e. by one bf16 ulp in
+    rare cases, far inside the bf16 tolerance.
+    """
+    f = np.ascontiguousarray(a, dtype=F32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    u = (u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)
+    return u.astype(np.uint32).view(F32)
+
+
+def round_act(a: np.ndarray, act: str) -> np.ndarray:
+    """Round to the activation storage type: 'bf16', 'f32', or 'f64' (none)."""
+    if act == "bf16":
+        return _to_bf16(a).astype(F64)
+    if act == "f32":
+        return np.asarray(a, dtype=F64).astype(F32).astype(F64)
+    if act == "f64":
+        return np.asarray(a, dtype=F64)
+    raise ValueError(act)
+
+
+# --------------------------------------------------------------------------
+# gate routing
+# --------------------------------------------------------------------------
+def router_logits(x: np.ndarray, w_gate: np.ndarray, b_gate: np.ndarray) -> np.ndarray:
+    """logits[t, e] = b[e] + sum_i x[t, i] * W_gate[i, e], accumulated in
+    float64 and stored as float32.  x: [T, d], W_gate: [d, E], b: [E]."""
+    z = np.asarray(x, F64) @ np.asarray(w_gate, F64) + np.asarray(b_gate, F64)[None, :]
+    return z.astype(F32)
+
+
+def topk_gate(logits: np.ndarray, k: int):
+    """Top-k experts per token and their renormalised gate weights.
+
+    idx[t, 0..k-1] lists the k largest logits in descending order; among
+    equal logits the lowest expert index comes first (float comparison, so
+    -0.0 and +0.0 tie).  w[t, j] = exp(L_j - L_0) / sum_i exp(L_i - L_0)
+    over the k chosen logits, which equals a softmax over all E followed by
+    renormalising the chosen k.  Returns idx int32 [T, k], w float32 [T, k].
+    """
+    L = np.asarray(logits, dtype=F32)
+    if not np.all(np.isfinite(L)):
+        raise ValueError("router logits must be finite")
+    T, E = L.shape
+    if not (1 <= k <= E):
+        raise ValueError("need 1 <= k <= E")
+    work = L.astype(F64).copy()
+    idx = np.empty((T, k), dtype=np.int32)
+    rows = np.arange(T)
+    for j in range(k):
+        # argmax returns the first (lowest-index) maximum; chosen entries
+        # are taken out of the running with -inf.
+        e = np.argmax(work, axis=1)
+        idx[:, j] = e
+        work[rows, e] = -np.inf
+    sel = L.astype(F64)[rows[:, None], idx]
+    p = np.exp(sel - sel[:, :1])
+    w = (p / p.sum(axis=1, keepdims=True)).astype(F32)
+    return idx, w
+
+
+def capacity(T: int, k: int, E: int, capacity_factor: float) -> int:
+    """C = ceil(cf * T * k / E) in float64 (cf taken as a float32), clamped to
+    [1, T]; T when cf <= 0 (dropless: no expert can receive more than T)."""
+    cf = float(np.float32(capacity_factor))
+    if cf <= 0.0:
+        return T
+    c = math.ceil(cf * T * k / E)
+    return max(1, min(T, c))
+
+
+# --------------------------------------------------------------------------
+# input encode
+# --------------------------------------------------------------------------
+def assign_slots(idx: np.ndarray, E: int, C: int) -> Dict[str, np.ndarray]:
+    """Walk slots s = t*k + j in order; each takes the next position in its
+    expert, and is kept iff that position is below the capacity C.
+
+    Returns counts_raw [E], counts_kept [E], offsets [E+1] (exclusive prefix
+    sum of counts_kept), slot_row [T*k] (row in the packed buffers, -1 when
+    dropped) and row_token [S_kept] (token held by each packed row).
+    """
+    T, k = idx.shape
+    flat = idx.reshape(-1)
+    S = flat.size
+    seen = [0] * E
+    pos = [0] * S
+    for s in range(S):
+        e = int(flat[s])
+        pos[s] = seen[e]
+        seen[e] += 1
+    counts_raw = np.array(seen, dtype=np.int32)
+    counts_kept = np.array([min(c, C) for c in seen], dtype=np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    run = 0
+    for e in range(E):
+        offsets[e] = run
+        run += int(counts_kept[e])
+    offsets[E] = run
+    slot_row = np.full(S, -1, dtype=np.int32)
+    row_token = np.full(run, -1, dtype=np.int32)
+    for s in range(S):
+        if pos[s] < C:
+            r = int(offsets[flat[s]]) + pos[s]
+            slot_row[s] = r
+            row_token[r] = s // k
+    return {"counts_raw": counts_raw, "counts_kept": counts_kept,
+            "offsets": offsets, "slot_row": slot_row, "row_token": row_token,
+            "drops": S - run}
+
+
+def encode(x: np.ndarray, row_token: np.ndarray) -> np.ndarray:
+    """x_perm[r] = x[row_token[r]] (an exact copy of the token's row)."""
+    return np.asarray(x)[np.asarray(row_token, dtype=np.int64)]
+
+
+# --------------------------------------------------------------------------
+# expert computation
+# --------------------------------------------------------------------------
+def expert_ffn(x_perm: np.ndarray, offsets: np.ndarray, w1: np.ndarray,
+               w2: np.ndarray, act: str):
+    """Per expert e, over packed rows offsets[e]..offsets[e+1]:
+    h = round(ReLU(x_perm_e @ W1[e]^T)), O = round(h @ W2[e]^T).
+    W1 is [E, F, d] and W2 is [E, d, F] (output x input)."""
+    E, F, d = w1.shape
+    R = x_perm.shape[0]
+    h = np.zeros((R, F), dtype=F64)
+    o = np.zeros((R, d), dtype=F64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        xe = np.asarray(x_perm[a:b], F64)
+        z = xe @ np.asarray(w1[e], F64).T
+        he = round_act(np.maximum(z, 0.0), act)
+        h[a:b] = he
+        o[a:b] = round_act(he @ np.asarray(w2[e], F64).T, act)
+    return h, o
+
+
+# --------------------------------------------------------------------------
+# output decode
+# --------------------------------------------------------------------------
+def decode(o: np.ndarray, w: np.ndarray, slot_row: np.ndarray, act: str) -> np.ndarray:
+    """y[t] = round(sum_j w[t, j] * O[slot_row[t*k + j]]) over kept slots,
+    accumulated in j order; a token whose slots were all dropped gets 0."""
+    T, k = w.shape
+    d = o.shape[1]
+    y = np.zeros((T, d), dtype=F64)
+    rows = slot_row.reshape(T, k)
+    for j in range(k):
+        r = rows[:, j]
+        kept = r >= 0
+        y[kept] += np.asarray(w[kept, j], F64)[:, None] * o[r[kept]]
+    return round_act(y, act)
+
+
+# --------------------------------------------------------------------------
+# whole forward
+# --------------------------------------------------------------------------
+def forward(x, w_gate, b_gate, w1, w2, k: int, capacity_factor: float, act: str,
+            logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """The layer forward.  If ``logits`` is given (float32 [T, E]) routing
+    starts from those logits instead of computing them."""
+    T = x.shape[0]
+    E = w1.shape[0]
+    if logits is None:
+        logits = router_logits(x, w_gate, b_gate)
+    idx, w = topk_gate(logits, k)
+    C = capacity(T, k, E, capacity_factor)
+    slots = assign_slots(idx, E, C)
+    x_perm = encode(x, slots["row_token"])
+    h, o = expert_ffn(x_perm, slots["offsets"], w1, w2, act)
+    y = decode(o, w, slots["slot_row"], act)
+    out = {"logits": logits, "idx": idx, "w": w, "C": C, "x_perm": x_perm,
+           "h": h, "o": o, "y": y}
+    out.update(slots)
+    return out
+
+
+# --------------------------------------------------------------------------
+# popularity
+# --------------------------------------------------------------------------
+def popularity_update(ring: np.ndarray, it: int, counts_raw: np.ndarray):
+    """Record this iteration's per-expert selections (pre-capacity) in slot
+    it % W of the ring and return (ring, window_sum), where window_sum sums
+    the last min(it + 1, W) iterations.  Exact integers."""
+    ring = np.array(ring, dtype=np.int64, copy=True)
+    W = ring.shape[0]
+    ring[it % W] = counts_raw
+    n = min(it + 1, W)
+    total = np.zeros(ring.shape[1], dtype=np.int64)
+    for back in range(n):
+        total += ring[(it - back) % W]
+    return ring.astype(np.int32), total.astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def backward(dy, fwd: Dict[str, np.ndarray], x, w_gate, w1, w2, act: str):
+    """Gradients of the layer for output gradient dy, given this module's own
+    forward results ``fwd``.
+
+    Output decode: dO[r] = w[t, j] dy[t] for the kept slot (t, j) held by row
+    r, and dg[t, j] = <dy[t], O[r]> (0 for a dropped slot).
+    FC2: dh = dO W2[e], dW2[e] = dO^T h; ReLU mask dz = dh * [h > 0];
+    FC1: dx_perm = dz W1[e], dW1[e] = dz^T x_perm.
+    Input encode: dx_exp[t] = sum of dx_perm over t's kept rows.
+    Gate: dlogits[t, idx_j] = w_j (dg_j - sum_i w_i dg_i), 0 elsewhere;
+    dW_gate = x^T dlogits, db = sum_t dlogits, dX = dx_exp + dlogits W_gate^T.
+    dX is stored in the activation type; weight gradients, db and dlogits
+    in float32.
+    """
+    dy = np.asarray(dy, F64)
+    T, d = dy.shape
+    idx, w = fwd["idx"], np.asarray(fwd["w"], F64)
+    k = idx.shape[1]
+    E, F, _ = w1.shape
+    slot_row = fwd["slot_row"].reshape(T, k)
+    offsets = fwd["offsets"]
+    h, o, x_perm = fwd["h"], fwd["o"], np.asarray(fwd["x_perm"], F64)
+    R = h.shape[0]
+
+    # output decode backward
+    d_o = np.zeros((R, d), dtype=F64)
+    dg = np.zeros((T, k), dtype=F64)
+    for j in range(k):
+        r = slot_row[:, j]
+        kept = r >= 0
+        d_o[r[kept]] = w[kept, j][:, None] * dy[kept]
+        dg[kept, j] = np.einsum("td,td->t", dy[kept], o[r[kept]])
+
+    # expert backward
+    dw1 = np.zeros((E, F, d), dtype=F64)
+    dw2 = np.zeros((E, d, F), dtype=F64)
+    dx_perm = np.zeros((R, d), dtype=F64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        dO = d_o[a:b]
+        he = h[a:b]
+        dh = dO @ np.asarray(w2[e], F64)
+        dz = dh * (he > 0.0)
+        dw2[e] = dO.T @ he
+        dx_perm[a:b] = dz @ np.asarray(w1[e], F64)
+        dw1[e] = dz.T @ x_perm[a:b]
+
+    # input encode backward (sum over the token's kept rows, in j order)
+    dx_exp = np.zeros((T, d), dtype=F64)
+    for j in range(k):
+        r = slot_row[:, j]
+        kept = r >= 0
+        dx_exp[kept] += dx_perm[r[kept]]
+
+    # gate backward
+    s = (w * dg).sum(axis=1, keepdims=True)
+    dsel = w * (dg - s)
+    dlogits = np.zeros((T, E), dtype=F64)
+    rows = np.arange(T)
+    for j in range(k):
+        dlogits[rows, idx[:, j]] += dsel[:, j]
+    dw_gate = np.asarray(x, F64).T @ dlogits
+    db = dlogits.sum(axis=0)
+    dx = dx_exp + dlogits @ np.asarray(w_gate, F64).T
+    return {"dx": round_act(dx, act), "dw1": dw1.astype(F32), "dw2": dw2.astype(F32),
+            "dw_gate": dw_gate.astype(F32), "db_gate": db.astype(F32),
+            "dlogits": dlogits.astype(F32), "dg": dg, "d_o": d_o, "dx_exp": dx_exp,
+            "dw1_f64": dw1, "dw2_f64": dw2, "dx_f64": dx}
+
+
+# --------------------------------------------------------------------------
+# per-token forms used to check single outputs of large problems
+# --------------------------------------------------------------------------
+def expert_row(xrow: np.ndarray, w1e: np.ndarray, w2e: np.ndarray, act: str):
+    """One token through one expert: (h, O) rounded as stored."""
+    z = np.asarray(w1e, F64) @ np.asarray(xrow, F64)
+    h = round_act(np.maximum(z, 0.0), act)
+    return h, round_act(np.asarray(w2e, F64) @ h, act)
+
+
+def token_output(t: int, x, w, idx, slot_row, w1, w2, act: str) -> np.ndarray:
+    """y[t] computed directly from token t's choices, without the packed
+    buffers (dense per-token evaluation)."""
+    k = idx.shape[1]
+    acc = np.zeros(x.shape[1], dtype=F64)
+    for j in range(k):
+        if slot_row[t * k + j] < 0:
+            continue
+        e = int(idx[t, j])
+        _, o = expert_row(x[t], w1[e], w2[e], act)
+        acc += float(w[t, j]) * o
+    return round_act(acc, act)

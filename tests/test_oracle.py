@@ -1,0 +1,429 @@
+"""Pins for the CPU reference (runs without a GPU).
+
+Each test ties a part of ``oracle.moe_oracle`` to something other than
+itself: a hand-worked example, a library routine, a closed form, an
+invariant, brute force on tiny inputs, torch autograd or finite differences.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import moe_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def rand(shape, seed, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
+
+
+# ---------------------------------------------------------------- routing
+def test_hand_worked_routing():
+    g = load("hand_routing.json")
+    L = np.array(g["logits"], dtype=np.float32)
+    L[3, 1] = -0.0
+    idx, w = orc.topk_gate(L, g["k"])
+    assert idx.tolist() == g["idx"]
+    e = math.e
+    want = [[e / (1 + e), 1 / (1 + e)], [0.5, 0.5], [0.5, 0.5],
+            [e ** 4 / (1 + e ** 4), 1 / (1 + e ** 4)]]
+    np.testing.assert_allclose(w, np.array(want), rtol=1e-7)
+    assert idx.reshape(-1).tolist() == g["expert_of_slot"]
+    for case in ("capacity_case", "dropless_case"):
+        c = g[case]
+        C = orc.capacity(g["T"], g["k"], g["E"], c["capacity_factor"])
+        assert C == c["C"]
+        s = orc.assign_slots(idx, g["E"], C)
+        for key in ("counts_raw", "counts_kept", "offsets", "slot_row", "row_token"):
+            assert s[key].tolist() == c[key], (case, key)
+        assert s["drops"] == c["drops"]
+
+
+def test_hand_worked_popularity():
+    p = load("hand_routing.json")["popularity_case"]
+    W = p["window"]
+    ring = np.zeros((W, 3), np.int32)
+    for it, (cnt, want) in enumerate(zip(p["counts_per_iteration"], p["window_sum_per_iteration"])):
+        ring, ws = orc.popularity_update(ring, it, np.array(cnt))
+        assert ws.tolist() == want
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_lexsort_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    T, E = 64, 7
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    if seed % 2:  # many exact ties
+        L = workloads.quantize_half_steps(L)
+    if seed == 5:  # signed zeros must tie
+        L[:, :3] = np.array([0.0, -0.0, 0.0], np.float32)
+        L[:, 3:] = -1.0
+    for k in (1, 2, 3, E):
+        idx, w = orc.topk_gate(L, k)
+        for t in range(T):
+            # lexsort: last key is primary -> primary -L, secondary index
+            order = np.lexsort((np.arange(E), -L[t].astype(np.float64) + 0.0))
+            assert idx[t].tolist() == order[:k].tolist()
+        assert np.all(np.diff(w, axis=1) <= 0)
+        np.testing.assert_allclose(w.astype(np.float64).sum(1), 1.0, atol=4 * 2 ** -23)
+
+
+def test_topk_all_equal_and_full_softmax():
+    T, E = 5, 6
+    L = np.full((T, E), 0.25, np.float32)
+    idx, w = orc.topk_gate(L, 3)
+    assert (idx == np.arange(3)).all()
+    np.testing.assert_array_equal(w, np.float32(1 / 3))
+    L = rand((T, E), 3)
+    idx, w = orc.topk_gate(L, E)
+    full = torch.softmax(torch.from_numpy(L.astype(np.float64)), dim=1).numpy()
+    np.testing.assert_allclose(w, np.take_along_axis(full, idx, 1), rtol=1e-6)
+
+
+def test_topk_rejects_nonfinite():
+    L = np.zeros((2, 3), np.float32)
+    L[1, 2] = np.nan
+    with pytest.raises(ValueError):
+        orc.topk_gate(L, 2)
+
+
+def test_router_logits_special_cases():
+    T, d, E = 9, 12, 5
+    x = rand((T, d), 1)
+    b = rand((E,), 2)
+    eye = np.zeros((d, E), np.float32)
+    eye[np.arange(E), np.arange(E)] = 1.0
+    np.testing.assert_array_equal(orc.router_logits(x, eye, b), x[:, :E] + b)
+    # against torch's float64 linear layer
+    wg = rand((d, E), 3)
+    lin = torch.nn.Linear(d, E, dtype=torch.float64)
+    with torch.no_grad():
+        lin.weight.copy_(torch.from_numpy(wg.T.astype(np.float64)))
+        lin.bias.copy_(torch.from_numpy(b.astype(np.float64)))
+        ref = lin(torch.from_numpy(x.astype(np.float64))).float().numpy()
+    np.testing.assert_array_equal(orc.router_logits(x, wg, b), ref)
+
+
+# ---------------------------------------------------------------- capacity / permutation
+def test_capacity_values():
+    assert orc.capacity(4096, 2, 16, 1.25) == 640
+    assert orc.capacity(4096, 2, 16, 1.0) == 512
+    assert orc.capacity(4096, 2, 16, 0.0) == 4096
+    assert orc.capacity(10, 1, 100, 0.01) == 1          # clamp below
+    assert orc.capacity(10, 4, 2, 5.0) == 10            # clamp above
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_assign_slots_dropless_is_stable_sort(seed):
+    rng = np.random.default_rng(seed)
+    T, E, k = 300, 9, 3
+    L = rng.standard_normal((T, E)).astype(np.float32) + np.log(np.arange(1, E + 1))[::-1].astype(np.float32)
+    idx, _ = orc.topk_gate(L, k)
+    s = orc.assign_slots(idx, E, orc.capacity(T, k, E, 0.0))
+    flat = idx.reshape(-1)
+    assert s["counts_raw"].tolist() == np.bincount(flat, minlength=E).tolist()
+    assert s["offsets"].tolist() == [0] + np.cumsum(s["counts_kept"]).tolist()
+    order = np.argsort(flat, kind="stable")          # library stable sort
+    assert s["row_token"].tolist() == (order // k).tolist()
+    assert sorted(s["slot_row"].tolist()) == list(range(T * k))  # bijection
+    assert (s["slot_row"][order] == np.arange(T * k)).all()
+
+
+@pytest.mark.parametrize("cf", [0.5, 0.8, 1.0])
+def test_assign_slots_capacity_bruteforce(cf):
+    rng = np.random.default_rng(7)
+    T, E, k = 40, 5, 2
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[:, 0] += 1.5  # make expert 0 overflow
+    idx, _ = orc.topk_gate(L, k)
+    C = orc.capacity(T, k, E, cf)
+    s = orc.assign_slots(idx, E, C)
+    flat = idx.reshape(-1)
+    S = T * k
+    kept_rows = []
+    for sl in range(S):
+        e = flat[sl]
+        pos = sum(1 for p in range(sl) if flat[p] == e)   # O(S^2) brute force
+        if pos < C:
+            row = sum(min(C, int((flat == ee).sum())) for ee in range(e)) + pos
+            assert s["slot_row"][sl] == row
+            assert s["row_token"][row] == sl // k
+            kept_rows.append(row)
+        else:
+            assert s["slot_row"][sl] == -1
+    assert sorted(kept_rows) == list(range(len(kept_rows)))
+    assert s["drops"] == S - len(kept_rows) == S - int(s["counts_kept"].sum())
+    assert (s["counts_kept"] <= C).all()
+    assert s["drops"] > 0
+
+
+# ---------------------------------------------------------------- experts
+def test_expert_ffn_is_torch_mlp_for_one_expert():
+    T, d, F = 17, 8, 24
+    x = rand((T, d), 4)
+    w1 = rand((1, F, d), 5, 0.3)
+    w2 = rand((1, d, F), 6, 0.3)
+    mlp = torch.nn.Sequential(torch.nn.Linear(d, F, bias=False, dtype=torch.float64),
+                              torch.nn.ReLU(),
+                              torch.nn.Linear(F, d, bias=False, dtype=torch.float64))
+    with torch.no_grad():
+        mlp[0].weight.copy_(torch.from_numpy(w1[0].astype(np.float64)))
+        mlp[2].weight.copy_(torch.from_numpy(w2[0].astype(np.float64)))
+        ref = mlp(torch.from_numpy(x.astype(np.float64))).numpy()
+    out = orc.forward(x, np.zeros((d, 1), np.float32), np.zeros(1, np.float32), w1, w2,
+                      k=1, capacity_factor=0.0, act="f64")
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+    assert out["idx"].tolist() == [[0]] * T
+    np.testing.assert_array_equal(out["w"], 1.0)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_identity_experts_give_weighted_input(act):
+    T, d, E, k = 50, 16, 4, 2
+    x = workloads.round_to_bf16(rand((T, d), 8)) if act == "bf16" else rand((T, d), 8)
+    w1, w2 = workloads.identity_experts(d, E)
+    out = orc.forward(x, rand((d, E), 9), rand((E,), 10), w1, w2, k, 0.0, act)
+    np.testing.assert_array_equal(out["o"], out["x_perm"].astype(np.float64))
+    wsum = out["w"].astype(np.float64).sum(1, keepdims=True)
+    ref = orc.round_act(wsum * x.astype(np.float64), act)
+    np.testing.assert_array_equal(out["y"], ref)
+    np.testing.assert_allclose(out["y"], x, rtol=2 ** -7 if act == "bf16" else 1e-6)
+
+
+def test_all_dropped_token_outputs_zero():
+    T, d, E, k = 8, 4, 2, 1
+    x = rand((T, d), 11)
+    b = np.array([5.0, -5.0], np.float32)   # everyone picks expert 0
+    w1, w2 = workloads.identity_experts(d, E)
+    out = orc.forward(x, np.zeros((d, E), np.float32), b, w1, w2, k, 0.5, "f32")
+    C = out["C"]
+    assert C == 2
+    assert (out["slot_row"][:C] >= 0).all() and (out["slot_row"][C:] == -1).all()
+    np.testing.assert_array_equal(out["y"][C:], 0.0)
+    np.testing.assert_allclose(out["y"][:C], x[:C], rtol=1e-7)
+
+
+@pytest.mark.parametrize("cf", [0.0, 0.6])
+def test_forward_equals_dense_per_token(cf):
+    T, d, F, E, k = 64, 12, 20, 6, 3
+    x = rand((T, d), 12)
+    wg = rand((d, E), 13)
+    b = rand((E,), 14)
+    w1 = rand((E, F, d), 15, 0.4)
+    w2 = rand((E, d, F), 16, 0.4)
+    out = orc.forward(x, wg, b, w1, w2, k, cf, "f64")
+    if cf:
+        assert out["drops"] > 0
+    for t in range(T):
+        ref = orc.token_output(t, x, out["w"], out["idx"], out["slot_row"], w1, w2, "f64")
+        np.testing.assert_allclose(out["y"][t], ref, rtol=1e-12, atol=1e-13)
+    # and against a torch dense evaluation that never permutes
+    xt = torch.from_numpy(x.astype(np.float64))
+    logits = torch.from_numpy(out["logits"].astype(np.float64))
+    top = torch.topk(logits, k, dim=1)
+    assert (top.indices.numpy() == out["idx"]).all()
+    wt = torch.softmax(top.values, dim=1)
+    y = torch.zeros_like(xt)
+    for t in range(T):
+        for j in range(k):
+            if out["slot_row"][t * k + j] < 0:
+                continue
+            e = int(top.indices[t, j])
+            hh = torch.relu(torch.nn.functional.linear(xt[t], torch.from_numpy(w1[e].astype(np.float64))))
+            y[t] += wt[t, j] * torch.nn.functional.linear(hh, torch.from_numpy(w2[e].astype(np.float64)))
+    # the oracle's weights are stored in float32, torch's stay float64
+    ref = y.numpy()
+    np.testing.assert_allclose(out["y"], ref, rtol=0, atol=2e-7 * np.abs(ref).max())
+
+
+def test_bf16_rounding_ties_to_even():
+    vals = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -(1.0 + 2 ** -8)], np.float64)
+    np.testing.assert_array_equal(orc.round_act(vals, "bf16"),
+                                  [1.0, 1.0 + 2 ** -6, 1.0, -1.0])
+    t = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(orc.round_act(vals, "bf16"), t)
+
+
+# ---------------------------------------------------------------- popularity
+def test_popularity_against_history():
+    rng = np.random.default_rng(3)
+    E, W = 7, 4
+    ring = np.zeros((W, E), np.int32)
+    hist = []
+    for it in range(11):
+        c = rng.integers(0, 1000, E)
+        hist.append(c)
+        ring, ws = orc.popularity_update(ring, it, c)
+        assert ws.tolist() == np.sum(hist[-W:], axis=0).tolist()
+
+
+# ---------------------------------------------------------------- backward
+def _dense_torch_loss(x, wg, b, w1, w2, k, slot_row, dy):
+    """Dense per-token forward in torch float64 with autograd; routing
+    structure (which experts, which slots survive) held fixed."""
+    T, d = x.shape
+    logits = x @ wg + b
+    top = torch.topk(logits.detach(), k, dim=1).indices
+    sel = torch.gather(logits, 1, top)
+    wt = torch.softmax(sel, dim=1)
+    y = []
+    for t in range(T):
+        acc = torch.zeros(d, dtype=torch.float64)
+        for j in range(k):
+            if slot_row[t * k + j] < 0:
+                continue
+            e = int(top[t, j])
+            hh = torch.relu(w1[e] @ x[t])
+            acc = acc + wt[t, j] * (w2[e] @ hh)
+        y.append(acc)
+    return (torch.stack(y) * dy).sum()
+
+
+@pytest.mark.parametrize("cf", [0.0, 0.5])
+def test_backward_matches_torch_autograd(cf):
+    T, d, F, E, k = 24, 8, 16, 4, 2
+    x = rand((T, d), 20)
+    wg = rand((d, E), 21)
+    b = rand((E,), 22)
+    w1 = rand((E, F, d), 23, 0.5)
+    w2 = rand((E, d, F), 24, 0.5)
+    dy = rand((T, d), 25)
+    fwd = orc.forward(x, wg, b, w1, w2, k, cf, "f64")
+    if cf:
+        assert fwd["drops"] > 0
+    g = orc.backward(dy, fwd, x, wg, w1, w2, "f64")
+    tx, twg, tb, tw1, tw2 = (torch.tensor(a.astype(np.float64), requires_grad=True)
+                            for a in (x, wg, b, w1, w2))
+    loss = _dense_torch_loss(tx, twg, tb, tw1, tw2, k, fwd["slot_row"],
+                             torch.from_numpy(dy.astype(np.float64)))
+    loss.backward()
+    # the oracle stores logits and gate weights in float32, torch keeps
+    # float64 throughout, so agreement is to float32 level, scaled by the
+    # tensor's largest entry (a missing term or a wrong sign is O(1))
+    for mine, ref in ((g["dx_f64"], tx.grad), (g["dw1_f64"], tw1.grad), (g["dw2_f64"], tw2.grad),
+                      (g["dw_gate"], twg.grad), (g["db_gate"], tb.grad)):
+        ref = ref.numpy()
+        np.testing.assert_allclose(mine, ref, rtol=0, atol=2e-6 * np.abs(ref).max())
+
+
+def _loss_f64(x, wg, b, w1, w2, k, cf, dy):
+    out = orc.forward(x, wg, b, w1, w2, k, cf, "f64",
+                      logits=None)
+    return float((out["y"] * dy).sum()), out
+
+
+@pytest.mark.parametrize("cf", [0.0, 0.5])
+def test_backward_finite_differences(cf):
+    """Central differences (step 1e-6) of sum(y * dy), in float64 end to end.
+    The router logits are computed in float64 here (no float32 rounding) so
+    the derivative is smooth; perturbations that change routing or cross a
+    ReLU kink are skipped."""
+    T, d, F, E, k = 8, 8, 16, 4, 2
+    x = rand((T, d), 30).astype(np.float64)
+    wg = rand((d, E), 31).astype(np.float64)
+    b = rand((E,), 32).astype(np.float64)
+    w1 = rand((E, F, d), 33, 0.5).astype(np.float64)
+    w2 = rand((E, d, F), 34, 0.5).astype(np.float64)
+    dy = rand((T, d), 35).astype(np.float64)
+
+    def run(x, wg, b, w1, w2):
+        logits = x @ wg + b  # float64 logits
+        T_, E_ = logits.shape
+        idx = np.argsort(-logits, axis=1, kind="stable")[:, :k].astype(np.int32)
+        sel = np.take_along_axis(logits, idx, 1)
+        p = np.exp(sel - sel[:, :1])
+        w = p / p.sum(1, keepdims=True)
+        C = orc.capacity(T_, k, E_, cf)
+        s = orc.assign_slots(idx, E_, C)
+        xp = orc.encode(x, s["row_token"])
+        h, o = orc.expert_ffn(xp, s["offsets"], w1, w2, "f64")
+        y = orc.decode(o, w, s["slot_row"], "f64")
+        fwd = {"idx": idx, "w": w, "h": h, "o": o, "x_perm": xp}
+        fwd.update(s)
+        z_margin = np.inf
+        for e in range(E_):
+            a, bb = s["offsets"][e], s["offsets"][e + 1]
+            if bb > a:
+                z_margin = min(z_margin, np.abs(xp[a:bb] @ w1[e].T).min())
+        return float((y * dy).sum()), fwd, idx, z_margin
+
+    base, fwd, idx0, margin = run(x, wg, b, w1, w2)
+    assert margin > 1e-3
+    if cf:
+        assert fwd["drops"] > 0
+    g = orc.backward(dy, fwd, x, wg, w1, w2, "f64")
+    grads = {"x": g["dx_f64"], "wg": g["dw_gate"], "b": g["db_gate"], "w1": g["dw1_f64"], "w2": g["dw2_f64"]}
+    params = {"x": x, "wg": wg, "b": b, "w1": w1, "w2": w2}
+    rng = np.random.default_rng(0)
+    h = 1e-6
+    checked = 0
+    for name, arr in params.items():
+        flat = arr.reshape(-1)
+        for i in rng.choice(flat.size, size=min(flat.size, 40), replace=False):
+            old = flat[i]
+            flat[i] = old + h
+            lp, _, ip, mp = run(**params)
+            flat[i] = old - h
+            lm, _, im, mm = run(**params)
+            flat[i] = old
+            if not ((ip == idx0).all() and (im == idx0).all()) or min(mp, mm) < 1e-4:
+                continue
+            fd = (lp - lm) / (2 * h)
+            an = float(grads[name].reshape(-1)[i])
+            tol = 1e-6 * max(1.0, abs(fd)) if name in ("x", "w1", "w2") else 2e-6 * max(1.0, abs(fd))
+            assert abs(fd - an) <= tol, (name, i, fd, an)
+            checked += 1
+    assert checked >= 150
+
+
+@pytest.mark.parametrize("act", ["f32", "f64"])
+def test_backward_identity_experts_closed_form(act):
+    """Identity experts, dropless: y = (sum_j w_j) x = x, so dX = dy and the
+    gate gets no gradient (sum of weights is constant)."""
+    T, d, E, k = 32, 8, 4, 2
+    x = rand((T, d), 40)
+    w1, w2 = workloads.identity_experts(d, E)
+    wg, b = rand((d, E), 41), rand((E,), 42)
+    dy = rand((T, d), 43)
+    fwd = orc.forward(x, wg, b, w1, w2, k, 0.0, act)
+    g = orc.backward(dy, fwd, x, wg, w1, w2, act)
+    np.testing.assert_allclose(g["dx"], dy, rtol=1e-6, atol=1e-7)
+    assert np.abs(g["dlogits"]).max() < 1e-6
+    assert np.abs(g["dw_gate"]).max() < 1e-5 and np.abs(g["db_gate"]).max() < 1e-5
+
+
+# ---------------------------------------------------------------- page sizes
+def test_page_expert_sizes():
+    g = load("popfetcher_sizes.json")
+    H, a = g["H"], g["alpha"]
+    w = workloads.Workload("p", T=1, d=H, F=a * H, E=1, k=1, capacity_factor=0.0,
+                           dtype="f32", x_std=1.0, zipf_s=None)
+    n = w.E * w.F * w.d * 2
+    assert n == g["expert_params"] and 4 * n == g["expert_bytes_fp32"]
+    assert n // (2 * H) == g["push_pull_crossover_tokens"]
+    assert 4 * w.d * w.F == g["fwd_ops_per_token"]
+
+
+# ---------------------------------------------------------------- workloads
+def test_workload_recipes():
+    ws = workloads.workloads()
+    assert [w.name for w in ws.values()] == ["tiny_fp32", "uniform_cf125", "skewed_zipf12",
+                                            "mixtral_shaped", "fine_grained"]
+    w = ws["fine_grained"]
+    o0, o1 = workloads.expert_order(w, 0), workloads.expert_order(w, 1)
+    assert sorted(o0) == list(range(w.E)) and sorted(o1) == list(range(w.E))
+    assert 0 < (o0 != o1).sum() <= 2 * w.drift_swaps
+    b = workloads.gate_bias(w, 0)
+    assert b.max() == 0.0 and np.isclose(b.min(), -np.log(w.E))
+    x = workloads.make_x(workloads.scaled(ws["skewed_zipf12"], T=8))
+    assert (workloads.round_to_bf16(x) == x).all()
