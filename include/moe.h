@@ -1,0 +1,194 @@
+/*
+ * moe.h - C ABI of libmoe, one GPU's mixture-of-experts layer on MI355X (gfx950).
+ *
+ * The layer follows the expert-parallel pipeline the survey "A Survey on
+ * Mixture of Experts" lays out in §5 (System Design), first paragraph:
+ * gate routing -> input encode -> expert computation -> output decode, here
+ * on one GPU (no All-to-All: the packed per-expert buffers are exactly what
+ * a dispatch would send).  Experts are FC -> ReLU -> FC with two weight
+ * matrices and no biases (PopFetcher notes, §2.1.1 and §5.1); the gate is a
+ * linear router with top-k selection (PopFetcher notes, §2.1.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers: every tensor argument is a DEVICE pointer to memory the caller
+ *   owns.  The library never allocates or frees device memory; scratch space
+ *   is a caller-provided workspace of moe_workspace_bytes(shape, op) bytes
+ *   (256-byte aligned).  The shape struct is a HOST pointer.
+ * - Layout: row-major and contiguous; tensors start 16-byte aligned.
+ *     x, y, dy, dx      [T, d]        activation type
+ *     w_gate            [d, E]        float32, b_gate [E] float32
+ *     logits            [T, E]        float32
+ *     topk_idx          [T, k]        int32, topk_w [T, k] float32
+ *     w1                [E, F, d]     activation type (output x input)
+ *     w2                [E, d, F]     activation type (output x input)
+ *     x_perm, out_perm  [T*k, d]      activation type (first S_kept rows used)
+ *     h                 [T*k, F]      activation type
+ *     slot_row          [T*k]         int32; slot s = t*k + j; -1 = dropped
+ *     row_token         [T*k]         int32; first S_kept entries valid
+ *     counts_*          [E] int32;  offsets [E+1] int32 (offsets[E] = S_kept)
+ *     dw1, dw2          same shapes as w1, w2, float32
+ *     dw_gate [d, E], db_gate [E], dlogits [T, E]: float32
+ *   Activation type: MOE_F32 (everything float32) or MOE_BF16 (bf16 storage,
+ *   float32 accumulation, round-to-nearest-even stores).
+ * - Asynchrony: every call only enqueues work on `stream` (a hipStream_t;
+ *   NULL = the default stream) and returns; it never synchronises and never
+ *   reads device data on the host.  Device faults show at the caller's next
+ *   synchronisation.
+ * - Errors: argument checks happen on the host before anything is enqueued;
+ *   a failing call enqueues nothing and returns a negative moe_status.
+ *   MOE_ERR_HIP means a launch was rejected after earlier launches of the
+ *   same call may already be enqueued.
+ * - Determinism: results are bitwise identical run to run (no float atomics;
+ *   integer results never depend on thread order).
+ * - Thread safety: the library keeps no state; concurrent calls need
+ *   distinct outputs and workspaces.
+ * - Routing semantics (the pages leave these open; this is the reading
+ *   taken): selection on the float32 logits, ties to the lowest expert index
+ *   (+0.0 == -0.0); gate weights are a softmax over the k selected logits;
+ *   capacity C = ceil(cf*T*k/E) clamped to [1, T], or T when cf <= 0
+ *   (dropless); slots claim capacity in slot order t*k + j; kept weights are
+ *   not renormalised after drops; a token with every slot dropped outputs 0.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null required pointer, bad size, k > E ... */
+#define MOE_ERR_UNSUPPORTED (-2) /* dtype or shape outside the compiled kernels */
+#define MOE_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
+#define MOE_ERR_HIP (-4)         /* a HIP launch failed */
+
+#define MOE_F32 0
+#define MOE_BF16 1
+
+/* Limits of the compiled kernels (MOE_ERR_UNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 8
+
+typedef struct moe_shape {
+  int32_t T;               /* tokens */
+  int32_t d_model;         /* d: multiple of 64 */
+  int32_t d_ff;            /* F: multiple of 64 */
+  int32_t E;               /* experts, 1..MOE_MAX_EXPERTS */
+  int32_t k;               /* experts per token, 1..min(E, MOE_MAX_TOPK) */
+  float capacity_factor;   /* <= 0: dropless */
+  int32_t act_dtype;       /* MOE_F32 or MOE_BF16 */
+} moe_shape;
+
+/* Operations, for moe_workspace_bytes. */
+#define MOE_OP_ROUTE 0
+#define MOE_OP_PERMUTE 1
+#define MOE_OP_EXPERT_FFN 2
+#define MOE_OP_COMBINE 3
+#define MOE_OP_FORWARD 4
+#define MOE_OP_BACKWARD 5
+
+/* Workspace bytes `op` needs for `shape` (0 if none).  Returns 0 and sets
+ * nothing on an invalid shape; validate with moe_check_shape first. */
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t op);
+
+/* MOE_OK if the shape is valid and supported, else the error code. */
+moe_status moe_check_shape(const moe_shape* shape);
+
+/* Expert capacity C (see the routing semantics above); -1 on a bad shape. */
+int32_t moe_capacity(const moe_shape* shape);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status status);
+
+/* Gate routing (A Survey on Mixture of Experts, §5 System Design, first
+ * paragraph: gate routing; PopFetcher notes §2.1.2: top-k selection).
+ * logits[t,e] = b_gate[e] + sum_i x[t,i] * w_gate[i,e] in float32, unless
+ * logits_in is given (then x/w_gate/b_gate may be NULL and those logits are
+ * used as they are).  Writes logits_out if non-NULL, the top-k experts in
+ * descending logit order, their renormalised weights, and counts_raw[e] =
+ * number of slots routed to e (before capacity).  Workspace: MOE_OP_ROUTE. */
+moe_status moe_route(const moe_shape* shape, const void* x, const float* w_gate,
+                     const float* b_gate, const float* logits_in, float* logits_out,
+                     int32_t* topk_idx, float* topk_w, int32_t* counts_raw,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Input encode (survey §5, first paragraph: gathering each expert's tokens
+ * into contiguous memory; capacity limit as in GShard, cited there).  From
+ * topk_idx: counts_kept[e] = min(raw count, C); offsets = exclusive prefix
+ * sum of counts_kept; slot_row[s] = offsets[e] + position of slot s among
+ * e's slots in slot order, or -1 if that position is >= C; row_token[r] =
+ * token of packed row r; x_perm[r] = x[row_token[r]] (exact copy).
+ * counts_raw may be NULL.  Workspace: MOE_OP_PERMUTE. */
+moe_status moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                       int32_t* counts_raw, int32_t* counts_kept, int32_t* offsets,
+                       int32_t* slot_row, int32_t* row_token, void* x_perm,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Expert computation (PopFetcher notes §2.1.1 FC-ReLU-FC and §5.1 weight
+ * shapes; survey §5 "expert computation" on the packed buffers).  For each
+ * expert e over packed rows offsets[e]..offsets[e+1]:
+ *   h = ReLU(x_perm_e * w1[e]^T), out_perm = h * w2[e]^T
+ * with float32 accumulation; h and out_perm stored in the activation type
+ * (h is kept for the backward).  Rows past offsets[E] are not touched.
+ * Workspace: MOE_OP_EXPERT_FFN (0 bytes; argument may be NULL). */
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int32_t* offsets,
+                          const void* w1, const void* w2, void* h, void* out_perm,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Output decode (survey §5, first paragraph: the inverse of input encode,
+ * restoring token order from the gating indices).  y[t] = sum over kept
+ * slots j, in order j = 0..k-1, of topk_w[t,j] * out_perm[slot_row[t*k+j]],
+ * accumulated in float32 and rounded once; 0 if all of t's slots dropped. */
+moe_status moe_combine(const moe_shape* shape, const void* out_perm, const float* topk_w,
+                       const int32_t* slot_row, void* y, void* stream);
+
+/* The whole forward: moe_route, moe_permute, moe_expert_ffn, moe_combine on
+ * one stream.  logits_out and counts_raw may be NULL.  Every other output
+ * is kept for moe_backward.  Workspace: MOE_OP_FORWARD. */
+moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gate,
+                       const float* b_gate, const void* w1, const void* w2, void* y,
+                       float* logits_out, int32_t* topk_idx, float* topk_w,
+                       int32_t* counts_raw, int32_t* counts_kept, int32_t* offsets,
+                       int32_t* slot_row, int32_t* row_token, void* x_perm, void* h,
+                       void* out_perm, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Backward of moe_forward for output gradient dy (PopFetcher notes §5.2.1:
+ * one GEMM pass forward, two backward - gradients of the inputs and of the
+ * expert parameters).  Reads the saved forward tensors and writes
+ *   dx [T,d]     full input gradient, expert path plus router path
+ *   dw1, dw2     float32; experts with no rows get zeros
+ *   dw_gate, db_gate  float32 gate gradients
+ *   dlogits      float32 [T,E] if non-NULL
+ * Gate: w = softmax of the selected logits, so dlogits[t, idx_j] =
+ * w_j (dg_j - sum_i w_i dg_i) with dg_j = <dy[t], out_perm[row_j]> (0 for a
+ * dropped slot); other logits get 0.  ReLU'(0) = 0, mask read from h.
+ * Workspace: MOE_OP_BACKWARD. */
+moe_status moe_backward(const moe_shape* shape, const void* dy, const void* x,
+                        const float* w_gate, const void* w1, const void* w2,
+                        const int32_t* topk_idx, const float* topk_w,
+                        const int32_t* slot_row, const int32_t* row_token,
+                        const int32_t* offsets, const void* x_perm, const void* h,
+                        const void* out_perm, void* dx, float* dw1, float* dw2,
+                        float* dw_gate, float* db_gate, float* dlogits,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-expert popularity over a sliding window of iterations (PopFetcher
+ * notes §3.1, routing-information collector; §4.2, Eq. 1: token
+ * distribution over the last s iterations).  Writes counts_raw into row
+ * iter % window of ring [window, E], then window_sum[e] = sum of the rows of
+ * the last min(iter + 1, window) iterations.  Rows of iterations not yet
+ * recorded are never read.  Integers, exact.  iter >= 0, 1 <= window <= 64. */
+moe_status moe_popularity_update(int32_t E, int32_t window, int64_t iter,
+                                 const int32_t* counts_raw, int32_t* ring,
+                                 int32_t* window_sum, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,197 @@
+"""Python binding of libmoe, one GPU's mixture-of-experts layer on MI355X.
+
+Argument marshalling only: every function here passes device pointers from
+torch tensors (and the current HIP stream) to the C entry point of the same
+name in ``include/moe.h`` and raises ``MoeError`` on a non-zero status.  All
+computation happens in the HIP kernels of ``libmoe.so``; if that library has
+not been built, importing works but the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "MOE_F32", "MOE_BF16", "MoeError", "MoeShape", "lib", "library_path",
+    "moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
+    "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+    "moe_backward", "moe_popularity_update", "OP",
+]
+
+MOE_F32 = 0
+MOE_BF16 = 1
+OP = {"route": 0, "permute": 1, "expert_ffn": 2, "combine": 3, "forward": 4, "backward": 5}
+EXPORTS = ["moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
+           "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+           "moe_backward", "moe_popularity_update"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.environ.get("MOE_LIBRARY", os.path.join(_HERE, "libmoe.so"))
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({_status_text(status)})")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_float), ("act_dtype", ctypes.c_int32)]
+
+    @classmethod
+    def make(cls, T, d, F, E, k, capacity_factor=0.0, act=MOE_BF16):
+        return cls(T, d, F, E, k, capacity_factor, act)
+
+
+_lib: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so (loaded on first use; raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise OSError(f"libmoe.so not built at {path}; run "
+                          "python -m mixture_experts_layer_33_amd.build")
+        L = ctypes.CDLL(path)
+        sp = ctypes.POINTER(MoeShape)
+        L.moe_workspace_bytes.argtypes = [sp, ctypes.c_int32]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_check_shape.argtypes = [sp]
+        L.moe_check_shape.restype = ctypes.c_int32
+        L.moe_capacity.argtypes = [sp]
+        L.moe_capacity.restype = ctypes.c_int32
+        L.moe_status_string.argtypes = [ctypes.c_int32]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_route.argtypes = [sp] + [_P] * 8 + [_P, ctypes.c_size_t, _P]
+        L.moe_permute.argtypes = [sp] + [_P] * 8 + [_P, ctypes.c_size_t, _P]
+        L.moe_expert_ffn.argtypes = [sp] + [_P] * 6 + [_P, ctypes.c_size_t, _P]
+        L.moe_combine.argtypes = [sp] + [_P] * 4 + [_P]
+        L.moe_forward.argtypes = [sp] + [_P] * 17 + [_P, ctypes.c_size_t, _P]
+        L.moe_backward.argtypes = [sp] + [_P] * 19 + [_P, ctypes.c_size_t, _P]
+        L.moe_popularity_update.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                            _P, _P, _P, _P]
+        for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+                     "moe_backward", "moe_popularity_update"):
+            getattr(L, name).restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return lib().moe_status_string(status).decode()
+    except OSError:
+        return "?"
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (None stays NULL); non-contiguous tensors
+    are refused rather than copied."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MoeError(status, what)
+
+
+def moe_workspace_bytes(shape: MoeShape, op) -> int:
+    op = OP[op] if isinstance(op, str) else op
+    return int(lib().moe_workspace_bytes(ctypes.byref(shape), op))
+
+
+def moe_check_shape(shape: MoeShape) -> int:
+    return int(lib().moe_check_shape(ctypes.byref(shape)))
+
+
+def moe_capacity(shape: MoeShape) -> int:
+    return int(lib().moe_capacity(ctypes.byref(shape)))
+
+
+def moe_status_string(status: int) -> str:
+    return _status_text(status)
+
+
+def moe_route(shape, x, w_gate, b_gate, logits_in, logits_out, topk_idx, topk_w, counts_raw,
+              workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check(lib().moe_route(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(b_gate),
+                           _ptr(logits_in), _ptr(logits_out), _ptr(topk_idx), _ptr(topk_w),
+                           _ptr(counts_raw), ws, nb, _stream(stream)), "moe_route")
+
+
+def moe_permute(shape, x, topk_idx, counts_raw, counts_kept, offsets, slot_row, row_token,
+                x_perm, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check(lib().moe_permute(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(counts_raw),
+                             _ptr(counts_kept), _ptr(offsets), _ptr(slot_row), _ptr(row_token),
+                             _ptr(x_perm), ws, nb, _stream(stream)), "moe_permute")
+
+
+def moe_expert_ffn(shape, x_perm, offsets, w1, w2, h, out_perm, workspace=None, stream=None):
+    ws, nb = _ws(workspace)
+    _check(lib().moe_expert_ffn(ctypes.byref(shape), _ptr(x_perm), _ptr(offsets), _ptr(w1),
+                                _ptr(w2), _ptr(h), _ptr(out_perm), ws, nb, _stream(stream)),
+           "moe_expert_ffn")
+
+
+def moe_combine(shape, out_perm, topk_w, slot_row, y, stream=None):
+    _check(lib().moe_combine(ctypes.byref(shape), _ptr(out_perm), _ptr(topk_w), _ptr(slot_row),
+                             _ptr(y), _stream(stream)), "moe_combine")
+
+
+def moe_forward(shape, x, w_gate, b_gate, w1, w2, y, logits_out, topk_idx, topk_w, counts_raw,
+                counts_kept, offsets, slot_row, row_token, x_perm, h, out_perm, workspace,
+                stream=None):
+    ws, nb = _ws(workspace)
+    _check(lib().moe_forward(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(b_gate), _ptr(w1),
+                             _ptr(w2), _ptr(y), _ptr(logits_out), _ptr(topk_idx), _ptr(topk_w),
+                             _ptr(counts_raw), _ptr(counts_kept), _ptr(offsets), _ptr(slot_row),
+                             _ptr(row_token), _ptr(x_perm), _ptr(h), _ptr(out_perm), ws, nb,
+                             _stream(stream)), "moe_forward")
+
+
+def moe_backward(shape, dy, x, w_gate, w1, w2, topk_idx, topk_w, slot_row, row_token, offsets,
+                 x_perm, h, out_perm, dx, dw1, dw2, dw_gate, db_gate, dlogits, workspace,
+                 stream=None):
+    ws, nb = _ws(workspace)
+    _check(lib().moe_backward(ctypes.byref(shape), _ptr(dy), _ptr(x), _ptr(w_gate), _ptr(w1),
+                              _ptr(w2), _ptr(topk_idx), _ptr(topk_w), _ptr(slot_row),
+                              _ptr(row_token), _ptr(offsets), _ptr(x_perm), _ptr(h),
+                              _ptr(out_perm), _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(dw_gate),
+                              _ptr(db_gate), _ptr(dlogits), ws, nb, _stream(stream)),
+           "moe_backward")
+
+
+def moe_popularity_update(E, window, it, counts_raw, ring, window_sum, stream=None):
+    _check(lib().moe_popularity_update(E, window, it, _ptr(counts_raw), _ptr(ring),
+                                       _ptr(window_sum), _stream(stream)),
+           "moe_popularity_update")

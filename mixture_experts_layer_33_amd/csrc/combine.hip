@@ -1,0 +1,400 @@
+// Output decode, the elementwise backward steps of the layer, and the
+// popularity window, on gfx950.
+//
+// A Survey on Mixture of Experts, §5 System Design (first paragraph): output
+// decode restores the original token order from the gating indices and, with
+// top-k gating, sums the k expert outputs weighted by the gate.  The backward
+// steps here are the transposes of decode, of the gate softmax and of encode.
+// PopFetcher notes §3.1 and §4.2 (Eq. 1): per-expert token counts over a
+// sliding window of iterations.
+//
+// All row work is one wavefront per token with 16-byte accesses; sums run in
+// float32 in a fixed order (slot order j = 0..k-1), never with atomics.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kRowThreads = 256;  // 4 tokens per workgroup
+
+// 16 bytes of activations as float32 values.
+template <typename ActT>
+struct Chunk;
+template <>
+struct Chunk<bf16> {
+  static constexpr int N = 8;
+  __device__ static void load(const bf16* p, float* v) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+  }
+  __device__ static void store(bf16* p, const float* v) {
+    bf16x8 a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x8*>(p) = a;
+  }
+};
+template <>
+struct Chunk<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* v) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = a[i];
+  }
+  __device__ static void store(float* p, const float* v) {
+    f32x4 a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = v[i];
+    *reinterpret_cast<f32x4*>(p) = a;
+  }
+};
+
+// Load token t's k (row, weight) pairs into every lane.
+__device__ __forceinline__ void token_slots(int t, int k, const int32_t* slot_row,
+                                            const float* topk_w, int* rows, float* w) {
+  const int lane = threadIdx.x & 63;
+  int r = -1;
+  float wv = 0.f;
+  if (lane < k) {
+    r = slot_row[(size_t)t * k + lane];
+    wv = topk_w[(size_t)t * k + lane];
+  }
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    rows[j] = __shfl(r, j, 64);
+    w[j] = __shfl(wv, j, 64);
+  }
+}
+
+template <typename ActT>
+__global__ void __launch_bounds__(kRowThreads)
+combine_kernel(const ActT* __restrict__ out_perm, const float* __restrict__ topk_w,
+               const int32_t* __restrict__ slot_row, ActT* __restrict__ y, int T, int d, int k) {
+  using CK = Chunk<ActT>;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int rows[MOE_MAX_TOPK];
+  float w[MOE_MAX_TOPK];
+  token_slots(t, k, slot_row, topk_w, rows, w);
+  for (int c = lane * CK::N; c < d; c += 64 * CK::N) {
+    float acc[CK::N];
+#pragma unroll
+    for (int i = 0; i < CK::N; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k && rows[j] >= 0) {
+        float v[CK::N];
+        CK::load(out_perm + (size_t)rows[j] * d + c, v);
+#pragma unroll
+        for (int i = 0; i < CK::N; ++i) acc[i] = fmaf(w[j], v[i], acc[i]);
+      }
+    }
+    CK::store(y + (size_t)t * d + c, acc);
+  }
+}
+
+// Decode backward.  For each kept slot (t, j) with row r:
+//   d_out[r] = w[t,j] * dy[t]      (stored in the activation type)
+//   dg[t,j]  = <dy[t], out_perm[r]>  (0 for a dropped slot)
+// then the gate softmax backward dsel[t,j] = w_j (dg_j - sum_i w_i dg_i),
+// and dlogits[t, :] (dense, optional) holding dsel at the selected experts.
+template <typename ActT>
+__global__ void __launch_bounds__(kRowThreads)
+combine_bwd_kernel(const ActT* __restrict__ dy, const ActT* __restrict__ out_perm,
+                   const float* __restrict__ topk_w, const int32_t* __restrict__ topk_idx,
+                   const int32_t* __restrict__ slot_row, ActT* __restrict__ d_out,
+                   float* __restrict__ dsel, float* __restrict__ dlogits, int T, int d, int E,
+                   int k) {
+  using CK = Chunk<ActT>;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int rows[MOE_MAX_TOPK];
+  float w[MOE_MAX_TOPK];
+  token_slots(t, k, slot_row, topk_w, rows, w);
+  float part[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) part[j] = 0.f;
+  for (int c = lane * CK::N; c < d; c += 64 * CK::N) {
+    float g[CK::N];
+    CK::load(dy + (size_t)t * d + c, g);
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k && rows[j] >= 0) {
+        float o[CK::N], s[CK::N];
+        CK::load(out_perm + (size_t)rows[j] * d + c, o);
+#pragma unroll
+        for (int i = 0; i < CK::N; ++i) {
+          part[j] = fmaf(g[i], o[i], part[j]);
+          s[i] = w[j] * g[i];
+        }
+        CK::store(d_out + (size_t)rows[j] * d + c, s);
+      }
+    }
+  }
+  float dg[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) dg[j] = wave_sum(part[j]);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j)
+    if (j < k) s = fmaf(w[j], dg[j], s);
+  float ds[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) ds[j] = w[j] * (dg[j] - s);
+  if (lane < k) {
+    float mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j == lane) mine = ds[j];
+    dsel[(size_t)t * k + lane] = mine;
+  }
+  if (dlogits != nullptr) {
+    int idx[MOE_MAX_TOPK];
+    const int my = (lane < k) ? topk_idx[(size_t)t * k + lane] : -1;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) idx[j] = __shfl(my, j, 64);
+    for (int e = lane; e < E; e += 64) {
+      float v = 0.f;
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOPK; ++j)
+        if (j < k && idx[j] == e) v = ds[j];
+      dlogits[(size_t)t * E + e] = v;
+    }
+  }
+}
+
+// w_gate [d, E] -> w_gate_t [E, d]
+__global__ void transpose_gate_kernel(const float* __restrict__ w_gate, float* __restrict__ wt,
+                                      int d, int E) {
+  __shared__ float tile[32][33];
+  const int i0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 256 threads: 32 x 8
+  for (int r = ty; r < 32; r += 8) {
+    const int i = i0 + r, e = e0 + tx;
+    tile[r][tx] = (i < d && e < E) ? w_gate[(size_t)i * E + e] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int e = e0 + r, i = i0 + tx;
+    if (e < E && i < d) wt[(size_t)e * d + i] = tile[tx][r];
+  }
+}
+
+// Encode backward plus the router's input gradient:
+//   dx[t] = sum_j dx_perm[row_j] + sum_j dsel[t,j] * w_gate[:, idx_j]
+// both sums in slot order, in float32, rounded once.
+template <typename ActT>
+__global__ void __launch_bounds__(kRowThreads)
+dx_kernel(const ActT* __restrict__ dx_perm, const float* __restrict__ dsel,
+          const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot_row,
+          const float* __restrict__ wt, ActT* __restrict__ dx, int T, int d, int k) {
+  using CK = Chunk<ActT>;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int rows[MOE_MAX_TOPK], idx[MOE_MAX_TOPK];
+  float ds[MOE_MAX_TOPK];
+  {
+    int r = -1, e = 0;
+    float v = 0.f;
+    if (lane < k) {
+      r = slot_row[(size_t)t * k + lane];
+      e = topk_idx[(size_t)t * k + lane];
+      v = dsel[(size_t)t * k + lane];
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      rows[j] = __shfl(r, j, 64);
+      idx[j] = __shfl(e, j, 64);
+      ds[j] = __shfl(v, j, 64);
+    }
+  }
+  for (int c = lane * CK::N; c < d; c += 64 * CK::N) {
+    float acc[CK::N];
+#pragma unroll
+    for (int i = 0; i < CK::N; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k && rows[j] >= 0) {
+        float v[CK::N];
+        CK::load(dx_perm + (size_t)rows[j] * d + c, v);
+#pragma unroll
+        for (int i = 0; i < CK::N; ++i) acc[i] += v[i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k) {
+        const float* wr = wt + (size_t)idx[j] * d + c;
+#pragma unroll
+        for (int i = 0; i < CK::N; ++i) acc[i] = fmaf(ds[j], wr[i], acc[i]);
+      }
+    }
+    CK::store(dx + (size_t)t * d + c, acc);
+  }
+}
+
+// Gate weight gradient dW_gate[i, e] = sum_t x[t, i] dlogits[t, e] and
+// db[e] = sum_t dlogits[t, e], with dlogits nonzero only at the k selected
+// experts.  Pass 1: token chunks x column slices; each thread owns one
+// column i and walks the chunk's tokens in order, adding into its own LDS
+// column of acc[e][i] (no two threads touch one cell).  Pass 2 sums the
+// chunk partials in chunk order.
+constexpr int kGateCols = 64;
+constexpr int kGateChunk = 2048;
+
+int gate_grad_chunks(int T) { return (T + kGateChunk - 1) / kGateChunk; }
+size_t gate_grad_partial_floats(int T, int d, int E) {
+  return (size_t)gate_grad_chunks(T) * (size_t)E * (size_t)(d + 1);
+}
+
+template <typename ActT>
+__global__ void __launch_bounds__(kGateCols)
+gate_partial_kernel(const ActT* __restrict__ x, const float* __restrict__ dsel,
+                    const int32_t* __restrict__ topk_idx, float* __restrict__ partial, int T,
+                    int d, int E, int k) {
+  extern __shared__ float acc[];  // [E][kGateCols] then db[E]
+  const int tid = threadIdx.x;
+  const int chunk = blockIdx.x;
+  const int i = blockIdx.y * kGateCols + tid;
+  float* db = acc + E * kGateCols;
+  for (int e = 0; e < E; ++e) acc[e * kGateCols + tid] = 0.f;
+  for (int e = tid; e < E; e += kGateCols) db[e] = 0.f;
+  __syncthreads();
+  const int t0 = chunk * kGateChunk;
+  const int t1 = min(T, t0 + kGateChunk);
+  const bool do_db = (blockIdx.y == 0 && tid == 0);
+  for (int t = t0; t < t1; ++t) {
+    const float xv = to_f32(x[(size_t)t * d + i]);
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[(size_t)t * k + j];
+      const float g = dsel[(size_t)t * k + j];
+      acc[e * kGateCols + tid] = fmaf(xv, g, acc[e * kGateCols + tid]);
+      if (do_db) db[e] += g;
+    }
+  }
+  __syncthreads();
+  // partial layout: [chunk][E][d + 1], column d holds db
+  float* p = partial + (size_t)chunk * E * (d + 1);
+  for (int e = 0; e < E; ++e) p[(size_t)e * (d + 1) + i] = acc[e * kGateCols + tid];
+  if (blockIdx.y == 0)
+    for (int e = tid; e < E; e += kGateCols) p[(size_t)e * (d + 1) + d] = db[e];
+}
+
+__global__ void gate_reduce_kernel(const float* __restrict__ partial, int n_chunks, int d, int E,
+                                   float* __restrict__ dw_gate, float* __restrict__ db_gate) {
+  const size_t n = (size_t)E * (d + 1);
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= n) return;
+  float s = 0.f;
+  for (int c = 0; c < n_chunks; ++c) s += partial[(size_t)c * n + q];
+  const int e = (int)(q / (d + 1)), i = (int)(q % (d + 1));
+  if (i < d)
+    dw_gate[(size_t)i * E + e] = s;
+  else
+    db_gate[e] = s;
+}
+
+__global__ void popularity_kernel(int E, int window, int64_t iter,
+                                  const int32_t* __restrict__ counts_raw,
+                                  int32_t* __restrict__ ring, int32_t* __restrict__ window_sum) {
+  const int slot = (int)(iter % window);
+  const int n = (int)((iter + 1 < (int64_t)window) ? iter + 1 : window);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int c = counts_raw[e];
+    ring[(size_t)slot * E + e] = c;
+    int s = c;
+    for (int b = 1; b < n; ++b) s += ring[(size_t)((slot - b + window) % window) * E + e];
+    window_sum[e] = s;
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+#define MOE_DISPATCH_ACT(act, KERNEL, grid, block, shm, s, ...)                          \
+  do {                                                                                    \
+    if ((act) == MOE_BF16)                                                                \
+      hipLaunchKernelGGL(KERNEL<bf16>, grid, block, shm, s, __VA_ARGS__);                 \
+    else                                                                                  \
+      hipLaunchKernelGGL(KERNEL<float>, grid, block, shm, s, __VA_ARGS__);                \
+  } while (0)
+
+hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,
+                          const int32_t* slot_row, void* y, int T, int d, int k, hipStream_t s) {
+  dim3 grid((T + 3) / 4), block(kRowThreads);
+  if (act == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<bf16>, grid, block, 0, s, (const bf16*)out_perm, topk_w,
+                       slot_row, (bf16*)y, T, d, k);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, (const float*)out_perm, topk_w,
+                       slot_row, (float*)y, T, d, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(int act, const void* dy, const void* out_perm,
+                              const float* topk_w, const int32_t* topk_idx,
+                              const int32_t* slot_row, void* d_out, float* dsel,
+                              float* dlogits, int T, int d, int E, int k, hipStream_t s) {
+  dim3 grid((T + 3) / 4), block(kRowThreads);
+  if (act == MOE_BF16)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16>, grid, block, 0, s, (const bf16*)dy,
+                       (const bf16*)out_perm, topk_w, topk_idx, slot_row, (bf16*)d_out, dsel,
+                       dlogits, T, d, E, k);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, block, 0, s, (const float*)dy,
+                       (const float*)out_perm, topk_w, topk_idx, slot_row, (float*)d_out, dsel,
+                       dlogits, T, d, E, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_gate(const float* w_gate, float* w_gate_t, int d, int E,
+                                 hipStream_t s) {
+  dim3 grid((d + 31) / 32, (E + 31) / 32), block(256);
+  hipLaunchKernelGGL(transpose_gate_kernel, grid, block, 0, s, w_gate, w_gate_t, d, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx(int act, const void* dx_perm, const float* dsel, const int32_t* topk_idx,
+                     const int32_t* slot_row, const float* w_gate_t, void* dx, int T, int d,
+                     int k, hipStream_t s) {
+  dim3 grid((T + 3) / 4), block(kRowThreads);
+  if (act == MOE_BF16)
+    hipLaunchKernelGGL(dx_kernel<bf16>, grid, block, 0, s, (const bf16*)dx_perm, dsel, topk_idx,
+                       slot_row, w_gate_t, (bf16*)dx, T, d, k);
+  else
+    hipLaunchKernelGGL(dx_kernel<float>, grid, block, 0, s, (const float*)dx_perm, dsel,
+                       topk_idx, slot_row, w_gate_t, (float*)dx, T, d, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_grad(int act, const void* x, const float* dsel, const int32_t* topk_idx,
+                            float* partial, float* dw_gate, float* db_gate, int T, int d, int E,
+                            int k, hipStream_t s) {
+  const int nc = gate_grad_chunks(T);
+  dim3 grid(nc, d / kGateCols), block(kGateCols);
+  const size_t shm = ((size_t)E * kGateCols + E) * sizeof(float);
+  if (act == MOE_BF16)
+    hipLaunchKernelGGL(gate_partial_kernel<bf16>, grid, block, shm, s, (const bf16*)x, dsel,
+                       topk_idx, partial, T, d, E, k);
+  else
+    hipLaunchKernelGGL(gate_partial_kernel<float>, grid, block, shm, s, (const float*)x, dsel,
+                       topk_idx, partial, T, d, E, k);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t n = (size_t)E * (d + 1);
+  hipLaunchKernelGGL(gate_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     partial, nc, d, E, dw_gate, db_gate);
+  return hipGetLastError();
+}
+
+hipError_t launch_popularity(int E, int window, int64_t iter, const int32_t* counts_raw,
+                             int32_t* ring, int32_t* window_sum, hipStream_t s) {
+  hipLaunchKernelGGL(popularity_kernel, dim3(1), dim3(256), 0, s, E, window, iter, counts_raw,
+                     ring, window_sum);
+  return hipGetLastError();
+}
+
+}  // namespace moe

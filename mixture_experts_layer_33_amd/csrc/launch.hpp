@@ -1,0 +1,64 @@
+// Host-side launchers of the gfx950 MoE kernels (internal to libmoe).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- gate routing (route.hip)
+// logits = x * w_gate + b (float32); top-k with lowest-index ties; weights =
+// softmax over the selected logits.
+hipError_t launch_route(int act, const void* x, const float* w_gate, const float* b_gate,
+                        const float* logits_in, float* logits_out, int32_t* topk_idx,
+                        float* topk_w, int T, int d, int E, int k, hipStream_t s);
+
+// ---- input encode (permute.hip)
+// Per tile of kRankTile slots: stable rank of each slot among the tile's
+// slots of the same expert, and the tile histogram hist[e][tile].
+hipError_t launch_rank_hist(const int32_t* topk_idx, int S, int E, int32_t* local_rank,
+                            int32_t* hist, int n_tiles, hipStream_t s);
+// Exclusive scan of hist over tiles per expert (tile_base, in place of hist
+// is not allowed), counts_raw and counts_kept = min(raw, C).
+hipError_t launch_scan(const int32_t* hist, int n_tiles, int E, int C, int32_t* tile_base,
+                       int32_t* counts_raw, int32_t* counts_kept, hipStream_t s);
+// slot_row, row_token, offsets and the row copy x -> x_perm.
+hipError_t launch_gather(int act, const void* x, const int32_t* topk_idx,
+                         const int32_t* local_rank, const int32_t* tile_base,
+                         const int32_t* counts_kept, int n_tiles, int T, int d, int E, int k,
+                         int C, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
+                         void* x_perm, hipStream_t s);
+
+// ---- output decode and the elementwise backward steps (combine.hip)
+hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,
+                          const int32_t* slot_row, void* y, int T, int d, int k, hipStream_t s);
+hipError_t launch_combine_bwd(int act, const void* dy, const void* out_perm,
+                              const float* topk_w, const int32_t* topk_idx,
+                              const int32_t* slot_row, void* d_out, float* dsel,
+                              float* dlogits, int T, int d, int E, int k, hipStream_t s);
+hipError_t launch_transpose_gate(const float* w_gate, float* w_gate_t, int d, int E,
+                                 hipStream_t s);
+hipError_t launch_dx(int act, const void* dx_perm, const float* dsel, const int32_t* topk_idx,
+                     const int32_t* slot_row, const float* w_gate_t, void* dx, int T, int d,
+                     int k, hipStream_t s);
+int gate_grad_chunks(int T);
+size_t gate_grad_partial_floats(int T, int d, int E);
+hipError_t launch_gate_grad(int act, const void* x, const float* dsel, const int32_t* topk_idx,
+                            float* partial, float* dw_gate, float* db_gate, int T, int d, int E,
+                            int k, hipStream_t s);
+hipError_t launch_popularity(int E, int window, int64_t iter, const int32_t* counts_raw,
+                             int32_t* ring, int32_t* window_sum, hipStream_t s);
+
+// ---- expert GEMMs (gemm.hip)
+// Forward: h = ReLU(x_perm W1[e]^T), out = h W2[e]^T over each expert's rows.
+hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets,
+                             const void* w1, const void* w2, void* h, void* out_perm,
+                             int S_max, int d, int F, int E, hipStream_t s);
+// Backward GEMMs: dz = (dO W2[e]) * [h > 0]; dW2[e] = dO^T h;
+// dx_perm = dz W1[e]; dW1[e] = dz^T x_perm.
+hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, const void* h,
+                             const int32_t* offsets, const void* w1, const void* w2,
+                             void* dz, void* dx_perm, float* dw1, float* dw2, int S_max,
+                             int d, int F, int E, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,322 @@
+// C ABI of libmoe: argument checks, workspace carving and the launch order of
+// each step.  The entry points and their semantics are documented in
+// include/moe.h.  Nothing here reads device memory or synchronises; every
+// call only enqueues kernels on the caller's stream.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t act_bytes(const moe_shape* s) { return s->act_dtype == MOE_BF16 ? 2 : 4; }
+
+int64_t slots(const moe_shape* s) { return (int64_t)s->T * s->k; }
+
+int rank_tiles(const moe_shape* s) { return (int)((slots(s) + kRankTile - 1) / kRankTile); }
+
+moe_status check_shape(const moe_shape* s) {
+  if (s == nullptr) return MOE_ERR_INVALID_ARG;
+  if (s->T <= 0 || s->d_model <= 0 || s->d_ff <= 0 || s->E <= 0 || s->k <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->k > s->E) return MOE_ERR_INVALID_ARG;
+  if (s->d_model % 64 != 0 || s->d_ff % 64 != 0) return MOE_ERR_INVALID_ARG;
+  if (isnan(s->capacity_factor) || isinf(s->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->E > MOE_MAX_EXPERTS || s->k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  // row indices, slot indices and per-row element offsets stay in int32
+  const int64_t S = slots(s);
+  if (S > (int64_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int capacity_of(const moe_shape* s) {
+  const double cf = (double)s->capacity_factor;
+  if (cf <= 0.0) return s->T;
+  const double c = ceil(cf * (double)s->T * (double)s->k / (double)s->E);
+  if (c < 1.0) return 1;
+  if (c > (double)s->T) return s->T;
+  return (int)c;
+}
+
+// Workspace carving: the routing/permutation buffers, then backward buffers.
+struct PermWs {
+  int32_t* local_rank;  // [S]
+  int32_t* hist;        // [E][n_tiles]
+  int32_t* tile_base;   // [E][n_tiles]
+  int32_t* counts_tmp;  // [E]
+};
+
+size_t perm_ws_bytes(const moe_shape* s) {
+  const size_t S = (size_t)slots(s);
+  const size_t nt = (size_t)rank_tiles(s) * (size_t)s->E;
+  return align_up(S * 4) + 2 * align_up(nt * 4) + align_up((size_t)s->E * 4);
+}
+
+PermWs carve_perm(const moe_shape* s, void* ws) {
+  char* p = static_cast<char*>(ws);
+  PermWs w;
+  const size_t S = (size_t)slots(s);
+  const size_t nt = (size_t)rank_tiles(s) * (size_t)s->E;
+  w.local_rank = reinterpret_cast<int32_t*>(p);
+  p += align_up(S * 4);
+  w.hist = reinterpret_cast<int32_t*>(p);
+  p += align_up(nt * 4);
+  w.tile_base = reinterpret_cast<int32_t*>(p);
+  p += align_up(nt * 4);
+  w.counts_tmp = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+struct BwdWs {
+  void* d_out;      // [S][d] act (later dx_perm)
+  void* dz;         // [S][F] act
+  float* dsel;      // [T][k]
+  float* w_gate_t;  // [E][d]
+  float* partial;   // gate-gradient chunk partials
+};
+
+size_t bwd_ws_bytes(const moe_shape* s) {
+  const size_t S = (size_t)slots(s), a = act_bytes(s);
+  return align_up(S * s->d_model * a) + align_up(S * s->d_ff * a) +
+         align_up((size_t)s->T * s->k * 4) + align_up((size_t)s->E * s->d_model * 4) +
+         align_up(gate_grad_partial_floats(s->T, s->d_model, s->E) * 4);
+}
+
+BwdWs carve_bwd(const moe_shape* s, void* ws) {
+  char* p = static_cast<char*>(ws);
+  const size_t S = (size_t)slots(s), a = act_bytes(s);
+  BwdWs w;
+  w.d_out = p;
+  p += align_up(S * s->d_model * a);
+  w.dz = p;
+  p += align_up(S * s->d_ff * a);
+  w.dsel = reinterpret_cast<float*>(p);
+  p += align_up((size_t)s->T * s->k * 4);
+  w.w_gate_t = reinterpret_cast<float*>(p);
+  p += align_up((size_t)s->E * s->d_model * 4);
+  w.partial = reinterpret_cast<float*>(p);
+  return w;
+}
+
+moe_status check_ws(const moe_shape* s, int op, const void* ws, size_t bytes) {
+  const size_t need = moe_workspace_bytes(s, op);
+  if (need == 0) return MOE_OK;
+  if (ws == nullptr || bytes < need) return MOE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+// all pointers non-null and 16-byte aligned
+template <typename... P>
+bool ptrs_ok(P... p) {
+  const void* arr[] = {static_cast<const void*>(p)...};
+  for (const void* q : arr)
+    if (q == nullptr || !aligned16(q)) return false;
+  return true;
+}
+
+bool opt_ok(const void* p) { return p == nullptr || aligned16(p); }
+
+#define MOE_HIP(expr)                                \
+  do {                                               \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP;    \
+  } while (0)
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// route kernel + per-tile ranks + scan (counts)
+moe_status do_route(const moe_shape* s, const void* x, const float* w_gate, const float* b_gate,
+                    const float* logits_in, float* logits_out, int32_t* idx, float* w,
+                    int32_t* counts_raw, int32_t* counts_kept, const PermWs& pw, hipStream_t st) {
+  MOE_HIP(launch_route(s->act_dtype, x, w_gate, b_gate, logits_in, logits_out, idx, w, s->T,
+                       s->d_model, s->E, s->k, st));
+  const int nt = rank_tiles(s);
+  MOE_HIP(launch_rank_hist(idx, (int)slots(s), s->E, pw.local_rank, pw.hist, nt, st));
+  MOE_HIP(launch_scan(pw.hist, nt, s->E, capacity_of(s), pw.tile_base, counts_raw,
+                      counts_kept ? counts_kept : pw.counts_tmp, st));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_check_shape(const moe_shape* shape) { return check_shape(shape); }
+
+size_t moe_workspace_bytes(const moe_shape* s, int32_t op) {
+  if (check_shape(s) != MOE_OK) return 0;
+  switch (op) {
+    case MOE_OP_ROUTE:
+    case MOE_OP_PERMUTE:
+    case MOE_OP_FORWARD:
+      return perm_ws_bytes(s);
+    case MOE_OP_EXPERT_FFN:
+    case MOE_OP_COMBINE:
+      return 0;
+    case MOE_OP_BACKWARD:
+      return bwd_ws_bytes(s);
+    default:
+      return 0;
+  }
+}
+
+int32_t moe_capacity(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return -1;
+  return capacity_of(s);
+}
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK:
+      return "ok";
+    case MOE_ERR_INVALID_ARG:
+      return "invalid argument (null or misaligned pointer, bad size, k > E, d or F not a multiple of 64)";
+    case MOE_ERR_UNSUPPORTED:
+      return "unsupported dtype or shape (E > 256, k > 8, T*k too large)";
+    case MOE_ERR_WORKSPACE:
+      return "workspace missing, misaligned or smaller than moe_workspace_bytes()";
+    case MOE_ERR_HIP:
+      return "HIP kernel launch failed";
+    default:
+      return "unknown status";
+  }
+}
+
+moe_status moe_route(const moe_shape* s, const void* x, const float* w_gate, const float* b_gate,
+                     const float* logits_in, float* logits_out, int32_t* topk_idx, float* topk_w,
+                     int32_t* counts_raw, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ptrs_ok(topk_idx, topk_w, counts_raw) || !opt_ok(logits_out) || !opt_ok(logits_in))
+    return MOE_ERR_INVALID_ARG;
+  if (logits_in == nullptr && !ptrs_ok(x, w_gate, b_gate)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
+  PermWs pw = carve_perm(s, ws);
+  return do_route(s, x, w_gate, b_gate, logits_in, logits_out, topk_idx, topk_w, counts_raw,
+                  nullptr, pw, as_stream(stream));
+}
+
+moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                       int32_t* counts_raw, int32_t* counts_kept, int32_t* offsets,
+                       int32_t* slot_row, int32_t* row_token, void* x_perm, void* ws,
+                       size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ptrs_ok(x, topk_idx, counts_kept, offsets, slot_row, row_token, x_perm) ||
+      !opt_ok(counts_raw))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_PERMUTE, ws, ws_bytes)) != MOE_OK) return st;
+  PermWs pw = carve_perm(s, ws);
+  hipStream_t stream_ = as_stream(stream);
+  const int nt = rank_tiles(s);
+  const int C = capacity_of(s);
+  MOE_HIP(launch_rank_hist(topk_idx, (int)slots(s), s->E, pw.local_rank, pw.hist, nt, stream_));
+  MOE_HIP(launch_scan(pw.hist, nt, s->E, C, pw.tile_base, counts_raw, counts_kept, stream_));
+  MOE_HIP(launch_gather(s->act_dtype, x, topk_idx, pw.local_rank, pw.tile_base, counts_kept, nt,
+                        s->T, s->d_model, s->E, s->k, C, offsets, slot_row, row_token, x_perm,
+                        stream_));
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_shape* s, const void* x_perm, const int32_t* offsets,
+                          const void* w1, const void* w2, void* h, void* out_perm, void* ws,
+                          size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ptrs_ok(x_perm, offsets, w1, w2, h, out_perm)) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, (int)slots(s),
+                            s->d_model, s->d_ff, s->E, as_stream(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_shape* s, const void* out_perm, const float* topk_w,
+                       const int32_t* slot_row, void* y, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ptrs_ok(out_perm, topk_w, slot_row, y)) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_combine(s->act_dtype, out_perm, topk_w, slot_row, y, s->T, s->d_model, s->k,
+                         as_stream(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_shape* s, const void* x, const float* w_gate,
+                       const float* b_gate, const void* w1, const void* w2, void* y,
+                       float* logits_out, int32_t* topk_idx, float* topk_w, int32_t* counts_raw,
+                       int32_t* counts_kept, int32_t* offsets, int32_t* slot_row,
+                       int32_t* row_token, void* x_perm, void* h, void* out_perm, void* ws,
+                       size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ptrs_ok(x, w_gate, b_gate, w1, w2, y, topk_idx, topk_w, counts_kept, offsets, slot_row,
+               row_token, x_perm, h, out_perm) ||
+      !opt_ok(logits_out) || !opt_ok(counts_raw))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_FORWARD, ws, ws_bytes)) != MOE_OK) return st;
+  PermWs pw = carve_perm(s, ws);
+  hipStream_t stream_ = as_stream(stream);
+  st = do_route(s, x, w_gate, b_gate, nullptr, logits_out, topk_idx, topk_w, counts_raw,
+                counts_kept, pw, stream_);
+  if (st != MOE_OK) return st;
+  const int nt = rank_tiles(s);
+  MOE_HIP(launch_gather(s->act_dtype, x, topk_idx, pw.local_rank, pw.tile_base, counts_kept, nt,
+                        s->T, s->d_model, s->E, s->k, capacity_of(s), offsets, slot_row,
+                        row_token, x_perm, stream_));
+  MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, (int)slots(s),
+                            s->d_model, s->d_ff, s->E, stream_));
+  MOE_HIP(launch_combine(s->act_dtype, out_perm, topk_w, slot_row, y, s->T, s->d_model, s->k,
+                         stream_));
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const float* w_gate,
+                        const void* w1, const void* w2, const int32_t* topk_idx,
+                        const float* topk_w, const int32_t* slot_row, const int32_t* row_token,
+                        const int32_t* offsets, const void* x_perm, const void* h,
+                        const void* out_perm, void* dx, float* dw1, float* dw2, float* dw_gate,
+                        float* db_gate, float* dlogits, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ptrs_ok(dy, x, w_gate, w1, w2, topk_idx, topk_w, slot_row, row_token, offsets, x_perm, h,
+               out_perm, dx, dw1, dw2, dw_gate, db_gate) ||
+      !opt_ok(dlogits))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_BACKWARD, ws, ws_bytes)) != MOE_OK) return st;
+  BwdWs bw = carve_bwd(s, ws);
+  hipStream_t stream_ = as_stream(stream);
+  const int act = s->act_dtype;
+  MOE_HIP(launch_combine_bwd(act, dy, out_perm, topk_w, topk_idx, slot_row, bw.d_out, bw.dsel,
+                             dlogits, s->T, s->d_model, s->E, s->k, stream_));
+  // dx_perm reuses d_out's memory: the FC1 dgrad runs after the FC2 wgrad,
+  // the last reader of d_out.
+  MOE_HIP(launch_expert_bwd(act, bw.d_out, x_perm, h, offsets, w1, w2, bw.dz, bw.d_out, dw1, dw2,
+                            (int)slots(s), s->d_model, s->d_ff, s->E, stream_));
+  MOE_HIP(launch_transpose_gate(w_gate, bw.w_gate_t, s->d_model, s->E, stream_));
+  MOE_HIP(launch_dx(act, bw.d_out, bw.dsel, topk_idx, slot_row, bw.w_gate_t, dx, s->T,
+                    s->d_model, s->k, stream_));
+  MOE_HIP(launch_gate_grad(act, x, bw.dsel, topk_idx, bw.partial, dw_gate, db_gate, s->T,
+                           s->d_model, s->E, s->k, stream_));
+  (void)row_token;
+  return MOE_OK;
+}
+
+moe_status moe_popularity_update(int32_t E, int32_t window, int64_t iter,
+                                 const int32_t* counts_raw, int32_t* ring, int32_t* window_sum,
+                                 void* stream) {
+  if (E <= 0 || window <= 0 || window > 64 || iter < 0) return MOE_ERR_INVALID_ARG;
+  if (!ptrs_ok(counts_raw, ring, window_sum)) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_popularity(E, window, iter, counts_raw, ring, window_sum, as_stream(stream)));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+"""Shared helpers of the GPU parity tests: uploads, downloads, tolerances.
+
+Tolerance (relative, scaled by the reference tensor's largest magnitude):
+2e-2 for bf16 activations, 1e-5 for float32; integer results bit-exact.
+"""
+import numpy as np
+import torch
+
+import workloads
+from mixture_experts_layer_33_amd import MOE_BF16, MOE_F32
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def act_code(dtype: str) -> int:
+    return MOE_BF16 if dtype == "bf16" else MOE_F32
+
+
+def up(a: np.ndarray, dtype: str = "f32", device="cuda") -> torch.Tensor:
+    """Upload a float32 array (bf16-representable when dtype is bf16)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def up_i32(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def down(t: torch.Tensor) -> np.ndarray:
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy()
+
+
+def assert_close(gpu, ref, tol, what=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
+    scale = np.abs(ref).max()
+    err = np.abs(gpu - ref).max() if gpu.size else 0.0
+    assert err <= tol * max(scale, 1e-30), f"{what}: max err {err:.3e} > {tol} * {scale:.3e}"
+    return err / max(scale, 1e-30)
+
+
+def assert_close_per_expert(gpu, ref, tol, what=""):
+    """Weight gradients: each expert's slice against its own scale; experts
+    whose reference slice is exactly zero must be exactly zero."""
+    for e in range(ref.shape[0]):
+        if not np.any(ref[e]):
+            assert not np.any(gpu[e]), f"{what}[{e}] must be all zeros"
+        else:
+            assert_close(gpu[e], ref[e], tol, f"{what}[{e}]")
+
+
+def make_case(w: workloads.Workload, it: int = 0, with_dy: bool = True):
+    inp = workloads.make_inputs(w, it, with_weights=True, with_dy=with_dy)
+    return inp
+
+
+def upload_case(inp, dtype):
+    return {
+        "x": up(inp["x"], dtype), "w_gate": up(inp["w_gate"]), "b_gate": up(inp["b_gate"]),
+        "w1": up(inp["w1"], dtype), "w2": up(inp["w2"], dtype),
+        **({"dy": up(inp["dy"], dtype)} if "dy" in inp else {}),
+    }
+
+
+def ambiguous_tokens(logits: np.ndarray, k: int, rel: float = 1e-5) -> np.ndarray:
+    """Tokens whose top-k set or order could flip under a perturbation of
+    the logits by rel * max|logits| (boundary or internal near-ties)."""
+    L = np.asarray(logits, dtype=np.float64)
+    srt = -np.sort(-L, axis=1)
+    band = 2 * rel * np.abs(L).max()
+    kk = min(k + 1, L.shape[1])
+    gaps = srt[:, :kk - 1] - srt[:, 1:kk]
+    return np.where((gaps <= band).any(axis=1))[0]
