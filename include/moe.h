@@ -123,6 +123,9 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_gate,
  * sum of counts_kept; slot_row[s] = offsets[e] + position of slot s among
  * e's slots in slot order, or -1 if that position is >= C; row_token[r] =
  * token of packed row r; x_perm[r] = x[row_token[r]] (exact copy).
+ * Dropped slots are listed after the kept rows: row_token[S_kept + j], for
+ * j < T*k - S_kept, is the slot index t*k+j' of the j-th dropped slot,
+ * ordered by expert and then by slot (moe_backward reads this list).
  * counts_raw may be NULL.  Workspace: MOE_OP_PERMUTE. */
 moe_status moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
                        int32_t* counts_raw, int32_t* counts_kept, int32_t* offsets,

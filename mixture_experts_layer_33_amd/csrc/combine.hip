@@ -100,14 +100,15 @@ combine_kernel(const ActT* __restrict__ out_perm, const float* __restrict__ topk
 //   d_out[r] = w[t,j] * dy[t]      (stored in the activation type)
 //   dg[t,j]  = <dy[t], out_perm[r]>  (0 for a dropped slot)
 // then the gate softmax backward dsel[t,j] = w_j (dg_j - sum_i w_i dg_i),
+// also written per packed row (dsel_perm[r]) for the gate weight gradient,
 // and dlogits[t, :] (dense, optional) holding dsel at the selected experts.
 template <typename ActT>
 __global__ void __launch_bounds__(kRowThreads)
 combine_bwd_kernel(const ActT* __restrict__ dy, const ActT* __restrict__ out_perm,
                    const float* __restrict__ topk_w, const int32_t* __restrict__ topk_idx,
                    const int32_t* __restrict__ slot_row, ActT* __restrict__ d_out,
-                   float* __restrict__ dsel, float* __restrict__ dlogits, int T, int d, int E,
-                   int k) {
+                   float* __restrict__ dsel, float* __restrict__ dsel_perm,
+                   float* __restrict__ dlogits, int T, int d, int E, int k) {
   using CK = Chunk<ActT>;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
@@ -151,6 +152,11 @@ combine_bwd_kernel(const ActT* __restrict__ dy, const ActT* __restrict__ out_per
     for (int j = 0; j < MOE_MAX_TOPK; ++j)
       if (j == lane) mine = ds[j];
     dsel[(size_t)t * k + lane] = mine;
+    int my_row = -1;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j == lane) my_row = rows[j];
+    if (my_row >= 0) dsel_perm[my_row] = mine;
   }
   if (dlogits != nullptr) {
     int idx[MOE_MAX_TOPK];
@@ -238,65 +244,66 @@ dx_kernel(const ActT* __restrict__ dx_perm, const float* __restrict__ dsel,
   }
 }
 
-// Gate weight gradient dW_gate[i, e] = sum_t x[t, i] dlogits[t, e] and
-// db[e] = sum_t dlogits[t, e], with dlogits nonzero only at the k selected
-// experts.  Pass 1: token chunks x column slices; each thread owns one
-// column i and walks the chunk's tokens in order, adding into its own LDS
-// column of acc[e][i] (no two threads touch one cell).  Pass 2 sums the
-// chunk partials in chunk order.
-constexpr int kGateCols = 64;
-constexpr int kGateChunk = 2048;
-
-int gate_grad_chunks(int T) { return (T + kGateChunk - 1) / kGateChunk; }
-size_t gate_grad_partial_floats(int T, int d, int E) {
-  return (size_t)gate_grad_chunks(T) * (size_t)E * (size_t)(d + 1);
-}
-
+// Gate weight gradient over packed rows (float32 path; the bf16 path folds
+// this product into FC1's weight-gradient GEMM):
+//   dW_gate[i, e] = sum over e's rows r of dsel_perm[r] * x_perm[r, i],
+//   db[e] = sum over e's rows of dsel_perm[r].
+// One thread per column walks the rows in order.
 template <typename ActT>
-__global__ void __launch_bounds__(kGateCols)
-gate_partial_kernel(const ActT* __restrict__ x, const float* __restrict__ dsel,
-                    const int32_t* __restrict__ topk_idx, float* __restrict__ partial, int T,
-                    int d, int E, int k) {
-  extern __shared__ float acc[];  // [E][kGateCols] then db[E]
-  const int tid = threadIdx.x;
-  const int chunk = blockIdx.x;
-  const int i = blockIdx.y * kGateCols + tid;
-  float* db = acc + E * kGateCols;
-  for (int e = 0; e < E; ++e) acc[e * kGateCols + tid] = 0.f;
-  for (int e = tid; e < E; e += kGateCols) db[e] = 0.f;
-  __syncthreads();
-  const int t0 = chunk * kGateChunk;
-  const int t1 = min(T, t0 + kGateChunk);
-  const bool do_db = (blockIdx.y == 0 && tid == 0);
-  for (int t = t0; t < t1; ++t) {
-    const float xv = to_f32(x[(size_t)t * d + i]);
-    for (int j = 0; j < k; ++j) {
-      const int e = topk_idx[(size_t)t * k + j];
-      const float g = dsel[(size_t)t * k + j];
-      acc[e * kGateCols + tid] = fmaf(xv, g, acc[e * kGateCols + tid]);
-      if (do_db) db[e] += g;
-    }
+__global__ void __launch_bounds__(64)
+gate_rows_kernel(const ActT* __restrict__ x_perm, const float* __restrict__ dsel_perm,
+                 const int32_t* __restrict__ offsets, float* __restrict__ dw_gate,
+                 float* __restrict__ db_gate, int d, int E) {
+  const int e = blockIdx.x;
+  const int i = blockIdx.y * 64 + threadIdx.x;
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  float acc = 0.f, db = 0.f;
+  for (int r = r0; r < r1; ++r) {
+    const float g = dsel_perm[r];
+    db += g;
+    if (i < d) acc = fmaf(g, to_f32(x_perm[(size_t)r * d + i]), acc);
   }
-  __syncthreads();
-  // partial layout: [chunk][E][d + 1], column d holds db
-  float* p = partial + (size_t)chunk * E * (d + 1);
-  for (int e = 0; e < E; ++e) p[(size_t)e * (d + 1) + i] = acc[e * kGateCols + tid];
-  if (blockIdx.y == 0)
-    for (int e = tid; e < E; e += kGateCols) p[(size_t)e * (d + 1) + d] = db[e];
+  if (i < d) dw_gate[(size_t)i * E + e] = acc;
+  if (blockIdx.y == 0 && threadIdx.x == 0) db_gate[e] = db;
 }
 
-__global__ void gate_reduce_kernel(const float* __restrict__ partial, int n_chunks, int d, int E,
-                                   float* __restrict__ dw_gate, float* __restrict__ db_gate) {
-  const size_t n = (size_t)E * (d + 1);
-  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= n) return;
-  float s = 0.f;
-  for (int c = 0; c < n_chunks; ++c) s += partial[(size_t)c * n + q];
-  const int e = (int)(q / (d + 1)), i = (int)(q % (d + 1));
-  if (i < d)
-    dw_gate[(size_t)i * E + e] = s;
-  else
-    db_gate[e] = s;
+// Dropped slots still carry gate gradient (through the renormalised
+// weights).  The permutation lists them after the kept rows:
+// row_token[S_kept + j] = slot of the j-th dropped slot, ordered by expert and
+// then slot.  Each workgroup finds its expert's run by binary search and adds
+// that run's contribution to dW_gate[:, e] and db[e] (written before by the
+// kept-row pass), walking the run in order.
+template <typename ActT>
+__global__ void __launch_bounds__(64)
+gate_dropped_kernel(const ActT* __restrict__ x, const float* __restrict__ dsel,
+                    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ offsets,
+                    const int32_t* __restrict__ row_token, float* __restrict__ dw_gate,
+                    float* __restrict__ db_gate, int S, int d, int E, int k) {
+  const int e = blockIdx.x;
+  const int i = blockIdx.y * 64 + threadIdx.x;
+  const int kept = offsets[E];
+  const int32_t* list = row_token + kept;
+  const int n = S - kept;
+  // first j with expert(list[j]) >= v
+  auto lower = [&](int v) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (topk_idx[list[mid]] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  const int j0 = lower(e), j1 = lower(e + 1);
+  if (j0 == j1) return;
+  float acc = 0.f, db = 0.f;
+  for (int j = j0; j < j1; ++j) {
+    const int s = list[j];
+    const float g = dsel[s];
+    db += g;
+    if (i < d) acc = fmaf(g, to_f32(x[(size_t)(s / k) * d + i]), acc);
+  }
+  if (i < d) dw_gate[(size_t)i * E + e] += acc;
+  if (blockIdx.y == 0 && threadIdx.x == 0) db_gate[e] += db;
 }
 
 __global__ void popularity_kernel(int E, int window, int64_t iter,
@@ -314,14 +321,6 @@ __global__ void popularity_kernel(int E, int window, int64_t iter,
 }
 
 // ---------------------------------------------------------------- launchers
-#define MOE_DISPATCH_ACT(act, KERNEL, grid, block, shm, s, ...)                          \
-  do {                                                                                    \
-    if ((act) == MOE_BF16)                                                                \
-      hipLaunchKernelGGL(KERNEL<bf16>, grid, block, shm, s, __VA_ARGS__);                 \
-    else                                                                                  \
-      hipLaunchKernelGGL(KERNEL<float>, grid, block, shm, s, __VA_ARGS__);                \
-  } while (0)
-
 hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,
                           const int32_t* slot_row, void* y, int T, int d, int k, hipStream_t s) {
   dim3 grid((T + 3) / 4), block(kRowThreads);
@@ -337,16 +336,17 @@ hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,
 hipError_t launch_combine_bwd(int act, const void* dy, const void* out_perm,
                               const float* topk_w, const int32_t* topk_idx,
                               const int32_t* slot_row, void* d_out, float* dsel,
-                              float* dlogits, int T, int d, int E, int k, hipStream_t s) {
+                              float* dsel_perm, float* dlogits, int T, int d, int E, int k,
+                              hipStream_t s) {
   dim3 grid((T + 3) / 4), block(kRowThreads);
   if (act == MOE_BF16)
     hipLaunchKernelGGL(combine_bwd_kernel<bf16>, grid, block, 0, s, (const bf16*)dy,
                        (const bf16*)out_perm, topk_w, topk_idx, slot_row, (bf16*)d_out, dsel,
-                       dlogits, T, d, E, k);
+                       dsel_perm, dlogits, T, d, E, k);
   else
     hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, block, 0, s, (const float*)dy,
                        (const float*)out_perm, topk_w, topk_idx, slot_row, (float*)d_out, dsel,
-                       dlogits, T, d, E, k);
+                       dsel_perm, dlogits, T, d, E, k);
   return hipGetLastError();
 }
 
@@ -370,23 +370,29 @@ hipError_t launch_dx(int act, const void* dx_perm, const float* dsel, const int3
   return hipGetLastError();
 }
 
-hipError_t launch_gate_grad(int act, const void* x, const float* dsel, const int32_t* topk_idx,
-                            float* partial, float* dw_gate, float* db_gate, int T, int d, int E,
-                            int k, hipStream_t s) {
-  const int nc = gate_grad_chunks(T);
-  dim3 grid(nc, d / kGateCols), block(kGateCols);
-  const size_t shm = ((size_t)E * kGateCols + E) * sizeof(float);
+hipError_t launch_gate_rows(int act, const void* x_perm, const float* dsel_perm,
+                            const int32_t* offsets, float* dw_gate, float* db_gate, int d, int E,
+                            hipStream_t s) {
+  dim3 grid(E, (d + 63) / 64), block(64);
   if (act == MOE_BF16)
-    hipLaunchKernelGGL(gate_partial_kernel<bf16>, grid, block, shm, s, (const bf16*)x, dsel,
-                       topk_idx, partial, T, d, E, k);
+    hipLaunchKernelGGL(gate_rows_kernel<bf16>, grid, block, 0, s, (const bf16*)x_perm, dsel_perm,
+                       offsets, dw_gate, db_gate, d, E);
   else
-    hipLaunchKernelGGL(gate_partial_kernel<float>, grid, block, shm, s, (const float*)x, dsel,
-                       topk_idx, partial, T, d, E, k);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const size_t n = (size_t)E * (d + 1);
-  hipLaunchKernelGGL(gate_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     partial, nc, d, E, dw_gate, db_gate);
+    hipLaunchKernelGGL(gate_rows_kernel<float>, grid, block, 0, s, (const float*)x_perm,
+                       dsel_perm, offsets, dw_gate, db_gate, d, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_dropped(int act, const void* x, const float* dsel, const int32_t* topk_idx,
+                               const int32_t* offsets, const int32_t* row_token, float* dw_gate,
+                               float* db_gate, int S, int d, int E, int k, hipStream_t s) {
+  dim3 grid(E, (d + 63) / 64), block(64);
+  if (act == MOE_BF16)
+    hipLaunchKernelGGL(gate_dropped_kernel<bf16>, grid, block, 0, s, (const bf16*)x, dsel,
+                       topk_idx, offsets, row_token, dw_gate, db_gate, S, d, E, k);
+  else
+    hipLaunchKernelGGL(gate_dropped_kernel<float>, grid, block, 0, s, (const float*)x, dsel,
+                       topk_idx, offsets, row_token, dw_gate, db_gate, S, d, E, k);
   return hipGetLastError();
 }
 

@@ -35,32 +35,46 @@ constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round robin
 
 enum Epi { EPI_RELU = 0, EPI_STORE = 1, EPI_MASK = 2, EPI_F32 = 3 };
 
-__device__ __forceinline__ int swz(int row, int kc) { return (row * 8 + (kc ^ (row & 7))) * 8; }
+// 16-byte chunk kc of LDS row `row` (rows of 64 bf16 = 8 chunks).  The XOR
+// uses row bits 0-2, 3-5 and 6-8 so that both 8 consecutive rows (MFMA
+// fragment reads) and rows 8 apart (transposed stores) spread over banks.
+__device__ __forceinline__ int swz(int row, int kc) {
+  return (row * 8 + (kc ^ ((row ^ (row >> 3) ^ (row >> 6)) & 7))) * 8;
+}
 
 // ---------------------------------------------------------------------------
 // Operand tile loaders: global -> registers -> LDS [ROWS][64] (bf16).
-// K-contiguous operand: element (r, k) at base[r * ld + k].
+// K-contiguous operand: element (r, k) at base[r * ld + k], copied straight
+// from global memory into LDS (global_load_lds_dwordx4: each lane's 16 bytes
+// land at the wave's LDS base + 16 * lane).  One wave instruction fills 8 LDS
+// rows; lane L fills row r0 + L/8 at chunk position L%8, so it fetches the
+// logical chunk that the swizzle puts there.  Rows >= nrows read row
+// nrows-1 (their results are never stored).
 template <int ROWS>
 struct LoadK {
-  static constexpr int N = ROWS * 8 / kGemmThreads;  // 16-byte chunks per thread
-  i32x4 v[N];
-  // rows >= nrows are clamped to row nrows-1 (their results are never stored)
-  __device__ void load(const bf16* base, int ld, int nrows, int k0) {
+  static constexpr int N = ROWS / 32;  // wave instructions per thread
+  uint32_t off[N];                     // byte offsets from the tile base (fixed over k)
+  int ready = 0;
+  __device__ void issue(const bf16* base, int ld, int nrows, int k0, int, bf16* lds) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (!ready) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int row = (i * 4 + wid) * 8 + (lane >> 3), p = lane & 7;
+        const int kc = p ^ ((row ^ (row >> 3) ^ (row >> 6)) & 7);
+        off[i] = (uint32_t)(((size_t)min(row, nrows - 1) * ld + kc * 8) * sizeof(bf16));
+      }
+      ready = 1;
+    }
+    const char* b = reinterpret_cast<const char*>(base + k0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int c = threadIdx.x + i * kGemmThreads;
-      const int r = min(c >> 3, nrows - 1), kc = c & 7;
-      v[i] = *reinterpret_cast<const i32x4*>(base + (size_t)r * ld + k0 + kc * 8);
+      const int r0 = (i * 4 + wid) * 8;
+      __builtin_amdgcn_global_load_lds(
+          b + off[i], (__attribute__((address_space(3))) void*)(lds + r0 * kBK), 16, 0, 0);
     }
   }
-  __device__ void store(bf16* lds) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = threadIdx.x + i * kGemmThreads;
-      const int r = c >> 3, kc = c & 7;
-      *reinterpret_cast<i32x4*>(lds + swz(r, kc)) = v[i];
-    }
-  }
+  __device__ void commit(bf16*) const {}
 };
 
 // MN-contiguous operand: element (r, k) at base[k * ld + r].  Each thread
@@ -89,6 +103,23 @@ struct LoadMN {
     return (int)__builtin_amdgcn_perm((unsigned)hi_src, (unsigned)lo_src,
                                       odd ? 0x07060302u : 0x05040100u);
   }
+  // Gate side product: acc[m] += sum_i sel[k0 + kb*KB + i] * v[i][m] over
+  // this thread's KB rows (sel rows past kmax read as 0); db += sum_i sel.
+  __device__ void gate(const float* sel, int k0, int kmax, float* acc, float* db) const {
+    const int kb = threadIdx.x / RB;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int k = k0 + kb * KB + i;
+      const float g = (k < kmax) ? sel[k] : 0.f;
+      *db += g;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const unsigned u = (unsigned)v[i][p];
+        acc[2 * p] = fmaf(g, __uint_as_float(u << 16), acc[2 * p]);
+        acc[2 * p + 1] = fmaf(g, __uint_as_float(u & 0xffff0000u), acc[2 * p + 1]);
+      }
+    }
+  }
   __device__ void store(bf16* lds) const {
     const int rb = threadIdx.x % RB, kb = threadIdx.x / RB;
 #pragma unroll
@@ -115,121 +146,183 @@ struct Loader;
 template <int ROWS>
 struct Loader<true, ROWS> {
   LoadK<ROWS> l;
-  __device__ void load(const bf16* base, int ld, int nrows, int k0, int) {
-    l.load(base, ld, nrows, k0);
+  __device__ void issue(const bf16* base, int ld, int nrows, int k0, int kmax, bf16* lds) {
+    l.issue(base, ld, nrows, k0, kmax, lds);
   }
-  __device__ void store(bf16* lds) const { l.store(lds); }
+  __device__ void commit(bf16* lds) const {}
 };
 template <int ROWS>
 struct Loader<false, ROWS> {
   LoadMN<ROWS> l;
-  __device__ void load(const bf16* base, int ld, int nrows, int k0, int kmax) {
+  __device__ void issue(const bf16* base, int ld, int nrows, int k0, int kmax, bf16*) {
     l.load(base, ld, nrows, k0, kmax);
   }
-  __device__ void store(bf16* lds) const { l.store(lds); }
+  __device__ void commit(bf16* lds) const { l.store(lds); }
 };
 
+// Wait for this wave's outstanding global loads (including the ones that
+// write LDS directly) before a barrier publishes the LDS tile.
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
-// One output tile: C[BM x BN] = sum_k A(r, k) B(n, k), k in [0, K).
-// A/B pointers address element (0, 0) of the tile; kmax bounds k for
-// MN-contiguous operands (wgrad's ragged expert rows).
-template <int BM, int BN, bool A_K, bool B_K>
+// One output tile: C[BM x BN] = sum_k A(m, k) B(n, k), k in [0, K), on 4
+// wavefronts in a 2 x 2 grid, each owning a (BM/2) x (BN/2) block.  The MFMA
+// takes the B tile as its first operand and the A tile as its second, so its
+// 16 x 16 result block is C^T: lane l holds C[m][n..n+3] with m = l % 16 and
+// n = 4 * (l / 16) (+ block offsets), four consecutive columns of one row,
+// which the epilogue writes as one 8- or 16-byte store.
+//
+// With GATE (MN-contiguous B only) and a non-null `gsel`, the tile also
+// accumulates g[n] = sum_k gsel[k] B(n, k) for its columns from the B
+// registers on their way to LDS (gacc: per thread, its 8 columns over its
+// rows) and sum_k gsel[k] (gdb); see gate_reduce().
+template <int BM, int BN, bool A_K, bool B_K, bool GATE = false>
 struct TileGemm {
   static constexpr int WM = BM / 2, WN = BN / 2;  // 2 x 2 waves
   static constexpr int FM = WM / 16, FN = WN / 16;
-  f32x4 acc[FM][FN];
+  static constexpr size_t kLds = (size_t)2 * (BM + BN) * kBK * sizeof(bf16);
+  f32x4 acc[FN][FM];  // acc[i][j]: n-block i, m-block j
+  float gacc[8];
+  float gdb;
 
   __device__ void run(const bf16* A, int lda, int a_rows, const bf16* B, int ldb, int b_rows,
-                      int K, bf16* lds) {
+                      int K, bf16* lds, const float* gsel = nullptr) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (GATE) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) gacc[m] = 0.f;
+      gdb = 0.f;
+    }
     const int nk = (K + kBK - 1) / kBK;
     if (nk == 0) return;
+    bf16* const a_lds = lds;                      // [2][BM][kBK]
+    bf16* const b_lds = lds + 2 * BM * kBK;       // [2][BN][kBK]
     Loader<A_K, BM> la;
     Loader<B_K, BN> lb;
-    la.load(A_K ? A : A, lda, a_rows, 0, K);
-    lb.load(B, ldb, b_rows, 0, K);
-    la.store(lds);
-    lb.store(lds + 2 * BM * kBK);
+    la.issue(A, lda, a_rows, 0, K, a_lds);
+    lb.issue(B, ldb, b_rows, 0, K, b_lds);
+    if constexpr (GATE) {
+      if (gsel) lb.l.gate(gsel, 0, K, gacc, &gdb);
+    }
+    la.commit(a_lds);
+    lb.commit(b_lds);
+    wait_vm();
     __syncthreads();
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int wm = wid >> 1, wn = wid & 1;
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
       const bool more = kt + 1 < nk;
+      bf16* const a_nxt = a_lds + (cur ^ 1) * (BM * kBK);
+      bf16* const b_nxt = b_lds + (cur ^ 1) * (BN * kBK);
       if (more) {
         if (A_K)
-          la.load(A, lda, a_rows, (kt + 1) * kBK, K);
+          la.issue(A, lda, a_rows, (kt + 1) * kBK, K, a_nxt);
         else
-          la.load(A + (size_t)(kt + 1) * kBK * lda, lda, a_rows, 0, K - (kt + 1) * kBK);
+          la.issue(A + (size_t)(kt + 1) * kBK * lda, lda, a_rows, 0, K - (kt + 1) * kBK, a_nxt);
         if (B_K)
-          lb.load(B, ldb, b_rows, (kt + 1) * kBK, K);
+          lb.issue(B, ldb, b_rows, (kt + 1) * kBK, K, b_nxt);
         else
-          lb.load(B + (size_t)(kt + 1) * kBK * ldb, ldb, b_rows, 0, K - (kt + 1) * kBK);
+          lb.issue(B + (size_t)(kt + 1) * kBK * ldb, ldb, b_rows, 0, K - (kt + 1) * kBK, b_nxt);
       }
-      const bf16* as = lds + cur * (BM * kBK);
-      const bf16* bs = lds + 2 * BM * kBK + cur * (BN * kBK);
+      const bf16* as = a_lds + cur * (BM * kBK);
+      const bf16* bs = b_lds + cur * (BN * kBK);
 #pragma unroll
       for (int ks = 0; ks < kBK / 32; ++ks) {
-        bf16x8 a[FM], b[FN];
+        bf16x8 a[FM];
         const int kc = ks * 4 + (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * WM + i * 16 + (lane & 15);
-          a[i] = *reinterpret_cast<const bf16x8*>(as + swz(r, kc));
+        for (int j = 0; j < FM; ++j) {
+          const int r = wm * WM + j * 16 + (lane & 15);
+          a[j] = *reinterpret_cast<const bf16x8*>(as + swz(r, kc));
         }
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int r = wn * WN + j * 16 + (lane & 15);
-          b[j] = *reinterpret_cast<const bf16x8*>(bs + swz(r, kc));
+        for (int i = 0; i < FN; ++i) {
+          const int r = wn * WN + i * 16 + (lane & 15);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(bs + swz(r, kc));
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[j], acc[i][j], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
       }
       if (more) {
-        la.store(lds + (cur ^ 1) * (BM * kBK));
-        lb.store(lds + 2 * BM * kBK + (cur ^ 1) * (BN * kBK));
+        if constexpr (GATE) {
+          if (gsel) lb.l.gate(gsel, (kt + 1) * kBK, K, gacc, &gdb);
+        }
+        la.commit(a_nxt);
+        lb.commit(b_nxt);
       }
+      wait_vm();
       __syncthreads();
+    }
+  }
+
+  // Sum the per-thread gate partials over the row groups (fixed order) and
+  // write out[n * out_stride] = g[n] for n < cols, and *db_out (if non-null).
+  // Uses the first LDS bytes; call after run() (which ends with a barrier).
+  __device__ void gate_reduce(float* red, int cols, float* out, int out_stride,
+                              float* db_out) const {
+    constexpr int RB = BN / 8, G = kGemmThreads / RB;
+    const int rb = threadIdx.x % RB, kb = threadIdx.x / RB;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) red[kb * BN + rb * 8 + m] = gacc[m];
+    if (rb == 0) red[G * BN + kb] = gdb;
+    __syncthreads();
+    for (int n = threadIdx.x; n < cols; n += kGemmThreads) {
+      float sum = 0.f;
+      for (int g = 0; g < G; ++g) sum += red[g * BN + n];
+      out[(size_t)n * out_stride] = sum;
+    }
+    if (db_out != nullptr && threadIdx.x == 0) {
+      float sum = 0.f;
+      for (int g = 0; g < G; ++g) sum += red[G * BN + g];
+      *db_out = sum;
     }
   }
 };
 
-// Epilogue: element (r, n) of the tile is acc[i][j][q] with
-// r = wm*WM + i*16 + (lane/16)*4 + q and n = wn*WN + j*16 + lane%16.
-template <int BM, int BN, bool A_K, bool B_K, int EPI>
-__device__ __forceinline__ void store_tile(const TileGemm<BM, BN, A_K, B_K>& tg, void* C, int ldc,
-                                           int rows, int cols, const bf16* aux, int ld_aux) {
-  using TG = TileGemm<BM, BN, A_K, B_K>;
+// Epilogue: lane holds C[m][n..n+3] of each 16 x 16 block (see TileGemm).
+// rows/cols bound the valid part of the tile (cols is a multiple of 4).
+template <int EPI, class TG>
+__device__ __forceinline__ void store_tile(const TG& tg, void* C, int ldc, int rows, int cols,
+                                           const bf16* aux, int ld_aux) {
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid >> 1, wn = wid & 1;
 #pragma unroll
-  for (int i = 0; i < TG::FM; ++i)
+  for (int j = 0; j < TG::FM; ++j) {
+    const int m = wm * TG::WM + j * 16 + (lane & 15);
+    if (m >= rows) continue;
 #pragma unroll
-    for (int j = 0; j < TG::FN; ++j) {
-      const int n = wn * TG::WN + j * 16 + (lane & 15);
+    for (int i = 0; i < TG::FN; ++i) {
+      const int n = wn * TG::WN + i * 16 + (lane >> 4) * 4;
       if (n >= cols) continue;
+      f32x4 v = tg.acc[i][j];
+      if constexpr (EPI == EPI_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + (size_t)m * ldc + n) = v;
+      } else {
+        if constexpr (EPI == EPI_RELU) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = wm * TG::WM + i * 16 + (lane >> 4) * 4 + q;
-        if (r >= rows) continue;
-        float v = tg.acc[i][j][q];
-        if constexpr (EPI == EPI_F32) {
-          reinterpret_cast<float*>(C)[(size_t)r * ldc + n] = v;
-        } else {
-          if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.f);
-          if constexpr (EPI == EPI_MASK) {
-            if (!((float)aux[(size_t)r * ld_aux + n] > 0.f)) v = 0.f;
-          }
-          reinterpret_cast<bf16*>(C)[(size_t)r * ldc + n] = (bf16)v;
+          for (int q = 0; q < 4; ++q) v[q] = fmaxf(v[q], 0.f);
         }
+        if constexpr (EPI == EPI_MASK) {
+          const bf16x4 hv = *reinterpret_cast<const bf16x4*>(aux + (size_t)m * ld_aux + n);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (!((float)hv[q] > 0.f)) v[q] = 0.f;
+        }
+        bf16x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = (bf16)v[q];
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(C) + (size_t)m * ldc + n) = o;
       }
     }
+    // keep the scheduler from hoisting every accumulator read to the top
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -302,8 +395,8 @@ rows_gemm_kernel(RowsArgs p) {
   } else {
     tg.run(A, p.K, rows, Bm + n0, p.N, cols, p.K, lds);
   }
-  store_tile<BM, BN, true, B_K, EPI>(tg, p.C + (size_t)row0 * p.N + n0, p.N, rows, cols,
-                                     p.aux ? p.aux + (size_t)row0 * p.N + n0 : nullptr, p.N);
+  store_tile<EPI>(tg, p.C + (size_t)row0 * p.N + n0, p.N, rows, cols,
+                  p.aux ? p.aux + (size_t)row0 * p.N + n0 : nullptr, p.N);
 }
 
 // ---------------------------------------------------------------------------
@@ -313,10 +406,18 @@ struct WgradArgs {
   const bf16* X2;  // [rows][N2]
   float* C;        // [E][N1][N2]
   const int32_t* offsets;
+  // gate gradient (GATE only): gsel[r] per packed row; dW_gate [N2][E], db [E]
+  const float* gsel;
+  float* dw_gate;
+  float* db_gate;
   int N1, N2, E;
 };
 
-template <int BM, int BN>
+// With GATE, the workgroups of the first N1 tile also produce the gate's
+// weight gradient over the same rows, dW_gate[:, e] = X2_e^T gsel_e and
+// db[e] = sum(gsel_e), from the X2 tiles they already stream (for FC1's
+// weight gradient X2 is x_perm and gsel the gate-softmax gradient per row).
+template <int BM, int BN, bool GATE>
 __global__ void __launch_bounds__(kGemmThreads)
 wgrad_kernel(WgradArgs p) {
   extern __shared__ __attribute__((aligned(16))) bf16 lds[];
@@ -344,11 +445,19 @@ wgrad_kernel(WgradArgs p) {
   const int n1 = t1 * BM, n2 = t2 * BN;
   const int r0 = p.offsets[e], K = s_cnt[e];
   const int rows = min(BM, p.N1 - n1), cols = min(BN, p.N2 - n2);
-  TileGemm<BM, BN, false, false> tg;
+  TileGemm<BM, BN, false, false, GATE> tg;
+  const bool gate_here = GATE && t1 == 0;
   tg.run(p.X1 + (size_t)r0 * p.N1 + n1, p.N1, rows, p.X2 + (size_t)r0 * p.N2 + n2, p.N2, cols, K,
-         lds);
-  store_tile<BM, BN, false, false, EPI_F32>(tg, p.C + (size_t)e * p.N1 * p.N2 + (size_t)n1 * p.N2 + n2,
-                                            p.N2, rows, cols, nullptr, 0);
+         lds, gate_here ? p.gsel + r0 : nullptr);
+  store_tile<EPI_F32>(tg, p.C + (size_t)e * p.N1 * p.N2 + (size_t)n1 * p.N2 + n2, p.N2, rows,
+                      cols, nullptr, 0);
+  if constexpr (GATE) {
+    if (gate_here) {
+      __syncthreads();
+      tg.gate_reduce(reinterpret_cast<float*>(lds), cols, p.dw_gate + (size_t)n2 * p.E + e, p.E,
+                     t2 == 0 ? p.db_gate + e : nullptr);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -398,46 +507,79 @@ f32_wgrad_kernel(const float* __restrict__ X1, const float* __restrict__ X2, flo
 
 // ---------------------------------------------------------------------------
 // launchers
-constexpr int kFwdBM = 128, kFwdBN = 128;
-constexpr int kWgBM = 128, kWgBN = 128;
 
-template <int BM, int BN>
-constexpr size_t gemm_lds_bytes() {
-  return (size_t)2 * (BM + BN) * kBK * sizeof(bf16);
+// Tile shape per product: the largest tiles (fewest LDS bytes per flop) that
+// still give every CU work.  `mt(bm)` = number of row tiles for tile height bm.
+struct Shape2 {
+  int bm, bn;
+};
+template <class MT>
+static Shape2 pick_tile(MT mt, int N) {
+  const long long want = 2 * 256;  // two tiles per CU
+  const Shape2 cand[] = {{256, 128}, {128, 256}, {128, 128}};
+  for (const Shape2& c : cand) {
+    const long long tiles = mt(c.bm) * (long long)((N + c.bn - 1) / c.bn);
+    if (tiles >= want) return c;
+  }
+  return {128, 128};
 }
 
 template <int BM, int BN, bool B_K, int EPI>
-static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const bf16* aux,
-                              const int32_t* offsets, long long b_stride, int K, int N, int E,
-                              int S_max, hipStream_t s) {
-  RowsArgs p{A, B, C, aux, offsets, b_stride, K, N, E};
+static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
   // worst case: sum over experts of ceil(rows_e / BM) <= S_max / BM + E
-  const long long mt_max = (S_max + BM - 1) / BM + E;
-  const long long nt = (N + BN - 1) / BN;
+  const long long mt_max = (S_max + BM - 1) / BM + p.E;
+  const long long nt = (p.N + BN - 1) / BN;
   const long long grid = mt_max * nt;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  constexpr size_t shm = gemm_lds_bytes<BM, BN>();
+  constexpr size_t shm = TileGemm<BM, BN, true, B_K>::kLds;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&rows_gemm_kernel<BM, BN, B_K, EPI>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI>), dim3((unsigned)grid), dim3(kGemmThreads),
-                     shm, s, p);
+  hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI>), dim3((unsigned)grid),
+                     dim3(kGemmThreads), shm, s, p);
   return hipGetLastError();
 }
 
-template <int BM, int BN>
-static hipError_t launch_wgrad(const bf16* X1, const bf16* X2, float* C, const int32_t* offsets,
-                               int N1, int N2, int E, hipStream_t s) {
-  WgradArgs p{X1, X2, C, offsets, N1, N2, E};
-  const long long grid = (long long)E * ((N1 + BM - 1) / BM) * ((N2 + BN - 1) / BN);
-  constexpr size_t shm = gemm_lds_bytes<BM, BN>();
+template <bool B_K, int EPI>
+static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const bf16* aux,
+                              const int32_t* offsets, long long b_stride, int K, int N, int E,
+                              int S_max, hipStream_t s) {
+  RowsArgs p{A, B, C, aux, offsets, b_stride, K, N, E};
+  // row tiles for an even spread of S_max rows over E experts
+  auto mt = [&](int bm) {
+    const long long per = ((long long)S_max / E + bm - 1) / bm;
+    return per * E;
+  };
+  const Shape2 t = pick_tile(mt, N);
+  if (t.bm == 256 && t.bn == 128) return launch_rows_t<256, 128, B_K, EPI>(p, S_max, s);
+  if (t.bm == 128 && t.bn == 256) return launch_rows_t<128, 256, B_K, EPI>(p, S_max, s);
+  return launch_rows_t<128, 128, B_K, EPI>(p, S_max, s);
+}
+
+template <int BM, int BN, bool GATE>
+static hipError_t launch_wgrad_t(const WgradArgs& p, hipStream_t s) {
+  const long long grid = (long long)p.E * ((p.N1 + BM - 1) / BM) * ((p.N2 + BN - 1) / BN);
+  constexpr size_t shm = TileGemm<BM, BN, false, false, GATE>::kLds;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&wgrad_kernel<BM, BN>),
+      reinterpret_cast<const void*>(&wgrad_kernel<BM, BN, GATE>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((wgrad_kernel<BM, BN>), dim3((unsigned)grid), dim3(kGemmThreads), shm, s, p);
+  hipLaunchKernelGGL((wgrad_kernel<BM, BN, GATE>), dim3((unsigned)grid), dim3(kGemmThreads), shm,
+                     s, p);
   return hipGetLastError();
+}
+
+template <bool GATE>
+static hipError_t launch_wgrad(const bf16* X1, const bf16* X2, float* C, const int32_t* offsets,
+                               const float* gsel, float* dw_gate, float* db_gate, int N1, int N2,
+                               int E, hipStream_t s) {
+  WgradArgs p{X1, X2, C, offsets, gsel, dw_gate, db_gate, N1, N2, E};
+  auto mt = [&](int bm) { return (long long)E * ((N1 + bm - 1) / bm); };
+  const Shape2 t = pick_tile(mt, N2);
+  if (t.bm == 256 && t.bn == 128) return launch_wgrad_t<256, 128, GATE>(p, s);
+  if (t.bm == 128 && t.bn == 256) return launch_wgrad_t<128, 256, GATE>(p, s);
+  return launch_wgrad_t<128, 128, GATE>(p, s);
 }
 
 #define MOE_TRY(expr)                         \
@@ -450,16 +592,16 @@ hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets
                              const void* w2, void* h, void* out_perm, int S_max, int d, int F,
                              int E, hipStream_t s) {
   if (act == MOE_BF16) {
-    MOE_TRY((launch_rows<kFwdBM, kFwdBN, true, EPI_RELU>(
-        (const bf16*)x_perm, (const bf16*)w1, (bf16*)h, nullptr, offsets, (long long)F * d, d, F,
-        E, S_max, s)));
-    MOE_TRY((launch_rows<kFwdBM, kFwdBN, true, EPI_STORE>(
-        (const bf16*)h, (const bf16*)w2, (bf16*)out_perm, nullptr, offsets, (long long)d * F, F,
-        d, E, S_max, s)));
+    MOE_TRY((launch_rows<true, EPI_RELU>((const bf16*)x_perm, (const bf16*)w1, (bf16*)h, nullptr,
+                                         offsets, (long long)F * d, d, F, E, S_max, s)));
+    MOE_TRY((launch_rows<true, EPI_STORE>((const bf16*)h, (const bf16*)w2, (bf16*)out_perm,
+                                          nullptr, offsets, (long long)d * F, F, d, E, S_max,
+                                          s)));
     return hipSuccess;
   }
   dim3 b(256);
-  dim3 g1((S_max + kF32Rows - 1) / kF32Rows, (F + 63) / 64), g2((S_max + kF32Rows - 1) / kF32Rows, (d + 63) / 64);
+  dim3 g1((S_max + kF32Rows - 1) / kF32Rows, (F + 63) / 64),
+      g2((S_max + kF32Rows - 1) / kF32Rows, (d + 63) / 64);
   hipLaunchKernelGGL((f32_rows_kernel<true, EPI_RELU>), g1, b, 0, s, (const float*)x_perm,
                      (const float*)w1, (float*)h, nullptr, offsets, d, F, E, S_max);
   MOE_TRY(hipGetLastError());
@@ -470,21 +612,24 @@ hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets
 
 hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, const void* h,
                              const int32_t* offsets, const void* w1, const void* w2, void* dz,
-                             void* dx_perm, float* dw1, float* dw2, int S_max, int d, int F,
-                             int E, hipStream_t s) {
+                             void* dx_perm, float* dw1, float* dw2, const float* dsel_perm,
+                             float* dw_gate, float* db_gate, int S_max, int d, int F, int E,
+                             hipStream_t s) {
   if (act == MOE_BF16) {
     // dz = (dO W2[e]) * [h > 0]: A = dO [rows][d], B = W2[e] as [K=d][N=F]
-    MOE_TRY((launch_rows<kFwdBM, kFwdBN, false, EPI_MASK>(
-        (const bf16*)d_out, (const bf16*)w2, (bf16*)dz, (const bf16*)h, offsets, (long long)d * F,
-        d, F, E, S_max, s)));
+    MOE_TRY((launch_rows<false, EPI_MASK>((const bf16*)d_out, (const bf16*)w2, (bf16*)dz,
+                                          (const bf16*)h, offsets, (long long)d * F, d, F, E,
+                                          S_max, s)));
     // dW2[e] = dO^T h  ([d][F])
-    MOE_TRY((launch_wgrad<kWgBM, kWgBN>((const bf16*)d_out, (const bf16*)h, dw2, offsets, d, F, E, s)));
+    MOE_TRY((launch_wgrad<false>((const bf16*)d_out, (const bf16*)h, dw2, offsets, nullptr,
+                                 nullptr, nullptr, d, F, E, s)));
     // dx_perm = dz W1[e]: A = dz [rows][F], B = W1[e] as [K=F][N=d]  (may reuse dO's memory)
-    MOE_TRY((launch_rows<kFwdBM, kFwdBN, false, EPI_STORE>(
-        (const bf16*)dz, (const bf16*)w1, (bf16*)dx_perm, nullptr, offsets, (long long)F * d, F,
-        d, E, S_max, s)));
-    // dW1[e] = dz^T x_perm  ([F][d])
-    MOE_TRY((launch_wgrad<kWgBM, kWgBN>((const bf16*)dz, (const bf16*)x_perm, dw1, offsets, F, d, E, s)));
+    MOE_TRY((launch_rows<false, EPI_STORE>((const bf16*)dz, (const bf16*)w1, (bf16*)dx_perm,
+                                           nullptr, offsets, (long long)F * d, F, d, E, S_max,
+                                           s)));
+    // dW1[e] = dz^T x_perm  ([F][d]), with the gate's dW_gate / db over the kept rows
+    MOE_TRY((launch_wgrad<true>((const bf16*)dz, (const bf16*)x_perm, dw1, offsets, dsel_perm,
+                                dw_gate, db_gate, F, d, E, s)));
     return hipSuccess;
   }
   dim3 b(256);

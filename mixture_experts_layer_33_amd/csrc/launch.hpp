@@ -9,9 +9,13 @@ namespace moe {
 // ---- gate routing (route.hip)
 // logits = x * w_gate + b (float32); top-k with lowest-index ties; weights =
 // softmax over the selected logits.
+// bf16 without logits_in runs the router on MFMA and needs `wsplit`
+// (route_split_bytes) for the split copy of W_gate.
 hipError_t launch_route(int act, const void* x, const float* w_gate, const float* b_gate,
                         const float* logits_in, float* logits_out, int32_t* topk_idx,
-                        float* topk_w, int T, int d, int E, int k, hipStream_t s);
+                        float* topk_w, int T, int d, int E, int k, void* wsplit, hipStream_t s);
+int route_padded_experts(int E);
+size_t route_split_bytes(int d, int E);
 
 // ---- input encode (permute.hip)
 // Per tile of kRankTile slots: stable rank of each slot among the tile's
@@ -23,9 +27,11 @@ hipError_t launch_rank_hist(const int32_t* topk_idx, int S, int E, int32_t* loca
 hipError_t launch_scan(const int32_t* hist, int n_tiles, int E, int C, int32_t* tile_base,
                        int32_t* counts_raw, int32_t* counts_kept, hipStream_t s);
 // slot_row, row_token, offsets and the row copy x -> x_perm.
+// Dropped slots are listed after the kept rows: row_token[S_kept + j].
 hipError_t launch_gather(int act, const void* x, const int32_t* topk_idx,
                          const int32_t* local_rank, const int32_t* tile_base,
-                         const int32_t* counts_kept, int n_tiles, int T, int d, int E, int k,
+                         const int32_t* counts_raw, const int32_t* counts_kept, int n_tiles,
+                         int T, int d, int E, int k,
                          int C, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
                          void* x_perm, hipStream_t s);
 
@@ -35,17 +41,21 @@ hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,
 hipError_t launch_combine_bwd(int act, const void* dy, const void* out_perm,
                               const float* topk_w, const int32_t* topk_idx,
                               const int32_t* slot_row, void* d_out, float* dsel,
-                              float* dlogits, int T, int d, int E, int k, hipStream_t s);
+                              float* dsel_perm, float* dlogits, int T, int d, int E, int k,
+                              hipStream_t s);
 hipError_t launch_transpose_gate(const float* w_gate, float* w_gate_t, int d, int E,
                                  hipStream_t s);
 hipError_t launch_dx(int act, const void* dx_perm, const float* dsel, const int32_t* topk_idx,
                      const int32_t* slot_row, const float* w_gate_t, void* dx, int T, int d,
                      int k, hipStream_t s);
-int gate_grad_chunks(int T);
-size_t gate_grad_partial_floats(int T, int d, int E);
-hipError_t launch_gate_grad(int act, const void* x, const float* dsel, const int32_t* topk_idx,
-                            float* partial, float* dw_gate, float* db_gate, int T, int d, int E,
-                            int k, hipStream_t s);
+// dW_gate / db over each expert's packed rows (float32 path) ...
+hipError_t launch_gate_rows(int act, const void* x_perm, const float* dsel_perm,
+                            const int32_t* offsets, float* dw_gate, float* db_gate, int d, int E,
+                            hipStream_t s);
+// ... plus the dropped slots listed after the kept rows in row_token.
+hipError_t launch_gate_dropped(int act, const void* x, const float* dsel, const int32_t* topk_idx,
+                               const int32_t* offsets, const int32_t* row_token, float* dw_gate,
+                               float* db_gate, int S, int d, int E, int k, hipStream_t s);
 hipError_t launch_popularity(int E, int window, int64_t iter, const int32_t* counts_raw,
                              int32_t* ring, int32_t* window_sum, hipStream_t s);
 
@@ -56,9 +66,11 @@ hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets
                              int S_max, int d, int F, int E, hipStream_t s);
 // Backward GEMMs: dz = (dO W2[e]) * [h > 0]; dW2[e] = dO^T h;
 // dx_perm = dz W1[e]; dW1[e] = dz^T x_perm.
+// bf16 also folds dW_gate / db over the kept rows into the FC1 wgrad.
 hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, const void* h,
                              const int32_t* offsets, const void* w1, const void* w2,
-                             void* dz, void* dx_perm, float* dw1, float* dw2, int S_max,
+                             void* dz, void* dx_perm, float* dw1, float* dw2,
+                             const float* dsel_perm, float* dw_gate, float* db_gate, int S_max,
                              int d, int F, int E, hipStream_t s);
 
 }  // namespace moe

@@ -52,13 +52,17 @@ struct PermWs {
   int32_t* local_rank;  // [S]
   int32_t* hist;        // [E][n_tiles]
   int32_t* tile_base;   // [E][n_tiles]
-  int32_t* counts_tmp;  // [E]
+  int32_t* raw_tmp;     // [E] raw counts when the caller passes none
+  int32_t* kept_tmp;    // [E] kept counts when the caller passes none
+  void* wsplit;         // [3][EP][d] bf16 split router weights (bf16 only)
 };
 
 size_t perm_ws_bytes(const moe_shape* s) {
   const size_t S = (size_t)slots(s);
   const size_t nt = (size_t)rank_tiles(s) * (size_t)s->E;
-  return align_up(S * 4) + 2 * align_up(nt * 4) + align_up((size_t)s->E * 4);
+  size_t b = align_up(S * 4) + 2 * align_up(nt * 4) + 2 * align_up((size_t)s->E * 4);
+  if (s->act_dtype == MOE_BF16) b += align_up(route_split_bytes(s->d_model, s->E));
+  return b;
 }
 
 PermWs carve_perm(const moe_shape* s, void* ws) {
@@ -72,23 +76,26 @@ PermWs carve_perm(const moe_shape* s, void* ws) {
   p += align_up(nt * 4);
   w.tile_base = reinterpret_cast<int32_t*>(p);
   p += align_up(nt * 4);
-  w.counts_tmp = reinterpret_cast<int32_t*>(p);
+  w.raw_tmp = reinterpret_cast<int32_t*>(p);
+  p += align_up((size_t)s->E * 4);
+  w.kept_tmp = reinterpret_cast<int32_t*>(p);
+  p += align_up((size_t)s->E * 4);
+  w.wsplit = (s->act_dtype == MOE_BF16) ? p : nullptr;
   return w;
 }
 
 struct BwdWs {
   void* d_out;      // [S][d] act (later dx_perm)
   void* dz;         // [S][F] act
-  float* dsel;      // [T][k]
+  float* dsel;      // [T][k]  gate-softmax gradient per slot
+  float* dsel_perm; // [S]     the same per packed row
   float* w_gate_t;  // [E][d]
-  float* partial;   // gate-gradient chunk partials
 };
 
 size_t bwd_ws_bytes(const moe_shape* s) {
   const size_t S = (size_t)slots(s), a = act_bytes(s);
-  return align_up(S * s->d_model * a) + align_up(S * s->d_ff * a) +
-         align_up((size_t)s->T * s->k * 4) + align_up((size_t)s->E * s->d_model * 4) +
-         align_up(gate_grad_partial_floats(s->T, s->d_model, s->E) * 4);
+  return align_up(S * s->d_model * a) + align_up(S * s->d_ff * a) + 2 * align_up(S * 4) +
+         align_up((size_t)s->E * s->d_model * 4);
 }
 
 BwdWs carve_bwd(const moe_shape* s, void* ws) {
@@ -100,10 +107,10 @@ BwdWs carve_bwd(const moe_shape* s, void* ws) {
   w.dz = p;
   p += align_up(S * s->d_ff * a);
   w.dsel = reinterpret_cast<float*>(p);
-  p += align_up((size_t)s->T * s->k * 4);
+  p += align_up(S * 4);
+  w.dsel_perm = reinterpret_cast<float*>(p);
+  p += align_up(S * 4);
   w.w_gate_t = reinterpret_cast<float*>(p);
-  p += align_up((size_t)s->E * s->d_model * 4);
-  w.partial = reinterpret_cast<float*>(p);
   return w;
 }
 
@@ -138,11 +145,11 @@ moe_status do_route(const moe_shape* s, const void* x, const float* w_gate, cons
                     const float* logits_in, float* logits_out, int32_t* idx, float* w,
                     int32_t* counts_raw, int32_t* counts_kept, const PermWs& pw, hipStream_t st) {
   MOE_HIP(launch_route(s->act_dtype, x, w_gate, b_gate, logits_in, logits_out, idx, w, s->T,
-                       s->d_model, s->E, s->k, st));
+                       s->d_model, s->E, s->k, pw.wsplit, st));
   const int nt = rank_tiles(s);
   MOE_HIP(launch_rank_hist(idx, (int)slots(s), s->E, pw.local_rank, pw.hist, nt, st));
-  MOE_HIP(launch_scan(pw.hist, nt, s->E, capacity_of(s), pw.tile_base, counts_raw,
-                      counts_kept ? counts_kept : pw.counts_tmp, st));
+  MOE_HIP(launch_scan(pw.hist, nt, s->E, capacity_of(s), pw.tile_base, counts_raw, counts_kept,
+                      st));
   return MOE_OK;
 }
 
@@ -202,7 +209,7 @@ moe_status moe_route(const moe_shape* s, const void* x, const float* w_gate, con
   if ((st = check_ws(s, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
   PermWs pw = carve_perm(s, ws);
   return do_route(s, x, w_gate, b_gate, logits_in, logits_out, topk_idx, topk_w, counts_raw,
-                  nullptr, pw, as_stream(stream));
+                  pw.kept_tmp, pw, as_stream(stream));
 }
 
 moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_idx,
@@ -219,10 +226,11 @@ moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_id
   hipStream_t stream_ = as_stream(stream);
   const int nt = rank_tiles(s);
   const int C = capacity_of(s);
+  int32_t* raw = counts_raw ? counts_raw : pw.raw_tmp;
   MOE_HIP(launch_rank_hist(topk_idx, (int)slots(s), s->E, pw.local_rank, pw.hist, nt, stream_));
-  MOE_HIP(launch_scan(pw.hist, nt, s->E, C, pw.tile_base, counts_raw, counts_kept, stream_));
-  MOE_HIP(launch_gather(s->act_dtype, x, topk_idx, pw.local_rank, pw.tile_base, counts_kept, nt,
-                        s->T, s->d_model, s->E, s->k, C, offsets, slot_row, row_token, x_perm,
+  MOE_HIP(launch_scan(pw.hist, nt, s->E, C, pw.tile_base, raw, counts_kept, stream_));
+  MOE_HIP(launch_gather(s->act_dtype, x, topk_idx, pw.local_rank, pw.tile_base, raw, counts_kept,
+                        nt, s->T, s->d_model, s->E, s->k, C, offsets, slot_row, row_token, x_perm,
                         stream_));
   return MOE_OK;
 }
@@ -265,12 +273,13 @@ moe_status moe_forward(const moe_shape* s, const void* x, const float* w_gate,
   if ((st = check_ws(s, MOE_OP_FORWARD, ws, ws_bytes)) != MOE_OK) return st;
   PermWs pw = carve_perm(s, ws);
   hipStream_t stream_ = as_stream(stream);
-  st = do_route(s, x, w_gate, b_gate, nullptr, logits_out, topk_idx, topk_w, counts_raw,
-                counts_kept, pw, stream_);
+  int32_t* raw = counts_raw ? counts_raw : pw.raw_tmp;
+  st = do_route(s, x, w_gate, b_gate, nullptr, logits_out, topk_idx, topk_w, raw, counts_kept, pw,
+                stream_);
   if (st != MOE_OK) return st;
   const int nt = rank_tiles(s);
-  MOE_HIP(launch_gather(s->act_dtype, x, topk_idx, pw.local_rank, pw.tile_base, counts_kept, nt,
-                        s->T, s->d_model, s->E, s->k, capacity_of(s), offsets, slot_row,
+  MOE_HIP(launch_gather(s->act_dtype, x, topk_idx, pw.local_rank, pw.tile_base, raw, counts_kept,
+                        nt, s->T, s->d_model, s->E, s->k, capacity_of(s), offsets, slot_row,
                         row_token, x_perm, stream_));
   MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, (int)slots(s),
                             s->d_model, s->d_ff, s->E, stream_));
@@ -296,17 +305,22 @@ moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const
   hipStream_t stream_ = as_stream(stream);
   const int act = s->act_dtype;
   MOE_HIP(launch_combine_bwd(act, dy, out_perm, topk_w, topk_idx, slot_row, bw.d_out, bw.dsel,
-                             dlogits, s->T, s->d_model, s->E, s->k, stream_));
+                             bw.dsel_perm, dlogits, s->T, s->d_model, s->E, s->k, stream_));
   // dx_perm reuses d_out's memory: the FC1 dgrad runs after the FC2 wgrad,
-  // the last reader of d_out.
+  // the last reader of d_out.  For bf16 the FC1 wgrad also writes dW_gate and
+  // db over the kept rows.
   MOE_HIP(launch_expert_bwd(act, bw.d_out, x_perm, h, offsets, w1, w2, bw.dz, bw.d_out, dw1, dw2,
-                            (int)slots(s), s->d_model, s->d_ff, s->E, stream_));
+                            bw.dsel_perm, dw_gate, db_gate, (int)slots(s), s->d_model, s->d_ff,
+                            s->E, stream_));
+  if (act != MOE_BF16)
+    MOE_HIP(launch_gate_rows(act, x_perm, bw.dsel_perm, offsets, dw_gate, db_gate, s->d_model,
+                             s->E, stream_));
+  if (capacity_of(s) < s->T)  // slots can be dropped: add their gate gradient
+    MOE_HIP(launch_gate_dropped(act, x, bw.dsel, topk_idx, offsets, row_token, dw_gate, db_gate,
+                                (int)slots(s), s->d_model, s->E, s->k, stream_));
   MOE_HIP(launch_transpose_gate(w_gate, bw.w_gate_t, s->d_model, s->E, stream_));
   MOE_HIP(launch_dx(act, bw.d_out, bw.dsel, topk_idx, slot_row, bw.w_gate_t, dx, s->T,
                     s->d_model, s->k, stream_));
-  MOE_HIP(launch_gate_grad(act, x, bw.dsel, topk_idx, bw.partial, dw_gate, db_gate, s->T,
-                           s->d_model, s->E, s->k, stream_));
-  (void)row_token;
   return MOE_OK;
 }
 

@@ -21,6 +21,9 @@
 //     in its expert is tile base + in-tile rank; it is kept iff that
 //     position is below C.  One wavefront per token reads the token's row
 //     once and writes it to each of its kept rows with 16-byte accesses.
+//     Dropped slots are listed after the kept rows, ordered by expert and
+//     then position: row_token[S_kept + j] = slot index (the backward needs
+//     them for the gate gradient).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -104,17 +107,24 @@ template <typename ActT>
 __global__ void __launch_bounds__(kGatherThreads)
 gather_kernel(const ActT* __restrict__ x, const int32_t* __restrict__ topk_idx,
               const int32_t* __restrict__ local_rank, const int32_t* __restrict__ tile_base,
-              const int32_t* __restrict__ counts_kept, int n_tiles, int T, int d, int E, int k,
-              int C, int32_t* __restrict__ offsets, int32_t* __restrict__ slot_row,
-              int32_t* __restrict__ row_token, ActT* __restrict__ x_perm) {
+              const int32_t* __restrict__ counts_raw, const int32_t* __restrict__ counts_kept,
+              int n_tiles, int T, int d, int E, int k, int C, int32_t* __restrict__ offsets,
+              int32_t* __restrict__ slot_row, int32_t* __restrict__ row_token,
+              ActT* __restrict__ x_perm) {
   __shared__ int off[MOE_MAX_EXPERTS + 1];
+  __shared__ int doff[MOE_MAX_EXPERTS + 1];
   __shared__ int scratch[kGatherThreads / 64 + 1];
   {
     const int e = threadIdx.x;
-    const int v = (e < E) ? counts_kept[e] : 0;
-    int total;
-    const int ex = block_exclusive_scan(v, scratch, &total);
-    if (e < E) off[e] = ex;
+    const int kept = (e < E) ? counts_kept[e] : 0;
+    const int drop = (e < E) ? counts_raw[e] - kept : 0;
+    int total, dtotal;
+    const int ex = block_exclusive_scan(kept, scratch, &total);
+    const int dex = block_exclusive_scan(drop, scratch, &dtotal);
+    if (e < E) {
+      off[e] = ex;
+      doff[e] = total + dex;  // dropped slots are listed after the kept rows
+    }
     if (e == 0) off[E] = total;
     __syncthreads();
     if (blockIdx.x == 0) {
@@ -130,9 +140,13 @@ gather_kernel(const ActT* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const int s = t * k + lane;
     const int e = topk_idx[s];
     const int pos = tile_base[(size_t)e * n_tiles + s / kRankTile] + local_rank[s];
-    if (pos < C) my_row = off[e] + pos;
+    if (pos < C) {
+      my_row = off[e] + pos;
+      row_token[my_row] = t;
+    } else {
+      row_token[doff[e] + pos - C] = s;
+    }
     slot_row[s] = my_row;
-    if (my_row >= 0) row_token[my_row] = t;
   }
   int rows[MOE_MAX_TOPK];
 #pragma unroll
@@ -166,18 +180,18 @@ hipError_t launch_scan(const int32_t* hist, int n_tiles, int E, int C, int32_t* 
 
 hipError_t launch_gather(int act, const void* x, const int32_t* topk_idx,
                          const int32_t* local_rank, const int32_t* tile_base,
-                         const int32_t* counts_kept, int n_tiles, int T, int d, int E, int k,
-                         int C, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
-                         void* x_perm, hipStream_t s) {
+                         const int32_t* counts_raw, const int32_t* counts_kept, int n_tiles,
+                         int T, int d, int E, int k, int C, int32_t* offsets, int32_t* slot_row,
+                         int32_t* row_token, void* x_perm, hipStream_t s) {
   dim3 grid((T + 3) / 4), block(kGatherThreads);
   if (act == MOE_BF16)
     hipLaunchKernelGGL(gather_kernel<bf16>, grid, block, 0, s, (const bf16*)x, topk_idx,
-                       local_rank, tile_base, counts_kept, n_tiles, T, d, E, k, C, offsets,
-                       slot_row, row_token, (bf16*)x_perm);
+                       local_rank, tile_base, counts_raw, counts_kept, n_tiles, T, d, E, k, C,
+                       offsets, slot_row, row_token, (bf16*)x_perm);
   else
     hipLaunchKernelGGL(gather_kernel<float>, grid, block, 0, s, (const float*)x, topk_idx,
-                       local_rank, tile_base, counts_kept, n_tiles, T, d, E, k, C, offsets,
-                       slot_row, row_token, (float*)x_perm);
+                       local_rank, tile_base, counts_raw, counts_kept, n_tiles, T, d, E, k, C,
+                       offsets, slot_row, row_token, (float*)x_perm);
   return hipGetLastError();
 }
 

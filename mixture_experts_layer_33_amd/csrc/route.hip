@@ -4,10 +4,11 @@
 // routing is the first step of the expert-parallel pipeline; PopFetcher
 // notes §2.1.2: each token goes to its top-k experts, k usually 1 or 2.
 //
-// One workgroup handles kRouteTok tokens.  The router product runs in
-// float32 FMA with W_gate staged through LDS; each token's logits then sit
-// in one 16-lane group, which selects the top k by k rounds of a 16-lane
-// (value, index) max reduction.
+// Two router kernels: for bf16 activations an MFMA kernel (three exact bf16
+// parts of W_gate, below); for float32 activations, or when the caller
+// passes the logits, a float32 FMA kernel with W_gate staged through LDS.  In
+// both, each token's logits sit in one 16-lane group, which selects the top k
+// by k rounds of a 16-lane (value, index) max reduction.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -124,9 +125,219 @@ route_kernel(const ActT* __restrict__ x, const float* __restrict__ w_gate,
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 activations: the router product on MFMA.  W_gate (float32) is split
+// exactly into three bf16 parts, W = hi + mid + lo (each part takes the next
+// 8 bits of the 24-bit significand), stored transposed as [3][EP][d] with
+// EP = E rounded up to 16 (extra rows zero).  bf16 x times each bf16 part is
+// exact in float32, so logits = sum over the three parts of x W_p with
+// float32 accumulation: float32 accuracy at matrix-core rate.
+__global__ void split_gate_kernel(const float* __restrict__ w_gate, bf16* __restrict__ wsplit,
+                                  int d, int E, int EP) {
+  __shared__ float tile[32][33];
+  const int i0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int r = ty; r < 32; r += 8) {
+    const int i = i0 + r, e = e0 + tx;
+    tile[r][tx] = (i < d && e < E) ? w_gate[(size_t)i * E + e] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int e = e0 + r, i = i0 + tx;
+    if (e < EP && i < d) {
+      const float v = tile[tx][r];
+      const bf16 hi = (bf16)v;
+      const float r1 = v - (float)hi;
+      const bf16 mid = (bf16)r1;
+      const bf16 lo = (bf16)(r1 - (float)mid);
+      const size_t plane = (size_t)EP * d;
+      wsplit[(size_t)e * d + i] = hi;
+      wsplit[plane + (size_t)e * d + i] = mid;
+      wsplit[2 * plane + (size_t)e * d + i] = lo;
+    }
+  }
+}
+
+constexpr int kRouteMfmaTok = 64;  // tokens per workgroup, 16 per wavefront
+
+// LDS row of BK bf16 (BK/8 16-byte chunks), chunks XOR-swizzled by row.
+template <int BK>
+__device__ __forceinline__ int rswz(int row, int kc) {
+  return row * BK + ((kc ^ (row & (BK / 8 - 1))) * 8);
+}
+
+template <int EP>
+__global__ void __launch_bounds__(256)
+route_mfma_kernel(const bf16* __restrict__ x, const bf16* __restrict__ wsplit,
+                  const float* __restrict__ b_gate, float* __restrict__ logits_out,
+                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int d, int E,
+                  int k) {
+  constexpr int BK = EP > 128 ? 32 : 64;
+  constexpr int FN = EP / 16;
+  constexpr int ROWS = 3 * EP;                    // LDS rows per stage
+  constexpr int CPR = BK / 8;                     // chunks per row
+  constexpr int NQ = ROWS * CPR;                  // chunks per stage
+  constexpr int NCH = (NQ + 255) / 256;           // chunks per thread
+  __shared__ __attribute__((aligned(16))) bf16 lds[2][ROWS * BK];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int t0 = blockIdx.x * kRouteMfmaTok + wid * 16;
+  const int ta = min(t0 + (lane & 15), T - 1);  // A-fragment row (clamped)
+  const bf16* xrow = x + (size_t)ta * d;
+  f32x4 acc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  i32x4 stage[NCH];
+  auto load_stage = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int q = tid + c * 256, row = q / CPR, kc = q % CPR;
+      if (NQ % 256 == 0 || q < NQ)
+        stage[c] = *reinterpret_cast<const i32x4*>(wsplit + (size_t)row * d + k0 + kc * 8);
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int q = tid + c * 256, row = q / CPR, kc = q % CPR;
+      if (NQ % 256 == 0 || q < NQ) *reinterpret_cast<i32x4*>(&lds[buf][rswz<BK>(row, kc)]) = stage[c];
+    }
+  };
+  const int nk = d / BK;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_stage((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int kc = ks * 4 + (lane >> 4);
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8*>(xrow + kt * BK + kc * 8);
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int row = p * EP + j * 16 + (lane & 15);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&lds[cur][rswz<BK>(row, kc)]);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        }
+    }
+    if (kt + 1 < nk) store_stage(cur ^ 1);
+    __syncthreads();
+  }
+
+  // lane holds tokens t0 + (lane/16)*4 + i (i < 4), experts j*16 + lane%16
+  const int g = lane & 15;
+  float bias[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int e = j * 16 + g;
+    bias[j] = (e < E) ? b_gate[e] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + (lane >> 4) * 4 + i;
+    float v[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) v[j] = acc[j][i] + bias[j];
+    if (logits_out != nullptr && t < T) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int e = j * 16 + g;
+        if (e < E) logits_out[(size_t)t * E + e] = v[j];
+      }
+    }
+    unsigned taken = 0;
+    float sv[MOE_MAX_TOPK];
+    int si[MOE_MAX_TOPK];
+    for (int r = 0; r < k; ++r) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int e = j * 16 + g;
+        if (e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
+          bv = v[j];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 15) == g) taken |= 1u << (bi >> 4);
+      sv[r] = bv;
+      si[r] = bi;
+    }
+    if (g == 0 && t < T) {
+      float pr[MOE_MAX_TOPK];
+      float sum = 0.f;
+      for (int r = 0; r < k; ++r) {
+        pr[r] = expf(sv[r] - sv[0]);
+        sum += pr[r];
+      }
+      const float inv = 1.0f / sum;
+      for (int r = 0; r < k; ++r) {
+        topk_idx[(size_t)t * k + r] = si[r];
+        topk_w[(size_t)t * k + r] = pr[r] * inv;
+      }
+    }
+  }
+}
+
+int route_padded_experts(int E) {
+  int ep = 16;
+  while (ep < E) ep *= 2;
+  return ep;
+}
+
+size_t route_split_bytes(int d, int E) {
+  return (size_t)3 * route_padded_experts(E) * d * sizeof(bf16);
+}
+
 hipError_t launch_route(int act, const void* x, const float* w_gate, const float* b_gate,
                         const float* logits_in, float* logits_out, int32_t* topk_idx,
-                        float* topk_w, int T, int d, int E, int k, hipStream_t s) {
+                        float* topk_w, int T, int d, int E, int k, void* wsplit, hipStream_t s) {
+  if (act == MOE_BF16 && logits_in == nullptr) {
+    const int EP = route_padded_experts(E);
+    hipLaunchKernelGGL(split_gate_kernel, dim3((d + 31) / 32, (EP + 31) / 32), dim3(256), 0, s,
+                       w_gate, (bf16*)wsplit, d, E, EP);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    dim3 grid((T + kRouteMfmaTok - 1) / kRouteMfmaTok), block(256);
+    const bf16* xs = (const bf16*)x;
+    const bf16* wsp = (const bf16*)wsplit;
+    switch (EP) {
+      case 16:
+        hipLaunchKernelGGL(route_mfma_kernel<16>, grid, block, 0, s, xs, wsp, b_gate, logits_out,
+                           topk_idx, topk_w, T, d, E, k);
+        break;
+      case 32:
+        hipLaunchKernelGGL(route_mfma_kernel<32>, grid, block, 0, s, xs, wsp, b_gate, logits_out,
+                           topk_idx, topk_w, T, d, E, k);
+        break;
+      case 64:
+        hipLaunchKernelGGL(route_mfma_kernel<64>, grid, block, 0, s, xs, wsp, b_gate, logits_out,
+                           topk_idx, topk_w, T, d, E, k);
+        break;
+      case 128:
+        hipLaunchKernelGGL(route_mfma_kernel<128>, grid, block, 0, s, xs, wsp, b_gate, logits_out,
+                           topk_idx, topk_w, T, d, E, k);
+        break;
+      default:
+        hipLaunchKernelGGL(route_mfma_kernel<256>, grid, block, 0, s, xs, wsp, b_gate, logits_out,
+                           topk_idx, topk_w, T, d, E, k);
+        break;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((T + kRouteTok - 1) / kRouteTok), block(kRouteThreads);
   if (act == MOE_BF16)
     hipLaunchKernelGGL(route_kernel<bf16>, grid, block, 0, s, (const bf16*)x, w_gate, b_gate,

@@ -83,6 +83,10 @@ def test_permute_bitexact(name):
     n = int(ref["offsets"][-1])
     np.testing.assert_array_equal(down(layer.row_token)[:n], ref["row_token"])
     np.testing.assert_array_equal(down(layer.x_perm)[:n], orc.encode(inp["x"], ref["row_token"]))
+    # dropped slots listed after the kept rows, by expert then slot
+    flat = idx.reshape(-1)
+    dropped = sorted(np.where(ref["slot_row"] < 0)[0].tolist(), key=lambda s: (flat[s], s))
+    np.testing.assert_array_equal(down(layer.row_token)[n:n + len(dropped)], dropped)
     if name.startswith("uniform_cf0") or name == "uniform_cf100":
         assert ref["drops"] > 0
 
