@@ -43,145 +43,162 @@ __device__ __forceinline__ int swz(int row, int kc) {
 }
 
 // ---------------------------------------------------------------------------
-// Operand tile loaders: global -> registers -> LDS [ROWS][64] (bf16).
-// K-contiguous operand: element (r, k) at base[r * ld + k], copied straight
-// from global memory into LDS (global_load_lds_dwordx4: each lane's 16 bytes
-// land at the wave's LDS base + 16 * lane).  One wave instruction fills 8 LDS
-// rows; lane L fills row r0 + L/8 at chunk position L%8, so it fetches the
-// logical chunk that the swizzle puts there.  Rows >= nrows read row
-// nrows-1 (their results are never stored).
+// Operand tiles, copied global -> LDS directly (global_load_lds_dwordx4: the
+// 16 bytes of lane L land at the wave's LDS base + 16 L; one wave instruction
+// fills 1 KiB).  Each lane fetches whichever global chunk the LDS swizzle
+// puts at its position.
+//
+// K-contiguous operand (element (r, k) at base[r * ld + k]): LDS [ROWS][64],
+// 16-byte chunk kc of row r at position kc ^ f(r); read back as one 16-byte
+// fragment per lane.  Rows >= nrows re-read row nrows-1 (never stored).
 template <int ROWS>
-struct LoadK {
-  static constexpr int N = ROWS / 32;  // wave instructions per thread
-  uint32_t off[N];                     // byte offsets from the tile base (fixed over k)
-  int ready = 0;
-  __device__ void issue(const bf16* base, int ld, int nrows, int k0, int, bf16* lds) {
+struct TileK {
+  static constexpr int N = ROWS / 32;  // wave instructions per thread per stage
+  uint32_t off[N];                     // byte offsets from the stage base
+  __device__ void init(int ld, int nrows) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    if (!ready) {
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int row = (i * 4 + wid) * 8 + (lane >> 3), p = lane & 7;
-        const int kc = p ^ ((row ^ (row >> 3) ^ (row >> 6)) & 7);
-        off[i] = (uint32_t)(((size_t)min(row, nrows - 1) * ld + kc * 8) * sizeof(bf16));
-      }
-      ready = 1;
-    }
-    const char* b = reinterpret_cast<const char*>(base + k0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int r0 = (i * 4 + wid) * 8;
-      __builtin_amdgcn_global_load_lds(
-          b + off[i], (__attribute__((address_space(3))) void*)(lds + r0 * kBK), 16, 0, 0);
+      const int row = (i * 4 + wid) * 8 + (lane >> 3), p = lane & 7;
+      const int kc = p ^ ((row ^ (row >> 3) ^ (row >> 6)) & 7);
+      off[i] = (uint32_t)(((size_t)min(row, nrows - 1) * ld + kc * 8) * sizeof(bf16));
     }
   }
-  __device__ void commit(bf16*) const {}
+  // stage with k in [k0, k0 + 64)
+  __device__ void issue(const bf16* base, int ld, int k0, int, bf16* lds) const {
+    const int wid = threadIdx.x >> 6;
+    const char* b = reinterpret_cast<const char*>(base + k0);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      __builtin_amdgcn_global_load_lds(
+          b + off[i], (__attribute__((address_space(3))) void*)(lds + (i * 4 + wid) * 8 * kBK),
+          16, 0, 0);
+  }
+  // 32 x 16 MFMA operand block at rows r0..r0+31, k = kk*16 ..: lane l holds
+  // row r0 + l%32, the 8 consecutive k from kk*16 + 8*(l/32)
+  __device__ static bf16x8 frag(const bf16* lds, int r0, int kk) {
+    const int lane = threadIdx.x & 63;
+    return *reinterpret_cast<const bf16x8*>(lds + swz(r0 + (lane & 31), kk * 2 + (lane >> 5)));
+  }
 };
 
-// MN-contiguous operand: element (r, k) at base[k * ld + r].  Each thread
-// loads KB consecutive k of 8 consecutive r and writes them transposed.
-// k >= kmax reads as zero; r >= nrows is clamped (never stored).
+// MN-contiguous operand (element (r, k) at base[k * ld + r]): LDS [64][ROWS]
+// as in memory, 16-byte chunk c of k-row k at position c ^ sw(k), read back
+// transposed by ds_read_b64_tr_b16.  Within each 16-lane group that
+// instruction hands lane i the elements M[4j + i/4][i%4] (j = 0..3) of the
+// 4-element pieces M[r] addressed by the group's lanes r; addressing k-row
+// kb + r/4, columns c0 + 4 (r%4) gives lane i four consecutive k of column
+// c0 + i.  Two reads give the 8 k of a fragment, in the same k order as the
+// K-contiguous fragments.  k rows >= kmax re-read row kmax-1 (zeroed in the
+// fragment where it matters); columns >= ncols re-read valid columns.
 template <int ROWS>
-struct LoadMN {
-  static constexpr int RB = ROWS / 8;                 // 8-row blocks
-  static constexpr int KB = kBK * RB / kGemmThreads;  // k per thread (4 or 8)
-  i32x4 v[KB];  // v[i] = 8 bf16 of k-row i, two per dword
-  __device__ void load(const bf16* base, int ld, int nrows, int k0, int kmax) {
-    const int rb = threadIdx.x % RB, kb = threadIdx.x / RB;
-    const int r = min(rb * 8, nrows - 8);
+struct TileMN {
+  static constexpr int R = ROWS * 2;          // bytes per k-row
+  static constexpr int CPR = R / 16;          // chunks per k-row
+  static constexpr int RPI = 1024 / R;        // k-rows per wave instruction
+  static constexpr int N = 64 / RPI / 4;      // wave instructions per thread per stage
+  __device__ static int sw(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
+  int kl[N];       // k-row of this lane's chunk, within the stage
+  uint32_t col[N]; // byte offset of its column chunk
+  __device__ void init(int ld, int ncols) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const int k = k0 + kb * KB + i;
-      if (k < kmax)
-        v[i] = *reinterpret_cast<const i32x4*>(base + (size_t)k * ld + r);
-      else
-        v[i] = i32x4{0, 0, 0, 0};
+    for (int i = 0; i < N; ++i) {
+      const int k = (i * 4 + wid) * RPI + lane / CPR, p = lane % CPR;
+      const int c = min(p ^ sw(k), ncols / 8 - 1);
+      kl[i] = k;
+      col[i] = (uint32_t)(c * 8 * sizeof(bf16));
     }
   }
-  // (v[i] element m, v[i+1] element m) as one dword: low halves for even m,
-  // high halves for odd m.
-  __device__ static int pair(int lo_src, int hi_src, int odd) {
-    return (int)__builtin_amdgcn_perm((unsigned)hi_src, (unsigned)lo_src,
-                                      odd ? 0x07060302u : 0x05040100u);
-  }
-  // Gate side product: acc[m] += sum_i sel[k0 + kb*KB + i] * v[i][m] over
-  // this thread's KB rows (sel rows past kmax read as 0); db += sum_i sel.
-  __device__ void gate(const float* sel, int k0, int kmax, float* acc, float* db) const {
-    const int kb = threadIdx.x / RB;
+  __device__ void issue(const bf16* base, int ld, int k0, int kmax, bf16* lds) const {
+    const int wid = threadIdx.x >> 6;
+    const char* b = reinterpret_cast<const char*>(base + (size_t)k0 * ld);
+    const int kend = kmax - k0;  // rows of this stage that exist
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const int k = k0 + kb * KB + i;
-      const float g = (k < kmax) ? sel[k] : 0.f;
-      *db += g;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const unsigned u = (unsigned)v[i][p];
-        acc[2 * p] = fmaf(g, __uint_as_float(u << 16), acc[2 * p]);
-        acc[2 * p + 1] = fmaf(g, __uint_as_float(u & 0xffff0000u), acc[2 * p + 1]);
-      }
+    for (int i = 0; i < N; ++i) {
+      const int k = min(kl[i], kend - 1);
+      __builtin_amdgcn_global_load_lds(
+          b + (uint32_t)(k * ld * (int)sizeof(bf16)) + col[i],
+          (__attribute__((address_space(3))) void*)(lds + (i * 4 + wid) * RPI * ROWS), 16, 0, 0);
     }
   }
-  __device__ void store(bf16* lds) const {
-    const int rb = threadIdx.x % RB, kb = threadIdx.x / RB;
+  // Same operand block from the transposed layout: 16-lane group G = l/16
+  // covers columns r0 + 16*(G&1) .. +15 and k from kk*16 + 8*(G>>1); two
+  // transposed reads of 4 k each.
+  __device__ static bf16x8 frag(const bf16* lds, int r0, int kk) {
+    typedef __attribute__((ext_vector_type(4))) short s16x4;
+    typedef __attribute__((ext_vector_type(2))) int i32x2;
+    const int lane = threadIdx.x & 63, G = lane >> 4, r = lane & 15;
+    const int n = r0 + 16 * (G & 1) + 4 * (r & 3);
+    i32x4 out;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int row = rb * 8 + m, p = m >> 1, odd = m & 1;
-      if constexpr (KB == 8) {
-        i32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = pair(v[2 * q][p], v[2 * q + 1][p], odd);
-        *reinterpret_cast<i32x4*>(lds + swz(row, kb)) = o;
-      } else {
-        typedef __attribute__((ext_vector_type(2))) int i32x2;
-        i32x2 o;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) o[q] = pair(v[2 * q][p], v[2 * q + 1][p], odd);
-        *reinterpret_cast<i32x2*>(lds + swz(row, kb >> 1) + (kb & 1) * 4) = o;
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int k = kk * 16 + 8 * (G >> 1) + h * 4 + (r >> 2);
+      const int byte = k * R + (((n >> 3) ^ sw(k)) << 4) + (((n >> 2) & 1) << 3);
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)((const char*)lds + byte));
+      // reinterpret all 8 bytes at once (element-wise casts of this result
+      // have been seen to be lowered wrongly)
+      const i32x2 w = __builtin_bit_cast(i32x2, v);
+      out[2 * h] = w[0];
+      out[2 * h + 1] = w[1];
     }
+    return __builtin_bit_cast(bf16x8, out);
+  }
+  // zero fragment entries whose k (stage-relative) is >= kend
+  __device__ static void mask_k(bf16x8& f, int kk, int kend) {
+    const int k0 = kk * 16 + ((threadIdx.x & 63) >> 5) * 8;
+    i32x4 w = __builtin_bit_cast(i32x4, f);  // element 2q = low half of dword q
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const unsigned keep = (k0 + 2 * q < kend ? 0x0000ffffu : 0u) |
+                            (k0 + 2 * q + 1 < kend ? 0xffff0000u : 0u);
+      w[q] = (int)((unsigned)w[q] & keep);
+    }
+    f = __builtin_bit_cast(bf16x8, w);
+  }
+  // 16 bytes (8 columns) of k-row k at column chunk c, for the gate product
+  __device__ static bf16x8 chunk(const bf16* lds, int k, int c) {
+    return *reinterpret_cast<const bf16x8*>((const char*)lds + k * R + ((c ^ sw(k)) << 4));
   }
 };
 
 template <bool KMAJOR, int ROWS>
-struct Loader;
+struct Tile;
 template <int ROWS>
-struct Loader<true, ROWS> {
-  LoadK<ROWS> l;
-  __device__ void issue(const bf16* base, int ld, int nrows, int k0, int kmax, bf16* lds) {
-    l.issue(base, ld, nrows, k0, kmax, lds);
-  }
-  __device__ void commit(bf16* lds) const {}
-};
+struct Tile<true, ROWS> : TileK<ROWS> {};
 template <int ROWS>
-struct Loader<false, ROWS> {
-  LoadMN<ROWS> l;
-  __device__ void issue(const bf16* base, int ld, int nrows, int k0, int kmax, bf16*) {
-    l.load(base, ld, nrows, k0, kmax);
-  }
-  __device__ void commit(bf16* lds) const { l.store(lds); }
-};
-
-// Wait for this wave's outstanding global loads (including the ones that
-// write LDS directly) before a barrier publishes the LDS tile.
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+struct Tile<false, ROWS> : TileMN<ROWS> {};
 
 // ---------------------------------------------------------------------------
 // One output tile: C[BM x BN] = sum_k A(m, k) B(n, k), k in [0, K), on 4
-// wavefronts in a 2 x 2 grid, each owning a (BM/2) x (BN/2) block.  The MFMA
-// takes the B tile as its first operand and the A tile as its second, so its
-// 16 x 16 result block is C^T: lane l holds C[m][n..n+3] with m = l % 16 and
-// n = 4 * (l / 16) (+ block offsets), four consecutive columns of one row,
-// which the epilogue writes as one 8- or 16-byte store.
+// wavefronts in a 2 x 2 grid, each owning a (BM/2) x (BN/2) block of 32 x 32
+// MFMA blocks (v_mfma_f32_32x32x16_bf16: twice the work per issue of the
+// 16 x 16 x 32 form, which measured at about 60% of its rate here).  The
+// MFMA takes the B tile as its first operand and the A tile as its second,
+// so each result block is C^T: lane l holds C[m][n..n+3] with m = l % 32 and
+// n = 4 * (l / 32) + 8p, four consecutive columns of one row, which the
+// epilogue writes as one 8- or 16-byte store.
 //
-// With GATE (MN-contiguous B only) and a non-null `gsel`, the tile also
-// accumulates g[n] = sum_k gsel[k] B(n, k) for its columns from the B
-// registers on their way to LDS (gacc: per thread, its 8 columns over its
-// rows) and sum_k gsel[k] (gdb); see gate_reduce().
+// Pipeline: three LDS stages, one barrier per 64-deep k step; stage kt+2 is
+// in flight while stage kt is computed, and before the barrier each wave
+// waits only for its loads of stage kt+1 (vmcnt = one stage's count).
+//
+// With GATE (B MN-contiguous) and a non-null `gsel`, the tile also forms
+// g[n] = sum_k gsel[k] B(n, k) for its columns from the LDS stages (gacc: per
+// thread, 8 columns over its share of the rows) and sum_k gsel[k] (gdb);
+// see gate_reduce().
 template <int BM, int BN, bool A_K, bool B_K, bool GATE = false>
 struct TileGemm {
   static constexpr int WM = BM / 2, WN = BN / 2;  // 2 x 2 waves
-  static constexpr int FM = WM / 16, FN = WN / 16;
-  static constexpr size_t kLds = (size_t)2 * (BM + BN) * kBK * sizeof(bf16);
-  f32x4 acc[FN][FM];  // acc[i][j]: n-block i, m-block j
+  static constexpr int FM = WM / 32, FN = WN / 32;  // 32 x 32 MFMA blocks per wave
+  static constexpr size_t kStageBytes = (size_t)(BM + BN) * kBK * sizeof(bf16);
+  // three stages when they fit in LDS (next to ~2 KiB of scheduler state),
+  // else two
+  static constexpr int kStages = 3 * kStageBytes <= 152 * 1024 ? 3 : 2;
+  static constexpr int kStageOps = Tile<A_K, BM>::N + Tile<B_K, BN>::N;
+  static constexpr size_t kLdsPipe = (size_t)kStages * kStageBytes;
+  f32x16 acc[FN][FM];  // acc[i][j]: n-block i, m-block j
   float gacc[8];
   float gdb;
 
@@ -190,7 +207,7 @@ struct TileGemm {
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
     if constexpr (GATE) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) gacc[m] = 0.f;
@@ -198,64 +215,102 @@ struct TileGemm {
     }
     const int nk = (K + kBK - 1) / kBK;
     if (nk == 0) return;
-    bf16* const a_lds = lds;                      // [2][BM][kBK]
-    bf16* const b_lds = lds + 2 * BM * kBK;       // [2][BN][kBK]
-    Loader<A_K, BM> la;
-    Loader<B_K, BN> lb;
-    la.issue(A, lda, a_rows, 0, K, a_lds);
-    lb.issue(B, ldb, b_rows, 0, K, b_lds);
-    if constexpr (GATE) {
-      if (gsel) lb.l.gate(gsel, 0, K, gacc, &gdb);
-    }
-    la.commit(a_lds);
-    lb.commit(b_lds);
-    wait_vm();
-    __syncthreads();
+    bf16* const a_lds = lds;                          // [3][BM * 64]
+    bf16* const b_lds = lds + kStages * BM * kBK;     // [3][BN * 64]
+    Tile<A_K, BM> ta;
+    Tile<B_K, BN> tb;
+    ta.init(lda, a_rows);
+    tb.init(ldb, b_rows);
+    auto issue = [&](int kt) {
+      const int s = kt % kStages;
+      ta.issue(A, lda, kt * kBK, K, a_lds + s * (BM * kBK));
+      tb.issue(B, ldb, kt * kBK, K, b_lds + s * (BN * kBK));
+    };
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int wm = wid >> 1, wn = wid & 1;
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      bf16* const a_nxt = a_lds + (cur ^ 1) * (BM * kBK);
-      bf16* const b_nxt = b_lds + (cur ^ 1) * (BN * kBK);
-      if (more) {
-        if (A_K)
-          la.issue(A, lda, a_rows, (kt + 1) * kBK, K, a_nxt);
-        else
-          la.issue(A + (size_t)(kt + 1) * kBK * lda, lda, a_rows, 0, K - (kt + 1) * kBK, a_nxt);
-        if (B_K)
-          lb.issue(B, ldb, b_rows, (kt + 1) * kBK, K, b_nxt);
-        else
-          lb.issue(B + (size_t)(kt + 1) * kBK * ldb, ldb, b_rows, 0, K - (kt + 1) * kBK, b_nxt);
-      }
-      const bf16* as = a_lds + cur * (BM * kBK);
-      const bf16* bs = b_lds + cur * (BN * kBK);
+    constexpr int kGateRows = GATE ? kBK * (BN / 8) / kGemmThreads : 1;
+    float gv[kGateRows];
+    auto compute = [&](int kt) {
+      const int s = kt % kStages;
+      const bf16* as = a_lds + s * (BM * kBK);
+      const bf16* bs = b_lds + s * (BN * kBK);
+      const int kend = K - kt * kBK;  // < 64 only on a ragged last step
 #pragma unroll
-      for (int ks = 0; ks < kBK / 32; ++ks) {
+      for (int kk = 0; kk < kBK / 16; ++kk) {
         bf16x8 a[FM];
-        const int kc = ks * 4 + (lane >> 4);
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
-          const int r = wm * WM + j * 16 + (lane & 15);
-          a[j] = *reinterpret_cast<const bf16x8*>(as + swz(r, kc));
+          const int r0 = wm * WM + j * 32;
+          if constexpr (A_K) {
+            a[j] = TileK<BM>::frag(as, r0, kk);
+          } else {
+            a[j] = TileMN<BM>::frag(as, r0, kk);
+            if (kend < kBK) TileMN<BM>::mask_k(a[j], kk, kend);
+          }
         }
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-          const int r = wn * WN + i * 16 + (lane & 15);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(bs + swz(r, kc));
+          const int r0 = wn * WN + i * 32;
+          bf16x8 b;
+          if constexpr (B_K)
+            b = TileK<BN>::frag(bs, r0, kk);
+          else
+            b = TileMN<BN>::frag(bs, r0, kk);
 #pragma unroll
           for (int j = 0; j < FM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a[j], acc[i][j], 0, 0, 0);
         }
       }
-      if (more) {
-        if constexpr (GATE) {
-          if (gsel) lb.l.gate(gsel, (kt + 1) * kBK, K, gacc, &gdb);
+      if constexpr (GATE) {
+        if (gsel != nullptr) {
+          // thread: 8 columns (chunk c) of rows kg*kGateRows .. of this stage
+          const int c = threadIdx.x % (BN / 8), kg = threadIdx.x / (BN / 8);
+#pragma unroll
+          for (int q = 0; q < kGateRows; ++q) {
+            const int k = kg * kGateRows + q;
+            const float g = gv[q];
+            const bf16x8 v = TileMN<BN>::chunk(bs, k, c);
+            gdb += g;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) gacc[m] = fmaf(g, (float)v[m], gacc[m]);
+          }
         }
-        la.commit(a_nxt);
-        lb.commit(b_nxt);
       }
-      wait_vm();
+    };
+    // gate weights of stage kt's rows for this thread (loaded before the
+    // stage kt+2 copies are issued, so waiting for them never waits for those)
+    auto load_gate = [&](int kt) {
+      if constexpr (GATE) {
+        if (gsel != nullptr) {
+          const int kg = threadIdx.x / (BN / 8);
+#pragma unroll
+          for (int q = 0; q < kGateRows; ++q) {
+            const int k = kt * kBK + kg * kGateRows + q;
+            gv[q] = (k < K) ? gsel[k] : 0.f;
+          }
+        }
+      }
+    };
+    // stages 0 .. kStages-2 in flight before the loop; step kt issues stage
+    // kt + kStages - 1 and, before its barrier, waits for stage kt+1 (with
+    // three stages the one issued this step may stay in flight)
+    issue(0);
+    if (kStages == 3 && nk > 1) {
+      issue(1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageOps) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool ahead = kt + kStages - 1 < nk;
+      load_gate(kt);
+      if (ahead) issue(kt + kStages - 1);
+      compute(kt);
+      if (kStages == 3 && ahead)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageOps) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
   }
@@ -283,45 +338,49 @@ struct TileGemm {
     }
   }
 };
-
-// Epilogue: lane holds C[m][n..n+3] of each 16 x 16 block (see TileGemm).
-// rows/cols bound the valid part of the tile (cols is a multiple of 4).
+// Epilogue: in each 32 x 32 block lane l holds C[m][n..n+3] for m = l%32 and
+// n = 4*(l/32) + 8p (p = 0..3) (see TileGemm).  rows/cols bound the valid
+// part of the tile (cols is a multiple of 4).
 template <int EPI, class TG>
 __device__ __forceinline__ void store_tile(const TG& tg, void* C, int ldc, int rows, int cols,
                                            const bf16* aux, int ld_aux) {
-  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid >> 1, wn = wid & 1;
 #pragma unroll
   for (int j = 0; j < TG::FM; ++j) {
-    const int m = wm * TG::WM + j * 16 + (lane & 15);
+    const int m = wm * TG::WM + j * 32 + (lane & 31);
     if (m >= rows) continue;
 #pragma unroll
     for (int i = 0; i < TG::FN; ++i) {
-      const int n = wn * TG::WN + i * 16 + (lane >> 4) * 4;
-      if (n >= cols) continue;
-      f32x4 v = tg.acc[i][j];
-      if constexpr (EPI == EPI_F32) {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + (size_t)m * ldc + n) = v;
-      } else {
-        if constexpr (EPI == EPI_RELU) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = fmaxf(v[q], 0.f);
+      for (int p = 0; p < 4; ++p) {
+        const int n = wn * TG::WN + i * 32 + 4 * (lane >> 5) + 8 * p;
+        if (n >= cols) continue;
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = tg.acc[i][j][4 * p + q];
+        if constexpr (EPI == EPI_F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + (size_t)m * ldc + n) = v;
+        } else {
+          if constexpr (EPI == EPI_RELU) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = fmaxf(v[q], 0.f);
+          }
+          if constexpr (EPI == EPI_MASK) {
+            const bf16x4 hv = *reinterpret_cast<const bf16x4*>(aux + (size_t)m * ld_aux + n);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (!((float)hv[q] > 0.f)) v[q] = 0.f;
+          }
+          bf16x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = (bf16)v[q];
+          *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(C) + (size_t)m * ldc + n) = o;
         }
-        if constexpr (EPI == EPI_MASK) {
-          const bf16x4 hv = *reinterpret_cast<const bf16x4*>(aux + (size_t)m * ld_aux + n);
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (!((float)hv[q] > 0.f)) v[q] = 0.f;
-        }
-        bf16x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = (bf16)v[q];
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(C) + (size_t)m * ldc + n) = o;
       }
+      // keep the scheduler from hoisting every accumulator read to the top
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // keep the scheduler from hoisting every accumulator read to the top
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -505,6 +564,21 @@ f32_wgrad_kernel(const float* __restrict__ X1, const float* __restrict__ X2, flo
   }
 }
 
+// Every kernel variant the launchers can pick, instantiated explicitly (so
+// each is emitted whatever order the launchers reference them in).
+#define MOE_ROWS_VARIANTS(BM, BN)                                        \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU>(RowsArgs);   \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE>(RowsArgs);  \
+  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_MASK>(RowsArgs);  \
+  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_STORE>(RowsArgs); \
+  template __global__ void wgrad_kernel<BM, BN, false>(WgradArgs);               \
+  template __global__ void wgrad_kernel<BM, BN, true>(WgradArgs);
+MOE_ROWS_VARIANTS(256, 256)
+MOE_ROWS_VARIANTS(256, 128)
+MOE_ROWS_VARIANTS(128, 256)
+MOE_ROWS_VARIANTS(128, 128)
+#undef MOE_ROWS_VARIANTS
+
 // ---------------------------------------------------------------------------
 // launchers
 
@@ -516,7 +590,7 @@ struct Shape2 {
 template <class MT>
 static Shape2 pick_tile(MT mt, int N) {
   const long long want = 2 * 256;  // two tiles per CU
-  const Shape2 cand[] = {{256, 128}, {128, 256}, {128, 128}};
+  const Shape2 cand[] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}};
   for (const Shape2& c : cand) {
     const long long tiles = mt(c.bm) * (long long)((N + c.bn - 1) / c.bn);
     if (tiles >= want) return c;
@@ -531,7 +605,7 @@ static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
   const long long nt = (p.N + BN - 1) / BN;
   const long long grid = mt_max * nt;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  constexpr size_t shm = TileGemm<BM, BN, true, B_K>::kLds;
+  constexpr size_t shm = TileGemm<BM, BN, true, B_K>::kLdsPipe;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&rows_gemm_kernel<BM, BN, B_K, EPI>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
@@ -552,6 +626,7 @@ static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const bf16*
     return per * E;
   };
   const Shape2 t = pick_tile(mt, N);
+  if (t.bm == 256 && t.bn == 256) return launch_rows_t<256, 256, B_K, EPI>(p, S_max, s);
   if (t.bm == 256 && t.bn == 128) return launch_rows_t<256, 128, B_K, EPI>(p, S_max, s);
   if (t.bm == 128 && t.bn == 256) return launch_rows_t<128, 256, B_K, EPI>(p, S_max, s);
   return launch_rows_t<128, 128, B_K, EPI>(p, S_max, s);
@@ -560,7 +635,7 @@ static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const bf16*
 template <int BM, int BN, bool GATE>
 static hipError_t launch_wgrad_t(const WgradArgs& p, hipStream_t s) {
   const long long grid = (long long)p.E * ((p.N1 + BM - 1) / BM) * ((p.N2 + BN - 1) / BN);
-  constexpr size_t shm = TileGemm<BM, BN, false, false, GATE>::kLds;
+  constexpr size_t shm = TileGemm<BM, BN, false, false, GATE>::kLdsPipe;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&wgrad_kernel<BM, BN, GATE>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
@@ -577,6 +652,7 @@ static hipError_t launch_wgrad(const bf16* X1, const bf16* X2, float* C, const i
   WgradArgs p{X1, X2, C, offsets, gsel, dw_gate, db_gate, N1, N2, E};
   auto mt = [&](int bm) { return (long long)E * ((N1 + bm - 1) / bm); };
   const Shape2 t = pick_tile(mt, N2);
+  if (t.bm == 256 && t.bn == 256) return launch_wgrad_t<256, 256, GATE>(p, s);
   if (t.bm == 256 && t.bn == 128) return launch_wgrad_t<256, 128, GATE>(p, s);
   if (t.bm == 128 && t.bn == 256) return launch_wgrad_t<128, 256, GATE>(p, s);
   return launch_wgrad_t<128, 128, GATE>(p, s);
