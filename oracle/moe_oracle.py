@@ -354,3 +354,51 @@ def token_output(t: int, x, w, idx, slot_row, w1, w2, act: str) -> np.ndarray:
         _, o = expert_row(x[t], w1[e], w2[e], act)
         acc += float(w[t, j]) * o
     return round_act(acc, act)
+
+
+def token_backward(t: int, dy_t, x, w_gate, w1, w2, idx, w, slot_row, act: str):
+    """dX[t] and dlogits[t] for one token, evaluated from that token alone
+    (no packed buffers): for each kept slot j with expert e, O_j = FFN_e(x_t)
+    as stored, dg_j = <dy_t, O_j>, and the expert path adds
+    W1[e]^T ((W2[e]^T (w_j dy_t)) * [h_j > 0]); the gate path adds
+    sum_j dsel_j W_gate[:, e_j] with dsel_j = w_j (dg_j - sum_i w_i dg_i).
+    Returns (dx_t rounded to act, dlogits_t float32 [E])."""
+    k = idx.shape[1]
+    E = w1.shape[0]
+    dy_t = np.asarray(dy_t, F64)
+    wt = np.asarray(w[t], F64)
+    dg = np.zeros(k)
+    dx = np.zeros(x.shape[1])
+    for j in range(k):
+        if slot_row[t * k + j] < 0:
+            continue
+        e = int(idx[t, j])
+        h, o = expert_row(x[t], w1[e], w2[e], act)
+        dg[j] = float(dy_t @ o)
+        dz = (np.asarray(w2[e], F64).T @ (wt[j] * dy_t)) * (h > 0.0)
+        dx += np.asarray(w1[e], F64).T @ dz
+    dsel = wt * (dg - float((wt * dg).sum()))
+    dlog = np.zeros(E)
+    for j in range(k):
+        dlog[int(idx[t, j])] += dsel[j]
+        dx += dsel[j] * np.asarray(w_gate, F64)[:, int(idx[t, j])]
+    return round_act(dx, act), dlog.astype(F32)
+
+
+def expert_weight_grad_entries(e: int, rows_f, rows_i, x_perm_e, dy_tok, w_rows, w1e, w2e,
+                               act: str):
+    """Selected entries of one expert's weight gradients, each summed over all
+    of the expert's packed rows r (token t_r, gate weight w_r):
+      dW2[e][i][f] = sum_r (w_r dy[t_r, i]) h[r, f]
+      dW1[e][f][i] = sum_r dz[r, f] x_perm[r, i],  dz[r, f] = (dO[r] . W2[e][:, f]) [h[r, f] > 0]
+    computing only the needed columns of h and dz.  x_perm_e [M, d],
+    dy_tok [M, d] (dy of each row's token), w_rows [M].  Returns
+    (dW1 entries [len(rows_f), len(rows_i)], dW2 entries [len(rows_i), len(rows_f)])."""
+    xp = np.asarray(x_perm_e, F64)
+    dO = np.asarray(w_rows, F64)[:, None] * np.asarray(dy_tok, F64)
+    fs = list(rows_f)
+    h = round_act(np.maximum(xp @ np.asarray(w1e, F64)[fs].T, 0.0), act)   # [M, nf]
+    dz = (dO @ np.asarray(w2e, F64)[:, fs]) * (h > 0.0)                    # [M, nf]
+    dw1 = dz.T @ xp[:, list(rows_i)]                                        # [nf, ni]
+    dw2 = dO[:, list(rows_i)].T @ h                                         # [ni, nf]
+    return dw1, dw2

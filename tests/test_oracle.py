@@ -427,3 +427,40 @@ def test_workload_recipes():
     assert b.max() == 0.0 and np.isclose(b.min(), -np.log(w.E))
     x = workloads.make_x(workloads.scaled(ws["skewed_zipf12"], T=8))
     assert (workloads.round_to_bf16(x) == x).all()
+
+
+@pytest.mark.parametrize("cf", [0.0, 0.6])
+def test_token_backward_matches_full_backward(cf):
+    T, d, F, E, k = 40, 16, 24, 5, 2
+    x = rand((T, d), 50)
+    wg, b = rand((d, E), 51), rand((E,), 52)
+    w1, w2 = rand((E, F, d), 53, 0.4), rand((E, d, F), 54, 0.4)
+    dy = rand((T, d), 55)
+    fwd = orc.forward(x, wg, b, w1, w2, k, cf, "f64")
+    g = orc.backward(dy, fwd, x, wg, w1, w2, "f64")
+    for t in range(T):
+        dx_t, dl_t = orc.token_backward(t, dy[t], x, wg, w1, w2, fwd["idx"], fwd["w"],
+                                        fwd["slot_row"], "f64")
+        np.testing.assert_allclose(dx_t, g["dx_f64"][t], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dl_t, g["dlogits"][t], rtol=1e-6, atol=1e-7)
+
+
+def test_weight_grad_entries_match_full_backward():
+    T, d, F, E, k = 60, 16, 24, 4, 2
+    x = rand((T, d), 60)
+    wg, b = rand((d, E), 61), rand((E,), 62)
+    w1, w2 = rand((E, F, d), 63, 0.4), rand((E, d, F), 64, 0.4)
+    dy = rand((T, d), 65)
+    fwd = orc.forward(x, wg, b, w1, w2, k, 0.0, "f64")
+    g = orc.backward(dy, fwd, x, wg, w1, w2, "f64")
+    fs, is_ = [0, 5, 23], [1, 7, 15]
+    for e in range(E):
+        a, bb = fwd["offsets"][e], fwd["offsets"][e + 1]
+        toks = fwd["row_token"][a:bb]
+        # gate weight of each row: the slot of token t that points at row r
+        wr = np.array([fwd["w"][t][list(fwd["slot_row"][t * k:(t + 1) * k]).index(r)]
+                       for t, r in zip(toks, range(a, bb))])
+        dw1, dw2 = orc.expert_weight_grad_entries(e, fs, is_, fwd["x_perm"][a:bb], dy[toks], wr,
+                                                  w1[e], w2[e], "f64")
+        np.testing.assert_allclose(dw1, g["dw1_f64"][e][np.ix_(fs, is_)], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dw2, g["dw2_f64"][e][np.ix_(is_, fs)], rtol=1e-10, atol=1e-12)
