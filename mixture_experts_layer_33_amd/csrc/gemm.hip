@@ -235,9 +235,8 @@ struct TileGemm {
       const bf16* as = a_lds + s * (BM * kBK);
       const bf16* bs = b_lds + s * (BN * kBK);
       const int kend = K - kt * kBK;  // < 64 only on a ragged last step
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        bf16x8 a[FM];
+      // all A and B fragments of one 16-deep k slice
+      auto load = [&](int kk, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
           const int r0 = wm * WM + j * 32;
@@ -251,16 +250,38 @@ struct TileGemm {
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
           const int r0 = wn * WN + i * 32;
-          bf16x8 b;
           if constexpr (B_K)
-            b = TileK<BN>::frag(bs, r0, kk);
+            b[i] = TileK<BN>::frag(bs, r0, kk);
           else
-            b = TileMN<BN>::frag(bs, r0, kk);
+            b[i] = TileMN<BN>::frag(bs, r0, kk);
+        }
+      };
+      auto mma = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
 #pragma unroll
           for (int j = 0; j < FM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a[j], acc[i][j], 0, 0, 0);
-        }
-      }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[i], a[j], acc[i][j], 0, 0, 0);
+      };
+      // software pipeline: slice kk+1's fragments load while slice kk's
+      // MFMAs run (two register sets, alternating)
+      // (scheduling barriers keep the compiler from sinking each load next
+      // to its first use, which exposes the LDS latency every 4 MFMAs)
+      bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
+      load(0, a0, b0);
+      load(1, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(2, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(3, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a1, b1);
       if constexpr (GATE) {
         if (gsel != nullptr) {
           // thread: 8 columns (chunk c) of rows kg*kGateRows .. of this stage

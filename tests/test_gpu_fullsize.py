@@ -1,0 +1,154 @@
+"""The four bf16 workloads at their full sizes, run exactly as bench.py runs
+them (moe_forward, moe_popularity_update, moe_backward on one stream), checked
+against the CPU reference on what it can compute at that size:
+
+* router logits for every token (float32, 1e-5 of the largest);
+* routing for every token; a token may only disagree where its top-k is a
+  near-tie within the logits tolerance (those tokens are then skipped);
+* counts, offsets and the slot rows bit-exact when no token disagrees;
+* y, dX and dlogits on sampled tokens, each from that token alone;
+* dW1 / dW2 entries of the hottest and a cold expert, each summed over all of
+  the expert's rows;
+* dW_gate = x^T dlogits and db = sum_t dlogits (properties at any size,
+  evaluated on the GPU's own dlogits) and dlogits on the sampled tokens;
+* the popularity window over the fine-grained workload's 8 drifting
+  iterations (exact integers).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import moe_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+from gpu_helpers import TOL, act_code, ambiguous_tokens, assert_close, down, up  # noqa: E402
+
+if torch.cuda.is_available():
+    from mixture_experts_layer_33_amd.layer import MoeLayer
+
+WL = workloads.workloads()
+N_TOKENS = 12
+
+
+def _setup(w, it=0, weights=None):
+    inp = workloads.make_inputs(w, it, with_weights=weights is None, with_dy=True)
+    if weights is not None:
+        inp.update(weights)
+    dev = {"x": up(inp["x"], w.dtype), "dy": up(inp["dy"], w.dtype),
+           "w_gate": up(inp["w_gate"]), "b_gate": up(inp["b_gate"]),
+           "w1": up(inp["w1"], w.dtype), "w2": up(inp["w2"], w.dtype)}
+    return inp, dev
+
+
+@pytest.mark.parametrize("name", ["uniform_cf125", "skewed_zipf12", "mixtral_shaped",
+                                  "fine_grained"])
+def test_full_size_sampled(name):
+    w = WL[name]
+    print(f"full-size {name}: {w.description}", flush=True)
+    inp, dev = _setup(w)
+    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, w.capacity_factor, act_code(w.dtype),
+                     window=w.window)
+    layer.forward(dev["x"], dev["w_gate"], dev["b_gate"], dev["w1"], dev["w2"])
+    layer.popularity(0)
+    layer.backward(dev["dy"], dev["x"], dev["w_gate"], dev["w1"], dev["w2"])
+    torch.cuda.synchronize()
+    tol = TOL[w.dtype]
+
+    L = orc.router_logits(inp["x"], inp["w_gate"], inp["b_gate"])
+    assert_close(down(layer.logits), L, 1e-5, "logits")
+    idx, wt = orc.topk_gate(L, w.k)
+    gidx = down(layer.topk_idx)
+    mism = np.where((gidx != idx).any(axis=1))[0]
+    assert set(mism.tolist()) <= set(ambiguous_tokens(L, w.k).tolist())
+    assert mism.size <= max(3, w.T // 2000)
+    C = orc.capacity(w.T, w.k, w.E, w.capacity_factor)
+    s = orc.assign_slots(idx, w.E, C)
+    if mism.size == 0:
+        for key in ("counts_raw", "counts_kept", "offsets", "slot_row"):
+            np.testing.assert_array_equal(down(getattr(layer, key)), s[key], err_msg=key)
+        n = int(s["offsets"][-1])
+        np.testing.assert_array_equal(down(layer.row_token)[:n], s["row_token"])
+        ring, ws = orc.popularity_update(np.zeros((w.window, w.E), np.int32), 0, s["counts_raw"])
+        np.testing.assert_array_equal(down(layer.window_sum), ws)
+    assert_close(down(layer.topk_w)[gidx == idx], wt[gidx == idx], 1e-5, "topk_w")
+
+    # sampled tokens (skipping near-tie disagreements)
+    rng = np.random.default_rng(0)
+    toks = [int(t) for t in rng.choice(w.T, size=N_TOKENS * 2, replace=False) if t not in mism]
+    toks = toks[:N_TOKENS]
+    y_g, dx_g, dl_g = down(layer.y), down(layer.dx), down(layer.dlogits)
+    for t in toks:
+        y_ref = orc.token_output(t, inp["x"], wt, idx, s["slot_row"], inp["w1"], inp["w2"],
+                                 w.dtype)
+        assert_close(y_g[t], y_ref, tol, f"y[{t}]")
+        dx_ref, dl_ref = orc.token_backward(t, inp["dy"][t], inp["x"], inp["w_gate"], inp["w1"],
+                                            inp["w2"], idx, wt, s["slot_row"], w.dtype)
+        assert_close(dx_g[t], dx_ref, tol, f"dx[{t}]")
+        assert_close(dl_g[t], dl_ref, tol, f"dlogits[{t}]")
+
+    # weight-gradient entries of the hottest and a cold non-empty expert
+    counts = s["counts_kept"]
+    touched = set(idx[mism].reshape(-1).tolist()) | set(gidx[mism].reshape(-1).tolist())
+    order = [e for e in np.argsort(-counts, kind="stable") if counts[e] > 0 and e not in touched]
+    dw1_g, dw2_g = down(layer.dw1), down(layer.dw2)
+    k = w.k
+    for e in (order[0], order[-1]):
+        a, b = int(s["offsets"][e]), int(s["offsets"][e + 1])
+        rows_tok = s["row_token"][a:b]
+        slot_of_row = np.empty(b - a, np.int64)
+        sr = s["slot_row"]
+        kept = np.where((sr >= a) & (sr < b))[0]
+        slot_of_row[sr[kept] - a] = kept
+        w_rows = wt.reshape(-1)[slot_of_row]
+        fs = sorted(rng.choice(w.F, size=3, replace=False).tolist())
+        is_ = sorted(rng.choice(w.d, size=3, replace=False).tolist())
+        dw1_ref, dw2_ref = orc.expert_weight_grad_entries(
+            e, fs, is_, inp["x"][rows_tok], inp["dy"][rows_tok], w_rows, inp["w1"][e],
+            inp["w2"][e], w.dtype)
+        scale1 = np.abs(dw1_ref).max()
+        scale2 = np.abs(dw2_ref).max()
+        assert np.abs(dw1_g[e][np.ix_(fs, is_)] - dw1_ref).max() <= tol * scale1, f"dw1[{e}]"
+        assert np.abs(dw2_g[e][np.ix_(is_, fs)] - dw2_ref).max() <= tol * scale2, f"dw2[{e}]"
+    del k
+
+    # gate gradients: dW_gate = x^T dlogits, db = sum_t dlogits (GPU's dlogits)
+    dwg_prop = inp["x"].astype(np.float64).T @ dl_g.astype(np.float64)
+    assert_close(down(layer.dw_gate), dwg_prop, 1e-4, "dw_gate vs x^T dlogits")
+    assert_close(down(layer.db_gate), dl_g.astype(np.float64).sum(0), 1e-4, "db vs sum dlogits")
+
+
+def test_fine_grained_popularity_over_drifting_iterations():
+    """Eight iterations whose expert ranking drifts; each iteration routes its
+    own tokens.  The GPU's window must be the sum of its last 4 raw counts
+    (a property), and equal the reference's window over the reference's own
+    routing on every expert that no near-tie disagreement touched."""
+    w = WL["fine_grained"]
+    wg = workloads.make_w_gate(w)
+    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, 0.0, act_code(w.dtype), window=w.window,
+                     backward=False)
+    ring = np.zeros((w.window, w.E), np.int32)
+    wgd = up(wg)
+    gpu_hist, touched_hist = [], []
+    for it in range(w.iters):
+        x = workloads.make_x(w, it)
+        b = workloads.gate_bias(w, it)
+        layer.route(up(x, w.dtype), wgd, up(b))
+        layer.popularity(it)
+        torch.cuda.synchronize()
+        L = orc.router_logits(x, wg, b)
+        idx, _ = orc.topk_gate(L, w.k)
+        gidx = down(layer.topk_idx)
+        mism = np.where((gidx != idx).any(axis=1))[0]
+        assert set(mism.tolist()) <= set(ambiguous_tokens(L, w.k).tolist())
+        touched_hist.append(set(idx[mism].reshape(-1).tolist()) | set(gidx[mism].reshape(-1).tolist()))
+        gpu_counts = down(layer.counts_raw)
+        gpu_hist.append(gpu_counts)
+        np.testing.assert_array_equal(gpu_counts, np.bincount(gidx.reshape(-1), minlength=w.E))
+        ws_gpu = down(layer.window_sum)
+        np.testing.assert_array_equal(ws_gpu, np.sum(gpu_hist[-w.window:], axis=0))
+        ring, ws_ref = orc.popularity_update(ring, it, np.bincount(idx.reshape(-1), minlength=w.E))
+        touched = set().union(*touched_hist[-w.window:])
+        keep = np.array([e not in touched for e in range(w.E)])
+        np.testing.assert_array_equal(ws_gpu[keep], ws_ref[keep])

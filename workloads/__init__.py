@@ -107,7 +107,11 @@ def workloads() -> Dict[str, Workload]:
 
 
 def scaled(w: Workload, **changes) -> Workload:
-    """A copy of a workload with some fields replaced (for small parity cases)."""
+    """A copy of a workload with some fields replaced (for small parity cases).
+    The description then lists the changed fields after the original's."""
+    if changes and "description" not in changes:
+        diff = " ".join(f"{k}={v}" for k, v in changes.items())
+        changes["description"] = f"{w.name} scaled to {diff}"
     return dataclasses.replace(w, **changes)
 
 
