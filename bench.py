@@ -3,19 +3,31 @@ the popularity window and the full backward, on seeded synthetic inputs.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = moe_forward + moe_popularity_update + moe_backward over one batch
-of T tokens.  Prints ONE JSON line on stdout (progress goes to stderr).
+One step = moe_route, moe_permute, moe_expert_ffn, moe_combine (the kernels of
+moe_forward, in its order), moe_popularity_update and moe_backward over one
+batch of T tokens.  Prints ONE JSON line on stdout (progress goes to stderr).
 
-value      = T * K / (time of K back-to-back steps), inputs resident in HBM
-roofline   = the grouped expert GEMM (moe_expert_ffn: FC1 + FC2 launches),
-             algorithmic 4*d*F*S_kept flops per call over its HIP-event time
+value        = T * K / (time of K back-to-back steps), inputs resident in HBM
+roofline     = the grouped expert GEMM kernel (rows_gemm_kernel; its FC1 and FC2
+               launches in moe_expert_ffn, 2*d*F*S_kept flops each), averaged
+               over the launches of the timed steps with HIP events recorded on
+               the launch stream around each moe_expert_ffn call
+traffic      = HBM bytes per launch of that kernel from the FETCH_SIZE and
+               WRITE_SIZE counters (profiles/rows_gemm_<workload>_hbm_traffic.md),
+               or null when the GEMM source changed since they were taken
 cpu_baseline = the CPU reference on a bounded sample of the same workload
+
+    python bench.py --summarize-traffic FETCH_CSV WRITE_CSV [--workload NAME]
+
+(no GPU) turns the counter files of two rocprofv3 --pmc runs of
+``bench.py --copy-calibration`` into that traffic summary.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -45,13 +57,129 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=20)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the HBM traffic summary from two counter runs (no GPU)")
+    p.add_argument("--command", default="",
+                   help="the command lines that produced the counter files (recorded)")
     return p.parse_args()
 
 
-def cpu_baseline(w: workloads.Workload, inp, budget_s: float = 20.0):
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_33_amd", "csrc", "gemm.hip")
+GEMM_KERNEL = "rows_gemm_kernel"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
+
+
+def traffic_path(name):
+    return os.path.join(ROOT, "profiles", f"rows_gemm_{name}_hbm_traffic.md")
+
+
+def gemm_source_hash():
+    import hashlib
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _counter_rows(path, counter):
+    import csv
+    with open(path, newline="") as f:
+        return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+
+def summarize_traffic(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the FC1 and FC2 launches,
+    each scaled by the same counter's reading for a 1 GiB device copy."""
+    w = workloads.workloads()[args.workload]
+    out = {}
+    lines = []
+    for counter, path in zip(("FETCH_SIZE", "WRITE_SIZE"), args.summarize_traffic):
+        rows = _counter_rows(path, counter)
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if r["Kernel_Name"].startswith(COPY_KERNEL)
+                  and float(r["Counter_Value"]) > COPY_BYTES / 1024 / 2]
+        if not copies:
+            raise SystemExit(f"{path}: no 1 GiB copy dispatch (run with --copy-calibration)")
+        scale = (COPY_BYTES / 1024) / (sum(copies) / len(copies))
+        per_kernel = {}
+        for r in rows:
+            # forward launches: K-contiguous weights, epilogue ReLU (FC1) or store (FC2)
+            if re.search(GEMM_KERNEL + r"<\d+, \d+, true, [01]>", r["Kernel_Name"]):
+                per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        if len(per_kernel) != 2:
+            raise SystemExit(f"{path}: expected the FC1 and FC2 forward GEMM kernels, "
+                             f"found {sorted(per_kernel)}")
+        out[counter] = {"copy_kib": sum(copies) / len(copies), "scale": scale,
+                        "kernels": {k: sum(v) / len(v) for k, v in per_kernel.items()},
+                        "dispatches": {k: len(v) for k, v in per_kernel.items()}}
+    names = sorted(out["FETCH_SIZE"]["kernels"])
+    per_launch = {}
+    for k in names:
+        fb = out["FETCH_SIZE"]["kernels"][k] * 1024 * out["FETCH_SIZE"]["scale"]
+        wb = out["WRITE_SIZE"]["kernels"][k] * 1024 * out["WRITE_SIZE"]["scale"]
+        per_launch[k] = {"fetch_bytes": fb, "write_bytes": wb}
+    mean = sum(v["fetch_bytes"] + v["write_bytes"] for v in per_launch.values()) / len(per_launch)
+    rec = {"workload": w.name, "gemm_source_sha256": gemm_source_hash(),
+           "traffic_bytes_per_launch": mean,
+           "fetch_scale": out["FETCH_SIZE"]["scale"], "write_scale": out["WRITE_SIZE"]["scale"],
+           "per_kernel": per_launch}
+    lines.append(f"# HBM traffic of rows_gemm_kernel (expert FFN forward), {w.name}")
+    lines.append("")
+    lines.append(f"Workload: {w.description}.")
+    lines.append("")
+    lines.append("Commands (run from the repository root on one MI355X):")
+    lines.append("")
+    lines.append("```")
+    lines.append(args.command.strip() or "(not recorded)")
+    lines.append("```")
+    lines.append("")
+    lines.append("Counters are KiB per dispatch, averaged over the dispatches of each kernel; "
+                 "each is scaled by 1 GiB / (the same counter's reading for the 1 GiB "
+                 f"device copy `{COPY_KERNEL}`).")
+    lines.append("")
+    lines.append("| counter | copy reading (KiB) | scale |")
+    lines.append("|---|---|---|")
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        lines.append(f"| {c} | {out[c]['copy_kib']:.0f} | {out[c]['scale']:.4f} |")
+    lines.append("")
+    lines.append("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |")
+    lines.append("|---|---|---|---|---|")
+    for k in names:
+        pl = per_launch[k]
+        lines.append(f"| `{k}` | {out['FETCH_SIZE']['dispatches'][k]} | "
+                     f"{out['FETCH_SIZE']['kernels'][k]:.0f} | "
+                     f"{out['WRITE_SIZE']['kernels'][k]:.0f} | "
+                     f"{pl['fetch_bytes'] + pl['write_bytes']:.4g} |")
+    lines.append("")
+    lines.append(f"Mean over the two launches: {mean:.4g} bytes per launch.")
+    lines.append("")
+    lines.append("traffic-json: " + json.dumps(rec))
+    os.makedirs(os.path.dirname(traffic_path(w.name)), exist_ok=True)
+    with open(traffic_path(w.name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(traffic_path(w.name))
+
+
+def load_traffic(name):
+    """Bytes per launch from the committed counter summary, or None when there
+    is none or the GEMM source has changed since it was taken."""
+    try:
+        with open(traffic_path(name)) as f:
+            for line in f:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    if rec["gemm_source_sha256"] == gemm_source_hash():
+                        return rec["traffic_bytes_per_launch"]
+                    log("traffic summary is stale (GEMM source changed): traffic = null")
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w: workloads.Workload, inp, budget_s: float = 12.0):
     """The CPU reference, as it stands, on a token sample of the workload:
     forward + backward on the first n tokens (same weights), n doubled until
-    one run takes a few seconds or the whole batch is done."""
+    a run takes a quarter of the budget or covers the whole batch; that run is
+    then repeated until about budget_s seconds of CPU work are done."""
     from oracle import moe_oracle as orc
     try:
         from threadpoolctl import threadpool_info
@@ -72,17 +200,22 @@ def cpu_baseline(w: workloads.Workload, inp, budget_s: float = 20.0):
         total_tok += n
         runs += 1
         log(f"cpu baseline: {n} tokens fwd+bwd in {dt:.2f} s")
-        if total_t > budget_s or n >= w.T or dt > budget_s / 4:
+        if total_t > budget_s:
             break
-        n = min(w.T, n * 2)
+        if n < w.T and dt < budget_s / 4:
+            n = min(w.T, n * 2)
     return {"value": total_tok / total_t, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{runs} runs of forward+backward on the first 256..{n} of {w.T} tokens "
-                      f"({w.name}), float64 NumPy, {total_t:.1f} s total"}
+                      f"({w.name}, {total_tok} tokens in all), float64 NumPy, "
+                      f"{total_t:.1f} s total"}
 
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -111,9 +244,17 @@ def main():
     stream = torch.cuda.current_stream()
 
     it_counter = [0]
+    ev = []  # (before, after) moe_expert_ffn in each timed step
 
-    def step():
-        layer.forward(x, w_gate, b_gate, w1, w2, logits_out=False)
+    def step(mark=None):
+        layer.route(x, w_gate, b_gate, logits_out=False, counts=False)
+        layer.permute(x)
+        if mark is not None:
+            mark[0].record(stream)
+        layer.expert_ffn(w1, w2)
+        if mark is not None:
+            mark[1].record(stream)
+        layer.combine()
         layer.popularity(it_counter[0])
         layer.backward(dy, x, w_gate, w1, w2, dlogits=False)
         it_counter[0] += 1
@@ -123,19 +264,24 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(ev[i])
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(end) / args.steps
     value = w.T / (ms / 1e3)
     s_kept = int(layer.offsets[-1].item())
-    log(f"step {ms:.3f} ms ({value:,.0f} tokens/s), wall {t_wall:.3f} s, S_kept {s_kept}")
+    # the GEMM kernel: two launches (FC1, FC2) per moe_expert_ffn call
+    gemm_launch_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps / 2
+    log(f"step {ms:.3f} ms ({value:,.0f} tokens/s), wall {t_wall:.3f} s, S_kept {s_kept}, "
+        f"GEMM launch {gemm_launch_ms * 1e3:.1f} us")
 
     # per-part event timings (same inputs, after the timed region)
     def time_it(fn, reps):
@@ -154,8 +300,8 @@ def main():
     t_bwd = time_it(lambda: layer.backward(dy, x, w_gate, w1, w2, dlogits=False), reps)
     t_ffn = time_it(lambda: layer.expert_ffn(w1, w2), reps)
     t_comb = time_it(lambda: layer.combine(), reps)
-    flops_ffn = 4.0 * w.d * w.F * s_kept
-    achieved = flops_ffn / (t_ffn / 1e3) / 1e12
+    flops_launch = 2.0 * w.d * w.F * s_kept
+    achieved = flops_launch / (gemm_launch_ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     comb_bytes = s_kept * w.d * (2 if w.dtype == "bf16" else 4) + \
         w.T * w.d * (2 if w.dtype == "bf16" else 4) + 8 * w.T * w.k
@@ -171,8 +317,8 @@ def main():
         torch.cuda.synchronize()
 
     out = {
-        "metric": "MoE-layer tokens/sec (route+permute+grouped FFN+combine, with popularity "
-                  "window and backward); % MFMA roofline of the grouped GEMM",
+        "metric": "MoE-layer tokens/sec (route+permute+grouped FFN+combine); "
+                  "% MFMA/HBM roofline",
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
@@ -180,9 +326,12 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d_model": w.d, "d_ff": w.F, "E": w.E,
                    "k": w.k, "capacity_factor": w.capacity_factor,
                    "step": "forward + popularity window + backward", "S_kept": s_kept},
-        "roofline": {"bound": "mfma", "kernel": "grouped expert GEMM (FC1+FC2 per call)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "rows_gemm_kernel (grouped expert GEMM, FC1 and FC2 launches)",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None},
+                     "frac": achieved / peak, "traffic": load_traffic(w.name),
+                     "flops_per_launch": flops_launch,
+                     "launch_us": gemm_launch_ms * 1e3},
         "parts_ms": {"forward": t_fwd, "backward": t_bwd, "expert_ffn": t_ffn,
                      "combine": t_comb},
     }

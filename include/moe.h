@@ -111,7 +111,11 @@ const char* moe_status_string(moe_status status);
  * logits_in is given (then x/w_gate/b_gate may be NULL and those logits are
  * used as they are).  Writes logits_out if non-NULL, the top-k experts in
  * descending logit order, their renormalised weights, and counts_raw[e] =
- * number of slots routed to e (before capacity).  Workspace: MOE_OP_ROUTE. */
+ * number of slots routed to e (before capacity).  counts_raw may be NULL:
+ * then only the routing kernel runs (moe_permute counts the slots again and
+ * can write counts_raw; moe_route followed by moe_permute with counts_raw
+ * given there launches exactly the kernels of moe_forward's first half).
+ * Workspace: MOE_OP_ROUTE. */
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_gate,
                      const float* b_gate, const float* logits_in, float* logits_out,
                      int32_t* topk_idx, float* topk_w, int32_t* counts_raw,

@@ -203,11 +203,17 @@ moe_status moe_route(const moe_shape* s, const void* x, const float* w_gate, con
                      int32_t* counts_raw, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (!ptrs_ok(topk_idx, topk_w, counts_raw) || !opt_ok(logits_out) || !opt_ok(logits_in))
+  if (!ptrs_ok(topk_idx, topk_w) || !opt_ok(counts_raw) || !opt_ok(logits_out) ||
+      !opt_ok(logits_in))
     return MOE_ERR_INVALID_ARG;
   if (logits_in == nullptr && !ptrs_ok(x, w_gate, b_gate)) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
   PermWs pw = carve_perm(s, ws);
+  if (counts_raw == nullptr) {  // routing only; moe_permute counts
+    MOE_HIP(launch_route(s->act_dtype, x, w_gate, b_gate, logits_in, logits_out, topk_idx,
+                         topk_w, s->T, s->d_model, s->E, s->k, pw.wsplit, as_stream(stream)));
+    return MOE_OK;
+  }
   return do_route(s, x, w_gate, b_gate, logits_in, logits_out, topk_idx, topk_w, counts_raw,
                   pw.kept_tmp, pw, as_stream(stream));
 }

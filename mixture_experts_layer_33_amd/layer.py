@@ -72,15 +72,16 @@ class MoeLayer:
                      self.dlogits if dlogits else None, self.ws_bwd, stream)
         return self.dx
 
-    def route(self, x, w_gate, b_gate, logits_in=None, stream=None):
+    def route(self, x, w_gate, b_gate, logits_in=None, logits_out=True, counts=True,
+              stream=None):
         moe_route(self.shape, x, w_gate, b_gate, logits_in,
-                  None if logits_in is not None else self.logits, self.topk_idx, self.topk_w,
-                  self.counts_raw, self.ws_fwd, stream)
+                  self.logits if logits_in is None and logits_out else None, self.topk_idx,
+                  self.topk_w, self.counts_raw if counts else None, self.ws_fwd, stream)
 
-    def permute(self, x, topk_idx=None, stream=None):
+    def permute(self, x, topk_idx=None, counts=True, stream=None):
         moe_permute(self.shape, x, self.topk_idx if topk_idx is None else topk_idx,
-                    self.counts_raw, self.counts_kept, self.offsets, self.slot_row,
-                    self.row_token, self.x_perm, self.ws_fwd, stream)
+                    self.counts_raw if counts else None, self.counts_kept, self.offsets,
+                    self.slot_row, self.row_token, self.x_perm, self.ws_fwd, stream)
 
     def expert_ffn(self, w1, w2, x_perm=None, offsets=None, stream=None):
         moe_expert_ffn(self.shape, self.x_perm if x_perm is None else x_perm,

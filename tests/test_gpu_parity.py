@@ -198,6 +198,33 @@ def test_bitwise_repeatable(name):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["skewed_zipf12", "uniform_cf050"])
+def test_forward_equals_its_entry_points(name):
+    """moe_route (no counts) + moe_permute + moe_expert_ffn + moe_combine give
+    bit-for-bit what moe_forward gives."""
+    w, inp, dev, layer = _setup(name)
+    names = ("y", "logits", "topk_idx", "topk_w", "counts_raw", "counts_kept", "offsets",
+             "slot_row", "row_token", "x_perm", "h", "out_perm")
+    layer.forward(dev["x"], dev["w_gate"], dev["b_gate"], dev["w1"], dev["w2"])
+    torch.cuda.synchronize()
+    ref = {n: getattr(layer, n).clone() for n in names}
+    for n in names:
+        getattr(layer, n).fill_(-7)
+    layer.route(dev["x"], dev["w_gate"], dev["b_gate"], counts=False)
+    layer.permute(dev["x"])
+    layer.expert_ffn(dev["w1"], dev["w2"])
+    layer.combine()
+    torch.cuda.synchronize()
+    S = int(ref["offsets"][-1].item())
+    for n in names:
+        a, b = getattr(layer, n), ref[n]
+        if n in ("x_perm", "h", "out_perm"):
+            a, b = a[:S], b[:S]
+        if n == "row_token":
+            a, b = a[:w.T * w.k], b[:w.T * w.k]
+        assert torch.equal(a, b), n
+
+
 def test_popularity_window():
     E, W = 32, 4
     layer = MoeLayer(8, 64, 64, E, 2, 0.0, act_code("f32"), window=W, backward=False)
