@@ -13,10 +13,11 @@
 //             dx = dz_e W1[e]                  A [rows][F]  B [F][d]   (NN)
 //   wgrad     dW2[e] = dO_e^T h_e              A [rows][d]  B [rows][F] (TN)
 //             dW1[e] = dz_e^T x_perm_e         A [rows][F]  B [rows][d] (TN)
-// Both operands always reach LDS as [row][64 k] bf16 tiles (16-byte chunks
-// XOR-swizzled by row) so every MFMA fragment is one 16-byte LDS read;
-// operands that are contiguous along M or N in memory are transposed in
-// registers on their way to LDS (8 consecutive k of one row per chunk).
+// Operands are copied global -> LDS by the buffer unit directly
+// (buffer_load_dwordx4 ... lds, no staging registers) and read back as MFMA
+// fragments: K-contiguous operands as 16-byte rows, M/N-contiguous operands
+// transposed by ds_read_b64_tr_b16.  Buffer range checks turn rows past the
+// end of an operand into zeros, so ragged tiles need no clamping or masking.
 //
 // Scheduling: forward and dgrad tiles cover each expert's packed rows; the
 // tile list is built inside the kernel from the device offsets (no host
@@ -35,108 +36,153 @@ constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round robin
 
 enum Epi { EPI_RELU = 0, EPI_STORE = 1, EPI_MASK = 2, EPI_F32 = 3 };
 
-// 16-byte chunk kc of LDS row `row` (rows of 64 bf16 = 8 chunks).  The XOR
-// uses row bits 0-2, 3-5 and 6-8 so that both 8 consecutive rows (MFMA
-// fragment reads) and rows 8 apart (transposed stores) spread over banks.
-__device__ __forceinline__ int swz(int row, int kc) {
-  return (row * 8 + (kc ^ ((row ^ (row >> 3) ^ (row >> 6)) & 7))) * 8;
+// ---------------------------------------------------------------------------
+// Buffer copies.  A raw buffer resource (stride 0) over an operand: loads at
+// byte offsets (voffset + soffset) >= `bytes` are out of range and return
+// zeros (what lands in LDS is then zero) without touching memory.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;   // untyped dword access
+constexpr uint32_t kPadOffset = 0x7ffffff0u;  // past every operand's range
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t u = ((uint64_t)uniform((uint32_t)(a >> 32)) << 32) | uniform((uint32_t)a);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0,
+                                           (int)uniform(bytes), kRsrcWord3);
+}
+// 16 bytes per lane from r at (voff + soff) to LDS at dst + 16 * lane
+__device__ __forceinline__ void copy16(Rsrc r, char* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, soff, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
-// Operand tiles, copied global -> LDS directly (global_load_lds_dwordx4: the
-// 16 bytes of lane L land at the wave's LDS base + 16 L; one wave instruction
-// fills 1 KiB).  Each lane fetches whichever global chunk the LDS swizzle
-// puts at its position.
+// Operand tiles.  Each stage holds 64 k of the tile; one wave instruction
+// copies 1 KiB.  issue<Q, NQ> issues the instructions i with i % NQ == Q, so
+// a stage's copies can be spread over NQ scheduling regions.
 //
-// K-contiguous operand (element (r, k) at base[r * ld + k]): LDS [ROWS][64],
-// 16-byte chunk kc of row r at position kc ^ f(r); read back as one 16-byte
-// fragment per lane.  Rows >= nrows re-read row nrows-1 (never stored).
+// K-contiguous operand (element (r, k) at base[r * ld + k]), valid rows
+// [0, nrows): LDS [ROWS][64] bf16, 16-byte chunk kc of row r at position
+// kc ^ ((r >> 1) & 7), so a fragment read (16-byte chunks of 16 consecutive
+// rows per 256 bytes of banks) is free of bank conflicts.  K is a multiple of
+// 64 for these operands.
 template <int ROWS>
 struct TileK {
-  static constexpr int N = ROWS / 32;  // wave instructions per thread per stage
-  uint32_t off[N];                     // byte offsets from the stage base
-  __device__ void init(int ld, int nrows) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  static constexpr int N = ROWS / 32;          // wave instructions per thread per stage
+  static constexpr int kBytes = ROWS * kBK * 2;
+  static constexpr int NLO = 4;                // lane offsets (one per 16-deep slice)
+  const bf16* base;
+  uint32_t bytes;
+  uint32_t off[N];
+  __device__ void init(const bf16* b, int ld, int nrows, int /*kmax*/, int wid) {
+    const int lane = threadIdx.x & 63;
+    base = b;
+    bytes = (uint32_t)nrows * (uint32_t)ld * 2u;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int row = (i * 4 + wid) * 8 + (lane >> 3), p = lane & 7;
-      const int kc = p ^ ((row ^ (row >> 3) ^ (row >> 6)) & 7);
-      off[i] = (uint32_t)(((size_t)min(row, nrows - 1) * ld + kc * 8) * sizeof(bf16));
+      const int row = (i * 4 + wid) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ ((row >> 1) & 7);
+      off[i] = (uint32_t)(row * ld + kc * 8) * 2u;
     }
   }
-  // stage with k in [k0, k0 + 64)
-  __device__ void issue(const bf16* base, int ld, int k0, int, bf16* lds) const {
-    const int wid = threadIdx.x >> 6;
-    const char* b = reinterpret_cast<const char*>(base + k0);
+  // resource and stage offset for the stage starting at k0 (dead: zeros)
+  __device__ Rsrc rsrc(bool live) const { return make_rsrc(base, live ? bytes : 0u); }
+  __device__ static uint32_t soff(int k0) { return (uint32_t)k0 * 2u; }
+  template <int Q, int NQ>
+  __device__ void issue(Rsrc r, uint32_t so, char* stage, int wid) const {
 #pragma unroll
     for (int i = 0; i < N; ++i)
-      __builtin_amdgcn_global_load_lds(
-          b + off[i], (__attribute__((address_space(3))) void*)(lds + (i * 4 + wid) * 8 * kBK),
-          16, 0, 0);
+      if (i % NQ == Q) copy16(r, stage + (i * 4 + wid) * 1024, off[i], so);
   }
-  // 32 x 16 MFMA operand block at rows r0..r0+31, k = kk*16 ..: lane l holds
-  // row r0 + l%32, the 8 consecutive k from kk*16 + 8*(l/32)
-  __device__ static bf16x8 frag(const bf16* lds, int r0, int kk) {
-    const int lane = threadIdx.x & 63;
-    return *reinterpret_cast<const bf16x8*>(lds + swz(r0 + (lane & 31), kk * 2 + (lane >> 5)));
+  static constexpr int issued(int Q, int NQ) {
+    int n = 0;
+    for (int i = 0; i < N; ++i) n += (i % NQ == Q);
+    return n;
+  }
+  // lane byte offsets: slice kk, lane l holds row l%32 of the block, k from
+  // kk*16 + 8*(l/32)
+  __device__ static void lane_offsets(uint32_t (&lo)[NLO]) {
+    const int lane = threadIdx.x & 63, r = lane & 31;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      lo[kk] = (uint32_t)(r * 8 + ((kk * 2 + (lane >> 5)) ^ ((r >> 1) & 7))) * 16u;
+  }
+  static constexpr int kReads = 1;  // LDS reads per fragment
+  // 32 x 16 MFMA operand block at rows r0..r0+31, slice kk
+  __device__ static bf16x8 frag(const char* stage, int r0, int kk, const uint32_t (&lo)[NLO]) {
+    return *reinterpret_cast<const bf16x8*>(stage + r0 * (kBK * 2) + lo[kk]);
   }
 };
 
-// MN-contiguous operand (element (r, k) at base[k * ld + r]): LDS [64][ROWS]
-// as in memory, 16-byte chunk c of k-row k at position c ^ sw(k), read back
-// transposed by ds_read_b64_tr_b16.  Within each 16-lane group that
+// M/N-contiguous operand (element (r, k) at base[k * ld + r]), valid columns
+// [0, ncols) and k rows [0, kmax): LDS [64][ROWS] as in memory, with a pitch
+// of ROWS*2 + 64 bytes (four unused 16-byte slots after each k-row) so that
+// four consecutive k-rows start in four different 64-byte groups of banks.
+// Read back transposed by ds_read_b64_tr_b16: within each 16-lane group that
 // instruction hands lane i the elements M[4j + i/4][i%4] (j = 0..3) of the
 // 4-element pieces M[r] addressed by the group's lanes r; addressing k-row
 // kb + r/4, columns c0 + 4 (r%4) gives lane i four consecutive k of column
 // c0 + i.  Two reads give the 8 k of a fragment, in the same k order as the
-// K-contiguous fragments.  k rows >= kmax re-read row kmax-1 (zeroed in the
-// fragment where it matters); columns >= ncols re-read valid columns.
+// K-contiguous fragments.  k rows >= kmax read as zeros (buffer range);
+// columns >= ncols re-read a valid column chunk; pad slots read nothing.
 template <int ROWS>
 struct TileMN {
-  static constexpr int R = ROWS * 2;          // bytes per k-row
-  static constexpr int CPR = R / 16;          // chunks per k-row
-  static constexpr int RPI = 1024 / R;        // k-rows per wave instruction
-  static constexpr int N = 64 / RPI / 4;      // wave instructions per thread per stage
-  __device__ static int sw(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
-  int kl[N];       // k-row of this lane's chunk, within the stage
-  uint32_t col[N]; // byte offset of its column chunk
-  __device__ void init(int ld, int ncols) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  static constexpr int R = ROWS * 2;            // bytes of a k-row
+  static constexpr int P = R + 64;              // LDS pitch
+  static constexpr int SPR = P / 16;            // 16-byte slots per k-row
+  static constexpr int N = kBK * SPR / 256;     // wave instructions per thread per stage
+  static constexpr int kBytes = kBK * P;
+  static constexpr int NLO = 1;
+  static_assert(kBK * SPR % 256 == 0, "stage must be whole wave instructions");
+  const bf16* base;
+  uint32_t bytes, ld2;
+  uint32_t off[N];
+  __device__ void init(const bf16* b, int ld, int ncols, int kmax, int wid) {
+    const int lane = threadIdx.x & 63;
+    base = b;
+    ld2 = (uint32_t)ld * 2u;
+    bytes = (uint32_t)kmax * ld2;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int k = (i * 4 + wid) * RPI + lane / CPR, p = lane % CPR;
-      const int c = min(p ^ sw(k), ncols / 8 - 1);
-      kl[i] = k;
-      col[i] = (uint32_t)(c * 8 * sizeof(bf16));
+      const int slot = (i * 4 + wid) * 64 + lane;
+      const int k = slot / SPR, s = slot % SPR;
+      off[i] = s < R / 16 ? (uint32_t)k * ld2 + (uint32_t)min(s, ncols / 8 - 1) * 16u
+                          : kPadOffset;
     }
   }
-  __device__ void issue(const bf16* base, int ld, int k0, int kmax, bf16* lds) const {
-    const int wid = threadIdx.x >> 6;
-    const char* b = reinterpret_cast<const char*>(base + (size_t)k0 * ld);
-    const int kend = kmax - k0;  // rows of this stage that exist
+  __device__ Rsrc rsrc(bool live) const { return make_rsrc(base, live ? bytes : 0u); }
+  __device__ uint32_t soff(int k0) const { return (uint32_t)k0 * ld2; }
+  template <int Q, int NQ>
+  __device__ void issue(Rsrc r, uint32_t so, char* stage, int wid) const {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int k = min(kl[i], kend - 1);
-      __builtin_amdgcn_global_load_lds(
-          b + (uint32_t)(k * ld * (int)sizeof(bf16)) + col[i],
-          (__attribute__((address_space(3))) void*)(lds + (i * 4 + wid) * RPI * ROWS), 16, 0, 0);
-    }
+    for (int i = 0; i < N; ++i)
+      if (i % NQ == Q) copy16(r, stage + (i * 4 + wid) * 1024, off[i], so);
   }
-  // Same operand block from the transposed layout: 16-lane group G = l/16
-  // covers columns r0 + 16*(G&1) .. +15 and k from kk*16 + 8*(G>>1); two
-  // transposed reads of 4 k each.
-  __device__ static bf16x8 frag(const bf16* lds, int r0, int kk) {
+  static constexpr int issued(int Q, int NQ) {
+    int n = 0;
+    for (int i = 0; i < N; ++i) n += (i % NQ == Q);
+    return n;
+  }
+  // 16-lane group G = l/16 covers columns r0 + 16*(G&1) .. +15 and k from
+  // kk*16 + 8*(G>>1): lane r of the group addresses k-row + r/4, column
+  // + 4*(r%4)
+  __device__ static void lane_offsets(uint32_t (&lo)[NLO]) {
+    const int lane = threadIdx.x & 63, G = lane >> 4, r = lane & 15;
+    lo[0] = (uint32_t)((8 * (G >> 1) + (r >> 2)) * P + (16 * (G & 1) + 4 * (r & 3)) * 2);
+  }
+  static constexpr int kReads = 2;
+  __device__ static bf16x8 frag(const char* stage, int r0, int kk, const uint32_t (&lo)[NLO]) {
     typedef __attribute__((ext_vector_type(4))) short s16x4;
     typedef __attribute__((ext_vector_type(2))) int i32x2;
-    const int lane = threadIdx.x & 63, G = lane >> 4, r = lane & 15;
-    const int n = r0 + 16 * (G & 1) + 4 * (r & 3);
     i32x4 out;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int k = kk * 16 + 8 * (G >> 1) + h * 4 + (r >> 2);
-      const int byte = k * R + (((n >> 3) ^ sw(k)) << 4) + (((n >> 2) & 1) << 3);
       const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)((const char*)lds + byte));
+          (__attribute__((address_space(3))) s16x4*)(stage + r0 * 2 + (kk * 16 + h * 4) * P +
+                                                     lo[0]));
       // reinterpret all 8 bytes at once (element-wise casts of this result
       // have been seen to be lowered wrongly)
       const i32x2 w = __builtin_bit_cast(i32x2, v);
@@ -145,21 +191,9 @@ struct TileMN {
     }
     return __builtin_bit_cast(bf16x8, out);
   }
-  // zero fragment entries whose k (stage-relative) is >= kend
-  __device__ static void mask_k(bf16x8& f, int kk, int kend) {
-    const int k0 = kk * 16 + ((threadIdx.x & 63) >> 5) * 8;
-    i32x4 w = __builtin_bit_cast(i32x4, f);  // element 2q = low half of dword q
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const unsigned keep = (k0 + 2 * q < kend ? 0x0000ffffu : 0u) |
-                            (k0 + 2 * q + 1 < kend ? 0xffff0000u : 0u);
-      w[q] = (int)((unsigned)w[q] & keep);
-    }
-    f = __builtin_bit_cast(bf16x8, w);
-  }
   // 16 bytes (8 columns) of k-row k at column chunk c, for the gate product
-  __device__ static bf16x8 chunk(const bf16* lds, int k, int c) {
-    return *reinterpret_cast<const bf16x8*>((const char*)lds + k * R + ((c ^ sw(k)) << 4));
+  __device__ static bf16x8 chunk(const char* stage, int k, int c) {
+    return *reinterpret_cast<const bf16x8*>(stage + k * P + c * 16);
   }
 };
 
@@ -169,6 +203,54 @@ template <int ROWS>
 struct Tile<true, ROWS> : TileK<ROWS> {};
 template <int ROWS>
 struct Tile<false, ROWS> : TileMN<ROWS> {};
+
+// Spread a region's LDS reads and copies between its MFMAs (one MFMA runs 32
+// cycles; the wave issues other instructions meanwhile).
+template <int NM, int ND, int NV>
+__device__ __forceinline__ void interleave() {
+  constexpr int a = NM < ND ? NM : ND;
+  constexpr int m2 = NM - a;
+  constexpr int b = m2 < NV ? m2 : NV;
+#pragma unroll
+  for (int t = 0; t < a; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+#pragma unroll
+  for (int t = 0; t < b; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+  }
+  if constexpr (ND > a) __builtin_amdgcn_sched_group_barrier(0x100, ND - a, 0);
+  if constexpr (NV > b) __builtin_amdgcn_sched_group_barrier(0x010, NV - b, 0);
+  if constexpr (m2 > b) __builtin_amdgcn_sched_group_barrier(0x008, m2 - b, 0);
+}
+
+template <int V>
+struct Ic {
+  static constexpr int value = V;
+};
+
+// The LDS stage buffers of a tile, each its own LDS object: the compiler can
+// then tell that the buffer being read is not the one the copies are filling
+// (with one shared array it waits for every copy before each transposed
+// read).  Unused third stages are 16 bytes.
+struct StageBufs {
+  char* a[3];
+  char* b[3];
+};
+template <class TG>
+__device__ __forceinline__ StageBufs tile_lds() {
+  constexpr int A3 = TG::kStages == 3 ? TG::TA::kBytes : 16;
+  constexpr int B3 = TG::kStages == 3 ? TG::TB::kBytes : 16;
+  __shared__ __attribute__((aligned(16))) char a0[TG::TA::kBytes];
+  __shared__ __attribute__((aligned(16))) char a1[TG::TA::kBytes];
+  __shared__ __attribute__((aligned(16))) char a2[A3];
+  __shared__ __attribute__((aligned(16))) char b0[TG::TB::kBytes];
+  __shared__ __attribute__((aligned(16))) char b1[TG::TB::kBytes];
+  __shared__ __attribute__((aligned(16))) char b2[B3];
+  return StageBufs{{a0, a1, a2}, {b0, b1, b2}};
+}
 
 // ---------------------------------------------------------------------------
 // One output tile: C[BM x BN] = sum_k A(m, k) B(n, k), k in [0, K), on 4
@@ -180,9 +262,14 @@ struct Tile<false, ROWS> : TileMN<ROWS> {};
 // n = 4 * (l / 32) + 8p, four consecutive columns of one row, which the
 // epilogue writes as one 8- or 16-byte store.
 //
-// Pipeline: three LDS stages, one barrier per 64-deep k step; stage kt+2 is
-// in flight while stage kt is computed, and before the barrier each wave
-// waits only for its loads of stage kt+1 (vmcnt = one stage's count).
+// Pipeline: 3 LDS stages (2 where 3 do not fit), one barrier per 64-deep k
+// step.  Step kt reads stage kt in four 16-deep slices, software-pipelined
+// over two register sets, and copies stage kt + stages - 1 into the buffer
+// stage kt - 1 used; the copies and the reads of the next slice are spread
+// between the MFMAs.  The last slice's MFMAs run after the barrier, covering
+// the latency of the first reads of the next stage.  Every step issues a full
+// stage of copies (past the end of K they are out of range and read nothing),
+// so a wave's outstanding-copy count is the same at every barrier.
 //
 // With GATE (B MN-contiguous) and a non-null `gsel`, the tile also forms
 // g[n] = sum_k gsel[k] B(n, k) for its columns from the LDS stages (gacc: per
@@ -190,20 +277,23 @@ struct Tile<false, ROWS> : TileMN<ROWS> {};
 // see gate_reduce().
 template <int BM, int BN, bool A_K, bool B_K, bool GATE = false>
 struct TileGemm {
+  using TA = Tile<A_K, BM>;
+  using TB = Tile<B_K, BN>;
   static constexpr int WM = BM / 2, WN = BN / 2;  // 2 x 2 waves
   static constexpr int FM = WM / 32, FN = WN / 32;  // 32 x 32 MFMA blocks per wave
-  static constexpr size_t kStageBytes = (size_t)(BM + BN) * kBK * sizeof(bf16);
-  // three stages when they fit in LDS (next to ~2 KiB of scheduler state),
-  // else two
-  static constexpr int kStages = 3 * kStageBytes <= 152 * 1024 ? 3 : 2;
-  static constexpr int kStageOps = Tile<A_K, BM>::N + Tile<B_K, BN>::N;
-  static constexpr size_t kLdsPipe = (size_t)kStages * kStageBytes;
+  static constexpr size_t kStageBytes = (size_t)TA::kBytes + TB::kBytes;
+  // three stages when they fit in LDS next to the kernels' own few KiB
+  static constexpr int kStages = 3 * kStageBytes + 4096 <= 160 * 1024 ? 3 : 2;
+  static constexpr int kStageOps = TA::N + TB::N;
+  static constexpr int kReads = FM * TA::kReads + FN * TB::kReads;  // LDS reads per slice
   f32x16 acc[FN][FM];  // acc[i][j]: n-block i, m-block j
   float gacc[8];
   float gdb;
 
+  // A: rows [0, a_rows) (K-contiguous) or columns [0, a_rows) over k rows
+  // [0, K) (MN-contiguous); likewise B.
   __device__ void run(const bf16* A, int lda, int a_rows, const bf16* B, int ldb, int b_rows,
-                      int K, bf16* lds, const float* gsel = nullptr) {
+                      int K, const StageBufs& L, const float* gsel = nullptr) {
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -215,73 +305,53 @@ struct TileGemm {
     }
     const int nk = (K + kBK - 1) / kBK;
     if (nk == 0) return;
-    bf16* const a_lds = lds;                          // [3][BM * 64]
-    bf16* const b_lds = lds + kStages * BM * kBK;     // [3][BN * 64]
-    Tile<A_K, BM> ta;
-    Tile<B_K, BN> tb;
-    ta.init(lda, a_rows);
-    tb.init(ldb, b_rows);
-    auto issue = [&](int kt) {
-      const int s = kt % kStages;
-      ta.issue(A, lda, kt * kBK, K, a_lds + s * (BM * kBK));
-      tb.issue(B, ldb, kt * kBK, K, b_lds + s * (BN * kBK));
-    };
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int wid = (int)uniform(threadIdx.x >> 6);
     const int wm = wid >> 1, wn = wid & 1;
+    TA ta;
+    TB tb;
+    ta.init(A, lda, a_rows, K, wid);
+    tb.init(B, ldb, b_rows, K, wid);
+    uint32_t alo[TA::NLO], blo[TB::NLO];
+    TA::lane_offsets(alo);
+    TB::lane_offsets(blo);
+
+    auto load = [&](const char* as, const char* bs, int kk, bf16x8(&a)[FM], bf16x8(&b)[FN]) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) a[j] = TA::frag(as, wm * WM + j * 32, kk, alo);
+#pragma unroll
+      for (int i = 0; i < FN; ++i) b[i] = TB::frag(bs, wn * WN + i * 32, kk, blo);
+    };
+    auto mma = [&](const bf16x8(&a)[FM], const bf16x8(&b)[FN]) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[i], a[j], acc[i][j], 0, 0, 0);
+    };
+    // a full stage of copies (prologue)
+    auto issue_all = [&](int kt, char* ad, char* bd) {
+      const bool live = kt < nk;
+      const Rsrc ra = ta.rsrc(live), rb = tb.rsrc(live);
+      const uint32_t sa = ta.soff(kt * kBK), sb = tb.soff(kt * kBK);
+      ta.template issue<0, 1>(ra, sa, ad, wid);
+      tb.template issue<0, 1>(rb, sb, bd, wid);
+    };
     constexpr int kGateRows = GATE ? kBK * (BN / 8) / kGemmThreads : 1;
     float gv[kGateRows];
-    auto compute = [&](int kt) {
-      const int s = kt % kStages;
-      const bf16* as = a_lds + s * (BM * kBK);
-      const bf16* bs = b_lds + s * (BN * kBK);
-      const int kend = K - kt * kBK;  // < 64 only on a ragged last step
-      // all A and B fragments of one 16-deep k slice
-      auto load = [&](int kk, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+    // gate weights of stage kt's rows for this thread
+    auto load_gate = [&](int kt) {
+      if constexpr (GATE) {
+        if (gsel != nullptr) {
+          const int kg = threadIdx.x / (BN / 8);
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          const int r0 = wm * WM + j * 32;
-          if constexpr (A_K) {
-            a[j] = TileK<BM>::frag(as, r0, kk);
-          } else {
-            a[j] = TileMN<BM>::frag(as, r0, kk);
-            if (kend < kBK) TileMN<BM>::mask_k(a[j], kk, kend);
+          for (int q = 0; q < kGateRows; ++q) {
+            const int k = kt * kBK + kg * kGateRows + q;
+            gv[q] = (k < K) ? gsel[k] : 0.f;
           }
         }
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-          const int r0 = wn * WN + i * 32;
-          if constexpr (B_K)
-            b[i] = TileK<BN>::frag(bs, r0, kk);
-          else
-            b[i] = TileMN<BN>::frag(bs, r0, kk);
-        }
-      };
-      auto mma = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-          for (int j = 0; j < FM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[i], a[j], acc[i][j], 0, 0, 0);
-      };
-      // software pipeline: slice kk+1's fragments load while slice kk's
-      // MFMAs run (two register sets, alternating)
-      // (scheduling barriers keep the compiler from sinking each load next
-      // to its first use, which exposes the LDS latency every 4 MFMAs)
-      bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
-      load(0, a0, b0);
-      load(1, a1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      load(2, a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(a1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-      load(3, a1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(a1, b1);
+      }
+    };
+    auto gate_stage = [&](const char* bs) {
       if constexpr (GATE) {
         if (gsel != nullptr) {
           // thread: 8 columns (chunk c) of rows kg*kGateRows .. of this stage
@@ -298,47 +368,98 @@ struct TileGemm {
         }
       }
     };
-    // gate weights of stage kt's rows for this thread (loaded before the
-    // stage kt+2 copies are issued, so waiting for them never waits for those)
-    auto load_gate = [&](int kt) {
-      if constexpr (GATE) {
-        if (gsel != nullptr) {
-          const int kg = threadIdx.x / (BN / 8);
-#pragma unroll
-          for (int q = 0; q < kGateRows; ++q) {
-            const int k = kt * kBK + kg * kGateRows + q;
-            gv[q] = (k < K) ? gsel[k] : 0.f;
-          }
-        }
-      }
-    };
-    // stages 0 .. kStages-2 in flight before the loop; step kt issues stage
-    // kt + kStages - 1 and, before its barrier, waits for stage kt+1 (with
-    // three stages the one issued this step may stay in flight)
-    issue(0);
-    if (kStages == 3 && nk > 1) {
-      issue(1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageOps) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool ahead = kt + kStages - 1 < nk;
-      load_gate(kt);
-      if (ahead) issue(kt + kStages - 1);
-      compute(kt);
-      if (kStages == 3 && ahead)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageOps) : "memory");
+    // Wait for this wave's copies of the next stage (with three stages those
+    // of the stage after it stay in flight) and its own LDS reads, then meet
+    // the other waves.  Written out because __syncthreads() adds a release
+    // fence, which waits for every outstanding copy.
+    auto sync = [&]() {
+      if constexpr (kStages == 3)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kStageOps) : "memory");
       else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
+    // step kt on stage S = kt % stages; FIRST: no previous slice to finish
+    auto step = [&](auto S_, auto FIRST_, int kt) {
+      constexpr int S = decltype(S_)::value;
+      constexpr bool FIRST = decltype(FIRST_)::value != 0;
+      constexpr int SD = (S + kStages - 1) % kStages;  // buffer of stage kt-1
+      const char* as = L.a[S];
+      const char* bs = L.b[S];
+      char* const ad = L.a[SD];
+      char* const bd = L.b[SD];
+      const int kd = kt + kStages - 1;
+      const bool live = kd < nk;
+      const Rsrc ra = ta.rsrc(live), rb = tb.rsrc(live);
+      const uint32_t sa = ta.soff(kd * kBK), sb = tb.soff(kd * kBK);
+      constexpr int NM = FM * FN;
+      load_gate(kt);
+      __builtin_amdgcn_sched_barrier(0);
+      // region 0: slice 0 -> set 0; finish slice 3 of step kt-1 (set 1)
+      load(as, bs, 0, a0, b0);
+      ta.template issue<0, 4>(ra, sa, ad, wid);
+      tb.template issue<0, 4>(rb, sb, bd, wid);
+      if constexpr (!FIRST) mma(a1, b1);
+      interleave<FIRST ? 0 : NM, kReads, TA::issued(0, 4) + TB::issued(0, 4)>();
+      __builtin_amdgcn_sched_barrier(0);
+      // region 1: slice 1 -> set 1; slice 0
+      load(as, bs, 1, a1, b1);
+      ta.template issue<1, 4>(ra, sa, ad, wid);
+      tb.template issue<1, 4>(rb, sb, bd, wid);
+      mma(a0, b0);
+      interleave<NM, kReads, TA::issued(1, 4) + TB::issued(1, 4)>();
+      __builtin_amdgcn_sched_barrier(0);
+      // region 2: slice 2 -> set 0; slice 1
+      load(as, bs, 2, a0, b0);
+      ta.template issue<2, 4>(ra, sa, ad, wid);
+      tb.template issue<2, 4>(rb, sb, bd, wid);
+      mma(a1, b1);
+      interleave<NM, kReads, TA::issued(2, 4) + TB::issued(2, 4)>();
+      __builtin_amdgcn_sched_barrier(0);
+      // region 3: slice 3 -> set 1; slice 2
+      load(as, bs, 3, a1, b1);
+      ta.template issue<3, 4>(ra, sa, ad, wid);
+      tb.template issue<3, 4>(rb, sb, bd, wid);
+      mma(a0, b0);
+      interleave<NM, kReads, TA::issued(3, 4) + TB::issued(3, 4)>();
+      __builtin_amdgcn_sched_barrier(0);
+      gate_stage(bs);
+      sync();
+    };
+
+    // prologue: stages 0 .. stages-2 in flight, wait for stage 0
+    issue_all(0, L.a[0], L.b[0]);
+    if constexpr (kStages == 3) issue_all(1, L.a[1], L.b[1]);
+    sync();
+    step(Ic<0>{}, Ic<1>{}, 0);
+    // whole rounds of `stages` steps, then the rest (one loop exit)
+    int kt = 1;
+    for (; kt + kStages <= nk; kt += kStages) {
+      step(Ic<1 % kStages>{}, Ic<0>{}, kt);
+      if constexpr (kStages == 3) {
+        step(Ic<2>{}, Ic<0>{}, kt + 1);
+        step(Ic<0>{}, Ic<0>{}, kt + 2);
+      } else {
+        step(Ic<0>{}, Ic<0>{}, kt + 1);
+      }
     }
+    if (kt < nk) {
+      step(Ic<1 % kStages>{}, Ic<0>{}, kt);
+      if constexpr (kStages == 3) {
+        if (kt + 1 < nk) step(Ic<2>{}, Ic<0>{}, kt + 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
+    // copies past the end are still in flight: let them land before the
+    // caller reuses LDS
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   // Sum the per-thread gate partials over the row groups (fixed order) and
   // write out[n * out_stride] = g[n] for n < cols, and *db_out (if non-null).
-  // Uses the first LDS bytes; call after run() (which ends with a barrier).
+  // `red` is LDS (a stage buffer); call after run() (which ends with a barrier).
   __device__ void gate_reduce(float* red, int cols, float* out, int out_stride,
                               float* db_out) const {
     constexpr int RB = BN / 8, G = kGemmThreads / RB;
@@ -421,7 +542,6 @@ struct RowsArgs {
 template <int BM, int BN, bool B_K, int EPI>
 __global__ void __launch_bounds__(kGemmThreads)
 rows_gemm_kernel(RowsArgs p) {
-  extern __shared__ __attribute__((aligned(16))) bf16 lds[];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int s_tstart[MOE_MAX_EXPERTS + 1];
   __shared__ int s_scratch[kGemmThreads / 64 + 1];
@@ -467,13 +587,15 @@ rows_gemm_kernel(RowsArgs p) {
   const int n0 = nt * BN;
   const int cols = min(BN, p.N - n0);
 
-  TileGemm<BM, BN, true, B_K> tg;
+  using TG = TileGemm<BM, BN, true, B_K>;
+  TG tg;
+  const StageBufs L = tile_lds<TG>();
   const bf16* A = p.A + (size_t)row0 * p.K;
   const bf16* Bm = p.B + (size_t)e * p.b_stride;
   if (B_K) {
-    tg.run(A, p.K, rows, Bm + (size_t)n0 * p.K, p.K, cols, p.K, lds);
+    tg.run(A, p.K, rows, Bm + (size_t)n0 * p.K, p.K, cols, p.K, L);
   } else {
-    tg.run(A, p.K, rows, Bm + n0, p.N, cols, p.K, lds);
+    tg.run(A, p.K, rows, Bm + n0, p.N, cols, p.K, L);
   }
   store_tile<EPI>(tg, p.C + (size_t)row0 * p.N + n0, p.N, rows, cols,
                   p.aux ? p.aux + (size_t)row0 * p.N + n0 : nullptr, p.N);
@@ -500,7 +622,6 @@ struct WgradArgs {
 template <int BM, int BN, bool GATE>
 __global__ void __launch_bounds__(kGemmThreads)
 wgrad_kernel(WgradArgs p) {
-  extern __shared__ __attribute__((aligned(16))) bf16 lds[];
   __shared__ int s_perm[MOE_MAX_EXPERTS];
   __shared__ int s_cnt[MOE_MAX_EXPERTS];
   const int tid = threadIdx.x;
@@ -525,16 +646,18 @@ wgrad_kernel(WgradArgs p) {
   const int n1 = t1 * BM, n2 = t2 * BN;
   const int r0 = p.offsets[e], K = s_cnt[e];
   const int rows = min(BM, p.N1 - n1), cols = min(BN, p.N2 - n2);
-  TileGemm<BM, BN, false, false, GATE> tg;
+  using TG = TileGemm<BM, BN, false, false, GATE>;
+  TG tg;
+  const StageBufs L = tile_lds<TG>();
   const bool gate_here = GATE && t1 == 0;
   tg.run(p.X1 + (size_t)r0 * p.N1 + n1, p.N1, rows, p.X2 + (size_t)r0 * p.N2 + n2, p.N2, cols, K,
-         lds, gate_here ? p.gsel + r0 : nullptr);
+         L, gate_here ? p.gsel + r0 : nullptr);
   store_tile<EPI_F32>(tg, p.C + (size_t)e * p.N1 * p.N2 + (size_t)n1 * p.N2 + n2, p.N2, rows,
                       cols, nullptr, 0);
   if constexpr (GATE) {
     if (gate_here) {
       __syncthreads();
-      tg.gate_reduce(reinterpret_cast<float*>(lds), cols, p.dw_gate + (size_t)n2 * p.E + e, p.E,
+      tg.gate_reduce(reinterpret_cast<float*>(L.a[0]), cols, p.dw_gate + (size_t)n2 * p.E + e, p.E,
                      t2 == 0 ? p.db_gate + e : nullptr);
     }
   }
@@ -626,13 +749,8 @@ static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
   const long long nt = (p.N + BN - 1) / BN;
   const long long grid = mt_max * nt;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  constexpr size_t shm = TileGemm<BM, BN, true, B_K>::kLdsPipe;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&rows_gemm_kernel<BM, BN, B_K, EPI>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI>), dim3((unsigned)grid),
-                     dim3(kGemmThreads), shm, s, p);
+                     dim3(kGemmThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -656,12 +774,7 @@ static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const bf16*
 template <int BM, int BN, bool GATE>
 static hipError_t launch_wgrad_t(const WgradArgs& p, hipStream_t s) {
   const long long grid = (long long)p.E * ((p.N1 + BM - 1) / BM) * ((p.N2 + BN - 1) / BN);
-  constexpr size_t shm = TileGemm<BM, BN, false, false, GATE>::kLdsPipe;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&wgrad_kernel<BM, BN, GATE>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((wgrad_kernel<BM, BN, GATE>), dim3((unsigned)grid), dim3(kGemmThreads), shm,
+  hipLaunchKernelGGL((wgrad_kernel<BM, BN, GATE>), dim3((unsigned)grid), dim3(kGemmThreads), 0,
                      s, p);
   return hipGetLastError();
 }
