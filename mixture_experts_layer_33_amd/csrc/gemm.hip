@@ -28,6 +28,10 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
+#include <cmath>
+#include <type_traits>
+
 namespace moe {
 
 constexpr int kBK = 64;          // k per LDS stage
@@ -275,7 +279,7 @@ __device__ __forceinline__ StageBufs tile_lds() {
 // g[n] = sum_k gsel[k] B(n, k) for its columns from the LDS stages (gacc: per
 // thread, 8 columns over its share of the rows) and sum_k gsel[k] (gdb);
 // see gate_reduce().
-template <int BM, int BN, bool A_K, bool B_K, bool GATE = false>
+template <int BM, int BN, bool A_K, bool B_K, bool GATE = false, int STAGES = 0>
 struct TileGemm {
   using TA = Tile<A_K, BM>;
   using TB = Tile<B_K, BN>;
@@ -283,7 +287,8 @@ struct TileGemm {
   static constexpr int FM = WM / 32, FN = WN / 32;  // 32 x 32 MFMA blocks per wave
   static constexpr size_t kStageBytes = (size_t)TA::kBytes + TB::kBytes;
   // three stages when they fit in LDS next to the kernels' own few KiB
-  static constexpr int kStages = 3 * kStageBytes + 4096 <= 160 * 1024 ? 3 : 2;
+  static constexpr int kStages =
+      STAGES != 0 ? STAGES : (3 * kStageBytes + 4096 <= 160 * 1024 ? 3 : 2);
   static constexpr int kStageOps = TA::N + TB::N;
   static constexpr int kReads = FM * TA::kReads + FN * TB::kReads;  // LDS reads per slice
   f32x16 acc[FN][FM];  // acc[i][j]: n-block i, m-block j
@@ -480,48 +485,93 @@ struct TileGemm {
     }
   }
 };
-// Epilogue: in each 32 x 32 block lane l holds C[m][n..n+3] for m = l%32 and
-// n = 4*(l/32) + 8p (p = 0..3) (see TileGemm).  rows/cols bound the valid
-// part of the tile (cols is a multiple of 4).
+// Epilogue, staged through LDS so that global stores are whole row segments
+// (the MFMA layout puts 32 different rows in one wave's store).  In each
+// 32 x 32 block lane l holds C[m][n..n+3] for m = l%32 and n = 4*(l/32) + 8p
+// (p = 0..3) (see TileGemm).  Each wave writes one 32-row strip of its block
+// at a time to its own LDS region (rows padded by 16 bytes, so the 32 rows of
+// a write fall in different banks), then reads it back as 16-byte pieces of
+// whole rows, applies the mask and stores.  ReLU and the bf16 rounding happen
+// on the way in.  EPI_MASK: `aux` is a bit mask, bit (n % 32) of word
+// aux[m * ld_aux + n / 32] keeps element (m, n); a lane's words for the whole
+// tile are loaded first, in one round trip.  rows/cols bound the valid part
+// of the tile (cols is a multiple of 8).  Call after run(); uses the stage
+// buffers.
 template <int EPI, class TG>
-__device__ __forceinline__ void store_tile(const TG& tg, void* C, int ldc, int rows, int cols,
-                                           const bf16* aux, int ld_aux) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+__device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, void* C, int ldc,
+                                           int rows, int cols, const uint32_t* aux, int ld_aux) {
+  using OutT = typename std::conditional<EPI == EPI_F32, float, bf16>::type;
+  constexpr int ES = sizeof(OutT);
+  constexpr int WN = TG::WN, WM = TG::WM;
+  constexpr int PITCH = WN * ES + 16;    // bytes per staged row
+  constexpr int CPR = WN * ES / 16;      // 16-byte pieces per row
+  constexpr int RPI = 64 / CPR;          // rows per wave instruction
+  static_assert(32 * PITCH <= TG::TA::kBytes && 32 * PITCH <= TG::TB::kBytes,
+                "a wave's strip must fit in one stage buffer");
+  const int lane = threadIdx.x & 63, wid = (int)uniform(threadIdx.x >> 6);
   const int wm = wid >> 1, wn = wid & 1;
+  // wave w stages in a[0], a[1], b[0], b[1]
+  char* const strip = wid == 0 ? L.a[0] : wid == 1 ? L.a[1] : wid == 2 ? L.b[0] : L.b[1];
+  const int n0 = wn * WN;
+  constexpr int IT = 32 / RPI;  // row-phase iterations per strip
+  uint32_t mw[EPI == EPI_MASK ? TG::FM * IT : 1];
+  if constexpr (EPI == EPI_MASK) {
+#pragma unroll
+    for (int j = 0; j < TG::FM; ++j)
+#pragma unroll
+      for (int t = 0; t < IT; ++t) {
+        const int m = wm * WM + j * 32 + t * RPI + lane / CPR;
+        const int n = n0 + (lane % CPR) * 8;
+        mw[j * IT + t] = m < rows ? aux[(size_t)m * ld_aux + n / 32] : 0u;
+      }
+  }
 #pragma unroll
   for (int j = 0; j < TG::FM; ++j) {
-    const int m = wm * TG::WM + j * 32 + (lane & 31);
-    if (m >= rows) continue;
+    const int m0 = wm * WM + j * 32;
+    // registers -> LDS
 #pragma unroll
     for (int i = 0; i < TG::FN; ++i) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int n = wn * TG::WN + i * 32 + 4 * (lane >> 5) + 8 * p;
-        if (n >= cols) continue;
-        f32x4 v;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = tg.acc[i][j][4 * p + q];
+        const int c = i * 32 + 4 * (lane >> 5) + 8 * p;
+        char* dst = strip + (lane & 31) * PITCH + c * ES;
         if constexpr (EPI == EPI_F32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + (size_t)m * ldc + n) = v;
+          f32x4 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = tg.acc[i][j][4 * p + q];
+          *reinterpret_cast<f32x4*>(dst) = v;
         } else {
-          if constexpr (EPI == EPI_RELU) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = fmaxf(v[q], 0.f);
-          }
-          if constexpr (EPI == EPI_MASK) {
-            const bf16x4 hv = *reinterpret_cast<const bf16x4*>(aux + (size_t)m * ld_aux + n);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (!((float)hv[q] > 0.f)) v[q] = 0.f;
-          }
           bf16x4 o;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = (bf16)v[q];
-          *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(C) + (size_t)m * ldc + n) = o;
+          for (int q = 0; q < 4; ++q) {
+            float v = tg.acc[i][j][4 * p + q];
+            if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+            o[q] = (bf16)v;
+          }
+          *reinterpret_cast<bf16x4*>(dst) = o;
         }
       }
-      // keep the scheduler from hoisting every accumulator read to the top
-      __builtin_amdgcn_sched_barrier(0);
+    }
+    // LDS -> global, whole row pieces (LDS accesses of one wave stay in order)
+#pragma unroll
+    for (int t = 0; t < IT; ++t) {
+      const int r = t * RPI + lane / CPR, c = (lane % CPR) * (16 / ES);
+      const i32x4 v = *reinterpret_cast<const i32x4*>(strip + r * PITCH + c * ES);
+      const int m = m0 + r, n = n0 + c;
+      if (m < rows && n < cols) {
+        const size_t at = (size_t)m * ldc + n;
+        if constexpr (EPI == EPI_MASK) {
+          const uint32_t keep = mw[j * IT + t] >> (n & 31);
+          i32x4 o = v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)  // dword q holds elements 2q (low) and 2q+1
+            o[q] &= (int)(((keep >> (2 * q)) & 1u ? 0x0000ffffu : 0u) |
+                          ((keep >> (2 * q + 1)) & 1u ? 0xffff0000u : 0u));
+          *reinterpret_cast<i32x4*>(reinterpret_cast<bf16*>(C) + at) = o;
+        } else {
+          *reinterpret_cast<i32x4*>(reinterpret_cast<OutT*>(C) + at) = v;
+        }
+      }
     }
   }
 }
@@ -533,7 +583,7 @@ struct RowsArgs {
   const bf16* A;        // [rows][K]
   const bf16* B;        // per expert: [N][K] (B_K) or [K][N]; expert stride b_stride
   bf16* C;              // [rows][N]
-  const bf16* aux;      // mask source for EPI_MASK, [rows][N]
+  const uint32_t* aux;  // EPI_MASK: keep bits, [rows][N / 32] words
   const int32_t* offsets;
   long long b_stride;
   int K, N, E;
@@ -597,8 +647,8 @@ rows_gemm_kernel(RowsArgs p) {
   } else {
     tg.run(A, p.K, rows, Bm + n0, p.N, cols, p.K, L);
   }
-  store_tile<EPI>(tg, p.C + (size_t)row0 * p.N + n0, p.N, rows, cols,
-                  p.aux ? p.aux + (size_t)row0 * p.N + n0 : nullptr, p.N);
+  store_tile<EPI>(tg, L, p.C + (size_t)row0 * p.N + n0, p.N, rows, cols,
+                  p.aux ? p.aux + (size_t)row0 * (p.N / 32) + n0 / 32 : nullptr, p.N / 32);
 }
 
 // ---------------------------------------------------------------------------
@@ -652,7 +702,7 @@ wgrad_kernel(WgradArgs p) {
   const bool gate_here = GATE && t1 == 0;
   tg.run(p.X1 + (size_t)r0 * p.N1 + n1, p.N1, rows, p.X2 + (size_t)r0 * p.N2 + n2, p.N2, cols, K,
          L, gate_here ? p.gsel + r0 : nullptr);
-  store_tile<EPI_F32>(tg, p.C + (size_t)e * p.N1 * p.N2 + (size_t)n1 * p.N2 + n2, p.N2, rows,
+  store_tile<EPI_F32>(tg, L, p.C + (size_t)e * p.N1 * p.N2 + (size_t)n1 * p.N2 + n2, p.N2, rows,
                       cols, nullptr, 0);
   if constexpr (GATE) {
     if (gate_here) {
@@ -660,6 +710,29 @@ wgrad_kernel(WgradArgs p) {
       tg.gate_reduce(reinterpret_cast<float*>(L.a[0]), cols, p.dw_gate + (size_t)n2 * p.E + e, p.E,
                      t2 == 0 ? p.db_gate + e : nullptr);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Keep bits of the ReLU for the FC1 input gradient: bit q of word w is
+// h[32 w + q] > 0 over the packed rows [0, offsets[E]) of h [rows][F] (F is a
+// multiple of 32, so a word never spans two rows).  The dgrad epilogue then
+// reads one bit per element instead of h.
+__global__ void __launch_bounds__(256)
+relu_bits_kernel(const bf16* __restrict__ h, const int32_t* __restrict__ offsets, int E, int F,
+                 uint32_t* __restrict__ bits) {
+  const long long total = (long long)offsets[E] * (F / 32);
+  for (long long w = (long long)blockIdx.x * 256 + threadIdx.x; w < total;
+       w += (long long)gridDim.x * 256) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(h + w * 32);
+    uint32_t b = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8 v = src[q];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) b |= ((float)v[t] > 0.f ? 1u : 0u) << (q * 8 + t);
+    }
+    bits[w] = b;
   }
 }
 
@@ -726,11 +799,34 @@ MOE_ROWS_VARIANTS(128, 128)
 // ---------------------------------------------------------------------------
 // launchers
 
-// Tile shape per product: the largest tiles (fewest LDS bytes per flop) that
-// still give every CU work.  `mt(bm)` = number of row tiles for tile height bm.
+// Tile shape per product.  Row-grouped products: a small cost model, time ~
+// (rounds of one tile per CU) x (tile area) / (relative speed of the shape on
+// random bf16 data: 128x256 and 256x128 tiles do the most work per cycle,
+// 128x128 the least), with the row tiles estimated as an even spread of
+// S_max rows plus half a ragged tile per expert.  Weight gradients: the
+// largest tiles that still give every CU two.
 struct Shape2 {
   int bm, bn;
 };
+static Shape2 pick_rows_tile(int S_max, int E, int N) {
+  struct C {
+    int bm, bn;
+    double speed;
+  };
+  const C cand[] = {{128, 256, 1.15}, {256, 128, 1.12}, {256, 256, 1.0}, {128, 128, 0.95}};
+  Shape2 best{128, 128};
+  double best_t = 1e300;
+  for (const C& c : cand) {
+    const double tiles = (double)((S_max + c.bm - 1) / c.bm + E / 2) * ((N + c.bn - 1) / c.bn);
+    const double rounds = std::ceil(tiles / 256.0);
+    const double t = rounds * c.bm * c.bn / c.speed;
+    if (t < best_t) {
+      best_t = t;
+      best = {c.bm, c.bn};
+    }
+  }
+  return best;
+}
 template <class MT>
 static Shape2 pick_tile(MT mt, int N) {
   const long long want = 2 * 256;  // two tiles per CU
@@ -755,16 +851,11 @@ static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
 }
 
 template <bool B_K, int EPI>
-static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const bf16* aux,
+static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const uint32_t* aux,
                               const int32_t* offsets, long long b_stride, int K, int N, int E,
                               int S_max, hipStream_t s) {
   RowsArgs p{A, B, C, aux, offsets, b_stride, K, N, E};
-  // row tiles for an even spread of S_max rows over E experts
-  auto mt = [&](int bm) {
-    const long long per = ((long long)S_max / E + bm - 1) / bm;
-    return per * E;
-  };
-  const Shape2 t = pick_tile(mt, N);
+  const Shape2 t = pick_rows_tile(S_max, E, N);
   if (t.bm == 256 && t.bn == 256) return launch_rows_t<256, 256, B_K, EPI>(p, S_max, s);
   if (t.bm == 256 && t.bn == 128) return launch_rows_t<256, 128, B_K, EPI>(p, S_max, s);
   if (t.bm == 128 && t.bn == 256) return launch_rows_t<128, 256, B_K, EPI>(p, S_max, s);
@@ -823,13 +914,19 @@ hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets
 hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, const void* h,
                              const int32_t* offsets, const void* w1, const void* w2, void* dz,
                              void* dx_perm, float* dw1, float* dw2, const float* dsel_perm,
-                             float* dw_gate, float* db_gate, int S_max, int d, int F, int E,
-                             hipStream_t s) {
+                             float* dw_gate, float* db_gate, uint32_t* relu_bits, int S_max,
+                             int d, int F, int E, hipStream_t s) {
   if (act == MOE_BF16) {
-    // dz = (dO W2[e]) * [h > 0]: A = dO [rows][d], B = W2[e] as [K=d][N=F]
+    // keep bits of the ReLU, then dz = (dO W2[e]) * [h > 0]: A = dO [rows][d],
+    // B = W2[e] as [K=d][N=F]
+    const long long words = (long long)S_max * (F / 32);
+    const int blocks = (int)std::min<long long>((words + 255) / 256, 4096);
+    hipLaunchKernelGGL(relu_bits_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, s,
+                       (const bf16*)h, offsets, E, F, relu_bits);
+    MOE_TRY(hipGetLastError());
     MOE_TRY((launch_rows<false, EPI_MASK>((const bf16*)d_out, (const bf16*)w2, (bf16*)dz,
-                                          (const bf16*)h, offsets, (long long)d * F, d, F, E,
-                                          S_max, s)));
+                                          relu_bits, offsets, (long long)d * F, d, F, E, S_max,
+                                          s)));
     // dW2[e] = dO^T h  ([d][F])
     MOE_TRY((launch_wgrad<false>((const bf16*)d_out, (const bf16*)h, dw2, offsets, nullptr,
                                  nullptr, nullptr, d, F, E, s)));

@@ -66,11 +66,12 @@ hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets
                              int S_max, int d, int F, int E, hipStream_t s);
 // Backward GEMMs: dz = (dO W2[e]) * [h > 0]; dW2[e] = dO^T h;
 // dx_perm = dz W1[e]; dW1[e] = dz^T x_perm.
-// bf16 also folds dW_gate / db over the kept rows into the FC1 wgrad.
+// bf16 also folds dW_gate / db over the kept rows into the FC1 wgrad and
+// uses relu_bits ([S_max][F/32] words of scratch) for the ReLU mask.
 hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, const void* h,
                              const int32_t* offsets, const void* w1, const void* w2,
                              void* dz, void* dx_perm, float* dw1, float* dw2,
-                             const float* dsel_perm, float* dw_gate, float* db_gate, int S_max,
-                             int d, int F, int E, hipStream_t s);
+                             const float* dsel_perm, float* dw_gate, float* db_gate,
+                             uint32_t* relu_bits, int S_max, int d, int F, int E, hipStream_t s);
 
 }  // namespace moe

@@ -90,12 +90,13 @@ struct BwdWs {
   float* dsel;      // [T][k]  gate-softmax gradient per slot
   float* dsel_perm; // [S]     the same per packed row
   float* w_gate_t;  // [E][d]
+  uint32_t* relu_bits;  // [S][F/32] keep bits of the ReLU (bf16 path)
 };
 
 size_t bwd_ws_bytes(const moe_shape* s) {
   const size_t S = (size_t)slots(s), a = act_bytes(s);
   return align_up(S * s->d_model * a) + align_up(S * s->d_ff * a) + 2 * align_up(S * 4) +
-         align_up((size_t)s->E * s->d_model * 4);
+         align_up((size_t)s->E * s->d_model * 4) + align_up(S * (size_t)s->d_ff / 8);
 }
 
 BwdWs carve_bwd(const moe_shape* s, void* ws) {
@@ -111,6 +112,8 @@ BwdWs carve_bwd(const moe_shape* s, void* ws) {
   w.dsel_perm = reinterpret_cast<float*>(p);
   p += align_up(S * 4);
   w.w_gate_t = reinterpret_cast<float*>(p);
+  p += align_up((size_t)s->E * s->d_model * 4);
+  w.relu_bits = reinterpret_cast<uint32_t*>(p);
   return w;
 }
 
@@ -316,8 +319,8 @@ moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const
   // the last reader of d_out.  For bf16 the FC1 wgrad also writes dW_gate and
   // db over the kept rows.
   MOE_HIP(launch_expert_bwd(act, bw.d_out, x_perm, h, offsets, w1, w2, bw.dz, bw.d_out, dw1, dw2,
-                            bw.dsel_perm, dw_gate, db_gate, (int)slots(s), s->d_model, s->d_ff,
-                            s->E, stream_));
+                            bw.dsel_perm, dw_gate, db_gate, bw.relu_bits, (int)slots(s),
+                            s->d_model, s->d_ff, s->E, stream_));
   if (act != MOE_BF16)
     MOE_HIP(launch_gate_rows(act, x_perm, bw.dsel_perm, offsets, dw_gate, db_gate, s->d_model,
                              s->E, stream_));
