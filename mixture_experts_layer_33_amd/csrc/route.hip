@@ -158,31 +158,43 @@ __global__ void split_gate_kernel(const float* __restrict__ w_gate, bf16* __rest
   }
 }
 
-constexpr int kRouteMfmaTok = 64;  // tokens per workgroup, 16 per wavefront
-
-// LDS row of BK bf16 (BK/8 16-byte chunks), chunks XOR-swizzled by row.
-template <int BK>
+// LDS row of SW bf16 (SW/8 16-byte chunks), chunks XOR-swizzled by the low
+// row bits so that the 16 rows of an MFMA operand read fall in different
+// banks.
+template <int SW>
 __device__ __forceinline__ int rswz(int row, int kc) {
-  return row * BK + ((kc ^ (row & (BK / 8 - 1))) * 8);
+  constexpr int XM = (SW / 8 < 16 ? SW / 8 : 16) - 1;
+  return row * SW + ((kc ^ (row & XM)) * 8);
 }
 
-template <int EP>
+// Router logits on MFMA (v_mfma_f32_16x16x32_bf16, 16 tokens x 16 experts per
+// block).  Four wavefronts; KS of them share one group of 16 tokens and split
+// the k range of every LDS stage between them, their partial logits summed
+// in LDS in a fixed order, so a workgroup covers 64 / KS tokens (KS > 1 gives
+// small batches enough workgroups).  The three bf16 parts of W_gate go
+// through LDS; x fragments are read straight from memory one stage ahead.
+template <int EP, int KS>
 __global__ void __launch_bounds__(256)
 route_mfma_kernel(const bf16* __restrict__ x, const bf16* __restrict__ wsplit,
                   const float* __restrict__ b_gate, float* __restrict__ logits_out,
                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int d, int E,
                   int k) {
-  constexpr int BK = EP > 128 ? 32 : 64;
+  constexpr int BK = EP > 128 ? 32 : 64;          // k per wavefront per stage
+  constexpr int SW = KS * BK;                     // k per stage
   constexpr int FN = EP / 16;
   constexpr int ROWS = 3 * EP;                    // LDS rows per stage
-  constexpr int CPR = BK / 8;                     // chunks per row
+  constexpr int CPR = SW / 8;                     // chunks per row
   constexpr int NQ = ROWS * CPR;                  // chunks per stage
   constexpr int NCH = (NQ + 255) / 256;           // chunks per thread
-  __shared__ __attribute__((aligned(16))) bf16 lds[2][ROWS * BK];
+  constexpr int TPW = 64 / KS;                    // tokens per workgroup
+  constexpr int NS = BK / 32;                     // MFMA k slices per wavefront per stage
+  __shared__ __attribute__((aligned(16))) bf16 lds[2][ROWS * SW];
+  __shared__ f32x4 red[KS > 1 ? 4 : 1][KS > 1 ? 64 * FN : 1];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int t0 = blockIdx.x * kRouteMfmaTok + wid * 16;
+  const int grp = wid / KS, ks = wid % KS;
+  const int t0 = blockIdx.x * TPW + grp * 16;
   const int ta = min(t0 + (lane & 15), T - 1);  // A-fragment row (clamped)
-  const bf16* xrow = x + (size_t)ta * d;
+  const bf16* xrow = x + (size_t)ta * d + ks * BK + (lane >> 4) * 8;
   f32x4 acc[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -200,32 +212,60 @@ route_mfma_kernel(const bf16* __restrict__ x, const bf16* __restrict__ wsplit,
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int q = tid + c * 256, row = q / CPR, kc = q % CPR;
-      if (NQ % 256 == 0 || q < NQ) *reinterpret_cast<i32x4*>(&lds[buf][rswz<BK>(row, kc)]) = stage[c];
+      if (NQ % 256 == 0 || q < NQ)
+        *reinterpret_cast<i32x4*>(&lds[buf][rswz<SW>(row, kc)]) = stage[c];
     }
   };
-  const int nk = d / BK;
+  bf16x8 xc[NS], xn[NS];
+  auto load_x = [&](int kt, bf16x8(&dst)[NS]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      dst[s] = *reinterpret_cast<const bf16x8*>(xrow + (size_t)kt * SW + s * 32);
+  };
+  const int nk = d / SW;
   load_stage(0);
+  load_x(0, xc);
   store_stage(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_stage((kt + 1) * BK);
+    if (kt + 1 < nk) {
+      load_stage((kt + 1) * SW);
+      load_x(kt + 1, xn);
+    }
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      const int kc = ks * 4 + (lane >> 4);
-      const bf16x8 a =
-          *reinterpret_cast<const bf16x8*>(xrow + kt * BK + kc * 8);
+    for (int s = 0; s < NS; ++s) {
+      const int kc = ks * (BK / 8) + s * 4 + (lane >> 4);
 #pragma unroll
       for (int p = 0; p < 3; ++p)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int row = p * EP + j * 16 + (lane & 15);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&lds[cur][rswz<BK>(row, kc)]);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&lds[cur][rswz<SW>(row, kc)]);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xc[s], b, acc[j], 0, 0, 0);
         }
     }
     if (kt + 1 < nk) store_stage(cur ^ 1);
     __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) xc[s] = xn[s];
+  }
+  if constexpr (KS > 1) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) red[wid][lane * FN + j] = acc[j];
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      f32x4 sum = red[wid][lane * FN + j];
+#pragma unroll
+      for (int q = 1; q < KS; ++q) {
+        const f32x4 o = red[wid + q][lane * FN + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[i] += o[i];
+      }
+      acc[j] = sum;
+    }
   }
 
   // lane holds tokens t0 + (lane/16)*4 + i (i < 4), experts j*16 + lane%16
@@ -311,31 +351,31 @@ hipError_t launch_route(int act, const void* x, const float* w_gate, const float
                        w_gate, (bf16*)wsplit, d, E, EP);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    dim3 grid((T + kRouteMfmaTok - 1) / kRouteMfmaTok), block(256);
+    // split each stage's k range over KS wavefronts when the batch is too
+    // small to give every CU two workgroups of 64 tokens (LDS and d permitting)
+    int ks = 1;
+    const int bk = EP > 128 ? 32 : 64;
+    const int max_ks = EP <= 32 ? 4 : EP == 64 ? 2 : 1;
+    while (ks < max_ks && (T + 64 / ks - 1) / (64 / ks) < 512 && d % (2 * ks * bk) == 0) ks *= 2;
+    dim3 grid((T + 64 / ks - 1) / (64 / ks)), block(256);
     const bf16* xs = (const bf16*)x;
     const bf16* wsp = (const bf16*)wsplit;
-    switch (EP) {
-      case 16:
-        hipLaunchKernelGGL(route_mfma_kernel<16>, grid, block, 0, s, xs, wsp, b_gate, logits_out,
-                           topk_idx, topk_w, T, d, E, k);
-        break;
-      case 32:
-        hipLaunchKernelGGL(route_mfma_kernel<32>, grid, block, 0, s, xs, wsp, b_gate, logits_out,
-                           topk_idx, topk_w, T, d, E, k);
-        break;
-      case 64:
-        hipLaunchKernelGGL(route_mfma_kernel<64>, grid, block, 0, s, xs, wsp, b_gate, logits_out,
-                           topk_idx, topk_w, T, d, E, k);
-        break;
-      case 128:
-        hipLaunchKernelGGL(route_mfma_kernel<128>, grid, block, 0, s, xs, wsp, b_gate, logits_out,
-                           topk_idx, topk_w, T, d, E, k);
-        break;
-      default:
-        hipLaunchKernelGGL(route_mfma_kernel<256>, grid, block, 0, s, xs, wsp, b_gate, logits_out,
-                           topk_idx, topk_w, T, d, E, k);
-        break;
+#define MOE_ROUTE(EPV, KSV)                                                                 \
+  hipLaunchKernelGGL((route_mfma_kernel<EPV, KSV>), grid, block, 0, s, xs, wsp, b_gate,      \
+                     logits_out, topk_idx, topk_w, T, d, E, k)
+    switch (EP * 8 + ks) {
+      case 16 * 8 + 4: MOE_ROUTE(16, 4); break;
+      case 16 * 8 + 2: MOE_ROUTE(16, 2); break;
+      case 16 * 8 + 1: MOE_ROUTE(16, 1); break;
+      case 32 * 8 + 4: MOE_ROUTE(32, 4); break;
+      case 32 * 8 + 2: MOE_ROUTE(32, 2); break;
+      case 32 * 8 + 1: MOE_ROUTE(32, 1); break;
+      case 64 * 8 + 2: MOE_ROUTE(64, 2); break;
+      case 64 * 8 + 1: MOE_ROUTE(64, 1); break;
+      case 128 * 8 + 1: MOE_ROUTE(128, 1); break;
+      default: MOE_ROUTE(256, 1); break;
     }
+#undef MOE_ROUTE
     return hipGetLastError();
   }
   dim3 grid((T + kRouteTok - 1) / kRouteTok), block(kRouteThreads);
