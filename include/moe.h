@@ -142,10 +142,15 @@ moe_status moe_permute(const moe_shape* shape, const void* x, const int32_t* top
  *   h = ReLU(x_perm_e * w1[e]^T), out_perm = h * w2[e]^T
  * with float32 accumulation; h and out_perm stored in the activation type
  * (h is kept for the backward).  Rows past offsets[E] are not touched.
+ * relu_bits (optional, bf16 only; NULL = not written): [T*k][d_ff/32]
+ * words, bit (f % 32) of word [r][f / 32] set iff h[r][f] > 0, over rows
+ * [0, offsets[E]); moe_backward can take it instead of deriving the ReLU
+ * mask from h.  Ignored for MOE_F32.
  * Workspace: MOE_OP_EXPERT_FFN (0 bytes; argument may be NULL). */
 moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int32_t* offsets,
                           const void* w1, const void* w2, void* h, void* out_perm,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          uint32_t* relu_bits, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Output decode (survey §5, first paragraph: the inverse of input encode,
  * restoring token order from the gating indices).  y[t] = sum over kept
@@ -155,15 +160,16 @@ moe_status moe_combine(const moe_shape* shape, const void* out_perm, const float
                        const int32_t* slot_row, void* y, void* stream);
 
 /* The whole forward: moe_route, moe_permute, moe_expert_ffn, moe_combine on
- * one stream.  logits_out and counts_raw may be NULL.  Every other output
- * is kept for moe_backward.  Workspace: MOE_OP_FORWARD. */
+ * one stream.  logits_out, counts_raw and relu_bits may be NULL.  Every
+ * other output (and relu_bits if given) is kept for moe_backward.
+ * Workspace: MOE_OP_FORWARD. */
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gate,
                        const float* b_gate, const void* w1, const void* w2, void* y,
                        float* logits_out, int32_t* topk_idx, float* topk_w,
                        int32_t* counts_raw, int32_t* counts_kept, int32_t* offsets,
                        int32_t* slot_row, int32_t* row_token, void* x_perm, void* h,
-                       void* out_perm, void* workspace, size_t workspace_bytes,
-                       void* stream);
+                       void* out_perm, uint32_t* relu_bits, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* Backward of moe_forward for output gradient dy (PopFetcher notes §5.2.1:
  * one GEMM pass forward, two backward - gradients of the inputs and of the
@@ -174,16 +180,18 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
  *   dlogits      float32 [T,E] if non-NULL
  * Gate: w = softmax of the selected logits, so dlogits[t, idx_j] =
  * w_j (dg_j - sum_i w_i dg_i) with dg_j = <dy[t], out_perm[row_j]> (0 for a
- * dropped slot); other logits get 0.  ReLU'(0) = 0, mask read from h.
- * Workspace: MOE_OP_BACKWARD. */
+ * dropped slot); other logits get 0.  ReLU'(0) = 0, mask [h > 0]: from
+ * relu_bits when given (as written by moe_forward / moe_expert_ffn for
+ * these h), else derived from h.  Workspace: MOE_OP_BACKWARD. */
 moe_status moe_backward(const moe_shape* shape, const void* dy, const void* x,
                         const float* w_gate, const void* w1, const void* w2,
                         const int32_t* topk_idx, const float* topk_w,
                         const int32_t* slot_row, const int32_t* row_token,
                         const int32_t* offsets, const void* x_perm, const void* h,
-                        const void* out_perm, void* dx, float* dw1, float* dw2,
-                        float* dw_gate, float* db_gate, float* dlogits,
-                        void* workspace, size_t workspace_bytes, void* stream);
+                        const void* out_perm, const uint32_t* relu_bits, void* dx,
+                        float* dw1, float* dw2, float* dw_gate, float* db_gate,
+                        float* dlogits, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* Per-expert popularity over a sliding window of iterations (PopFetcher
  * notes §3.1, routing-information collector; §4.2, Eq. 1: token

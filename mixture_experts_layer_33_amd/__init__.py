@@ -73,10 +73,10 @@ def lib() -> ctypes.CDLL:
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_route.argtypes = [sp] + [_P] * 8 + [_P, ctypes.c_size_t, _P]
         L.moe_permute.argtypes = [sp] + [_P] * 8 + [_P, ctypes.c_size_t, _P]
-        L.moe_expert_ffn.argtypes = [sp] + [_P] * 6 + [_P, ctypes.c_size_t, _P]
+        L.moe_expert_ffn.argtypes = [sp] + [_P] * 7 + [_P, ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [sp] + [_P] * 4 + [_P]
-        L.moe_forward.argtypes = [sp] + [_P] * 17 + [_P, ctypes.c_size_t, _P]
-        L.moe_backward.argtypes = [sp] + [_P] * 19 + [_P, ctypes.c_size_t, _P]
+        L.moe_forward.argtypes = [sp] + [_P] * 18 + [_P, ctypes.c_size_t, _P]
+        L.moe_backward.argtypes = [sp] + [_P] * 20 + [_P, ctypes.c_size_t, _P]
         L.moe_popularity_update.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                             _P, _P, _P, _P]
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
@@ -156,11 +156,12 @@ def moe_permute(shape, x, topk_idx, counts_raw, counts_kept, offsets, slot_row, 
                              _ptr(x_perm), ws, nb, _stream(stream)), "moe_permute")
 
 
-def moe_expert_ffn(shape, x_perm, offsets, w1, w2, h, out_perm, workspace=None, stream=None):
+def moe_expert_ffn(shape, x_perm, offsets, w1, w2, h, out_perm, relu_bits=None, workspace=None,
+                   stream=None):
     ws, nb = _ws(workspace)
     _check(lib().moe_expert_ffn(ctypes.byref(shape), _ptr(x_perm), _ptr(offsets), _ptr(w1),
-                                _ptr(w2), _ptr(h), _ptr(out_perm), ws, nb, _stream(stream)),
-           "moe_expert_ffn")
+                                _ptr(w2), _ptr(h), _ptr(out_perm), _ptr(relu_bits), ws, nb,
+                                _stream(stream)), "moe_expert_ffn")
 
 
 def moe_combine(shape, out_perm, topk_w, slot_row, y, stream=None):
@@ -169,26 +170,26 @@ def moe_combine(shape, out_perm, topk_w, slot_row, y, stream=None):
 
 
 def moe_forward(shape, x, w_gate, b_gate, w1, w2, y, logits_out, topk_idx, topk_w, counts_raw,
-                counts_kept, offsets, slot_row, row_token, x_perm, h, out_perm, workspace,
-                stream=None):
+                counts_kept, offsets, slot_row, row_token, x_perm, h, out_perm, relu_bits,
+                workspace, stream=None):
     ws, nb = _ws(workspace)
     _check(lib().moe_forward(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(b_gate), _ptr(w1),
                              _ptr(w2), _ptr(y), _ptr(logits_out), _ptr(topk_idx), _ptr(topk_w),
                              _ptr(counts_raw), _ptr(counts_kept), _ptr(offsets), _ptr(slot_row),
-                             _ptr(row_token), _ptr(x_perm), _ptr(h), _ptr(out_perm), ws, nb,
-                             _stream(stream)), "moe_forward")
+                             _ptr(row_token), _ptr(x_perm), _ptr(h), _ptr(out_perm),
+                             _ptr(relu_bits), ws, nb, _stream(stream)), "moe_forward")
 
 
 def moe_backward(shape, dy, x, w_gate, w1, w2, topk_idx, topk_w, slot_row, row_token, offsets,
-                 x_perm, h, out_perm, dx, dw1, dw2, dw_gate, db_gate, dlogits, workspace,
-                 stream=None):
+                 x_perm, h, out_perm, relu_bits, dx, dw1, dw2, dw_gate, db_gate, dlogits,
+                 workspace, stream=None):
     ws, nb = _ws(workspace)
     _check(lib().moe_backward(ctypes.byref(shape), _ptr(dy), _ptr(x), _ptr(w_gate), _ptr(w1),
                               _ptr(w2), _ptr(topk_idx), _ptr(topk_w), _ptr(slot_row),
                               _ptr(row_token), _ptr(offsets), _ptr(x_perm), _ptr(h),
-                              _ptr(out_perm), _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(dw_gate),
-                              _ptr(db_gate), _ptr(dlogits), ws, nb, _stream(stream)),
-           "moe_backward")
+                              _ptr(out_perm), _ptr(relu_bits), _ptr(dx), _ptr(dw1), _ptr(dw2),
+                              _ptr(dw_gate), _ptr(db_gate), _ptr(dlogits), ws, nb,
+                              _stream(stream)), "moe_backward")
 
 
 def moe_popularity_update(E, window, it, counts_raw, ring, window_sum, stream=None):

@@ -499,7 +499,8 @@ struct TileGemm {
 // buffers.
 template <int EPI, class TG>
 __device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, void* C, int ldc,
-                                           int rows, int cols, const uint32_t* aux, int ld_aux) {
+                                           int rows, int cols, const uint32_t* aux, int ld_aux,
+                                           uint8_t* bits_out = nullptr) {
   using OutT = typename std::conditional<EPI == EPI_F32, float, bf16>::type;
   constexpr int ES = sizeof(OutT);
   constexpr int WN = TG::WN, WM = TG::WM;
@@ -570,6 +571,15 @@ __device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, voi
           *reinterpret_cast<i32x4*>(reinterpret_cast<bf16*>(C) + at) = o;
         } else {
           *reinterpret_cast<i32x4*>(reinterpret_cast<OutT*>(C) + at) = v;
+          if constexpr (EPI == EPI_RELU) {
+            if (bits_out != nullptr) {  // byte n/8 of row m: bit q <=> element n + q > 0
+              const bf16x8 hv = __builtin_bit_cast(bf16x8, v);
+              uint32_t b = 0;
+#pragma unroll
+              for (int q = 0; q < 8; ++q) b |= ((float)hv[q] > 0.f ? 1u : 0u) << q;
+              bits_out[(size_t)m * (ldc / 8) + n / 8] = (uint8_t)b;
+            }
+          }
         }
       }
     }
@@ -584,6 +594,7 @@ struct RowsArgs {
   const bf16* B;        // per expert: [N][K] (B_K) or [K][N]; expert stride b_stride
   bf16* C;              // [rows][N]
   const uint32_t* aux;  // EPI_MASK: keep bits, [rows][N / 32] words
+  uint8_t* bits_out;    // EPI_RELU (optional): keep bits [C > 0], [rows][N / 8] bytes
   const int32_t* offsets;
   long long b_stride;
   int K, N, E;
@@ -648,7 +659,8 @@ rows_gemm_kernel(RowsArgs p) {
     tg.run(A, p.K, rows, Bm + n0, p.N, cols, p.K, L);
   }
   store_tile<EPI>(tg, L, p.C + (size_t)row0 * p.N + n0, p.N, rows, cols,
-                  p.aux ? p.aux + (size_t)row0 * (p.N / 32) + n0 / 32 : nullptr, p.N / 32);
+                  p.aux ? p.aux + (size_t)row0 * (p.N / 32) + n0 / 32 : nullptr, p.N / 32,
+                  p.bits_out ? p.bits_out + (size_t)row0 * (p.N / 8) + n0 / 8 : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -853,8 +865,8 @@ static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
 template <bool B_K, int EPI>
 static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const uint32_t* aux,
                               const int32_t* offsets, long long b_stride, int K, int N, int E,
-                              int S_max, hipStream_t s) {
-  RowsArgs p{A, B, C, aux, offsets, b_stride, K, N, E};
+                              int S_max, hipStream_t s, uint32_t* bits_out = nullptr) {
+  RowsArgs p{A, B, C, aux, reinterpret_cast<uint8_t*>(bits_out), offsets, b_stride, K, N, E};
   const Shape2 t = pick_rows_tile(S_max, E, N);
   if (t.bm == 256 && t.bn == 256) return launch_rows_t<256, 256, B_K, EPI>(p, S_max, s);
   if (t.bm == 256 && t.bn == 128) return launch_rows_t<256, 128, B_K, EPI>(p, S_max, s);
@@ -890,11 +902,12 @@ static hipError_t launch_wgrad(const bf16* X1, const bf16* X2, float* C, const i
   } while (0)
 
 hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets, const void* w1,
-                             const void* w2, void* h, void* out_perm, int S_max, int d, int F,
-                             int E, hipStream_t s) {
+                             const void* w2, void* h, void* out_perm, uint32_t* relu_bits,
+                             int S_max, int d, int F, int E, hipStream_t s) {
   if (act == MOE_BF16) {
     MOE_TRY((launch_rows<true, EPI_RELU>((const bf16*)x_perm, (const bf16*)w1, (bf16*)h, nullptr,
-                                         offsets, (long long)F * d, d, F, E, S_max, s)));
+                                         offsets, (long long)F * d, d, F, E, S_max, s,
+                                         relu_bits)));
     MOE_TRY((launch_rows<true, EPI_STORE>((const bf16*)h, (const bf16*)w2, (bf16*)out_perm,
                                           nullptr, offsets, (long long)d * F, F, d, E, S_max,
                                           s)));
@@ -914,16 +927,21 @@ hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets
 hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, const void* h,
                              const int32_t* offsets, const void* w1, const void* w2, void* dz,
                              void* dx_perm, float* dw1, float* dw2, const float* dsel_perm,
-                             float* dw_gate, float* db_gate, uint32_t* relu_bits, int S_max,
-                             int d, int F, int E, hipStream_t s) {
+                             float* dw_gate, float* db_gate, const uint32_t* relu_bits_in,
+                             uint32_t* relu_bits_ws, int S_max, int d, int F, int E,
+                             hipStream_t s) {
   if (act == MOE_BF16) {
-    // keep bits of the ReLU, then dz = (dO W2[e]) * [h > 0]: A = dO [rows][d],
-    // B = W2[e] as [K=d][N=F]
-    const long long words = (long long)S_max * (F / 32);
-    const int blocks = (int)std::min<long long>((words + 255) / 256, 4096);
-    hipLaunchKernelGGL(relu_bits_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, s,
-                       (const bf16*)h, offsets, E, F, relu_bits);
-    MOE_TRY(hipGetLastError());
+    // keep bits of the ReLU (unless the forward kept them), then
+    // dz = (dO W2[e]) * [h > 0]: A = dO [rows][d], B = W2[e] as [K=d][N=F]
+    const uint32_t* relu_bits = relu_bits_in;
+    if (relu_bits == nullptr) {
+      const long long words = (long long)S_max * (F / 32);
+      const int blocks = (int)std::min<long long>((words + 255) / 256, 4096);
+      hipLaunchKernelGGL(relu_bits_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, s,
+                         (const bf16*)h, offsets, E, F, relu_bits_ws);
+      MOE_TRY(hipGetLastError());
+      relu_bits = relu_bits_ws;
+    }
     MOE_TRY((launch_rows<false, EPI_MASK>((const bf16*)d_out, (const bf16*)w2, (bf16*)dz,
                                           relu_bits, offsets, (long long)d * F, d, F, E, S_max,
                                           s)));

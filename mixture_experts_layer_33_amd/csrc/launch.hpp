@@ -61,17 +61,20 @@ hipError_t launch_popularity(int E, int window, int64_t iter, const int32_t* cou
 
 // ---- expert GEMMs (gemm.hip)
 // Forward: h = ReLU(x_perm W1[e]^T), out = h W2[e]^T over each expert's rows.
+// relu_bits (bf16, optional): keep bits [h > 0] written by FC1's epilogue.
 hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets,
                              const void* w1, const void* w2, void* h, void* out_perm,
-                             int S_max, int d, int F, int E, hipStream_t s);
+                             uint32_t* relu_bits, int S_max, int d, int F, int E, hipStream_t s);
 // Backward GEMMs: dz = (dO W2[e]) * [h > 0]; dW2[e] = dO^T h;
 // dx_perm = dz W1[e]; dW1[e] = dz^T x_perm.
 // bf16 also folds dW_gate / db over the kept rows into the FC1 wgrad and
-// uses relu_bits ([S_max][F/32] words of scratch) for the ReLU mask.
+// takes the ReLU mask from relu_bits_in if non-null, else derives it from h
+// into relu_bits_ws ([S_max][F/32] words of scratch).
 hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, const void* h,
                              const int32_t* offsets, const void* w1, const void* w2,
                              void* dz, void* dx_perm, float* dw1, float* dw2,
                              const float* dsel_perm, float* dw_gate, float* db_gate,
-                             uint32_t* relu_bits, int S_max, int d, int F, int E, hipStream_t s);
+                             const uint32_t* relu_bits_in, uint32_t* relu_bits_ws, int S_max,
+                             int d, int F, int E, hipStream_t s);
 
 }  // namespace moe

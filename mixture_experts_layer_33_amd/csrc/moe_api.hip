@@ -245,15 +245,16 @@ moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_id
 }
 
 moe_status moe_expert_ffn(const moe_shape* s, const void* x_perm, const int32_t* offsets,
-                          const void* w1, const void* w2, void* h, void* out_perm, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          const void* w1, const void* w2, void* h, void* out_perm,
+                          uint32_t* relu_bits, void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (!ptrs_ok(x_perm, offsets, w1, w2, h, out_perm)) return MOE_ERR_INVALID_ARG;
-  MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, (int)slots(s),
-                            s->d_model, s->d_ff, s->E, as_stream(stream)));
+  if (!ptrs_ok(x_perm, offsets, w1, w2, h, out_perm) || !opt_ok(relu_bits))
+    return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, relu_bits,
+                            (int)slots(s), s->d_model, s->d_ff, s->E, as_stream(stream)));
   return MOE_OK;
 }
 
@@ -271,13 +272,13 @@ moe_status moe_forward(const moe_shape* s, const void* x, const float* w_gate,
                        const float* b_gate, const void* w1, const void* w2, void* y,
                        float* logits_out, int32_t* topk_idx, float* topk_w, int32_t* counts_raw,
                        int32_t* counts_kept, int32_t* offsets, int32_t* slot_row,
-                       int32_t* row_token, void* x_perm, void* h, void* out_perm, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       int32_t* row_token, void* x_perm, void* h, void* out_perm,
+                       uint32_t* relu_bits, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!ptrs_ok(x, w_gate, b_gate, w1, w2, y, topk_idx, topk_w, counts_kept, offsets, slot_row,
                row_token, x_perm, h, out_perm) ||
-      !opt_ok(logits_out) || !opt_ok(counts_raw))
+      !opt_ok(logits_out) || !opt_ok(counts_raw) || !opt_ok(relu_bits))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, MOE_OP_FORWARD, ws, ws_bytes)) != MOE_OK) return st;
   PermWs pw = carve_perm(s, ws);
@@ -290,8 +291,8 @@ moe_status moe_forward(const moe_shape* s, const void* x, const float* w_gate,
   MOE_HIP(launch_gather(s->act_dtype, x, topk_idx, pw.local_rank, pw.tile_base, raw, counts_kept,
                         nt, s->T, s->d_model, s->E, s->k, capacity_of(s), offsets, slot_row,
                         row_token, x_perm, stream_));
-  MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, (int)slots(s),
-                            s->d_model, s->d_ff, s->E, stream_));
+  MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, relu_bits,
+                            (int)slots(s), s->d_model, s->d_ff, s->E, stream_));
   MOE_HIP(launch_combine(s->act_dtype, out_perm, topk_w, slot_row, y, s->T, s->d_model, s->k,
                          stream_));
   return MOE_OK;
@@ -301,13 +302,14 @@ moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const
                         const void* w1, const void* w2, const int32_t* topk_idx,
                         const float* topk_w, const int32_t* slot_row, const int32_t* row_token,
                         const int32_t* offsets, const void* x_perm, const void* h,
-                        const void* out_perm, void* dx, float* dw1, float* dw2, float* dw_gate,
-                        float* db_gate, float* dlogits, void* ws, size_t ws_bytes, void* stream) {
+                        const void* out_perm, const uint32_t* relu_bits, void* dx, float* dw1,
+                        float* dw2, float* dw_gate, float* db_gate, float* dlogits, void* ws,
+                        size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!ptrs_ok(dy, x, w_gate, w1, w2, topk_idx, topk_w, slot_row, row_token, offsets, x_perm, h,
                out_perm, dx, dw1, dw2, dw_gate, db_gate) ||
-      !opt_ok(dlogits))
+      !opt_ok(dlogits) || !opt_ok(relu_bits))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, MOE_OP_BACKWARD, ws, ws_bytes)) != MOE_OK) return st;
   BwdWs bw = carve_bwd(s, ws);
@@ -319,8 +321,8 @@ moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const
   // the last reader of d_out.  For bf16 the FC1 wgrad also writes dW_gate and
   // db over the kept rows.
   MOE_HIP(launch_expert_bwd(act, bw.d_out, x_perm, h, offsets, w1, w2, bw.dz, bw.d_out, dw1, dw2,
-                            bw.dsel_perm, dw_gate, db_gate, bw.relu_bits, (int)slots(s),
-                            s->d_model, s->d_ff, s->E, stream_));
+                            bw.dsel_perm, dw_gate, db_gate, relu_bits, bw.relu_bits,
+                            (int)slots(s), s->d_model, s->d_ff, s->E, stream_));
   if (act != MOE_BF16)
     MOE_HIP(launch_gate_rows(act, x_perm, bw.dsel_perm, offsets, dw_gate, db_gate, s->d_model,
                              s->E, stream_));

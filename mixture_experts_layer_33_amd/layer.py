@@ -44,6 +44,11 @@ class MoeLayer:
         self.x_perm = z(S, d, dt=self.dtype)
         self.h = z(S, F, dt=self.dtype)
         self.out_perm = z(S, d, dt=self.dtype)
+        # keep bits of the ReLU, written by the forward and read by the
+        # backward (bf16 only); relu_bits_used = False makes the backward
+        # derive the mask from h instead
+        self.relu_bits = z(S, F // 32, dt=i32) if act == MOE_BF16 else None
+        self.relu_bits_used = True
         self.ws_fwd = z(max(moe_workspace_bytes(self.shape, "forward"), 256), dt=torch.uint8)
         self.window = window
         self.ring = torch.zeros(window, E, dtype=i32, device=device)
@@ -62,13 +67,15 @@ class MoeLayer:
         moe_forward(self.shape, x, w_gate, b_gate, w1, w2, self.y,
                     self.logits if logits_out else None, self.topk_idx, self.topk_w,
                     self.counts_raw, self.counts_kept, self.offsets, self.slot_row,
-                    self.row_token, self.x_perm, self.h, self.out_perm, self.ws_fwd, stream)
+                    self.row_token, self.x_perm, self.h, self.out_perm, self.relu_bits,
+                    self.ws_fwd, stream)
         return self.y
 
     def backward(self, dy, x, w_gate, w1, w2, dlogits=True, stream=None):
         moe_backward(self.shape, dy, x, w_gate, w1, w2, self.topk_idx, self.topk_w,
                      self.slot_row, self.row_token, self.offsets, self.x_perm, self.h,
-                     self.out_perm, self.dx, self.dw1, self.dw2, self.dw_gate, self.db_gate,
+                     self.out_perm, self.relu_bits if self.relu_bits_used else None, self.dx,
+                     self.dw1, self.dw2, self.dw_gate, self.db_gate,
                      self.dlogits if dlogits else None, self.ws_bwd, stream)
         return self.dx
 
@@ -86,7 +93,7 @@ class MoeLayer:
     def expert_ffn(self, w1, w2, x_perm=None, offsets=None, stream=None):
         moe_expert_ffn(self.shape, self.x_perm if x_perm is None else x_perm,
                        self.offsets if offsets is None else offsets, w1, w2, self.h,
-                       self.out_perm, None, stream)
+                       self.out_perm, self.relu_bits, None, stream)
 
     def combine(self, out_perm=None, topk_w=None, slot_row=None, stream=None):
         moe_combine(self.shape, self.out_perm if out_perm is None else out_perm,

@@ -93,21 +93,24 @@ def test_entry_points_reject_bad_arguments_before_launch():
     # null required pointers
     assert L.moe_route(bs, P, P, P, None, None, None, P, P, P, ws, None) == -1
     assert L.moe_permute(bs, P, P, None, P, P, None, P, P, P, ws, None) == -1
-    assert L.moe_expert_ffn(bs, P, P, P, P, None, P, None, 0, None) == -1
+    assert L.moe_expert_ffn(bs, P, P, P, P, None, P, None, None, 0, None) == -1
+    # optional relu_bits must still be 16-byte aligned
+    assert L.moe_expert_ffn(bs, P, P, P, P, P, P, P + 4, None, 0, None) == -1
     assert L.moe_combine(bs, P, P, P, None, None) == -1
     # misaligned pointer
     assert L.moe_combine(bs, P, P, P + 4, P, None) == -1
     # workspace too small / missing / misaligned
     assert L.moe_route(bs, P, P, P, None, None, P, P, P, P, ws - 1, None) == -3
     assert L.moe_permute(bs, P, P, None, P, P, P, P, P, None, ws, None) == -3
-    assert L.moe_forward(bs, P, P, P, P, P, P, None, P, P, None, P, P, P, P, P, P, P,
+    assert L.moe_forward(bs, P, P, P, P, P, P, None, P, P, None, P, P, P, P, P, P, P, None,
                          P + 16, ws, None) == -3
-    args = [P] * 19
-    args[18] = None  # dlogits optional
+    args = [P] * 20
+    args[13] = None  # relu_bits optional
+    args[19] = None  # dlogits optional
     assert L.moe_backward(bs, *args, P, bws - 256, None) == -3
     # bad shape wins over everything else
     bad = ctypes.byref(shape(k=0))
-    assert L.moe_forward(bad, *([P] * 17), P, ws, None) == -1
+    assert L.moe_forward(bad, *([P] * 18), P, ws, None) == -1
     # popularity window limits
     assert L.moe_popularity_update(8, 0, 0, P, P, P, None) == -1
     assert L.moe_popularity_update(8, 65, 0, P, P, P, None) == -1

@@ -225,6 +225,30 @@ def test_forward_equals_its_entry_points(name):
         assert torch.equal(a, b), n
 
 
+@pytest.mark.parametrize("name", ["skewed_zipf12", "uniform_cf050"])
+def test_forward_relu_bits_and_backward_with_or_without_them(name):
+    """The keep bits the forward writes are exactly [h > 0] over the kept
+    rows, and the backward gives bit-for-bit the same results whether it is
+    handed them or derives the mask from h itself."""
+    w, inp, dev, layer = _setup(name)
+    layer.forward(dev["x"], dev["w_gate"], dev["b_gate"], dev["w1"], dev["w2"])
+    torch.cuda.synchronize()
+    n = int(layer.offsets[-1].item())
+    h = down(layer.h)[:n]
+    bits = down(layer.relu_bits)[:n].view(np.uint32)
+    expect = np.packbits((h > 0).reshape(n, -1, 32), axis=-1, bitorder="little")
+    np.testing.assert_array_equal(bits, expect.reshape(n, -1, 4).view(np.uint32)[..., 0])
+    names = ("dx", "dw1", "dw2", "dw_gate", "db_gate", "dlogits")
+    layer.backward(dev["dy"], dev["x"], dev["w_gate"], dev["w1"], dev["w2"])
+    torch.cuda.synchronize()
+    ref = {k: getattr(layer, k).clone() for k in names}
+    layer.relu_bits_used = False
+    layer.backward(dev["dy"], dev["x"], dev["w_gate"], dev["w1"], dev["w2"])
+    torch.cuda.synchronize()
+    for k in names:
+        assert torch.equal(getattr(layer, k), ref[k]), k
+
+
 def test_popularity_window():
     E, W = 32, 4
     layer = MoeLayer(8, 64, 64, E, 2, 0.0, act_code("f32"), window=W, backward=False)
