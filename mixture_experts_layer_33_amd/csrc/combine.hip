@@ -68,6 +68,69 @@ __device__ __forceinline__ void token_slots(int t, int k, const int32_t* slot_ro
   }
 }
 
+// w_gate [d, E] -> w_gate_t [E, d], 32 x 32 tile `tile_id` (row-major over
+// ceil(d/32) x ceil(E/32) tiles) by one 256-thread workgroup
+__device__ __forceinline__ void transpose_gate_tile(const float* __restrict__ w_gate,
+                                                    float* __restrict__ wt, int d, int E,
+                                                    int tile_id) {
+  __shared__ float tile[32][33];
+  const int te = (E + 31) / 32;
+  const int i0 = (tile_id / te) * 32, e0 = (tile_id % te) * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 256 threads: 32 x 8
+  for (int r = ty; r < 32; r += 8) {
+    const int i = i0 + r, e = e0 + tx;
+    tile[r][tx] = (i < d && e < E) ? w_gate[(size_t)i * E + e] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int e = e0 + r, i = i0 + tx;
+    if (e < E && i < d) wt[(size_t)e * d + i] = tile[tx][r];
+  }
+}
+
+// Dropped slots still carry gate gradient (through the renormalised
+// weights).  The permutation lists them after the kept rows:
+// row_token[S_kept + j] = slot of the j-th dropped slot, ordered by expert and
+// then slot.  Block `b` (of E x ceil(d/256)) finds its expert's run by binary
+// search and adds that run's contribution to dW_gate[:, e] and db[e]
+// (written before by the kept-row pass), walking the run in order.
+template <typename ActT>
+__device__ __forceinline__ void gate_dropped_block(const ActT* __restrict__ x,
+                                                   const float* __restrict__ dsel,
+                                                   const int32_t* __restrict__ topk_idx,
+                                                   const int32_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ row_token,
+                                                   float* __restrict__ dw_gate,
+                                                   float* __restrict__ db_gate, int S, int d,
+                                                   int E, int k, int b) {
+  const int cb = (d + 255) / 256;
+  const int e = b / cb;
+  const int i = (b % cb) * 256 + threadIdx.x;
+  const int kept = offsets[E];
+  const int32_t* list = row_token + kept;
+  const int n = S - kept;
+  // first j with expert(list[j]) >= v
+  auto lower = [&](int v) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (topk_idx[list[mid]] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  const int j0 = lower(e), j1 = lower(e + 1);
+  if (j0 == j1) return;
+  float acc = 0.f, db = 0.f;
+  for (int j = j0; j < j1; ++j) {
+    const int s = list[j];
+    const float g = dsel[s];
+    db += g;
+    if (i < d) acc = fmaf(g, to_f32(x[(size_t)(s / k) * d + i]), acc);
+  }
+  if (i < d) dw_gate[(size_t)i * E + e] += acc;
+  if (b % cb == 0 && threadIdx.x == 0) db_gate[e] += db;
+}
+
 template <typename ActT>
 __global__ void __launch_bounds__(kRowThreads)
 combine_kernel(const ActT* __restrict__ out_perm, const float* __restrict__ topk_w,
@@ -102,14 +165,21 @@ combine_kernel(const ActT* __restrict__ out_perm, const float* __restrict__ topk
 // then the gate softmax backward dsel[t,j] = w_j (dg_j - sum_i w_i dg_i),
 // also written per packed row (dsel_perm[r]) for the gate weight gradient,
 // and dlogits[t, :] (dense, optional) holding dsel at the selected experts.
+// Workgroups past the tokens write W_gate^T for dx_kernel.
 template <typename ActT>
 __global__ void __launch_bounds__(kRowThreads)
 combine_bwd_kernel(const ActT* __restrict__ dy, const ActT* __restrict__ out_perm,
                    const float* __restrict__ topk_w, const int32_t* __restrict__ topk_idx,
                    const int32_t* __restrict__ slot_row, ActT* __restrict__ d_out,
                    float* __restrict__ dsel, float* __restrict__ dsel_perm,
-                   float* __restrict__ dlogits, int T, int d, int E, int k) {
+                   float* __restrict__ dlogits, const float* __restrict__ w_gate,
+                   float* __restrict__ w_gate_t, int T, int d, int E, int k) {
   using CK = Chunk<ActT>;
+  const int tok_blocks = (T + kRowThreads / 64 - 1) / (kRowThreads / 64);
+  if ((int)blockIdx.x >= tok_blocks) {  // the blocks past the tokens transpose W_gate
+    transpose_gate_tile(w_gate, w_gate_t, d, E, blockIdx.x - tok_blocks);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -173,32 +243,26 @@ combine_bwd_kernel(const ActT* __restrict__ dy, const ActT* __restrict__ out_per
   }
 }
 
-// w_gate [d, E] -> w_gate_t [E, d]
-__global__ void transpose_gate_kernel(const float* __restrict__ w_gate, float* __restrict__ wt,
-                                      int d, int E) {
-  __shared__ float tile[32][33];
-  const int i0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 256 threads: 32 x 8
-  for (int r = ty; r < 32; r += 8) {
-    const int i = i0 + r, e = e0 + tx;
-    tile[r][tx] = (i < d && e < E) ? w_gate[(size_t)i * E + e] : 0.f;
-  }
-  __syncthreads();
-  for (int r = ty; r < 32; r += 8) {
-    const int e = e0 + r, i = i0 + tx;
-    if (e < E && i < d) wt[(size_t)e * d + i] = tile[tx][r];
-  }
-}
-
 // Encode backward plus the router's input gradient:
 //   dx[t] = sum_j dx_perm[row_j] + sum_j dsel[t,j] * w_gate[:, idx_j]
-// both sums in slot order, in float32, rounded once.
+// both sums in slot order, in float32, rounded once.  With drops possible,
+// workgroups past the tokens add the dropped slots' gate gradient
+// (gate_dropped_block).
 template <typename ActT>
 __global__ void __launch_bounds__(kRowThreads)
 dx_kernel(const ActT* __restrict__ dx_perm, const float* __restrict__ dsel,
           const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot_row,
-          const float* __restrict__ wt, ActT* __restrict__ dx, int T, int d, int k) {
+          const float* __restrict__ wt, ActT* __restrict__ dx, int T, int d, int k,
+          const ActT* __restrict__ x, const int32_t* __restrict__ offsets,
+          const int32_t* __restrict__ row_token, float* __restrict__ dw_gate,
+          float* __restrict__ db_gate, int E) {
   using CK = Chunk<ActT>;
+  const int tok_blocks = (T + kRowThreads / 64 - 1) / (kRowThreads / 64);
+  if ((int)blockIdx.x >= tok_blocks) {  // the blocks past the tokens: dropped slots
+    gate_dropped_block(x, dsel, topk_idx, offsets, row_token, dw_gate, db_gate, T * k, d, E, k,
+                       blockIdx.x - tok_blocks);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -267,45 +331,6 @@ gate_rows_kernel(const ActT* __restrict__ x_perm, const float* __restrict__ dsel
   if (blockIdx.y == 0 && threadIdx.x == 0) db_gate[e] = db;
 }
 
-// Dropped slots still carry gate gradient (through the renormalised
-// weights).  The permutation lists them after the kept rows:
-// row_token[S_kept + j] = slot of the j-th dropped slot, ordered by expert and
-// then slot.  Each workgroup finds its expert's run by binary search and adds
-// that run's contribution to dW_gate[:, e] and db[e] (written before by the
-// kept-row pass), walking the run in order.
-template <typename ActT>
-__global__ void __launch_bounds__(64)
-gate_dropped_kernel(const ActT* __restrict__ x, const float* __restrict__ dsel,
-                    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ offsets,
-                    const int32_t* __restrict__ row_token, float* __restrict__ dw_gate,
-                    float* __restrict__ db_gate, int S, int d, int E, int k) {
-  const int e = blockIdx.x;
-  const int i = blockIdx.y * 64 + threadIdx.x;
-  const int kept = offsets[E];
-  const int32_t* list = row_token + kept;
-  const int n = S - kept;
-  // first j with expert(list[j]) >= v
-  auto lower = [&](int v) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (topk_idx[list[mid]] < v) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-  };
-  const int j0 = lower(e), j1 = lower(e + 1);
-  if (j0 == j1) return;
-  float acc = 0.f, db = 0.f;
-  for (int j = j0; j < j1; ++j) {
-    const int s = list[j];
-    const float g = dsel[s];
-    db += g;
-    if (i < d) acc = fmaf(g, to_f32(x[(size_t)(s / k) * d + i]), acc);
-  }
-  if (i < d) dw_gate[(size_t)i * E + e] += acc;
-  if (blockIdx.y == 0 && threadIdx.x == 0) db_gate[e] += db;
-}
-
 __global__ void popularity_kernel(int E, int window, int64_t iter,
                                   const int32_t* __restrict__ counts_raw,
                                   int32_t* __restrict__ ring, int32_t* __restrict__ window_sum) {
@@ -336,37 +361,38 @@ hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,
 hipError_t launch_combine_bwd(int act, const void* dy, const void* out_perm,
                               const float* topk_w, const int32_t* topk_idx,
                               const int32_t* slot_row, void* d_out, float* dsel,
-                              float* dsel_perm, float* dlogits, int T, int d, int E, int k,
-                              hipStream_t s) {
-  dim3 grid((T + 3) / 4), block(kRowThreads);
+                              float* dsel_perm, float* dlogits, const float* w_gate,
+                              float* w_gate_t, int T, int d, int E, int k, hipStream_t s) {
+  const int tok_blocks = (T + 3) / 4;
+  const int tr_blocks = ((d + 31) / 32) * ((E + 31) / 32);
+  dim3 grid(tok_blocks + tr_blocks), block(kRowThreads);
   if (act == MOE_BF16)
     hipLaunchKernelGGL(combine_bwd_kernel<bf16>, grid, block, 0, s, (const bf16*)dy,
                        (const bf16*)out_perm, topk_w, topk_idx, slot_row, (bf16*)d_out, dsel,
-                       dsel_perm, dlogits, T, d, E, k);
+                       dsel_perm, dlogits, w_gate, w_gate_t, T, d, E, k);
   else
     hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, block, 0, s, (const float*)dy,
                        (const float*)out_perm, topk_w, topk_idx, slot_row, (float*)d_out, dsel,
-                       dsel_perm, dlogits, T, d, E, k);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_gate(const float* w_gate, float* w_gate_t, int d, int E,
-                                 hipStream_t s) {
-  dim3 grid((d + 31) / 32, (E + 31) / 32), block(256);
-  hipLaunchKernelGGL(transpose_gate_kernel, grid, block, 0, s, w_gate, w_gate_t, d, E);
+                       dsel_perm, dlogits, w_gate, w_gate_t, T, d, E, k);
   return hipGetLastError();
 }
 
 hipError_t launch_dx(int act, const void* dx_perm, const float* dsel, const int32_t* topk_idx,
                      const int32_t* slot_row, const float* w_gate_t, void* dx, int T, int d,
-                     int k, hipStream_t s) {
-  dim3 grid((T + 3) / 4), block(kRowThreads);
+                     int k, bool dropped, const void* x, const int32_t* offsets,
+                     const int32_t* row_token, float* dw_gate, float* db_gate, int E,
+                     hipStream_t s) {
+  const int tok_blocks = (T + 3) / 4;
+  const int drop_blocks = dropped ? E * ((d + 255) / 256) : 0;
+  dim3 grid(tok_blocks + drop_blocks), block(kRowThreads);
   if (act == MOE_BF16)
     hipLaunchKernelGGL(dx_kernel<bf16>, grid, block, 0, s, (const bf16*)dx_perm, dsel, topk_idx,
-                       slot_row, w_gate_t, (bf16*)dx, T, d, k);
+                       slot_row, w_gate_t, (bf16*)dx, T, d, k, (const bf16*)x, offsets,
+                       row_token, dw_gate, db_gate, E);
   else
     hipLaunchKernelGGL(dx_kernel<float>, grid, block, 0, s, (const float*)dx_perm, dsel,
-                       topk_idx, slot_row, w_gate_t, (float*)dx, T, d, k);
+                       topk_idx, slot_row, w_gate_t, (float*)dx, T, d, k, (const float*)x,
+                       offsets, row_token, dw_gate, db_gate, E);
   return hipGetLastError();
 }
 
@@ -380,19 +406,6 @@ hipError_t launch_gate_rows(int act, const void* x_perm, const float* dsel_perm,
   else
     hipLaunchKernelGGL(gate_rows_kernel<float>, grid, block, 0, s, (const float*)x_perm,
                        dsel_perm, offsets, dw_gate, db_gate, d, E);
-  return hipGetLastError();
-}
-
-hipError_t launch_gate_dropped(int act, const void* x, const float* dsel, const int32_t* topk_idx,
-                               const int32_t* offsets, const int32_t* row_token, float* dw_gate,
-                               float* db_gate, int S, int d, int E, int k, hipStream_t s) {
-  dim3 grid(E, (d + 63) / 64), block(64);
-  if (act == MOE_BF16)
-    hipLaunchKernelGGL(gate_dropped_kernel<bf16>, grid, block, 0, s, (const bf16*)x, dsel,
-                       topk_idx, offsets, row_token, dw_gate, db_gate, S, d, E, k);
-  else
-    hipLaunchKernelGGL(gate_dropped_kernel<float>, grid, block, 0, s, (const float*)x, dsel,
-                       topk_idx, offsets, row_token, dw_gate, db_gate, S, d, E, k);
   return hipGetLastError();
 }
 

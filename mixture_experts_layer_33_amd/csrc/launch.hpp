@@ -38,24 +38,24 @@ hipError_t launch_gather(int act, const void* x, const int32_t* topk_idx,
 // ---- output decode and the elementwise backward steps (combine.hip)
 hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,
                           const int32_t* slot_row, void* y, int T, int d, int k, hipStream_t s);
+// Decode backward; its extra workgroups also write w_gate_t = W_gate^T.
 hipError_t launch_combine_bwd(int act, const void* dy, const void* out_perm,
                               const float* topk_w, const int32_t* topk_idx,
                               const int32_t* slot_row, void* d_out, float* dsel,
-                              float* dsel_perm, float* dlogits, int T, int d, int E, int k,
-                              hipStream_t s);
-hipError_t launch_transpose_gate(const float* w_gate, float* w_gate_t, int d, int E,
-                                 hipStream_t s);
-hipError_t launch_dx(int act, const void* dx_perm, const float* dsel, const int32_t* topk_idx,
-                     const int32_t* slot_row, const float* w_gate_t, void* dx, int T, int d,
-                     int k, hipStream_t s);
-// dW_gate / db over each expert's packed rows (float32 path) ...
+                              float* dsel_perm, float* dlogits, const float* w_gate,
+                              float* w_gate_t, int T, int d, int E, int k, hipStream_t s);
+// dW_gate / db over each expert's packed rows (float32 path; bf16 folds it
+// into the FC1 weight gradient) ...
 hipError_t launch_gate_rows(int act, const void* x_perm, const float* dsel_perm,
                             const int32_t* offsets, float* dw_gate, float* db_gate, int d, int E,
                             hipStream_t s);
-// ... plus the dropped slots listed after the kept rows in row_token.
-hipError_t launch_gate_dropped(int act, const void* x, const float* dsel, const int32_t* topk_idx,
-                               const int32_t* offsets, const int32_t* row_token, float* dw_gate,
-                               float* db_gate, int S, int d, int E, int k, hipStream_t s);
+// dX; with `dropped`, its extra workgroups add the gate gradient of the
+// dropped slots listed after the kept rows in row_token to dW_gate / db.
+hipError_t launch_dx(int act, const void* dx_perm, const float* dsel, const int32_t* topk_idx,
+                     const int32_t* slot_row, const float* w_gate_t, void* dx, int T, int d,
+                     int k, bool dropped, const void* x, const int32_t* offsets,
+                     const int32_t* row_token, float* dw_gate, float* db_gate, int E,
+                     hipStream_t s);
 hipError_t launch_popularity(int E, int window, int64_t iter, const int32_t* counts_raw,
                              int32_t* ring, int32_t* window_sum, hipStream_t s);
 

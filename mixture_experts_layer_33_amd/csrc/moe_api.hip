@@ -316,7 +316,8 @@ moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const
   hipStream_t stream_ = as_stream(stream);
   const int act = s->act_dtype;
   MOE_HIP(launch_combine_bwd(act, dy, out_perm, topk_w, topk_idx, slot_row, bw.d_out, bw.dsel,
-                             bw.dsel_perm, dlogits, s->T, s->d_model, s->E, s->k, stream_));
+                             bw.dsel_perm, dlogits, w_gate, bw.w_gate_t, s->T, s->d_model, s->E,
+                             s->k, stream_));
   // dx_perm reuses d_out's memory: the FC1 dgrad runs after the FC2 wgrad,
   // the last reader of d_out.  For bf16 the FC1 wgrad also writes dW_gate and
   // db over the kept rows.
@@ -326,12 +327,10 @@ moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const
   if (act != MOE_BF16)
     MOE_HIP(launch_gate_rows(act, x_perm, bw.dsel_perm, offsets, dw_gate, db_gate, s->d_model,
                              s->E, stream_));
-  if (capacity_of(s) < s->T)  // slots can be dropped: add their gate gradient
-    MOE_HIP(launch_gate_dropped(act, x, bw.dsel, topk_idx, offsets, row_token, dw_gate, db_gate,
-                                (int)slots(s), s->d_model, s->E, s->k, stream_));
-  MOE_HIP(launch_transpose_gate(w_gate, bw.w_gate_t, s->d_model, s->E, stream_));
+  // with a capacity below T slots can be dropped: dx also adds their gate gradient
   MOE_HIP(launch_dx(act, bw.d_out, bw.dsel, topk_idx, slot_row, bw.w_gate_t, dx, s->T,
-                    s->d_model, s->k, stream_));
+                    s->d_model, s->k, capacity_of(s) < s->T, x, offsets, row_token, dw_gate,
+                    db_gate, s->E, stream_));
   return MOE_OK;
 }
 
