@@ -632,18 +632,24 @@ rows_gemm_kernel(RowsArgs p) {
   const int x = bid % kXcds, i = bid / kXcds;
   const int q = total / kXcds, rmd = total % kXcds;
   const int logical = x * q + min(x, rmd) + i;
-  // group 8 m-tiles; walk n inside the group column by column
-  constexpr int G = 8;
-  const int grp = logical / (G * NT);
-  const int gm0 = grp * G;
-  const int gsz = min(G, MT - gm0);
-  const int in = logical - grp * G * NT;
-  const int mt = gm0 + in % gsz;
-  const int nt = in / gsz;
-  if (tid < p.E && s_tstart[tid] <= mt && mt < s_tstart[tid + 1]) s_expert = tid;
+  // Expert by expert (tiles of expert e: logical [s_tstart[e] * NT,
+  // s_tstart[e+1] * NT)); inside an expert, groups of up to 8 m-tiles, n
+  // walked column by column inside a group.  A group never mixes experts, so
+  // the workgroups running together on one XCD share one expert's weights.
+  if (tid < p.E && s_tstart[tid] * NT <= logical && logical < s_tstart[tid + 1] * NT)
+    s_expert = tid;
   __syncthreads();
   const int e = s_expert;
-  const int row0 = s_off[e] + (mt - s_tstart[e]) * BM;
+  constexpr int G = 8;
+  const int mte = s_tstart[e + 1] - s_tstart[e];
+  const int j = logical - s_tstart[e] * NT;
+  const int grp = j / (G * NT);
+  const int gm0 = grp * G;
+  const int gsz = min(G, mte - gm0);
+  const int in = j - grp * G * NT;
+  const int mt = gm0 + in % gsz;  // m-tile within the expert
+  const int nt = in / gsz;
+  const int row0 = s_off[e] + mt * BM;
   const int rows = min(BM, s_off[e + 1] - row0);
   const int n0 = nt * BN;
   const int cols = min(BN, p.N - n0);
@@ -701,7 +707,19 @@ wgrad_kernel(WgradArgs p) {
   __syncthreads();
   const int T1 = (p.N1 + BM - 1) / BM, T2 = (p.N2 + BN - 1) / BN;
   const int per = T1 * T2;
-  const int bid = blockIdx.x;
+  // Workgroup bid runs on XCD bid % 8.  Tiles are handed out in chunks of 8
+  // consecutive tiles (one expert, neighbouring output columns, sharing the
+  // X1 tile), chunk c to XCD c % 8, so the hottest-first order holds across
+  // the XCDs and each XCD's L2 serves a chunk's shared operand once.  The
+  // tail past the last whole round of chunks keeps bid order.
+  constexpr int CH = 8;
+  const int total = gridDim.x;
+  const int full = total / (kXcds * CH) * (kXcds * CH);
+  int bid = blockIdx.x;
+  if (bid < full) {
+    const int x = bid % kXcds, i = bid / kXcds;
+    bid = ((i / CH) * kXcds + x) * CH + i % CH;
+  }
   const int rank = bid / per, in = bid % per;
   const int e = s_perm[rank];
   const int t1 = in / T2, t2 = in % T2;
