@@ -44,7 +44,7 @@ brute force, library special cases, closed forms and finite differences.
 from __future__ import annotations
 
 import math
-from typing import Dict, Optional
+from typing import Dict, List, Optional
 
 import numpy as np
 
@@ -134,20 +134,39 @@ def capacity(T: int, k: int, E: int, capacity_factor: float) -> int:
 # --------------------------------------------------------------------------
 # input encode
 # --------------------------------------------------------------------------
-def assign_slots(idx: np.ndarray, E: int, C: int) -> Dict[str, np.ndarray]:
-    """Walk slots s = t*k + j in order; each takes the next position in its
-    expert, and is kept iff that position is below the capacity C.
+def priority_order(T: int, k: int, priority: str = "slot") -> List[int]:
+    """The order in which slots claim expert capacity.
+
+    "slot": s = t*k + j in increasing order (each expert keeps its earliest
+    tokens).  "choice": every token's first choice in token order, then every
+    token's second choice, and so on - the GShard gating that the PopFetcher
+    notes (§2.2 capacity limit, §8.2 the two routing mechanisms) name beside
+    plain top-k.
+    """
+    if priority == "slot":
+        return list(range(T * k))
+    if priority == "choice":
+        return [t * k + j for j in range(k) for t in range(T)]
+    raise ValueError(f"unknown capacity priority {priority!r}")
+
+
+def assign_slots(idx: np.ndarray, E: int, C: int, priority: str = "slot"
+                 ) -> Dict[str, np.ndarray]:
+    """Walk the slots in priority order (priority_order); each takes the next
+    position in its expert, and is kept iff that position is below the
+    capacity C.  Packed rows follow the positions: row = offsets[e] + pos.
 
     Returns counts_raw [E], counts_kept [E], offsets [E+1] (exclusive prefix
     sum of counts_kept), slot_row [T*k] (row in the packed buffers, -1 when
-    dropped) and row_token [S_kept] (token held by each packed row).
+    dropped) and row_token [S_kept] (token held by each packed row), plus
+    "dropped": the dropped slots ordered by expert, then position.
     """
     T, k = idx.shape
     flat = idx.reshape(-1)
     S = flat.size
     seen = [0] * E
     pos = [0] * S
-    for s in range(S):
+    for s in priority_order(T, k, priority):
         e = int(flat[s])
         pos[s] = seen[e]
         seen[e] += 1
@@ -166,9 +185,10 @@ def assign_slots(idx: np.ndarray, E: int, C: int) -> Dict[str, np.ndarray]:
             r = int(offsets[flat[s]]) + pos[s]
             slot_row[s] = r
             row_token[r] = s // k
+    dropped = sorted((int(flat[s]), pos[s], s) for s in range(S) if pos[s] >= C)
     return {"counts_raw": counts_raw, "counts_kept": counts_kept,
             "offsets": offsets, "slot_row": slot_row, "row_token": row_token,
-            "drops": S - run}
+            "drops": S - run, "dropped": np.array([s for _, _, s in dropped], dtype=np.int32)}
 
 
 def encode(x: np.ndarray, row_token: np.ndarray) -> np.ndarray:
@@ -221,16 +241,17 @@ def decode(o: np.ndarray, w: np.ndarray, slot_row: np.ndarray, act: str) -> np.n
 # whole forward
 # --------------------------------------------------------------------------
 def forward(x, w_gate, b_gate, w1, w2, k: int, capacity_factor: float, act: str,
-            logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+            logits: Optional[np.ndarray] = None, priority: str = "slot") -> Dict[str, np.ndarray]:
     """The layer forward.  If ``logits`` is given (float32 [T, E]) routing
-    starts from those logits instead of computing them."""
+    starts from those logits instead of computing them.  ``priority`` is the
+    capacity priority (priority_order)."""
     T = x.shape[0]
     E = w1.shape[0]
     if logits is None:
         logits = router_logits(x, w_gate, b_gate)
     idx, w = topk_gate(logits, k)
     C = capacity(T, k, E, capacity_factor)
-    slots = assign_slots(idx, E, C)
+    slots = assign_slots(idx, E, C, priority)
     x_perm = encode(x, slots["row_token"])
     h, o = expert_ffn(x_perm, slots["offsets"], w1, w2, act)
     y = decode(o, w, slots["slot_row"], act)

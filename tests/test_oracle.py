@@ -49,6 +49,54 @@ def test_hand_worked_routing():
         assert s["drops"] == c["drops"]
 
 
+def test_hand_worked_capacity_priorities():
+    """Slot order and GShard's choice-major order on the hand-worked fixture
+    (C = 1 tells them apart: token 3's first choice beats token 0's second)."""
+    g = load("hand_routing.json")
+    L = np.array(g["logits"], dtype=np.float32)
+    L[3, 1] = -0.0
+    idx, _ = orc.topk_gate(L, g["k"])
+    cases = [("slot", g["slot_order_C1_case"])] + [("choice", c) for c in g["choice_major_cases"]]
+    for prio, c in cases:
+        C = orc.capacity(g["T"], g["k"], g["E"], c["capacity_factor"])
+        assert C == c["C"]
+        s = orc.assign_slots(idx, g["E"], C, prio)
+        for key in ("counts_raw", "counts_kept", "offsets", "slot_row", "row_token", "dropped"):
+            assert s[key].tolist() == c[key], (prio, c["C"], key)
+        assert s["drops"] == c["drops"]
+
+
+@pytest.mark.parametrize("cf", [0.5, 0.8, 1.0])
+def test_choice_major_capacity_bruteforce(cf):
+    """Position of a slot = number of slots of the same expert that come
+    earlier in (choice, token) order, counted directly."""
+    rng = np.random.default_rng(11)
+    T, E, k = 37, 5, 3
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[:, 1] += 1.2
+    idx, _ = orc.topk_gate(L, k)
+    C = orc.capacity(T, k, E, cf)
+    s = orc.assign_slots(idx, E, C, "choice")
+    n_kept = [0] * E
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            pos = sum(1 for jj in range(k) for tt in range(T)
+                      if idx[tt, jj] == e and (jj, tt) < (j, t))
+            if pos < C:
+                n_kept[e] += 1
+                row = int(s["offsets"][e]) + pos
+                assert s["slot_row"][t * k + j] == row
+                assert s["row_token"][row] == t
+            else:
+                assert s["slot_row"][t * k + j] == -1
+    assert s["counts_kept"].tolist() == n_kept
+    assert s["drops"] == T * k - sum(n_kept) > 0
+    # dropped list: by expert, then position
+    exp = [int(idx.reshape(-1)[q]) for q in s["dropped"]]
+    assert exp == sorted(exp)
+
+
 def test_hand_worked_popularity():
     p = load("hand_routing.json")["popularity_case"]
     W = p["window"]
