@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="uniform_cf125", choices=list(workloads.workloads()))
+    p.add_argument("--priority", default=None, choices=["slot", "choice"],
+                   help="capacity priority (default: the workload's)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-reps", type=int, default=20)
     p.add_argument("--copy-calibration", action="store_true",
@@ -193,7 +195,7 @@ def cpu_baseline(w: workloads.Workload, inp, budget_s: float = 12.0):
         dy = inp["dy"][:n]
         t0 = time.perf_counter()
         fwd = orc.forward(x, inp["w_gate"], inp["b_gate"], inp["w1"], inp["w2"], w.k,
-                          w.capacity_factor, w.dtype)
+                          w.capacity_factor, w.dtype, priority=w.priority)
         orc.backward(dy, fwd, x, inp["w_gate"], inp["w1"], inp["w2"], w.dtype)
         dt = time.perf_counter() - t0
         total_t += dt
@@ -228,6 +230,9 @@ def main():
         raise SystemExit("bench.py needs an MI355X GPU")
     moe.lib()  # fails loudly when libmoe.so is missing
     w = workloads.workloads()[args.workload]
+    if args.priority is not None and args.priority != w.priority:
+        w = workloads.scaled(w, priority=args.priority,
+                             description=f"{w.description}, {args.priority}-major capacity")
     log(f"workload {w.name}: {w.description}")
     inp = workloads.make_inputs(w, 0, with_weights=True, with_dy=True)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -240,7 +245,8 @@ def main():
     w_gate, b_gate = up(inp["w_gate"], False), up(inp["b_gate"], False)
     w1, w2 = up(inp["w1"]), up(inp["w2"])
     act = moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32
-    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, w.capacity_factor, act, window=w.window)
+    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, w.capacity_factor, act, window=w.window,
+                     priority=w.priority)
     stream = torch.cuda.current_stream()
 
     it_counter = [0]
@@ -325,6 +331,7 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights)",
         "config": {"workload": w.name, "T": w.T, "d_model": w.d, "d_ff": w.F, "E": w.E,
                    "k": w.k, "capacity_factor": w.capacity_factor,
+                   "capacity_priority": w.priority,
                    "step": "forward + popularity window + backward", "S_kept": s_kept},
         "roofline": {"bound": "mfma",
                      "kernel": "rows_gemm_kernel (grouped expert GEMM, FC1 and FC2 launches)",

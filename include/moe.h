@@ -47,8 +47,9 @@
  *   taken): selection on the float32 logits, ties to the lowest expert index
  *   (+0.0 == -0.0); gate weights are a softmax over the k selected logits;
  *   capacity C = ceil(cf*T*k/E) clamped to [1, T], or T when cf <= 0
- *   (dropless); slots claim capacity in slot order t*k + j; kept weights are
- *   not renormalised after drops; a token with every slot dropped outputs 0.
+ *   (dropless); slots claim capacity in the shape's capacity_priority order
+ *   (slot order t*k + j by default); kept weights are not renormalised
+ *   after drops; a token with every slot dropped outputs 0.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -70,6 +71,14 @@ typedef int32_t moe_status;
 #define MOE_F32 0
 #define MOE_BF16 1
 
+/* Capacity priority: the order in which slots claim expert capacity (and the
+ * order of an expert's packed rows).  SLOT: s = t*k + j increasing, so each
+ * expert keeps its earliest tokens.  CHOICE: every token's first choice in
+ * token order, then every second choice, ... (the GShard gating that the
+ * PopFetcher notes name beside plain top-k, §2.2 and §8.2). */
+#define MOE_PRIORITY_SLOT 0
+#define MOE_PRIORITY_CHOICE 1
+
 /* Limits of the compiled kernels (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 8
@@ -82,6 +91,7 @@ typedef struct moe_shape {
   int32_t k;               /* experts per token, 1..min(E, MOE_MAX_TOPK) */
   float capacity_factor;   /* <= 0: dropless */
   int32_t act_dtype;       /* MOE_F32 or MOE_BF16 */
+  int32_t capacity_priority; /* MOE_PRIORITY_SLOT or MOE_PRIORITY_CHOICE */
 } moe_shape;
 
 /* Operations, for moe_workspace_bytes. */
@@ -125,11 +135,11 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_gate,
  * into contiguous memory; capacity limit as in GShard, cited there).  From
  * topk_idx: counts_kept[e] = min(raw count, C); offsets = exclusive prefix
  * sum of counts_kept; slot_row[s] = offsets[e] + position of slot s among
- * e's slots in slot order, or -1 if that position is >= C; row_token[r] =
- * token of packed row r; x_perm[r] = x[row_token[r]] (exact copy).
- * Dropped slots are listed after the kept rows: row_token[S_kept + j], for
- * j < T*k - S_kept, is the slot index t*k+j' of the j-th dropped slot,
- * ordered by expert and then by slot (moe_backward reads this list).
+ * e's slots in capacity-priority order, or -1 if that position is >= C;
+ * row_token[r] = token of packed row r; x_perm[r] = x[row_token[r]] (exact
+ * copy).  Dropped slots are listed after the kept rows: row_token[S_kept + j],
+ * for j < T*k - S_kept, is the slot index t*k+j' of the j-th dropped slot,
+ * ordered by expert and then by position (moe_backward reads this list).
  * counts_raw may be NULL.  Workspace: MOE_OP_PERMUTE. */
 moe_status moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
                        int32_t* counts_raw, int32_t* counts_kept, int32_t* offsets,

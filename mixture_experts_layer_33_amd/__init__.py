@@ -16,11 +16,12 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MoeError", "MoeShape", "lib", "library_path",
     "moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-    "moe_backward", "moe_popularity_update", "OP",
+    "moe_backward", "moe_popularity_update", "OP", "PRIORITY",
 ]
 
 MOE_F32 = 0
 MOE_BF16 = 1
+PRIORITY = {"slot": 0, "choice": 1}  # capacity priority (MOE_PRIORITY_*)
 OP = {"route": 0, "permute": 1, "expert_ffn": 2, "combine": 3, "forward": 4, "backward": 5}
 EXPORTS = ["moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
@@ -42,11 +43,12 @@ class MoeError(RuntimeError):
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32),
-                ("capacity_factor", ctypes.c_float), ("act_dtype", ctypes.c_int32)]
+                ("capacity_factor", ctypes.c_float), ("act_dtype", ctypes.c_int32),
+                ("capacity_priority", ctypes.c_int32)]
 
     @classmethod
-    def make(cls, T, d, F, E, k, capacity_factor=0.0, act=MOE_BF16):
-        return cls(T, d, F, E, k, capacity_factor, act)
+    def make(cls, T, d, F, E, k, capacity_factor=0.0, act=MOE_BF16, priority="slot"):
+        return cls(T, d, F, E, k, capacity_factor, act, PRIORITY[priority])
 
 
 _lib: Optional[ctypes.CDLL] = None

@@ -20,8 +20,8 @@ size_t route_split_bytes(int d, int E);
 // ---- input encode (permute.hip)
 // Per tile of kRankTile slots: stable rank of each slot among the tile's
 // slots of the same expert, and the tile histogram hist[e][tile].
-hipError_t launch_rank_hist(const int32_t* topk_idx, int S, int E, int32_t* local_rank,
-                            int32_t* hist, int n_tiles, hipStream_t s);
+hipError_t launch_rank_hist(const int32_t* topk_idx, int T, int k, bool choice, int E,
+                            int32_t* local_rank, int32_t* hist, int n_tiles, hipStream_t s);
 // Exclusive scan of hist over tiles per expert (tile_base, in place of hist
 // is not allowed), counts_raw and counts_kept = min(raw, C).
 hipError_t launch_scan(const int32_t* hist, int n_tiles, int E, int C, int32_t* tile_base,
@@ -32,8 +32,8 @@ hipError_t launch_gather(int act, const void* x, const int32_t* topk_idx,
                          const int32_t* local_rank, const int32_t* tile_base,
                          const int32_t* counts_raw, const int32_t* counts_kept, int n_tiles,
                          int T, int d, int E, int k,
-                         int C, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
-                         void* x_perm, hipStream_t s);
+                         int C, bool choice, int32_t* offsets, int32_t* slot_row,
+                         int32_t* row_token, void* x_perm, hipStream_t s);
 
 // ---- output decode and the elementwise backward steps (combine.hip)
 hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,

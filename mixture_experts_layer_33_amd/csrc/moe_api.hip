@@ -31,10 +31,17 @@ moe_status check_shape(const moe_shape* s) {
   if (s->d_model % 64 != 0 || s->d_ff % 64 != 0) return MOE_ERR_INVALID_ARG;
   if (isnan(s->capacity_factor) || isinf(s->capacity_factor)) return MOE_ERR_INVALID_ARG;
   if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->capacity_priority != MOE_PRIORITY_SLOT && s->capacity_priority != MOE_PRIORITY_CHOICE)
+    return MOE_ERR_INVALID_ARG;
   if (s->E > MOE_MAX_EXPERTS || s->k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   // row indices, slot indices and per-row element offsets stay in int32
   const int64_t S = slots(s);
   if (S > (int64_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  // the GEMM's buffer resources address an operand tile in 31-bit offsets
+  const int64_t wide = s->d_model > s->d_ff ? s->d_model : s->d_ff;
+  const int64_t limit = 0x7ffffff0;  // bytes addressable from one resource
+  if (S * wide * 2 >= limit || (int64_t)s->d_model * s->d_ff * 2 >= limit)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -150,7 +157,8 @@ moe_status do_route(const moe_shape* s, const void* x, const float* w_gate, cons
   MOE_HIP(launch_route(s->act_dtype, x, w_gate, b_gate, logits_in, logits_out, idx, w, s->T,
                        s->d_model, s->E, s->k, pw.wsplit, st));
   const int nt = rank_tiles(s);
-  MOE_HIP(launch_rank_hist(idx, (int)slots(s), s->E, pw.local_rank, pw.hist, nt, st));
+  MOE_HIP(launch_rank_hist(idx, s->T, s->k, s->capacity_priority == MOE_PRIORITY_CHOICE, s->E,
+                           pw.local_rank, pw.hist, nt, st));
   MOE_HIP(launch_scan(pw.hist, nt, s->E, capacity_of(s), pw.tile_base, counts_raw, counts_kept,
                       st));
   return MOE_OK;
@@ -236,11 +244,13 @@ moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_id
   const int nt = rank_tiles(s);
   const int C = capacity_of(s);
   int32_t* raw = counts_raw ? counts_raw : pw.raw_tmp;
-  MOE_HIP(launch_rank_hist(topk_idx, (int)slots(s), s->E, pw.local_rank, pw.hist, nt, stream_));
+  MOE_HIP(launch_rank_hist(topk_idx, s->T, s->k, s->capacity_priority == MOE_PRIORITY_CHOICE,
+                           s->E, pw.local_rank, pw.hist, nt, stream_));
   MOE_HIP(launch_scan(pw.hist, nt, s->E, C, pw.tile_base, raw, counts_kept, stream_));
   MOE_HIP(launch_gather(s->act_dtype, x, topk_idx, pw.local_rank, pw.tile_base, raw, counts_kept,
-                        nt, s->T, s->d_model, s->E, s->k, C, offsets, slot_row, row_token, x_perm,
-                        stream_));
+                        nt, s->T, s->d_model, s->E, s->k, C,
+                        s->capacity_priority == MOE_PRIORITY_CHOICE, offsets, slot_row, row_token,
+                        x_perm, stream_));
   return MOE_OK;
 }
 
@@ -289,8 +299,9 @@ moe_status moe_forward(const moe_shape* s, const void* x, const float* w_gate,
   if (st != MOE_OK) return st;
   const int nt = rank_tiles(s);
   MOE_HIP(launch_gather(s->act_dtype, x, topk_idx, pw.local_rank, pw.tile_base, raw, counts_kept,
-                        nt, s->T, s->d_model, s->E, s->k, capacity_of(s), offsets, slot_row,
-                        row_token, x_perm, stream_));
+                        nt, s->T, s->d_model, s->E, s->k, capacity_of(s),
+                        s->capacity_priority == MOE_PRIORITY_CHOICE, offsets, slot_row, row_token,
+                        x_perm, stream_));
   MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, relu_bits,
                             (int)slots(s), s->d_model, s->d_ff, s->E, stream_));
   MOE_HIP(launch_combine(s->act_dtype, out_perm, topk_w, slot_row, y, s->T, s->d_model, s->k,

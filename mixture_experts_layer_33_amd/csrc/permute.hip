@@ -8,7 +8,11 @@
 // §2.2) drops the slots beyond an expert's capacity.
 //
 // Three kernels, no host round trip:
-//  1. rank_hist: tiles of kRankTile slots.  Each 64-slot wavefront finds, for
+// Slots are ranked in capacity-priority order: position q of the walk is slot
+// s(q) = q (slot order) or (q % T) * k + q / T (choice-major: all first
+// choices, then all second choices, ...); ranks and tiles are over q.
+//
+//  1. rank_hist: tiles of kRankTile positions.  Each 64-slot wavefront finds, for
 //     every lane, the lower lanes routed to the same expert with ceil(log2)
 //     ballots over the expert id bits (warp-level multisplit), which gives the
 //     stable rank inside the wavefront; LDS counters carry the rank across
@@ -32,8 +36,9 @@ namespace moe {
 constexpr int kRankThreads = 256;
 
 __global__ void __launch_bounds__(kRankThreads)
-rank_hist_kernel(const int32_t* __restrict__ topk_idx, int S, int E,
+rank_hist_kernel(const int32_t* __restrict__ topk_idx, int T, int k, bool choice, int E,
                  int32_t* __restrict__ local_rank, int32_t* __restrict__ hist, int n_tiles) {
+  const int S = T * k;
   __shared__ int running[MOE_MAX_EXPERTS + 1];
   __shared__ int wcnt[kRankThreads / 64][MOE_MAX_EXPERTS + 1];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -47,8 +52,9 @@ rank_hist_kernel(const int32_t* __restrict__ topk_idx, int S, int E,
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int tile = blockIdx.x;
   for (int r = 0; r < kRankTile / kRankThreads; ++r) {
-    const int s = tile * kRankTile + r * kRankThreads + tid;
-    const bool valid = s < S;
+    const int q = tile * kRankTile + r * kRankThreads + tid;
+    const bool valid = q < S;
+    const int s = choice ? (q % T) * k + q / T : q;
     const int e = valid ? topk_idx[s] : E;
     uint64_t m = ~0ull;
     for (int b = 0; b < nbits; ++b) {
@@ -61,7 +67,7 @@ rank_hist_kernel(const int32_t* __restrict__ topk_idx, int S, int E,
     __syncthreads();
     int rank = running[e] + rank_w;
     for (int w = 0; w < wid; ++w) rank += wcnt[w][e];
-    if (valid) local_rank[s] = rank;
+    if (valid) local_rank[q] = rank;
     __syncthreads();
     for (int i = tid; i <= E; i += kRankThreads) {
       int add = 0;
@@ -108,7 +114,8 @@ __global__ void __launch_bounds__(kGatherThreads)
 gather_kernel(const ActT* __restrict__ x, const int32_t* __restrict__ topk_idx,
               const int32_t* __restrict__ local_rank, const int32_t* __restrict__ tile_base,
               const int32_t* __restrict__ counts_raw, const int32_t* __restrict__ counts_kept,
-              int n_tiles, int T, int d, int E, int k, int C, int32_t* __restrict__ offsets,
+              int n_tiles, int T, int d, int E, int k, int C, bool choice,
+              int32_t* __restrict__ offsets,
               int32_t* __restrict__ slot_row, int32_t* __restrict__ row_token,
               ActT* __restrict__ x_perm) {
   __shared__ int off[MOE_MAX_EXPERTS + 1];
@@ -138,8 +145,9 @@ gather_kernel(const ActT* __restrict__ x, const int32_t* __restrict__ topk_idx,
   int my_row = -1;
   if (lane < k) {
     const int s = t * k + lane;
+    const int q = choice ? lane * T + t : s;  // position in the capacity walk
     const int e = topk_idx[s];
-    const int pos = tile_base[(size_t)e * n_tiles + s / kRankTile] + local_rank[s];
+    const int pos = tile_base[(size_t)e * n_tiles + q / kRankTile] + local_rank[q];
     if (pos < C) {
       my_row = off[e] + pos;
       row_token[my_row] = t;
@@ -164,10 +172,10 @@ gather_kernel(const ActT* __restrict__ x, const int32_t* __restrict__ topk_idx,
   }
 }
 
-hipError_t launch_rank_hist(const int32_t* topk_idx, int S, int E, int32_t* local_rank,
-                            int32_t* hist, int n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(rank_hist_kernel, dim3(n_tiles), dim3(kRankThreads), 0, s, topk_idx, S, E,
-                     local_rank, hist, n_tiles);
+hipError_t launch_rank_hist(const int32_t* topk_idx, int T, int k, bool choice, int E,
+                            int32_t* local_rank, int32_t* hist, int n_tiles, hipStream_t s) {
+  hipLaunchKernelGGL(rank_hist_kernel, dim3(n_tiles), dim3(kRankThreads), 0, s, topk_idx, T, k,
+                     choice, E, local_rank, hist, n_tiles);
   return hipGetLastError();
 }
 
@@ -181,17 +189,17 @@ hipError_t launch_scan(const int32_t* hist, int n_tiles, int E, int C, int32_t* 
 hipError_t launch_gather(int act, const void* x, const int32_t* topk_idx,
                          const int32_t* local_rank, const int32_t* tile_base,
                          const int32_t* counts_raw, const int32_t* counts_kept, int n_tiles,
-                         int T, int d, int E, int k, int C, int32_t* offsets, int32_t* slot_row,
-                         int32_t* row_token, void* x_perm, hipStream_t s) {
+                         int T, int d, int E, int k, int C, bool choice, int32_t* offsets,
+                         int32_t* slot_row, int32_t* row_token, void* x_perm, hipStream_t s) {
   dim3 grid((T + 3) / 4), block(kGatherThreads);
   if (act == MOE_BF16)
     hipLaunchKernelGGL(gather_kernel<bf16>, grid, block, 0, s, (const bf16*)x, topk_idx,
                        local_rank, tile_base, counts_raw, counts_kept, n_tiles, T, d, E, k, C,
-                       offsets, slot_row, row_token, (bf16*)x_perm);
+                       choice, offsets, slot_row, row_token, (bf16*)x_perm);
   else
     hipLaunchKernelGGL(gather_kernel<float>, grid, block, 0, s, (const float*)x, topk_idx,
                        local_rank, tile_base, counts_raw, counts_kept, n_tiles, T, d, E, k, C,
-                       offsets, slot_row, row_token, (float*)x_perm);
+                       choice, offsets, slot_row, row_token, (float*)x_perm);
   return hipGetLastError();
 }
 

@@ -19,8 +19,8 @@ def act_torch_dtype(act: int):
 
 class MoeLayer:
     def __init__(self, T, d, F, E, k, capacity_factor=0.0, act=MOE_BF16, device="cuda",
-                 window=4, backward=True):
-        self.shape = MoeShape.make(T, d, F, E, k, capacity_factor, act)
+                 window=4, backward=True, priority="slot"):
+        self.shape = MoeShape.make(T, d, F, E, k, capacity_factor, act, priority)
         st = moe_check_shape(self.shape)
         if st != 0:
             raise ValueError(f"bad shape: {moe_status_string(st)}")

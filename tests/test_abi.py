@@ -35,10 +35,13 @@ def test_library_loads_with_all_symbols_resolved():
 
 
 def shape(**kw):
-    base = dict(T=64, d=128, F=256, E=8, k=2, capacity_factor=0.0, act=moe.MOE_BF16)
+    base = dict(T=64, d=128, F=256, E=8, k=2, capacity_factor=0.0, act=moe.MOE_BF16,
+                priority="slot")
     base.update(kw)
-    return moe.MoeShape.make(base["T"], base["d"], base["F"], base["E"], base["k"],
-                             base["capacity_factor"], base["act"])
+    s = moe.MoeShape.make(base["T"], base["d"], base["F"], base["E"], base["k"],
+                          base["capacity_factor"], base["act"])
+    s.capacity_priority = base.get("prio_code", moe.PRIORITY[base["priority"]])
+    return s
 
 
 @needs_lib
@@ -49,6 +52,9 @@ def shape(**kw):
     ({"d": 100}, -1), ({"F": 96}, -1),
     ({"E": 257}, -2), ({"act": 7}, -2),
     ({"capacity_factor": float("nan")}, -1), ({"capacity_factor": float("inf")}, -1),
+    ({"priority": "choice"}, 0), ({"prio_code": 2}, -1), ({"prio_code": -1}, -1),
+    # one GEMM operand would exceed the 2 GiB a buffer resource addresses
+    ({"T": 1 << 17, "k": 4, "d": 4096}, -2), ({"d": 32768, "F": 32768}, -2),
 ])
 def test_shape_validation(kw, status):
     assert moe.moe_check_shape(shape(**kw)) == status

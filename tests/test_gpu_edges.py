@@ -31,6 +31,10 @@ EDGES = {
     "heavy_drops": W(BASE, T=402, d=128, F=128, E=4, k=1, capacity_factor=0.1),
     "heavy_drops_k3": W(BASE, T=299, d=128, F=192, E=6, k=3, capacity_factor=0.3),
     "wide_F_ragged": W(BASE, T=130, d=192, F=704, E=3, k=2),
+    "heavy_drops_k3_choice": W(BASE, T=299, d=128, F=192, E=6, k=3, capacity_factor=0.3,
+                               priority="choice"),
+    "single_expert_choice": W(BASE, T=301, d=128, F=192, E=1, k=1, zipf_s=None,
+                              capacity_factor=0.5, priority="choice"),
 }
 
 
@@ -39,12 +43,13 @@ def run_case(w, b_override=None):
     if b_override is not None:
         inp["b_gate"] = b_override
     dev = upload_case(inp, w.dtype)
-    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, w.capacity_factor, act_code(w.dtype))
+    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, w.capacity_factor, act_code(w.dtype),
+                     priority=w.priority)
     layer.forward(dev["x"], dev["w_gate"], dev["b_gate"], dev["w1"], dev["w2"])
     layer.backward(dev["dy"], dev["x"], dev["w_gate"], dev["w1"], dev["w2"])
     torch.cuda.synchronize()
     fwd = orc.forward(inp["x"], inp["w_gate"], inp["b_gate"], inp["w1"], inp["w2"], w.k,
-                      w.capacity_factor, w.dtype)
+                      w.capacity_factor, w.dtype, priority=w.priority)
     bwd = orc.backward(inp["dy"], fwd, inp["x"], inp["w_gate"], inp["w1"], inp["w2"], w.dtype)
     return inp, layer, fwd, bwd
 
@@ -55,7 +60,7 @@ def test_edge_end_to_end(name):
     inp, layer, fwd, bwd = run_case(w)
     mism = compare_end_to_end(w, layer, fwd, bwd)
     assert mism.size == 0
-    if name.startswith("heavy_drops"):
+    if name.startswith("heavy_drops") or name.endswith("_choice"):
         assert fwd["drops"] > 0
         dropped_all = (fwd["slot_row"].reshape(w.T, w.k) < 0).all(axis=1)
         assert dropped_all.any()

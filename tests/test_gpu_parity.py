@@ -38,6 +38,11 @@ SMALL = {
     "skewed_zipf12": workloads.scaled(WL["skewed_zipf12"], T=1500, d=256, F=448),
     "mixtral_shaped": workloads.scaled(WL["mixtral_shaped"], T=1200, d=256, F=448),
     "fine_grained": workloads.scaled(WL["fine_grained"], T=2100, d=256, F=128),
+    # GShard's choice-major capacity priority
+    "uniform_cf100_choice": workloads.scaled(WL["uniform_cf125"], T=1000, d=256, F=320,
+                                             capacity_factor=1.0, priority="choice"),
+    "skewed_cf080_choice": workloads.scaled(WL["skewed_zipf12"], T=1500, d=128, F=192,
+                                            capacity_factor=0.8, priority="choice"),
 }
 
 
@@ -45,7 +50,8 @@ def _setup(name, it=0):
     w = SMALL[name]
     inp = workloads.make_inputs(w, it, with_weights=True, with_dy=True)
     dev = upload_case(inp, w.dtype)
-    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, w.capacity_factor, act_code(w.dtype))
+    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, w.capacity_factor, act_code(w.dtype),
+                     priority=w.priority)
     return w, inp, dev, layer
 
 
@@ -75,7 +81,8 @@ def test_permute_bitexact(name):
     w, inp, dev, layer = _setup(name)
     L = orc.router_logits(inp["x"], inp["w_gate"], inp["b_gate"])
     idx, _ = orc.topk_gate(L, w.k)
-    ref = orc.assign_slots(idx, w.E, orc.capacity(w.T, w.k, w.E, w.capacity_factor))
+    ref = orc.assign_slots(idx, w.E, orc.capacity(w.T, w.k, w.E, w.capacity_factor),
+                         w.priority)
     layer.permute(dev["x"], topk_idx=up_i32(idx))
     torch.cuda.synchronize()
     for key in ("counts_raw", "counts_kept", "offsets", "slot_row"):
@@ -83,10 +90,8 @@ def test_permute_bitexact(name):
     n = int(ref["offsets"][-1])
     np.testing.assert_array_equal(down(layer.row_token)[:n], ref["row_token"])
     np.testing.assert_array_equal(down(layer.x_perm)[:n], orc.encode(inp["x"], ref["row_token"]))
-    # dropped slots listed after the kept rows, by expert then slot
-    flat = idx.reshape(-1)
-    dropped = sorted(np.where(ref["slot_row"] < 0)[0].tolist(), key=lambda s: (flat[s], s))
-    np.testing.assert_array_equal(down(layer.row_token)[n:n + len(dropped)], dropped)
+    # dropped slots listed after the kept rows, by expert then position
+    np.testing.assert_array_equal(down(layer.row_token)[n:n + ref["drops"]], ref["dropped"])
     if name.startswith("uniform_cf0") or name == "uniform_cf100":
         assert ref["drops"] > 0
 
@@ -96,7 +101,8 @@ def test_expert_ffn(name):
     w, inp, dev, layer = _setup(name)
     L = orc.router_logits(inp["x"], inp["w_gate"], inp["b_gate"])
     idx, _ = orc.topk_gate(L, w.k)
-    s = orc.assign_slots(idx, w.E, orc.capacity(w.T, w.k, w.E, w.capacity_factor))
+    s = orc.assign_slots(idx, w.E, orc.capacity(w.T, w.k, w.E, w.capacity_factor),
+                         w.priority)
     x_perm = orc.encode(inp["x"], s["row_token"])
     n = x_perm.shape[0]
     xp = torch.zeros(w.T * w.k, w.d, dtype=layer.dtype, device="cuda")
@@ -118,7 +124,8 @@ def test_combine(name):
     w, inp, dev, layer = _setup(name)
     L = orc.router_logits(inp["x"], inp["w_gate"], inp["b_gate"])
     idx, wt = orc.topk_gate(L, w.k)
-    s = orc.assign_slots(idx, w.E, orc.capacity(w.T, w.k, w.E, w.capacity_factor))
+    s = orc.assign_slots(idx, w.E, orc.capacity(w.T, w.k, w.E, w.capacity_factor),
+                         w.priority)
     x_perm = orc.encode(inp["x"], s["row_token"])
     _, o = orc.expert_ffn(x_perm, s["offsets"], inp["w1"], inp["w2"], w.dtype)
     n = o.shape[0]
@@ -138,7 +145,7 @@ def _end_to_end(name, it=0):
     layer.backward(dev["dy"], dev["x"], dev["w_gate"], dev["w1"], dev["w2"])
     torch.cuda.synchronize()
     fwd = orc.forward(inp["x"], inp["w_gate"], inp["b_gate"], inp["w1"], inp["w2"], w.k,
-                      w.capacity_factor, w.dtype)
+                      w.capacity_factor, w.dtype, priority=w.priority)
     bwd = orc.backward(inp["dy"], fwd, inp["x"], inp["w_gate"], inp["w1"], inp["w2"], w.dtype)
     return w, inp, layer, fwd, bwd
 

@@ -70,6 +70,7 @@ class Workload:
     window: int = 4
     drift_swaps: int = 0
     description: str = ""
+    priority: str = "slot"  # capacity priority: "slot" or "choice" (choice-major)
 
     def tokens(self) -> int:
         return self.T
