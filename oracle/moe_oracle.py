@@ -29,12 +29,18 @@ only where the layer stores a tensor):
   is the reading taken here);
 * the backward pass of all of the above (the notes' §5.2.1 counts one GEMM
   forward and two backward per expert layer: gradient w.r.t. input and
-  w.r.t. parameters).
+  w.r.t. parameters);
+* an expert-parallel dispatch plan: demand-based replication of hot experts
+  under a cap on extra copies (Fast MoE Inference via Predictive Prefetching
+  and Expert Replication: "deep physical replication" by token demand and
+  "capacity limitation" by GPU memory) and least-loaded placement of the
+  copies on ranks (LLEP notes, §2.1: work goes to the least-loaded GPU).
 
 Readings of points the pages leave open (each is listed in the design notes):
 selection on the fp32 logits, ties to the lowest index, weights = softmax over
 the k selected logits; capacity C = ceil(cf*T*k/E) clamped to [1, T] (T when
-dropless); slots claim capacity in slot order t*k+j; kept weights are not
+dropless); slots claim capacity in slot order t*k+j (or choice-major); kept
+weights are not
 renormalised after drops; ReLU'(0) = 0 with the mask taken from the stored h;
 the k expert outputs are summed in j order.
 
@@ -423,3 +429,60 @@ def expert_weight_grad_entries(e: int, rows_f, rows_i, x_perm_e, dy_tok, w_rows,
     dw1 = dz.T @ xp[:, list(rows_i)]                                        # [nf, ni]
     dw2 = dO[:, list(rows_i)].T @ h                                         # [ni, nf]
     return dw1, dw2
+
+
+# --------------------------------------------------------------------------
+# expert-parallel dispatch plan
+# --------------------------------------------------------------------------
+def replica_counts(counts, extra: int) -> List[int]:
+    """Copies per expert.  Every expert has one; each of the ``extra`` copies
+    the memory budget allows goes, one at a time, to the expert with the most
+    rows per copy (counts[e] / copies[e], compared exactly; ties to the lowest
+    expert index) - demand-based replication under a memory cap."""
+    c = [int(v) for v in counts]
+    r = [1] * len(c)
+    for _ in range(extra):
+        best = 0
+        for e in range(1, len(c)):
+            if c[e] * r[best] > c[best] * r[e]:
+                best = e
+        r[best] += 1
+    return r
+
+
+def ep_plan(offsets, extra: int, R: int) -> Dict[str, np.ndarray]:
+    """Replicas of each expert (replica_counts) over its packed rows
+    offsets[e]..offsets[e+1]: copy i of expert e takes rows offsets[e] +
+    [floor(i c / r), floor((i+1) c / r)).  Copies are placed on R ranks
+    longest first (decreasing rows, ties by copy index p), each on the rank
+    with the fewest rows so far (ties to the lowest rank).  Copy p of expert
+    e is p = replica_start[e] + i."""
+    off = [int(v) for v in offsets]
+    E = len(off) - 1
+    counts = [off[e + 1] - off[e] for e in range(E)]
+    r = replica_counts(counts, extra)
+    start = [0]
+    for e in range(E):
+        start.append(start[-1] + r[e])
+    P = start[-1]
+    row0 = [0] * P
+    rows = [0] * P
+    for e in range(E):
+        for i in range(r[e]):
+            a = (i * counts[e]) // r[e]
+            b = ((i + 1) * counts[e]) // r[e]
+            row0[start[e] + i] = off[e] + a
+            rows[start[e] + i] = b - a
+    order = sorted(range(P), key=lambda p: (-rows[p], p))
+    load = [0] * R
+    rank = [0] * P
+    for p in order:
+        best = 0
+        for q in range(1, R):
+            if load[q] < load[best]:
+                best = q
+        rank[p] = best
+        load[best] += rows[p]
+    i32 = lambda v: np.array(v, dtype=np.int32)  # noqa: E731
+    return {"replica_start": i32(start), "replica_row0": i32(row0), "replica_rows": i32(rows),
+            "replica_rank": i32(rank), "rank_rows": i32(load)}

@@ -512,3 +512,55 @@ def test_weight_grad_entries_match_full_backward():
                                                   w1[e], w2[e], "f64")
         np.testing.assert_allclose(dw1, g["dw1_f64"][e][np.ix_(fs, is_)], rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(dw2, g["dw2_f64"][e][np.ix_(is_, fs)], rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- dispatch plan
+def test_hand_worked_ep_plan():
+    g = load("ep_plan.json")
+    out = orc.ep_plan(g["offsets"], g["extra"], g["R"])
+    for key in ("replica_start", "replica_row0", "replica_rows", "replica_rank", "rank_rows"):
+        assert out[key].tolist() == g[key], key
+
+
+@pytest.mark.parametrize("seed,extra", [(0, 0), (1, 5), (2, 40), (3, 200)])
+def test_replica_counts_are_the_largest_quotients(seed, extra):
+    """Greedy one-at-a-time replication equals taking the `extra` largest
+    quotients c_e / j (j = 1, 2, ...) in (value desc, expert asc, j asc)
+    order - a different formulation, evaluated with exact fractions."""
+    from fractions import Fraction
+    rng = np.random.default_rng(seed)
+    E = 37
+    counts = rng.integers(0, 500, E)
+    counts[3] = 0
+    counts[7] = counts[9]  # ties
+    cand = [(Fraction(int(counts[e]), j), e, j) for e in range(E) for j in range(1, extra + 2)]
+    cand.sort(key=lambda c: (-c[0], c[1], c[2]))
+    want = [1] * E
+    for _, e, _ in cand[:extra]:
+        want[e] += 1
+    assert orc.replica_counts(counts, extra) == want
+
+
+@pytest.mark.parametrize("seed,extra,R", [(0, 0, 8), (1, 16, 8), (2, 64, 16), (3, 3, 1), (4, 9, 64)])
+def test_ep_plan_invariants(seed, extra, R):
+    rng = np.random.default_rng(seed)
+    E = 50
+    counts = (rng.zipf(1.3, E) * 7) % 3000
+    counts[::11] = 0
+    off = np.concatenate([[0], np.cumsum(counts)])
+    out = orc.ep_plan(off, extra, R)
+    start, row0, rows, rank = (out[k] for k in ("replica_start", "replica_row0", "replica_rows",
+                                                "replica_rank"))
+    assert start[-1] == E + extra
+    for e in range(E):
+        seg = slice(start[e], start[e + 1])
+        # copies tile the expert's rows in order, sizes differ by at most one
+        assert row0[seg][0] == off[e] and (row0[seg] + rows[seg])[-1] == off[e + 1]
+        assert (row0[seg][1:] == (row0[seg] + rows[seg])[:-1]).all()
+        assert rows[seg].max() - rows[seg].min() <= 1
+    load = np.bincount(rank, weights=rows, minlength=R).astype(np.int64)
+    assert load.tolist() == out["rank_rows"].tolist()
+    assert load.sum() == counts.sum()
+    # list scheduling bound (Graham): the fullest rank exceeds the mean by at
+    # most one copy
+    assert load.max() <= load.sum() / R + rows.max() + 1e-9
