@@ -306,6 +306,15 @@ def main():
     t_bwd = time_it(lambda: layer.backward(dy, x, w_gate, w1, w2, dlogits=False), reps)
     t_ffn = time_it(lambda: layer.expert_ffn(w1, w2), reps)
     t_comb = time_it(lambda: layer.combine(), reps)
+    # dispatch plan for 8 ranks with one extra copy per expert (not part of
+    # the step: the planning that would feed an All-to-All)
+    R_plan, extra_plan = 8, w.E
+    zi = lambda n: torch.empty(n, dtype=torch.int32, device="cuda")  # noqa: E731
+    plan = [zi(w.E + 1), zi(w.E + extra_plan), zi(w.E + extra_plan), zi(w.E + extra_plan),
+            zi(R_plan)]
+    t_plan = time_it(lambda: moe.moe_ep_plan(w.E, R_plan, extra_plan, layer.offsets, *plan), reps)
+    rank_rows = plan[4].cpu().numpy()
+    plan_balance = float(rank_rows.max() / max(rank_rows.mean(), 1e-9))
     flops_launch = 2.0 * w.d * w.F * s_kept
     achieved = flops_launch / (gemm_launch_ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -340,7 +349,9 @@ def main():
                      "flops_per_launch": flops_launch,
                      "launch_us": gemm_launch_ms * 1e3},
         "parts_ms": {"forward": t_fwd, "backward": t_bwd, "expert_ffn": t_ffn,
-                     "combine": t_comb},
+                     "combine": t_comb, "ep_plan_8_ranks": t_plan},
+        "ep_plan": {"ranks": R_plan, "extra_copies": extra_plan,
+                    "max_over_mean_rank_rows": plan_balance},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (CPU reference) ...")

@@ -82,6 +82,8 @@ typedef int32_t moe_status;
 /* Limits of the compiled kernels (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 8
+#define MOE_PLAN_MAX_RANKS 64
+#define MOE_PLAN_MAX_COPIES 1024 /* E + extra copies in moe_ep_plan */
 
 typedef struct moe_shape {
   int32_t T;               /* tokens */
@@ -212,6 +214,29 @@ moe_status moe_backward(const moe_shape* shape, const void* dy, const void* x,
 moe_status moe_popularity_update(int32_t E, int32_t window, int64_t iter,
                                  const int32_t* counts_raw, int32_t* ring,
                                  int32_t* window_sum, void* stream);
+
+/* Expert-parallel dispatch plan from one GPU's packed rows (offsets [E+1]
+ * from moe_permute; counts c_e = offsets[e+1] - offsets[e]).
+ * - Copies (Fast MoE Inference via Predictive Prefetching and Expert
+ *   Replication: replication by token demand, capped by GPU memory): every
+ *   expert has one copy and the `extra` copies the memory budget allows go
+ *   one at a time to the expert with the most rows per copy (c_e / r_e,
+ *   compared exactly; ties to the lowest index).  Copies of expert e are
+ *   p = replica_start[e] .. replica_start[e+1]-1; copy i takes the packed
+ *   rows offsets[e] + [floor(i c/r), floor((i+1) c/r)) (replica_row0,
+ *   replica_rows) - one contiguous range, as the All-to-All sends them.
+ * - Placement (LLEP notes §2.1: work goes to the least-loaded GPU): copies in
+ *   order of decreasing rows (ties by copy index) each go to the rank with
+ *   the fewest rows so far (ties to the lowest rank): replica_rank[p];
+ *   rank_rows[r] = rows rank r computes (the All-to-All split sizes).
+ * All arrays are int32 device memory: replica_start [E+1], replica_row0,
+ * replica_rows, replica_rank [E+extra], rank_rows [R].  Limits: 1 <= E <=
+ * MOE_MAX_EXPERTS, 1 <= R <= MOE_PLAN_MAX_RANKS, 0 <= extra,
+ * E + extra <= MOE_PLAN_MAX_COPIES (else MOE_ERR_INVALID_ARG).  One
+ * workgroup; enqueues only. */
+moe_status moe_ep_plan(int32_t E, int32_t R, int32_t extra, const int32_t* offsets,
+                       int32_t* replica_start, int32_t* replica_row0, int32_t* replica_rows,
+                       int32_t* replica_rank, int32_t* rank_rows, void* stream);
 
 #ifdef __cplusplus
 }

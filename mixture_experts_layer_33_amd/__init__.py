@@ -16,7 +16,7 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MoeError", "MoeShape", "lib", "library_path",
     "moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-    "moe_backward", "moe_popularity_update", "OP", "PRIORITY",
+    "moe_backward", "moe_popularity_update", "moe_ep_plan", "OP", "PRIORITY",
 ]
 
 MOE_F32 = 0
@@ -25,7 +25,7 @@ PRIORITY = {"slot": 0, "choice": 1}  # capacity priority (MOE_PRIORITY_*)
 OP = {"route": 0, "permute": 1, "expert_ffn": 2, "combine": 3, "forward": 4, "backward": 5}
 EXPORTS = ["moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_backward", "moe_popularity_update"]
+           "moe_backward", "moe_popularity_update", "moe_ep_plan"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -79,10 +79,11 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [sp] + [_P] * 4 + [_P]
         L.moe_forward.argtypes = [sp] + [_P] * 18 + [_P, ctypes.c_size_t, _P]
         L.moe_backward.argtypes = [sp] + [_P] * 20 + [_P, ctypes.c_size_t, _P]
+        L.moe_ep_plan.argtypes = [ctypes.c_int32] * 3 + [_P] * 6 + [_P]
         L.moe_popularity_update.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                             _P, _P, _P, _P]
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-                     "moe_backward", "moe_popularity_update"):
+                     "moe_backward", "moe_popularity_update", "moe_ep_plan"):
             getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -198,3 +199,10 @@ def moe_popularity_update(E, window, it, counts_raw, ring, window_sum, stream=No
     _check(lib().moe_popularity_update(E, window, it, _ptr(counts_raw), _ptr(ring),
                                        _ptr(window_sum), _stream(stream)),
            "moe_popularity_update")
+
+
+def moe_ep_plan(E, R, extra, offsets, replica_start, replica_row0, replica_rows, replica_rank,
+                rank_rows, stream=None):
+    _check(lib().moe_ep_plan(E, R, extra, _ptr(offsets), _ptr(replica_start), _ptr(replica_row0),
+                             _ptr(replica_rows), _ptr(replica_rank), _ptr(rank_rows),
+                             _stream(stream)), "moe_ep_plan")

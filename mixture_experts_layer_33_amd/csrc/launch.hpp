@@ -77,4 +77,9 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
                              const uint32_t* relu_bits_in, uint32_t* relu_bits_ws, int S_max,
                              int d, int F, int E, hipStream_t s);
 
+// ---- expert-parallel dispatch plan (plan.hip)
+hipError_t launch_ep_plan(int E, int R, int extra, const int32_t* offsets,
+                          int32_t* replica_start, int32_t* replica_row0, int32_t* replica_rows,
+                          int32_t* replica_rank, int32_t* rank_rows, hipStream_t s);
+
 }  // namespace moe

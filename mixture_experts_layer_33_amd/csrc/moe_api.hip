@@ -354,4 +354,17 @@ moe_status moe_popularity_update(int32_t E, int32_t window, int64_t iter,
   return MOE_OK;
 }
 
+moe_status moe_ep_plan(int32_t E, int32_t R, int32_t extra, const int32_t* offsets,
+                       int32_t* replica_start, int32_t* replica_row0, int32_t* replica_rows,
+                       int32_t* replica_rank, int32_t* rank_rows, void* stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || R < 1 || R > MOE_PLAN_MAX_RANKS || extra < 0 ||
+      E + extra > MOE_PLAN_MAX_COPIES)
+    return MOE_ERR_INVALID_ARG;
+  if (!ptrs_ok(offsets, replica_start, replica_row0, replica_rows, replica_rank, rank_rows))
+    return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_ep_plan(E, R, extra, offsets, replica_start, replica_row0, replica_rows,
+                         replica_rank, rank_rows, as_stream(stream)));
+  return MOE_OK;
+}
+
 }  // extern "C"

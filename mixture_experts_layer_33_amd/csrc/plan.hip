@@ -1,0 +1,154 @@
+// Expert-parallel dispatch plan on gfx950: which copies of which experts run
+// on which rank, from the per-expert packed-row counts.
+//
+// Fast MoE Inference via Predictive Prefetching and Expert Replication:
+// experts are replicated by token demand ("deep physical replication"), with
+// the number of copies capped by GPU memory ("capacity limitation").  MoE
+// training optimisation: the LLEP algorithm and dynamic load balancing, §2.1:
+// work goes to the least-loaded GPU.  A Survey on Mixture of Experts, §5
+// System Design (first paragraph): the packed per-expert rows are what the
+// All-to-All dispatch sends, so a copy's rows are one contiguous range.
+//
+// One workgroup: the copy counts by a wavefront-wide argmax per extra copy,
+// the row split and a rank order of the copies in parallel, then the
+// least-loaded placement with one rank per lane.  Everything is integer, so
+// the plan is exact and deterministic.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kPlanThreads = 256;
+
+// (c_a / r_a, expert a) ranks before (c_b / r_b, expert b): more rows per
+// copy, or equal and a lower index
+__device__ __forceinline__ bool more_per_copy(int ca, int ra, int ea, int cb, int rb, int eb) {
+  const long long l = (long long)ca * rb, r = (long long)cb * ra;
+  return l > r || (l == r && ea < eb);
+}
+
+__global__ void __launch_bounds__(kPlanThreads)
+ep_plan_kernel(int E, int R, int extra, const int32_t* __restrict__ offsets,
+               int32_t* __restrict__ replica_start, int32_t* __restrict__ replica_row0,
+               int32_t* __restrict__ replica_rows, int32_t* __restrict__ replica_rank,
+               int32_t* __restrict__ rank_rows) {
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_rep[MOE_MAX_EXPERTS];
+  __shared__ int s_start[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_rows[MOE_PLAN_MAX_COPIES];
+  __shared__ int s_order[MOE_PLAN_MAX_COPIES];
+  __shared__ int s_scratch[kPlanThreads / 64 + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int e = tid; e <= E; e += kPlanThreads) s_off[e] = offsets[e];
+  __syncthreads();
+
+  // 1. copies per expert: one wavefront, lane owns experts lane + 64 q
+  if (tid < 64) {
+    constexpr int Q = MOE_MAX_EXPERTS / 64;
+    int c[Q], r[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = lane + 64 * q;
+      c[q] = e < E ? s_off[e + 1] - s_off[e] : 0;
+      r[q] = 1;
+    }
+    for (int it = 0; it < extra; ++it) {
+      int bc = 0, br = 1, be = 0x7fffffff;  // ranks after every expert
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int e = lane + 64 * q;
+        if (e < E && more_per_copy(c[q], r[q], e, bc, br, be)) {
+          bc = c[q];
+          br = r[q];
+          be = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const int oc = __shfl_xor(bc, o, 64), orr = __shfl_xor(br, o, 64),
+                  oe = __shfl_xor(be, o, 64);
+        if (more_per_copy(oc, orr, oe, bc, br, be)) {
+          bc = oc;
+          br = orr;
+          be = oe;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        if (lane + 64 * q == be) ++r[q];
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E) s_rep[e] = r[q];
+    }
+  }
+  __syncthreads();
+
+  // 2. copy index ranges: exclusive prefix of the copy counts
+  {
+    int total;
+    const int ex = block_exclusive_scan(tid < E ? s_rep[tid] : 0, s_scratch, &total);
+    if (tid < E) s_start[tid] = ex;
+    if (tid == 0) s_start[E] = total;
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += kPlanThreads) replica_start[e] = s_start[e];
+
+  // 3. copy i of expert e: rows offsets[e] + [floor(i c / r), floor((i+1) c / r))
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const long long c = s_off[e + 1] - s_off[e];
+    const int rr = s_rep[e];
+    for (int i = 0; i < rr; ++i) {
+      const int a = (int)((i * c) / rr), b = (int)(((i + 1) * c) / rr);
+      const int p = s_start[e] + i;
+      s_rows[p] = b - a;
+      replica_row0[p] = s_off[e] + a;
+      replica_rows[p] = b - a;
+    }
+  }
+  __syncthreads();
+
+  // 4. placement order: decreasing rows, ties by copy index
+  const int P = s_start[E];
+  for (int p = tid; p < P; p += kPlanThreads) {
+    const int n = s_rows[p];
+    int pos = 0;
+    for (int q = 0; q < P; ++q) {
+      const int m = s_rows[q];
+      pos += (m > n) || (m == n && q < p);
+    }
+    s_order[pos] = p;
+  }
+  __syncthreads();
+
+  // 5. least-loaded placement: lane = rank
+  if (tid < 64) {
+    int load = lane < R ? 0 : 0x7fffffff;
+    for (int j = 0; j < P; ++j) {
+      const int p = s_order[j];
+      int bl = load, bq = lane;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const int ol = __shfl_xor(bl, o, 64), oq = __shfl_xor(bq, o, 64);
+        if (ol < bl || (ol == bl && oq < bq)) {
+          bl = ol;
+          bq = oq;
+        }
+      }
+      if (lane == bq) load += s_rows[p];
+      if (lane == 0) replica_rank[p] = bq;
+    }
+    if (lane < R) rank_rows[lane] = load;
+  }
+}
+
+hipError_t launch_ep_plan(int E, int R, int extra, const int32_t* offsets,
+                          int32_t* replica_start, int32_t* replica_row0, int32_t* replica_rows,
+                          int32_t* replica_rank, int32_t* rank_rows, hipStream_t s) {
+  hipLaunchKernelGGL(ep_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, E, R, extra, offsets,
+                     replica_start, replica_row0, replica_rows, replica_rank, rank_rows);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -117,6 +117,14 @@ def test_entry_points_reject_bad_arguments_before_launch():
     # bad shape wins over everything else
     bad = ctypes.byref(shape(k=0))
     assert L.moe_forward(bad, *([P] * 18), P, ws, None) == -1
+    # dispatch plan limits
+    assert L.moe_ep_plan(0, 8, 0, P, P, P, P, P, P, None) == -1
+    assert L.moe_ep_plan(257, 8, 0, P, P, P, P, P, P, None) == -1
+    assert L.moe_ep_plan(16, 0, 0, P, P, P, P, P, P, None) == -1
+    assert L.moe_ep_plan(16, 65, 0, P, P, P, P, P, P, None) == -1
+    assert L.moe_ep_plan(16, 8, -1, P, P, P, P, P, P, None) == -1
+    assert L.moe_ep_plan(256, 8, 769, P, P, P, P, P, P, None) == -1
+    assert L.moe_ep_plan(16, 8, 0, P, P, P, P, None, P, None) == -1
     # popularity window limits
     assert L.moe_popularity_update(8, 0, 0, P, P, P, None) == -1
     assert L.moe_popularity_update(8, 65, 0, P, P, P, None) == -1
