@@ -486,3 +486,68 @@ def ep_plan(offsets, extra: int, R: int) -> Dict[str, np.ndarray]:
     i32 = lambda v: np.array(v, dtype=np.int32)  # noqa: E731
     return {"replica_start": i32(start), "replica_row0": i32(row0), "replica_rows": i32(rows),
             "replica_rank": i32(rank), "rank_rows": i32(load)}
+
+
+# --------------------------------------------------------------------------
+# cross-layer expert correlation and popularity prediction
+# --------------------------------------------------------------------------
+def cooccurrence(idx_a: np.ndarray, idx_b: np.ndarray, E_a: int, E_b: int) -> np.ndarray:
+    """counts[x][x'] = number of (token, choice in layer j, choice in layer
+    j+1) triples with expert x in layer j and x' in layer j+1 (PopFetcher
+    notes §4.1: the tuple (x, x') of a token's selections in consecutive
+    layers).  Exact integers."""
+    T = idx_a.shape[0]
+    out = np.zeros((E_a, E_b), dtype=np.int64)
+    for t in range(T):
+        for x in idx_a[t]:
+            for y in idx_b[t]:
+                out[int(x), int(y)] += 1
+    return out
+
+
+def window_update(ring: np.ndarray, it: int, current: np.ndarray):
+    """Put this iteration's table in slot it % W of the ring and return
+    (ring, sum of the last min(it + 1, W) iterations) - the sliding window of
+    §4.2 applied to the co-occurrence counts.  Exact integers."""
+    ring = np.array(ring, dtype=np.int64, copy=True)
+    W = ring.shape[0]
+    ring[it % W] = current
+    n = min(it + 1, W)
+    total = np.zeros_like(ring[0])
+    for b in range(n):
+        total += ring[(it - b) % W]
+    return ring, total
+
+
+def predict_popularity(counts_a, cooc) -> np.ndarray:
+    """Popularity of the next layer's experts from this layer's selections
+    (PopFetcher notes §4.2, Eq. 2 and Eq. 3, whose bodies are missing from the
+    page; the reading taken): P(x' | x) = cooc[x][x'] / sum_x'' cooc[x][x''];
+    pred[x'] = sum over x in index order of counts_a[x] * P(x' | x), each
+    product and sum one float64 operation (x with an all-zero row adds
+    nothing)."""
+    E_a, E_b = cooc.shape
+    pred = [0.0] * E_b
+    for h in range(E_b):
+        acc = 0.0
+        for i in range(E_a):
+            row = int(np.sum(cooc[i]))
+            if row == 0:
+                continue
+            p = float(int(cooc[i][h])) / float(row)
+            acc = acc + float(int(counts_a[i])) * p
+        pred[h] = acc
+    return np.array(pred, dtype=np.float64)
+
+
+def rank_experts(pred) -> np.ndarray:
+    """Experts by decreasing predicted popularity, ties to the lower index."""
+    return np.array(sorted(range(len(pred)), key=lambda h: (-pred[h], h)), dtype=np.int32)
+
+
+def top_hit_rate(pred, actual, n: int = 5) -> float:
+    """Share of the n experts predicted most popular that are among the n
+    actually most popular (both ranked with ties to the lower index)."""
+    a = set(rank_experts(pred)[:n].tolist())
+    b = set(rank_experts(np.asarray(actual, dtype=np.float64))[:n].tolist())
+    return len(a & b) / n

@@ -564,3 +564,71 @@ def test_ep_plan_invariants(seed, extra, R):
     # list scheduling bound (Graham): the fullest rank exceeds the mean by at
     # most one copy
     assert load.max() <= load.sum() / R + rows.max() + 1e-9
+
+
+# ---------------------------------------------------------------- cross-layer correlation
+def test_hand_worked_cooccurrence_and_prediction():
+    g = load("cooccurrence.json")
+    ring = np.zeros((g["window"], g["E_a"], g["E_b"]), np.int64)
+    for it, step in enumerate(g["iterations"]):
+        c = orc.cooccurrence(np.array(step["idx_a"]), np.array(step["idx_b"]), g["E_a"], g["E_b"])
+        assert c.tolist() == step["cooc"]
+        ring, ws = orc.window_update(ring, it, c)
+        assert ws.tolist() == step["window_sum"]
+    p = g["predict_case"]
+    pred = orc.predict_popularity(np.array(p["counts_a"]), np.array(p["cooc"]))
+    assert pred.tolist() == p["pred"]
+    assert orc.rank_experts(pred).tolist() == p["order"]
+
+
+def test_cooccurrence_is_a_product_of_one_hot_matrices():
+    rng = np.random.default_rng(3)
+    T, Ea, Eb, ka, kb = 300, 9, 7, 3, 2
+    ia = np.stack([rng.choice(Ea, ka, replace=False) for _ in range(T)])
+    ib = np.stack([rng.choice(Eb, kb, replace=False) for _ in range(T)])
+    A = np.zeros((T, Ea), np.int64)
+    B = np.zeros((T, Eb), np.int64)
+    np.add.at(A, (np.repeat(np.arange(T), ka), ia.reshape(-1)), 1)
+    np.add.at(B, (np.repeat(np.arange(T), kb), ib.reshape(-1)), 1)
+    c = orc.cooccurrence(ia, ib, Ea, Eb)
+    np.testing.assert_array_equal(c, A.T @ B)
+    # each layer-j selection pairs with k_b layer-(j+1) selections
+    np.testing.assert_array_equal(c.sum(1), kb * np.bincount(ia.reshape(-1), minlength=Ea))
+
+
+def test_window_update_matches_popularity_window():
+    rng = np.random.default_rng(4)
+    ring2 = np.zeros((3, 5, 1), np.int64)
+    ring1 = np.zeros((3, 5), np.int32)
+    for it in range(7):
+        c = rng.integers(0, 100, 5)
+        ring2, ws2 = orc.window_update(ring2, it, c[:, None])
+        ring1, ws1 = orc.popularity_update(ring1, it, c)
+        np.testing.assert_array_equal(ws2[:, 0], ws1)
+
+
+def test_prediction_special_cases():
+    # deterministic successor: every token's next-layer expert is f(x)
+    rng = np.random.default_rng(5)
+    E, T = 11, 500
+    f = rng.permutation(E)
+    ia = rng.integers(0, E, (T, 1))
+    ib = f[ia]
+    c = orc.cooccurrence(ia, ib, E, E)
+    counts = rng.integers(0, 1000, E)
+    pred = orc.predict_popularity(counts, c)
+    want = np.zeros(E)
+    seen = np.bincount(ia[:, 0], minlength=E) > 0
+    for x in range(E):
+        if seen[x]:
+            want[f[x]] += counts[x]
+    np.testing.assert_array_equal(pred, want)
+    # independent layers: P(x'|x) = q(x') for every x, so pred = (sum of the
+    # counts of seen x) * q
+    q = np.array([3, 0, 5, 2], np.int64)
+    u = np.array([4, 1, 0, 7, 2], np.int64)
+    cnt = np.array([10, 20, 30, 40, 50])
+    pred = orc.predict_popularity(cnt, np.outer(u, q))
+    np.testing.assert_allclose(pred, (10 + 20 + 40 + 50) * q / q.sum(), rtol=1e-15)
+    assert orc.top_hit_rate(pred, q, n=2) == 1.0
+    assert orc.top_hit_rate(pred, q[::-1], n=2) == 0.0
