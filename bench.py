@@ -315,6 +315,24 @@ def main():
     t_plan = time_it(lambda: moe.moe_ep_plan(w.E, R_plan, extra_plan, layer.offsets, *plan), reps)
     rank_rows = plan[4].cpu().numpy()
     plan_balance = float(rank_rows.max() / max(rank_rows.mean(), 1e-9))
+    # cross-layer co-occurrence window and next-layer popularity prediction,
+    # with this layer's routing as layer j and seeded successor choices as j+1
+    idx_b = torch.from_numpy(workloads.next_layer_choices(layer.topk_idx.cpu().numpy(), w.E,
+                                                          w.k, 0)).cuda()
+    co_ring = torch.zeros((w.window, w.E, w.E), dtype=torch.int32, device="cuda")
+    co_sum = torch.zeros((w.E, w.E), dtype=torch.int32, device="cuda")
+    co_it = [0]
+
+    def co_update():
+        moe.moe_cooccurrence_update(w.E, w.E, w.k, w.k, w.T, w.window, co_it[0], layer.topk_idx,
+                                    idx_b, co_ring, co_sum)
+        co_it[0] += 1
+
+    t_co = time_it(co_update, reps)
+    pred = torch.empty(w.E, dtype=torch.float64, device="cuda")
+    order = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    t_pred = time_it(lambda: moe.moe_predict_popularity(w.E, w.E, layer.counts_raw, co_sum, pred,
+                                                        order), reps)
     flops_launch = 2.0 * w.d * w.F * s_kept
     achieved = flops_launch / (gemm_launch_ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -349,7 +367,8 @@ def main():
                      "flops_per_launch": flops_launch,
                      "launch_us": gemm_launch_ms * 1e3},
         "parts_ms": {"forward": t_fwd, "backward": t_bwd, "expert_ffn": t_ffn,
-                     "combine": t_comb, "ep_plan_8_ranks": t_plan},
+                     "combine": t_comb, "ep_plan_8_ranks": t_plan,
+                     "cooccurrence_update": t_co, "predict_popularity": t_pred},
         "ep_plan": {"ranks": R_plan, "extra_copies": extra_plan,
                     "max_over_mean_rank_rows": plan_balance},
     }

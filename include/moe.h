@@ -238,6 +238,35 @@ moe_status moe_ep_plan(int32_t E, int32_t R, int32_t extra, const int32_t* offse
                        int32_t* replica_start, int32_t* replica_row0, int32_t* replica_rows,
                        int32_t* replica_rank, int32_t* rank_rows, void* stream);
 
+/* Cross-layer expert correlation (PopFetcher notes §4.1: a token choosing
+ * expert x in layer j and x' in layer j+1 gives the tuple (x, x')).  Counts
+ * this iteration's tuples of T tokens, idx_a [T, k_a] (layer j, experts
+ * < E_a) against idx_b [T, k_b] (layer j+1, experts < E_b), into
+ * ring[iter % window] ([window][E_a][E_b] int32) and writes window_sum
+ * [E_a][E_b] = sum of the last min(iter + 1, window) slices (the sliding
+ * window of §4.2).  Exact integers.  Limits: 1 <= E_a, E_b <=
+ * MOE_MAX_EXPERTS, 1 <= k <= MOE_MAX_TOPK (k_a <= E_a, k_b <= E_b),
+ * 1 <= window <= 64, iter >= 0, T >= 1, else MOE_ERR_INVALID_ARG; expert
+ * ids outside the ranges are a precondition violation.  Device pointers;
+ * enqueues only. */
+moe_status moe_cooccurrence_update(int32_t E_a, int32_t E_b, int32_t k_a, int32_t k_b,
+                                   int32_t T, int32_t window, int64_t iter,
+                                   const int32_t* idx_a, const int32_t* idx_b, int32_t* ring,
+                                   int32_t* window_sum, void* stream);
+
+/* Next-layer popularity from this layer's selections (PopFetcher notes
+ * §4.2, Eq. 2 and Eq. 3, bodies missing from the page; reading taken):
+ * P(x'|x) = cooc[x][x'] / sum_x'' cooc[x][x''] and
+ * pred[x'] = sum over x = 0..E_a-1 (rows with zero total skipped) of
+ * counts_a[x] * P(x'|x), each quotient, product and sum one correctly rounded
+ * float64 operation in that order.  order [E_b] lists the experts by
+ * decreasing pred, ties to the lower index.  counts_a [E_a], cooc
+ * [E_a][E_b] int32 (e.g. moe_cooccurrence_update's window_sum), pred [E_b]
+ * float64, order [E_b] int32; device pointers; enqueues only. */
+moe_status moe_predict_popularity(int32_t E_a, int32_t E_b, const int32_t* counts_a,
+                                  const int32_t* cooc, double* pred, int32_t* order,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

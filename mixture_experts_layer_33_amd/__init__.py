@@ -16,7 +16,8 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MoeError", "MoeShape", "lib", "library_path",
     "moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-    "moe_backward", "moe_popularity_update", "moe_ep_plan", "OP", "PRIORITY",
+    "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
+    "moe_predict_popularity", "OP", "PRIORITY",
 ]
 
 MOE_F32 = 0
@@ -25,7 +26,8 @@ PRIORITY = {"slot": 0, "choice": 1}  # capacity priority (MOE_PRIORITY_*)
 OP = {"route": 0, "permute": 1, "expert_ffn": 2, "combine": 3, "forward": 4, "backward": 5}
 EXPORTS = ["moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_backward", "moe_popularity_update", "moe_ep_plan"]
+           "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
+           "moe_predict_popularity"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -80,10 +82,13 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [sp] + [_P] * 18 + [_P, ctypes.c_size_t, _P]
         L.moe_backward.argtypes = [sp] + [_P] * 20 + [_P, ctypes.c_size_t, _P]
         L.moe_ep_plan.argtypes = [ctypes.c_int32] * 3 + [_P] * 6 + [_P]
+        L.moe_cooccurrence_update.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_int64] + [_P] * 5
+        L.moe_predict_popularity.argtypes = [ctypes.c_int32] * 2 + [_P] * 5
         L.moe_popularity_update.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                             _P, _P, _P, _P]
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-                     "moe_backward", "moe_popularity_update", "moe_ep_plan"):
+                     "moe_backward", "moe_popularity_update", "moe_ep_plan",
+                     "moe_cooccurrence_update", "moe_predict_popularity"):
             getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -206,3 +211,15 @@ def moe_ep_plan(E, R, extra, offsets, replica_start, replica_row0, replica_rows,
     _check(lib().moe_ep_plan(E, R, extra, _ptr(offsets), _ptr(replica_start), _ptr(replica_row0),
                              _ptr(replica_rows), _ptr(replica_rank), _ptr(rank_rows),
                              _stream(stream)), "moe_ep_plan")
+
+
+def moe_cooccurrence_update(E_a, E_b, k_a, k_b, T, window, it, idx_a, idx_b, ring, window_sum,
+                            stream=None):
+    _check(lib().moe_cooccurrence_update(E_a, E_b, k_a, k_b, T, window, it, _ptr(idx_a),
+                                         _ptr(idx_b), _ptr(ring), _ptr(window_sum),
+                                         _stream(stream)), "moe_cooccurrence_update")
+
+
+def moe_predict_popularity(E_a, E_b, counts_a, cooc, pred, order, stream=None):
+    _check(lib().moe_predict_popularity(E_a, E_b, _ptr(counts_a), _ptr(cooc), _ptr(pred),
+                                        _ptr(order), _stream(stream)), "moe_predict_popularity")

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "plan.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "plan.hip",
+           "correl.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

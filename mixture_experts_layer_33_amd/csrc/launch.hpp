@@ -82,4 +82,11 @@ hipError_t launch_ep_plan(int E, int R, int extra, const int32_t* offsets,
                           int32_t* replica_start, int32_t* replica_row0, int32_t* replica_rows,
                           int32_t* replica_rank, int32_t* rank_rows, hipStream_t s);
 
+// ---- cross-layer correlation and popularity prediction (correl.hip)
+hipError_t launch_cooccurrence(int E_a, int E_b, int k_a, int k_b, int T, int window,
+                               int64_t iter, const int32_t* idx_a, const int32_t* idx_b,
+                               int32_t* ring, int32_t* window_sum, hipStream_t s);
+hipError_t launch_predict(int E_a, int E_b, const int32_t* counts_a, const int32_t* cooc,
+                          double* pred, int32_t* order, hipStream_t s);
+
 }  // namespace moe

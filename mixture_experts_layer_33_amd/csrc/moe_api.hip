@@ -367,4 +367,28 @@ moe_status moe_ep_plan(int32_t E, int32_t R, int32_t extra, const int32_t* offse
   return MOE_OK;
 }
 
+moe_status moe_cooccurrence_update(int32_t E_a, int32_t E_b, int32_t k_a, int32_t k_b,
+                                   int32_t T, int32_t window, int64_t iter,
+                                   const int32_t* idx_a, const int32_t* idx_b, int32_t* ring,
+                                   int32_t* window_sum, void* stream) {
+  if (E_a < 1 || E_b < 1 || E_a > MOE_MAX_EXPERTS || E_b > MOE_MAX_EXPERTS || k_a < 1 ||
+      k_b < 1 || k_a > MOE_MAX_TOPK || k_b > MOE_MAX_TOPK || k_a > E_a || k_b > E_b || T < 1 ||
+      window < 1 || window > 64 || iter < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (!ptrs_ok(idx_a, idx_b, ring, window_sum)) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_cooccurrence(E_a, E_b, k_a, k_b, T, window, iter, idx_a, idx_b, ring,
+                              window_sum, as_stream(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_predict_popularity(int32_t E_a, int32_t E_b, const int32_t* counts_a,
+                                  const int32_t* cooc, double* pred, int32_t* order,
+                                  void* stream) {
+  if (E_a < 1 || E_b < 1 || E_a > MOE_MAX_EXPERTS || E_b > MOE_MAX_EXPERTS)
+    return MOE_ERR_INVALID_ARG;
+  if (!ptrs_ok(counts_a, cooc, pred, order)) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_predict(E_a, E_b, counts_a, cooc, pred, order, as_stream(stream)));
+  return MOE_OK;
+}
+
 }  // extern "C"

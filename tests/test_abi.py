@@ -125,6 +125,14 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.moe_ep_plan(16, 8, -1, P, P, P, P, P, P, None) == -1
     assert L.moe_ep_plan(256, 8, 769, P, P, P, P, P, P, None) == -1
     assert L.moe_ep_plan(16, 8, 0, P, P, P, P, None, P, None) == -1
+    # correlation limits
+    assert L.moe_cooccurrence_update(0, 8, 2, 2, 10, 4, 0, P, P, P, P, None) == -1
+    assert L.moe_cooccurrence_update(8, 8, 9, 2, 10, 4, 0, P, P, P, P, None) == -1
+    assert L.moe_cooccurrence_update(8, 8, 2, 2, 10, 65, 0, P, P, P, P, None) == -1
+    assert L.moe_cooccurrence_update(8, 8, 2, 2, 10, 4, -1, P, P, P, P, None) == -1
+    assert L.moe_cooccurrence_update(8, 8, 2, 2, 10, 4, 0, P, None, P, P, None) == -1
+    assert L.moe_predict_popularity(8, 257, P, P, P, P, None) == -1
+    assert L.moe_predict_popularity(8, 8, P, P, None, P, None) == -1
     # popularity window limits
     assert L.moe_popularity_update(8, 0, 0, P, P, P, None) == -1
     assert L.moe_popularity_update(8, 65, 0, P, P, P, None) == -1

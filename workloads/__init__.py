@@ -27,7 +27,8 @@ from typing import Dict, Optional
 import numpy as np
 
 SEED = 0
-TAGS = {"x": 1, "w_gate": 2, "order": 3, "w1": 4, "w2": 5, "dy": 6, "drift": 7}
+TAGS = {"x": 1, "w_gate": 2, "order": 3, "w1": 4, "w2": 5, "dy": 6, "drift": 7,
+        "successor": 8, "next_layer": 9}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -199,3 +200,37 @@ def quantize_half_steps(a: np.ndarray) -> np.ndarray:
     """Round values to multiples of 0.5 (a tie-heavy routing input)."""
     return (np.round(np.asarray(a, dtype=np.float64) * 2.0) / 2.0).astype(np.float32)
 
+
+
+def next_layer_choices(idx_a: np.ndarray, E_b: int, k_b: int, it: int = 0,
+                       follow: float = 0.7) -> np.ndarray:
+    """Synthetic top-k choices of the following layer, correlated with this
+    layer's: a seeded successor map sends expert x to x' = succ[x]; each of a
+    token's k_b choices is, with probability ``follow``, the successor of its
+    next unused layer-j choice, else a uniformly drawn expert; choices are
+    made distinct by skipping repeats.  The successor map is fixed across
+    iterations; the coin flips and draws change with ``it``.  (Input
+    generation only: the pages' cross-layer tuples, not a learned router.)"""
+    T, k_a = idx_a.shape
+    succ = rng("successor", 0).permutation(E_b)
+    g = rng("next_layer", it)
+    flips = g.random((T, 4 * k_b))
+    draws = g.integers(0, E_b, (T, 4 * k_b))
+    out = np.empty((T, k_b), dtype=np.int32)
+    for t in range(T):
+        chosen = []
+        a = 0
+        c = 0
+        while len(chosen) < k_b:
+            if c < 4 * k_b and flips[t, c] < follow and a < k_a:
+                cand = int(succ[int(idx_a[t, a]) % E_b])
+                a += 1
+            elif c < 4 * k_b:
+                cand = int(draws[t, c])
+            else:
+                cand = (chosen[-1] + 1) % E_b if chosen else 0
+            c += 1
+            if cand not in chosen:
+                chosen.append(cand)
+        out[t] = chosen
+    return out
