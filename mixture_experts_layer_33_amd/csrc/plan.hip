@@ -1,9 +1,9 @@
 // Expert-parallel dispatch plan on gfx950: which copies of which experts run
 // on which rank, from the per-expert packed-row counts.
 //
-// Fast MoE Inference via Predictive Prefetching and Expert Replication:
-// experts are replicated by token demand ("deep physical replication"), with
-// the number of copies capped by GPU memory ("capacity limitation").  MoE
+// Fast MoE Inference via Predictive Prefetching and Expert Replication, main
+// contributions 2 and 3: experts get physical copies by token demand, and the
+// number of copies is capped by GPU memory.  MoE
 // training optimisation: the LLEP algorithm and dynamic load balancing, §2.1:
 // work goes to the least-loaded GPU.  A Survey on Mixture of Experts, §5
 // System Design (first paragraph): the packed per-expert rows are what the

@@ -32,9 +32,14 @@ only where the layer stores a tensor):
   w.r.t. parameters);
 * an expert-parallel dispatch plan: demand-based replication of hot experts
   under a cap on extra copies (Fast MoE Inference via Predictive Prefetching
-  and Expert Replication: "deep physical replication" by token demand and
-  "capacity limitation" by GPU memory) and least-loaded placement of the
-  copies on ranks (LLEP notes, §2.1: work goes to the least-loaded GPU).
+  and Expert Replication, main contributions 2 and 3: physical copies of
+  experts by token demand, their number limited by GPU memory) and
+  least-loaded placement of the copies on ranks (LLEP notes, §2.1: work goes
+  to the least-loaded GPU);
+* cross-layer expert correlation and popularity prediction (PopFetcher notes
+  §4.1: tuples of a token's selections in consecutive layers; §4.2, Eq. 2
+  and Eq. 3, bodies missing: conditional probabilities from the windowed
+  tuple counts weight this layer's counts to predict the next layer's).
 
 Readings of points the pages leave open (each is listed in the design notes):
 selection on the fp32 logits, ties to the lowest index, weights = softmax over

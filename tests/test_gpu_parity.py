@@ -43,6 +43,10 @@ SMALL = {
                                              capacity_factor=1.0, priority="choice"),
     "skewed_cf080_choice": workloads.scaled(WL["skewed_zipf12"], T=1500, d=128, F=192,
                                             capacity_factor=0.8, priority="choice"),
+    # top-1 (Switch-style) routing: one weight of 1 per token, with and without drops
+    "uniform_top1_cf100": workloads.scaled(WL["uniform_cf125"], T=1000, d=256, F=320, k=1,
+                                           capacity_factor=1.0),
+    "skewed_top1": workloads.scaled(WL["skewed_zipf12"], T=1500, d=128, F=192, k=1),
 }
 
 
