@@ -306,6 +306,9 @@ def main():
     t_bwd = time_it(lambda: layer.backward(dy, x, w_gate, w1, w2, dlogits=False), reps)
     t_ffn = time_it(lambda: layer.expert_ffn(w1, w2), reps)
     t_comb = time_it(lambda: layer.combine(), reps)
+    # the gather/scatter-fused forward (same y, no packed token copy)
+    t_fused = time_it(lambda: layer.forward_fused(x, w_gate, b_gate, w1, w2, logits_out=False),
+                      reps)
     # dispatch plan for 8 ranks with one extra copy per expert (not part of
     # the step: the planning that would feed an All-to-All)
     R_plan, extra_plan = 8, w.E
@@ -338,7 +341,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     comb_bytes = s_kept * w.d * (2 if w.dtype == "bf16" else 4) + \
         w.T * w.d * (2 if w.dtype == "bf16" else 4) + 8 * w.T * w.k
-    log(f"forward {t_fwd:.3f} ms, backward {t_bwd:.3f} ms, expert FFN {t_ffn:.3f} ms "
+    log(f"forward {t_fwd:.3f} ms (gather/scatter-fused {t_fused:.3f} ms), backward {t_bwd:.3f} ms, expert FFN {t_ffn:.3f} ms "
         f"({achieved:.1f} TFLOP/s), combine {t_comb*1e3:.1f} us "
         f"({comb_bytes / (t_comb / 1e3) / 1e9:.0f} GB/s)")
 
@@ -366,7 +369,7 @@ def main():
                      "frac": achieved / peak, "traffic": load_traffic(w.name),
                      "flops_per_launch": flops_launch,
                      "launch_us": gemm_launch_ms * 1e3},
-        "parts_ms": {"forward": t_fwd, "backward": t_bwd, "expert_ffn": t_ffn,
+        "parts_ms": {"forward": t_fwd, "forward_fused": t_fused, "backward": t_bwd, "expert_ffn": t_ffn,
                      "combine": t_comb, "ep_plan_8_ranks": t_plan,
                      "cooccurrence_update": t_co, "predict_popularity": t_pred},
         "ep_plan": {"ranks": R_plan, "extra_copies": extra_plan,

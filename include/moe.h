@@ -103,6 +103,7 @@ typedef struct moe_shape {
 #define MOE_OP_COMBINE 3
 #define MOE_OP_FORWARD 4
 #define MOE_OP_BACKWARD 5
+#define MOE_OP_FORWARD_FUSED 6
 
 /* Workspace bytes `op` needs for `shape` (0 if none).  Returns 0 and sets
  * nothing on an invalid shape; validate with moe_check_shape first. */
@@ -182,6 +183,27 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
                        int32_t* slot_row, int32_t* row_token, void* x_perm, void* h,
                        void* out_perm, uint32_t* relu_bits, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* Gather/scatter-fused forward (A Survey on Mixture of Experts, §5.1
+ * Computation: ScatterMoE's grouped product on scattered rows avoids
+ * copying tokens into per-expert groups).  Same routing and the same y,
+ * bit for bit, as moe_forward, without the packed copy x_perm: the first
+ * expert GEMM reads row row_token[r] of x for packed row r, the second
+ * stores each kept slot's expert output at that slot, out_slot[t*k+j]
+ * ([T*k][d_model], activation type; rows of dropped slots are not
+ * written), and the decode reads slot rows directly.  topk_idx, topk_w,
+ * counts, offsets, slot_row, row_token, h and relu_bits are as moe_forward
+ * writes them; out_slot[s] = out_perm[slot_row[s]] for every kept slot s.
+ * For inference or any forward not followed by moe_backward, which takes
+ * moe_forward's packed tensors.  logits_out, counts_raw and relu_bits may
+ * be NULL.  Workspace: MOE_OP_FORWARD_FUSED. */
+moe_status moe_forward_fused(const moe_shape* shape, const void* x, const float* w_gate,
+                             const float* b_gate, const void* w1, const void* w2, void* y,
+                             float* logits_out, int32_t* topk_idx, float* topk_w,
+                             int32_t* counts_raw, int32_t* counts_kept, int32_t* offsets,
+                             int32_t* slot_row, int32_t* row_token, void* h, void* out_slot,
+                             uint32_t* relu_bits, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Backward of moe_forward for output gradient dy (PopFetcher notes §5.2.1:
  * one GEMM pass forward, two backward - gradients of the inputs and of the

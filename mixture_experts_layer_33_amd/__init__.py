@@ -16,17 +16,18 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MoeError", "MoeShape", "lib", "library_path",
     "moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-    "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
+    "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
     "moe_predict_popularity", "OP", "PRIORITY",
 ]
 
 MOE_F32 = 0
 MOE_BF16 = 1
 PRIORITY = {"slot": 0, "choice": 1}  # capacity priority (MOE_PRIORITY_*)
-OP = {"route": 0, "permute": 1, "expert_ffn": 2, "combine": 3, "forward": 4, "backward": 5}
+OP = {"route": 0, "permute": 1, "expert_ffn": 2, "combine": 3, "forward": 4, "backward": 5,
+      "forward_fused": 6}
 EXPORTS = ["moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
+           "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
            "moe_predict_popularity"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn.argtypes = [sp] + [_P] * 7 + [_P, ctypes.c_size_t, _P]
         L.moe_combine.argtypes = [sp] + [_P] * 4 + [_P]
         L.moe_forward.argtypes = [sp] + [_P] * 18 + [_P, ctypes.c_size_t, _P]
+        L.moe_forward_fused.argtypes = [sp] + [_P] * 17 + [_P, ctypes.c_size_t, _P]
         L.moe_backward.argtypes = [sp] + [_P] * 20 + [_P, ctypes.c_size_t, _P]
         L.moe_ep_plan.argtypes = [ctypes.c_int32] * 3 + [_P] * 6 + [_P]
         L.moe_cooccurrence_update.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_int64] + [_P] * 5
@@ -87,7 +89,7 @@ def lib() -> ctypes.CDLL:
         L.moe_popularity_update.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                             _P, _P, _P, _P]
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-                     "moe_backward", "moe_popularity_update", "moe_ep_plan",
+                     "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan",
                      "moe_cooccurrence_update", "moe_predict_popularity"):
             getattr(L, name).restype = ctypes.c_int32
         _lib = L
@@ -186,6 +188,18 @@ def moe_forward(shape, x, w_gate, b_gate, w1, w2, y, logits_out, topk_idx, topk_
                              _ptr(counts_raw), _ptr(counts_kept), _ptr(offsets), _ptr(slot_row),
                              _ptr(row_token), _ptr(x_perm), _ptr(h), _ptr(out_perm),
                              _ptr(relu_bits), ws, nb, _stream(stream)), "moe_forward")
+
+
+def moe_forward_fused(shape, x, w_gate, b_gate, w1, w2, y, logits_out, topk_idx, topk_w,
+                      counts_raw, counts_kept, offsets, slot_row, row_token, h, out_slot,
+                      relu_bits, workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check(lib().moe_forward_fused(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(b_gate),
+                                   _ptr(w1), _ptr(w2), _ptr(y), _ptr(logits_out), _ptr(topk_idx),
+                                   _ptr(topk_w), _ptr(counts_raw), _ptr(counts_kept),
+                                   _ptr(offsets), _ptr(slot_row), _ptr(row_token), _ptr(h),
+                                   _ptr(out_slot), _ptr(relu_bits), ws, nb, _stream(stream)),
+           "moe_forward_fused")
 
 
 def moe_backward(shape, dy, x, w_gate, w1, w2, topk_idx, topk_w, slot_row, row_token, offsets,

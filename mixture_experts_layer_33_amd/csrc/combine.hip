@@ -134,7 +134,8 @@ __device__ __forceinline__ void gate_dropped_block(const ActT* __restrict__ x,
 template <typename ActT>
 __global__ void __launch_bounds__(kRowThreads)
 combine_kernel(const ActT* __restrict__ out_perm, const float* __restrict__ topk_w,
-               const int32_t* __restrict__ slot_row, ActT* __restrict__ y, int T, int d, int k) {
+               const int32_t* __restrict__ slot_row, ActT* __restrict__ y, int T, int d, int k,
+               bool slot_order) {
   using CK = Chunk<ActT>;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
@@ -142,6 +143,11 @@ combine_kernel(const ActT* __restrict__ out_perm, const float* __restrict__ topk
   int rows[MOE_MAX_TOPK];
   float w[MOE_MAX_TOPK];
   token_slots(t, k, slot_row, topk_w, rows, w);
+  if (slot_order) {  // expert outputs stored by slot (gather-fused forward)
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (rows[j] >= 0) rows[j] = t * k + j;
+  }
   for (int c = lane * CK::N; c < d; c += 64 * CK::N) {
     float acc[CK::N];
 #pragma unroll
@@ -347,14 +353,15 @@ __global__ void popularity_kernel(int E, int window, int64_t iter,
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,
-                          const int32_t* slot_row, void* y, int T, int d, int k, hipStream_t s) {
+                          const int32_t* slot_row, void* y, int T, int d, int k, hipStream_t s,
+                          bool slot_order) {
   dim3 grid((T + 3) / 4), block(kRowThreads);
   if (act == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<bf16>, grid, block, 0, s, (const bf16*)out_perm, topk_w,
-                       slot_row, (bf16*)y, T, d, k);
+                       slot_row, (bf16*)y, T, d, k, slot_order);
   else
     hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, (const float*)out_perm, topk_w,
-                       slot_row, (float*)y, T, d, k);
+                       slot_row, (float*)y, T, d, k, slot_order);
   return hipGetLastError();
 }
 

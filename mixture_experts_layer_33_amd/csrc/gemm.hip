@@ -92,6 +92,20 @@ struct TileK {
       off[i] = (uint32_t)(row * ld + kc * 8) * 2u;
     }
   }
+  // Gathered rows: tile row r is row idx[r] of b ([src_rows][ld]); rows past
+  // nrows point past the resource's range and land as zeros.
+  __device__ void init_gather(const bf16* b, int ld, int nrows, int src_rows,
+                              const int32_t* idx, int wid) {
+    const int lane = threadIdx.x & 63;
+    base = b;
+    bytes = (uint32_t)src_rows * (uint32_t)ld * 2u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int row = (i * 4 + wid) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ ((row >> 1) & 7);
+      off[i] = row < nrows ? (uint32_t)(idx[row] * ld + kc * 8) * 2u : kPadOffset;
+    }
+  }
   // resource and stage offset for the stage starting at k0 (dead: zeros)
   __device__ Rsrc rsrc(bool live) const { return make_rsrc(base, live ? bytes : 0u); }
   __device__ static uint32_t soff(int k0) { return (uint32_t)k0 * 2u; }
@@ -296,9 +310,11 @@ struct TileGemm {
   float gdb;
 
   // A: rows [0, a_rows) (K-contiguous) or columns [0, a_rows) over k rows
-  // [0, K) (MN-contiguous); likewise B.
+  // [0, K) (MN-contiguous); likewise B.  With a_idx (K-contiguous A only),
+  // tile row r is row a_idx[r] of A ([a_src_rows][lda]).
   __device__ void run(const bf16* A, int lda, int a_rows, const bf16* B, int ldb, int b_rows,
-                      int K, const StageBufs& L, const float* gsel = nullptr) {
+                      int K, const StageBufs& L, const float* gsel = nullptr,
+                      const int32_t* a_idx = nullptr, int a_src_rows = 0) {
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -314,7 +330,14 @@ struct TileGemm {
     const int wm = wid >> 1, wn = wid & 1;
     TA ta;
     TB tb;
-    ta.init(A, lda, a_rows, K, wid);
+    if constexpr (A_K) {
+      if (a_idx != nullptr)
+        ta.init_gather(A, lda, a_rows, a_src_rows, a_idx, wid);
+      else
+        ta.init(A, lda, a_rows, K, wid);
+    } else {
+      ta.init(A, lda, a_rows, K, wid);
+    }
     tb.init(B, ldb, b_rows, K, wid);
     uint32_t alo[TA::NLO], blo[TB::NLO];
     TA::lane_offsets(alo);
@@ -497,10 +520,13 @@ struct TileGemm {
 // tile are loaded first, in one round trip.  rows/cols bound the valid part
 // of the tile (cols is a multiple of 8).  Call after run(); uses the stage
 // buffers.
+// With crow, tile row m is stored at row crow[m] of C (C then points at the
+// tile's first column of row 0).
 template <int EPI, class TG>
 __device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, void* C, int ldc,
                                            int rows, int cols, const uint32_t* aux, int ld_aux,
-                                           uint8_t* bits_out = nullptr) {
+                                           uint8_t* bits_out = nullptr,
+                                           const int32_t* crow = nullptr) {
   using OutT = typename std::conditional<EPI == EPI_F32, float, bf16>::type;
   constexpr int ES = sizeof(OutT);
   constexpr int WN = TG::WN, WM = TG::WM;
@@ -516,6 +542,14 @@ __device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, voi
   const int n0 = wn * WN;
   constexpr int IT = 32 / RPI;  // row-phase iterations per strip
   uint32_t mw[EPI == EPI_MASK ? TG::FM * IT : 1];
+  int cr[TG::FM * IT];  // destination row of each staged row this lane stores
+#pragma unroll
+  for (int j = 0; j < TG::FM; ++j)
+#pragma unroll
+    for (int t = 0; t < IT; ++t) {
+      const int m = wm * WM + j * 32 + t * RPI + lane / CPR;
+      cr[j * IT + t] = crow == nullptr ? m : (m < rows ? crow[m] : 0);
+    }
   if constexpr (EPI == EPI_MASK) {
 #pragma unroll
     for (int j = 0; j < TG::FM; ++j)
@@ -560,7 +594,7 @@ __device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, voi
       const i32x4 v = *reinterpret_cast<const i32x4*>(strip + r * PITCH + c * ES);
       const int m = m0 + r, n = n0 + c;
       if (m < rows && n < cols) {
-        const size_t at = (size_t)m * ldc + n;
+        const size_t at = (size_t)cr[j * IT + t] * ldc + n;
         if constexpr (EPI == EPI_MASK) {
           const uint32_t keep = mw[j * IT + t] >> (n & 31);
           i32x4 o = v;
@@ -596,11 +630,16 @@ struct RowsArgs {
   const uint32_t* aux;  // EPI_MASK: keep bits, [rows][N / 32] words
   uint8_t* bits_out;    // EPI_RELU (optional): keep bits [C > 0], [rows][N / 8] bytes
   const int32_t* offsets;
+  // MAP_GATHER_A: packed row r of A is row a_map[r] of A ([a_src_rows][K]);
+  // MAP_SCATTER_C: packed row r is stored at row c_map[r] of C
+  const int32_t* a_map;
+  const int32_t* c_map;
   long long b_stride;
-  int K, N, E;
+  int K, N, E, a_src_rows;
 };
+enum RowMap { MAP_NONE = 0, MAP_GATHER_A = 1, MAP_SCATTER_C = 2 };
 
-template <int BM, int BN, bool B_K, int EPI>
+template <int BM, int BN, bool B_K, int EPI, int MAP>
 __global__ void __launch_bounds__(kGemmThreads)
 rows_gemm_kernel(RowsArgs p) {
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
@@ -657,16 +696,26 @@ rows_gemm_kernel(RowsArgs p) {
   using TG = TileGemm<BM, BN, true, B_K>;
   TG tg;
   const StageBufs L = tile_lds<TG>();
-  const bf16* A = p.A + (size_t)row0 * p.K;
   const bf16* Bm = p.B + (size_t)e * p.b_stride;
-  if (B_K) {
-    tg.run(A, p.K, rows, Bm + (size_t)n0 * p.K, p.K, cols, p.K, L);
+  if constexpr (MAP == MAP_GATHER_A) {
+    static_assert(B_K, "gathered rows are a forward (NT) product");
+    tg.run(p.A, p.K, rows, Bm + (size_t)n0 * p.K, p.K, cols, p.K, L, nullptr, p.a_map + row0,
+           p.a_src_rows);
   } else {
-    tg.run(A, p.K, rows, Bm + n0, p.N, cols, p.K, L);
+    const bf16* A = p.A + (size_t)row0 * p.K;
+    if (B_K) {
+      tg.run(A, p.K, rows, Bm + (size_t)n0 * p.K, p.K, cols, p.K, L);
+    } else {
+      tg.run(A, p.K, rows, Bm + n0, p.N, cols, p.K, L);
+    }
   }
-  store_tile<EPI>(tg, L, p.C + (size_t)row0 * p.N + n0, p.N, rows, cols,
-                  p.aux ? p.aux + (size_t)row0 * (p.N / 32) + n0 / 32 : nullptr, p.N / 32,
-                  p.bits_out ? p.bits_out + (size_t)row0 * (p.N / 8) + n0 / 8 : nullptr);
+  if constexpr (MAP == MAP_SCATTER_C) {
+    store_tile<EPI>(tg, L, p.C + n0, p.N, rows, cols, nullptr, 0, nullptr, p.c_map + row0);
+  } else {
+    store_tile<EPI>(tg, L, p.C + (size_t)row0 * p.N + n0, p.N, rows, cols,
+                    p.aux ? p.aux + (size_t)row0 * (p.N / 32) + n0 / 32 : nullptr, p.N / 32,
+                    p.bits_out ? p.bits_out + (size_t)row0 * (p.N / 8) + n0 / 8 : nullptr);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -773,9 +822,11 @@ constexpr int kF32Rows = 16;
 // C[r][n] = epi(sum_k A[r][k] B_e(n, k)); B_e(n,k) = B[e][n][k] (B_K) or B[e][k][n].
 template <bool B_K, int EPI>
 __global__ void __launch_bounds__(256)
+// Optional maps as in RowsArgs: A row a_map[r], C row c_map[r] (null: r).
 f32_rows_kernel(const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C,
                 const float* __restrict__ aux, const int32_t* __restrict__ offsets, int K, int N,
-                int E, int S_max) {
+                int E, int S_max, const int32_t* __restrict__ a_map,
+                const int32_t* __restrict__ c_map) {
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   for (int i = threadIdx.x; i <= E; i += 256) s_off[i] = offsets[i];
   __syncthreads();
@@ -784,14 +835,15 @@ f32_rows_kernel(const float* __restrict__ A, const float* __restrict__ B, float*
   if (r >= s_off[E] || r >= S_max) return;
   int e = 0;
   while (!(s_off[e] <= r && r < s_off[e + 1])) ++e;
-  const float* a = A + (size_t)r * K;
+  const float* a = A + (size_t)(a_map ? a_map[r] : r) * K;
   const float* b = B + (size_t)e * N * K;
+  const size_t cr = (size_t)(c_map ? c_map[r] : r);
   for (int n = blockIdx.y * 64 + g; n < min(N, blockIdx.y * 64 + 64); n += 16) {
     float acc = 0.f;
     for (int k = 0; k < K; ++k) acc = fmaf(a[k], B_K ? b[(size_t)n * K + k] : b[(size_t)k * N + n], acc);
     if (EPI == EPI_RELU) acc = fmaxf(acc, 0.f);
     if (EPI == EPI_MASK && !(aux[(size_t)r * N + n] > 0.f)) acc = 0.f;
-    C[(size_t)r * N + n] = acc;
+    C[cr * N + n] = acc;
   }
 }
 
@@ -813,12 +865,14 @@ f32_wgrad_kernel(const float* __restrict__ X1, const float* __restrict__ X2, flo
 
 // Every kernel variant the launchers can pick, instantiated explicitly (so
 // each is emitted whatever order the launchers reference them in).
-#define MOE_ROWS_VARIANTS(BM, BN)                                        \
-  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU>(RowsArgs);   \
-  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE>(RowsArgs);  \
-  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_MASK>(RowsArgs);  \
-  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_STORE>(RowsArgs); \
-  template __global__ void wgrad_kernel<BM, BN, false>(WgradArgs);               \
+#define MOE_ROWS_VARIANTS(BM, BN)                                                      \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_NONE>(RowsArgs);       \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_NONE>(RowsArgs);      \
+  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_MASK, MAP_NONE>(RowsArgs);      \
+  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_STORE, MAP_NONE>(RowsArgs);     \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_GATHER_A>(RowsArgs);   \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_SCATTER_C>(RowsArgs); \
+  template __global__ void wgrad_kernel<BM, BN, false>(WgradArgs);                             \
   template __global__ void wgrad_kernel<BM, BN, true>(WgradArgs);
 MOE_ROWS_VARIANTS(256, 256)
 MOE_ROWS_VARIANTS(256, 128)
@@ -868,28 +922,31 @@ static Shape2 pick_tile(MT mt, int N) {
   return {128, 128};
 }
 
-template <int BM, int BN, bool B_K, int EPI>
+template <int BM, int BN, bool B_K, int EPI, int MAP>
 static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
   // worst case: sum over experts of ceil(rows_e / BM) <= S_max / BM + E
   const long long mt_max = (S_max + BM - 1) / BM + p.E;
   const long long nt = (p.N + BN - 1) / BN;
   const long long grid = mt_max * nt;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI, MAP>), dim3((unsigned)grid),
                      dim3(kGemmThreads), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool B_K, int EPI>
+template <bool B_K, int EPI, int MAP = MAP_NONE>
 static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const uint32_t* aux,
                               const int32_t* offsets, long long b_stride, int K, int N, int E,
-                              int S_max, hipStream_t s, uint32_t* bits_out = nullptr) {
-  RowsArgs p{A, B, C, aux, reinterpret_cast<uint8_t*>(bits_out), offsets, b_stride, K, N, E};
+                              int S_max, hipStream_t s, uint32_t* bits_out = nullptr,
+                              const int32_t* a_map = nullptr, const int32_t* c_map = nullptr,
+                              int a_src_rows = 0) {
+  RowsArgs p{A, B, C, aux, reinterpret_cast<uint8_t*>(bits_out), offsets, a_map, c_map,
+             b_stride, K, N, E, a_src_rows};
   const Shape2 t = pick_rows_tile(S_max, E, N);
-  if (t.bm == 256 && t.bn == 256) return launch_rows_t<256, 256, B_K, EPI>(p, S_max, s);
-  if (t.bm == 256 && t.bn == 128) return launch_rows_t<256, 128, B_K, EPI>(p, S_max, s);
-  if (t.bm == 128 && t.bn == 256) return launch_rows_t<128, 256, B_K, EPI>(p, S_max, s);
-  return launch_rows_t<128, 128, B_K, EPI>(p, S_max, s);
+  if (t.bm == 256 && t.bn == 256) return launch_rows_t<256, 256, B_K, EPI, MAP>(p, S_max, s);
+  if (t.bm == 256 && t.bn == 128) return launch_rows_t<256, 128, B_K, EPI, MAP>(p, S_max, s);
+  if (t.bm == 128 && t.bn == 256) return launch_rows_t<128, 256, B_K, EPI, MAP>(p, S_max, s);
+  return launch_rows_t<128, 128, B_K, EPI, MAP>(p, S_max, s);
 }
 
 template <int BM, int BN, bool GATE>
@@ -935,10 +992,40 @@ hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets
   dim3 g1((S_max + kF32Rows - 1) / kF32Rows, (F + 63) / 64),
       g2((S_max + kF32Rows - 1) / kF32Rows, (d + 63) / 64);
   hipLaunchKernelGGL((f32_rows_kernel<true, EPI_RELU>), g1, b, 0, s, (const float*)x_perm,
-                     (const float*)w1, (float*)h, nullptr, offsets, d, F, E, S_max);
+                     (const float*)w1, (float*)h, nullptr, offsets, d, F, E, S_max, nullptr,
+                     nullptr);
   MOE_TRY(hipGetLastError());
   hipLaunchKernelGGL((f32_rows_kernel<true, EPI_STORE>), g2, b, 0, s, (const float*)h,
-                     (const float*)w2, (float*)out_perm, nullptr, offsets, F, d, E, S_max);
+                     (const float*)w2, (float*)out_perm, nullptr, offsets, F, d, E, S_max,
+                     nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_fwd_fused(int act, const void* x, const int32_t* row_token, int T,
+                                   const int32_t* offsets, const int32_t* row_slot,
+                                   const void* w1, const void* w2, void* h, void* out_slot,
+                                   uint32_t* relu_bits, int S_max, int d, int F, int E,
+                                   hipStream_t s) {
+  if (act == MOE_BF16) {
+    // FC1 reads token rows x[row_token[r]]; FC2 stores row r at slot row_slot[r]
+    MOE_TRY((launch_rows<true, EPI_RELU, MAP_GATHER_A>(
+        (const bf16*)x, (const bf16*)w1, (bf16*)h, nullptr, offsets, (long long)F * d, d, F, E,
+        S_max, s, relu_bits, row_token, nullptr, T)));
+    MOE_TRY((launch_rows<true, EPI_STORE, MAP_SCATTER_C>(
+        (const bf16*)h, (const bf16*)w2, (bf16*)out_slot, nullptr, offsets, (long long)d * F, F,
+        d, E, S_max, s, nullptr, nullptr, row_slot, 0)));
+    return hipSuccess;
+  }
+  dim3 b(256);
+  dim3 g1((S_max + kF32Rows - 1) / kF32Rows, (F + 63) / 64),
+      g2((S_max + kF32Rows - 1) / kF32Rows, (d + 63) / 64);
+  hipLaunchKernelGGL((f32_rows_kernel<true, EPI_RELU>), g1, b, 0, s, (const float*)x,
+                     (const float*)w1, (float*)h, nullptr, offsets, d, F, E, S_max, row_token,
+                     nullptr);
+  MOE_TRY(hipGetLastError());
+  hipLaunchKernelGGL((f32_rows_kernel<true, EPI_STORE>), g2, b, 0, s, (const float*)h,
+                     (const float*)w2, (float*)out_slot, nullptr, offsets, F, d, E, S_max,
+                     nullptr, row_slot);
   return hipGetLastError();
 }
 
@@ -979,14 +1066,14 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
   const int rt = (S_max + kF32Rows - 1) / kF32Rows;
   hipLaunchKernelGGL((f32_rows_kernel<false, EPI_MASK>), dim3(rt, (F + 63) / 64), b, 0, s,
                      (const float*)d_out, (const float*)w2, (float*)dz, (const float*)h, offsets, d,
-                     F, E, S_max);
+                     F, E, S_max, nullptr, nullptr);
   MOE_TRY(hipGetLastError());
   hipLaunchKernelGGL(f32_wgrad_kernel, dim3(E, (d + 15) / 16, (F + 63) / 64), b, 0, s,
                      (const float*)d_out, (const float*)h, dw2, offsets, d, F);
   MOE_TRY(hipGetLastError());
   hipLaunchKernelGGL((f32_rows_kernel<false, EPI_STORE>), dim3(rt, (d + 63) / 64), b, 0, s,
                      (const float*)dz, (const float*)w1, (float*)dx_perm, nullptr, offsets, F, d,
-                     E, S_max);
+                     E, S_max, nullptr, nullptr);
   MOE_TRY(hipGetLastError());
   hipLaunchKernelGGL(f32_wgrad_kernel, dim3(E, (F + 15) / 16, (d + 63) / 64), b, 0, s,
                      (const float*)dz, (const float*)x_perm, dw1, offsets, F, d);

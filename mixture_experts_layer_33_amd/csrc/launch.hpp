@@ -34,10 +34,19 @@ hipError_t launch_gather(int act, const void* x, const int32_t* topk_idx,
                          int T, int d, int E, int k,
                          int C, bool choice, int32_t* offsets, int32_t* slot_row,
                          int32_t* row_token, void* x_perm, hipStream_t s);
+// The same indices without the row copy, plus row_slot[r] = slot of kept row r.
+hipError_t launch_index(const int32_t* topk_idx, const int32_t* local_rank,
+                        const int32_t* tile_base, const int32_t* counts_raw,
+                        const int32_t* counts_kept, int n_tiles, int T, int E, int k, int C,
+                        bool choice, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
+                        int32_t* row_slot, hipStream_t s);
 
 // ---- output decode and the elementwise backward steps (combine.hip)
+// slot_order: expert output of kept slot s is row s of out_perm (else row
+// slot_row[s]).
 hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,
-                          const int32_t* slot_row, void* y, int T, int d, int k, hipStream_t s);
+                          const int32_t* slot_row, void* y, int T, int d, int k, hipStream_t s,
+                          bool slot_order = false);
 // Decode backward; its extra workgroups also write w_gate_t = W_gate^T.
 hipError_t launch_combine_bwd(int act, const void* dy, const void* out_perm,
                               const float* topk_w, const int32_t* topk_idx,
@@ -65,6 +74,13 @@ hipError_t launch_popularity(int E, int window, int64_t iter, const int32_t* cou
 hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets,
                              const void* w1, const void* w2, void* h, void* out_perm,
                              uint32_t* relu_bits, int S_max, int d, int F, int E, hipStream_t s);
+// Gather/scatter-fused forward: FC1 reads token rows x[row_token[r]] ([T][d]);
+// FC2 stores packed row r at row row_slot[r] of out_slot ([T*k][d]).
+hipError_t launch_expert_fwd_fused(int act, const void* x, const int32_t* row_token, int T,
+                                   const int32_t* offsets, const int32_t* row_slot,
+                                   const void* w1, const void* w2, void* h, void* out_slot,
+                                   uint32_t* relu_bits, int S_max, int d, int F, int E,
+                                   hipStream_t s);
 // Backward GEMMs: dz = (dO W2[e]) * [h > 0]; dW2[e] = dO^T h;
 // dx_perm = dz W1[e]; dW1[e] = dz^T x_perm.
 // bf16 also folds dW_gate / db over the kept rows into the FC1 wgrad and

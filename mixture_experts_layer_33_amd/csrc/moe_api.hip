@@ -182,6 +182,8 @@ size_t moe_workspace_bytes(const moe_shape* s, int32_t op) {
       return 0;
     case MOE_OP_BACKWARD:
       return bwd_ws_bytes(s);
+    case MOE_OP_FORWARD_FUSED:  // + row_slot [S]
+      return perm_ws_bytes(s) + align_up((size_t)slots(s) * 4);
     default:
       return 0;
   }
@@ -306,6 +308,38 @@ moe_status moe_forward(const moe_shape* s, const void* x, const float* w_gate,
                             (int)slots(s), s->d_model, s->d_ff, s->E, stream_));
   MOE_HIP(launch_combine(s->act_dtype, out_perm, topk_w, slot_row, y, s->T, s->d_model, s->k,
                          stream_));
+  return MOE_OK;
+}
+
+moe_status moe_forward_fused(const moe_shape* s, const void* x, const float* w_gate,
+                             const float* b_gate, const void* w1, const void* w2, void* y,
+                             float* logits_out, int32_t* topk_idx, float* topk_w,
+                             int32_t* counts_raw, int32_t* counts_kept, int32_t* offsets,
+                             int32_t* slot_row, int32_t* row_token, void* h, void* out_slot,
+                             uint32_t* relu_bits, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ptrs_ok(x, w_gate, b_gate, w1, w2, y, topk_idx, topk_w, counts_kept, offsets, slot_row,
+               row_token, h, out_slot) ||
+      !opt_ok(logits_out) || !opt_ok(counts_raw) || !opt_ok(relu_bits))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_FORWARD_FUSED, ws, ws_bytes)) != MOE_OK) return st;
+  PermWs pw = carve_perm(s, ws);
+  int32_t* row_slot = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + perm_ws_bytes(s));
+  hipStream_t stream_ = as_stream(stream);
+  int32_t* raw = counts_raw ? counts_raw : pw.raw_tmp;
+  st = do_route(s, x, w_gate, b_gate, nullptr, logits_out, topk_idx, topk_w, raw, counts_kept, pw,
+                stream_);
+  if (st != MOE_OK) return st;
+  MOE_HIP(launch_index(topk_idx, pw.local_rank, pw.tile_base, raw, counts_kept, rank_tiles(s),
+                       s->T, s->E, s->k, capacity_of(s),
+                       s->capacity_priority == MOE_PRIORITY_CHOICE, offsets, slot_row, row_token,
+                       row_slot, stream_));
+  MOE_HIP(launch_expert_fwd_fused(s->act_dtype, x, row_token, s->T, offsets, row_slot, w1, w2, h,
+                                  out_slot, relu_bits, (int)slots(s), s->d_model, s->d_ff, s->E,
+                                  stream_));
+  MOE_HIP(launch_combine(s->act_dtype, out_slot, topk_w, slot_row, y, s->T, s->d_model, s->k,
+                         stream_, true));
   return MOE_OK;
 }
 

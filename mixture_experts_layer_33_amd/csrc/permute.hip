@@ -28,6 +28,9 @@
 //     Dropped slots are listed after the kept rows, ordered by expert and
 //     then position: row_token[S_kept + j] = slot index (the backward needs
 //     them for the gate gradient).
+//  3'. index (the gather-fused forward): the same indices with one thread per
+//     slot and no row copy, plus row_slot[r] = the slot of kept row r; the
+//     expert GEMM then reads token rows through row_token itself.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -183,6 +186,64 @@ hipError_t launch_scan(const int32_t* hist, int n_tiles, int E, int C, int32_t* 
                        int32_t* counts_raw, int32_t* counts_kept, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(E), dim3(kScanThreads), 0, s, hist, n_tiles, E, C,
                      tile_base, counts_raw, counts_kept);
+  return hipGetLastError();
+}
+
+// Index-only encode: offsets, slot_row, row_token (kept rows, then the
+// dropped-slot list) and row_slot, one thread per slot.
+__global__ void __launch_bounds__(kGatherThreads)
+index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ local_rank,
+             const int32_t* __restrict__ tile_base, const int32_t* __restrict__ counts_raw,
+             const int32_t* __restrict__ counts_kept, int n_tiles, int T, int E, int k, int C,
+             bool choice, int32_t* __restrict__ offsets, int32_t* __restrict__ slot_row,
+             int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot) {
+  __shared__ int off[MOE_MAX_EXPERTS + 1];
+  __shared__ int doff[MOE_MAX_EXPERTS + 1];
+  __shared__ int scratch[kGatherThreads / 64 + 1];
+  {
+    const int e = threadIdx.x;
+    const int kept = (e < E) ? counts_kept[e] : 0;
+    const int drop = (e < E) ? counts_raw[e] - kept : 0;
+    int total, dtotal;
+    const int ex = block_exclusive_scan(kept, scratch, &total);
+    const int dex = block_exclusive_scan(drop, scratch, &dtotal);
+    if (e < E) {
+      off[e] = ex;
+      doff[e] = total + dex;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      if (e < E) offsets[e] = ex;
+      if (e == 0) offsets[E] = total;
+    }
+  }
+  const long long s = (long long)blockIdx.x * kGatherThreads + threadIdx.x;
+  if (s >= (long long)T * k) return;
+  const int t = (int)(s / k), j = (int)(s - (long long)t * k);
+  const int q = choice ? j * T + t : (int)s;
+  const int e = topk_idx[s];
+  const int pos = tile_base[(size_t)e * n_tiles + q / kRankTile] + local_rank[q];
+  int row = -1;
+  if (pos < C) {
+    row = off[e] + pos;
+    row_token[row] = t;
+    row_slot[row] = (int)s;
+  } else {
+    row_token[doff[e] + pos - C] = (int)s;
+  }
+  slot_row[s] = row;
+}
+
+hipError_t launch_index(const int32_t* topk_idx, const int32_t* local_rank,
+                        const int32_t* tile_base, const int32_t* counts_raw,
+                        const int32_t* counts_kept, int n_tiles, int T, int E, int k, int C,
+                        bool choice, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
+                        int32_t* row_slot, hipStream_t s) {
+  const long long S = (long long)T * k;
+  dim3 grid((unsigned)((S + kGatherThreads - 1) / kGatherThreads)), block(kGatherThreads);
+  hipLaunchKernelGGL(index_kernel, grid, block, 0, s, topk_idx, local_rank, tile_base,
+                     counts_raw, counts_kept, n_tiles, T, E, k, C, choice, offsets, slot_row,
+                     row_token, row_slot);
   return hipGetLastError();
 }
 

@@ -9,8 +9,8 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_BF16, MOE_F32, MoeShape, moe_backward, moe_capacity, moe_check_shape,
-               moe_combine, moe_expert_ffn, moe_forward, moe_permute, moe_popularity_update,
-               moe_route, moe_status_string, moe_workspace_bytes)
+               moe_combine, moe_expert_ffn, moe_forward, moe_forward_fused, moe_permute,
+               moe_popularity_update, moe_route, moe_status_string, moe_workspace_bytes)
 
 
 def act_torch_dtype(act: int):
@@ -69,6 +69,22 @@ class MoeLayer:
                     self.counts_raw, self.counts_kept, self.offsets, self.slot_row,
                     self.row_token, self.x_perm, self.h, self.out_perm, self.relu_bits,
                     self.ws_fwd, stream)
+        return self.y
+
+    def forward_fused(self, x, w_gate, b_gate, w1, w2, logits_out=True, stream=None):
+        """The gather/scatter-fused forward: same y and indices as forward(),
+        expert outputs by slot in ``out_slot`` and no x_perm; not for the
+        backward."""
+        if getattr(self, "out_slot", None) is None:
+            self.out_slot = torch.empty(self.T * self.k, self.d, dtype=self.dtype,
+                                        device=self.device)
+            nb = max(moe_workspace_bytes(self.shape, "forward_fused"), 256)
+            self.ws_fused = torch.empty(nb, dtype=torch.uint8, device=self.device)
+        moe_forward_fused(self.shape, x, w_gate, b_gate, w1, w2, self.y,
+                          self.logits if logits_out else None, self.topk_idx, self.topk_w,
+                          self.counts_raw, self.counts_kept, self.offsets, self.slot_row,
+                          self.row_token, self.h, self.out_slot, self.relu_bits, self.ws_fused,
+                          stream)
         return self.y
 
     def backward(self, dy, x, w_gate, w1, w2, dlogits=True, stream=None):

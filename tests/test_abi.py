@@ -80,6 +80,9 @@ def test_workspace_sizes():
     S = s.T * s.k
     assert moe.moe_workspace_bytes(s, "backward") >= S * (s.d_model + s.d_ff) * 2 + 2 * S * 4
     assert moe.moe_workspace_bytes(shape(T=0), "forward") == 0
+    # the gather-fused forward adds the row -> slot map
+    fused = moe.moe_workspace_bytes(s, "forward_fused")
+    assert fused >= moe.moe_workspace_bytes(s, "forward") + S * 4
 
 
 class FakePtr(int):
@@ -117,6 +120,21 @@ def test_entry_points_reject_bad_arguments_before_launch():
     # bad shape wins over everything else
     bad = ctypes.byref(shape(k=0))
     assert L.moe_forward(bad, *([P] * 18), P, ws, None) == -1
+    # gather-fused forward: null output, misaligned relu_bits, workspace of the unfused forward
+    fws = moe.moe_workspace_bytes(s, "forward_fused")
+    fargs = [P] * 17
+    fargs[6] = None   # logits_out optional
+    fargs[9] = None   # counts_raw optional
+    fargs[16] = None  # relu_bits optional
+    assert L.moe_forward_fused(bs, *fargs, P, fws - 1, None) == -3
+    assert L.moe_forward_fused(bs, *fargs, P, ws, None) == -3
+    nul = list(fargs)
+    nul[15] = None    # out_slot
+    assert L.moe_forward_fused(bs, *nul, P, fws, None) == -1
+    mis = list(fargs)
+    mis[16] = P + 4
+    assert L.moe_forward_fused(bs, *mis, P, fws, None) == -1
+    assert L.moe_forward_fused(bad, *([P] * 17), P, fws, None) == -1
     # dispatch plan limits
     assert L.moe_ep_plan(0, 8, 0, P, P, P, P, P, P, None) == -1
     assert L.moe_ep_plan(257, 8, 0, P, P, P, P, P, P, None) == -1
