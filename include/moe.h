@@ -159,7 +159,11 @@ moe_status moe_permute(const moe_shape* shape, const void* x, const int32_t* top
  * words, bit (f % 32) of word [r][f / 32] set iff h[r][f] > 0, over rows
  * [0, offsets[E]); moe_backward can take it instead of deriving the ReLU
  * mask from h.  Ignored for MOE_F32.
- * Workspace: MOE_OP_EXPERT_FFN (0 bytes; argument may be NULL). */
+ * Workspace: MOE_OP_EXPERT_FFN: bf16 needs 64 MiB of scratch for float32
+ * partial tiles (when the last round of GEMM tiles would leave compute
+ * units idle, its tiles are split along the reduction dimension and summed
+ * in a fixed order, so results are deterministic); MOE_F32 needs none (the
+ * argument may then be NULL). */
 moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int32_t* offsets,
                           const void* w1, const void* w2, void* h, void* out_perm,
                           uint32_t* relu_bits, void* workspace, size_t workspace_bytes,

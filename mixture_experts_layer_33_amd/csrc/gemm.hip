@@ -634,10 +634,122 @@ struct RowsArgs {
   // MAP_SCATTER_C: packed row r is stored at row c_map[r] of C
   const int32_t* a_map;
   const int32_t* c_map;
+  // split tail (null: off): float32 partial tiles, kMaxSplitUnits x BM x BN
+  float* partial;
   long long b_stride;
   int K, N, E, a_src_rows;
+  int cus;  // compute units: workgroups of one full round of tiles
 };
 enum RowMap { MAP_NONE = 0, MAP_GATHER_A = 1, MAP_SCATTER_C = 2 };
+
+// Split tail.  With one workgroup per CU, a launch of `total` tiles runs
+// total / cus full rounds and a last round that leaves most CUs idle when
+// only a few tiles remain.  The first n_dp tiles run whole; each of the
+// `tail` remaining tiles runs as s segments of its K range on separate
+// workgroups (so the last round fills the chip), which store float32
+// partial tiles; rows_fixup_kernel then sums each tile's segments in
+// segment order and applies the epilogue.  Deterministic: the plan depends
+// only on the tile count, K and the CU count.
+constexpr int kMaxSplitUnits = 256;  // partial tiles the workspace holds
+constexpr int kMaxSplit = 16;
+// A split pays only when it cuts the last round to a quarter or less: the
+// fixup reads s partial tiles per tail tile (measured: 2-way splits of
+// 16-step tiles cost more in the fixup than they save).
+constexpr int kMinSplit = 4;
+constexpr int kMinSplitSteps = 4;    // k steps (of kBK) per segment, at least
+struct SplitPlan {
+  int n_dp, tail, s;
+};
+__host__ __device__ inline SplitPlan split_plan(int total, int nk, int cus, bool enabled) {
+  SplitPlan p{total, 0, 1};
+  if (!enabled || cus <= 0) return p;
+  const int tail = total % cus;
+  if (tail == 0) return p;
+  const int fill = (cus < kMaxSplitUnits ? cus : kMaxSplitUnits) / tail;
+  const int deep = nk / kMinSplitSteps;
+  int s = fill < deep ? fill : deep;
+  s = s < kMaxSplit ? s : kMaxSplit;
+  if (s < kMinSplit) return p;
+  p.n_dp = total - tail;
+  p.tail = tail;
+  p.s = s;
+  return p;
+}
+
+// Per-expert m-tile counts and their prefix sum (shared arrays, whole block).
+template <int BM>
+__device__ __forceinline__ void rows_scan(const RowsArgs& p, int* s_off, int* s_tstart,
+                                          int* s_scratch) {
+  const int tid = threadIdx.x;
+  int mt = 0;
+  if (tid < p.E) {
+    const int a = p.offsets[tid], b = p.offsets[tid + 1];
+    s_off[tid] = a;
+    if (tid == p.E - 1) s_off[p.E] = b;
+    mt = (b - a + BM - 1) / BM;
+  }
+  int total;
+  const int ex = block_exclusive_scan(mt, s_scratch, &total);
+  if (tid < p.E) s_tstart[tid] = ex;
+  if (tid == 0) s_tstart[p.E] = total;
+  __syncthreads();
+}
+
+struct RowTile {
+  int e, row0, rows, n0, cols;
+};
+// Tile `logical` (whole block, uniform): expert by expert (tiles of expert e
+// are logical [s_tstart[e] * NT, s_tstart[e+1] * NT)); inside an expert,
+// groups of up to 8 m-tiles, n walked column by column inside a group.  A
+// group never mixes experts, so the workgroups running together on one XCD
+// share one expert's weights.
+template <int BM, int BN>
+__device__ __forceinline__ RowTile find_tile(int logical, int NT, int N, int E, const int* s_off,
+                                             const int* s_tstart, int* s_expert) {
+  const int tid = threadIdx.x;
+  if (tid < E && s_tstart[tid] * NT <= logical && logical < s_tstart[tid + 1] * NT)
+    *s_expert = tid;
+  __syncthreads();
+  RowTile t;
+  t.e = *s_expert;
+  constexpr int G = 8;
+  const int mte = s_tstart[t.e + 1] - s_tstart[t.e];
+  const int j = logical - s_tstart[t.e] * NT;
+  const int grp = j / (G * NT);
+  const int gm0 = grp * G;
+  const int gsz = min(G, mte - gm0);
+  const int in = j - grp * G * NT;
+  const int mt = gm0 + in % gsz;  // m-tile within the expert
+  const int nt = in / gsz;
+  t.row0 = s_off[t.e] + mt * BM;
+  t.rows = min(BM, s_off[t.e + 1] - t.row0);
+  t.n0 = nt * BN;
+  t.cols = min(BN, N - t.n0);
+  return t;
+}
+
+// A partial tile in the accumulators' own layout: wave w, block (i, j),
+// lane l holds 16 floats at ((w * FN + i) * FM + j) * 1024 + 16 l, element
+// 4p + q being C[m][n] with m = 32 j + l % 32 and n = 32 i + 4 (l / 32) +
+// 8p + q within the wave's WM x WN part (see TileGemm).
+template <class TG>
+__device__ __forceinline__ void store_partial(const TG& tg, float* dst) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < TG::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < TG::FM; ++j) {
+      f32x4* o = reinterpret_cast<f32x4*>(
+          dst + ((size_t)(wid * TG::FN + i) * TG::FM + j) * 1024 + lane * 16);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = tg.acc[i][j][4 * p + q];
+        o[p] = v;
+      }
+    }
+}
 
 template <int BM, int BN, bool B_K, int EPI, int MAP>
 __global__ void __launch_bounds__(kGemmThreads)
@@ -646,75 +758,138 @@ rows_gemm_kernel(RowsArgs p) {
   __shared__ int s_tstart[MOE_MAX_EXPERTS + 1];
   __shared__ int s_scratch[kGemmThreads / 64 + 1];
   __shared__ int s_expert;
-  const int tid = threadIdx.x;
-  // m-tiles per expert and their prefix sum
-  {
-    int mt = 0;
-    if (tid < p.E) {
-      const int a = p.offsets[tid], b = p.offsets[tid + 1];
-      s_off[tid] = a;
-      if (tid == p.E - 1) s_off[p.E] = b;
-      mt = (b - a + BM - 1) / BM;
-    }
-    int total;
-    const int ex = block_exclusive_scan(mt, s_scratch, &total);
-    if (tid < p.E) s_tstart[tid] = ex;
-    if (tid == 0) s_tstart[p.E] = total;
-    __syncthreads();
-  }
+  rows_scan<BM>(p, s_off, s_tstart, s_scratch);
   const int MT = s_tstart[p.E];
   const int NT = (p.N + BN - 1) / BN;
   const int total = MT * NT;
+  const int nk = p.K / kBK;
+  const SplitPlan sp = split_plan(total, nk, p.cus, p.partial != nullptr);
   const int bid = blockIdx.x;
-  if (bid >= total) return;
-  // XCD-contiguous ranges: workgroup bid runs on XCD bid % 8.
-  const int x = bid % kXcds, i = bid / kXcds;
-  const int q = total / kXcds, rmd = total % kXcds;
-  const int logical = x * q + min(x, rmd) + i;
-  // Expert by expert (tiles of expert e: logical [s_tstart[e] * NT,
-  // s_tstart[e+1] * NT)); inside an expert, groups of up to 8 m-tiles, n
-  // walked column by column inside a group.  A group never mixes experts, so
-  // the workgroups running together on one XCD share one expert's weights.
-  if (tid < p.E && s_tstart[tid] * NT <= logical && logical < s_tstart[tid + 1] * NT)
-    s_expert = tid;
-  __syncthreads();
-  const int e = s_expert;
-  constexpr int G = 8;
-  const int mte = s_tstart[e + 1] - s_tstart[e];
-  const int j = logical - s_tstart[e] * NT;
-  const int grp = j / (G * NT);
-  const int gm0 = grp * G;
-  const int gsz = min(G, mte - gm0);
-  const int in = j - grp * G * NT;
-  const int mt = gm0 + in % gsz;  // m-tile within the expert
-  const int nt = in / gsz;
-  const int row0 = s_off[e] + mt * BM;
-  const int rows = min(BM, s_off[e + 1] - row0);
-  const int n0 = nt * BN;
-  const int cols = min(BN, p.N - n0);
+  int logical, seg = -1;
+  if (bid < sp.n_dp) {
+    // XCD-contiguous ranges: workgroup bid runs on XCD bid % 8.
+    const int x = bid % kXcds, i = bid / kXcds;
+    const int q = sp.n_dp / kXcds, rmd = sp.n_dp % kXcds;
+    logical = x * q + min(x, rmd) + i;
+  } else {
+    const int u = bid - sp.n_dp;  // split unit: tile n_dp + u / s, segment u % s
+    if (u >= sp.tail * sp.s) return;
+    logical = sp.n_dp + u / sp.s;
+    seg = u % sp.s;
+  }
+  const RowTile t = find_tile<BM, BN>(logical, NT, p.N, p.E, s_off, s_tstart, &s_expert);
+  // k range of this workgroup (whole K unless a segment of a split tile)
+  const int k0 = seg < 0 ? 0 : (seg * nk / sp.s) * kBK;
+  const int k1 = seg < 0 ? p.K : ((seg + 1) * nk / sp.s) * kBK;
 
   using TG = TileGemm<BM, BN, true, B_K>;
   TG tg;
   const StageBufs L = tile_lds<TG>();
-  const bf16* Bm = p.B + (size_t)e * p.b_stride;
+  const bf16* Bm = p.B + (size_t)t.e * p.b_stride;
   if constexpr (MAP == MAP_GATHER_A) {
     static_assert(B_K, "gathered rows are a forward (NT) product");
-    tg.run(p.A, p.K, rows, Bm + (size_t)n0 * p.K, p.K, cols, p.K, L, nullptr, p.a_map + row0,
-           p.a_src_rows);
+    tg.run(p.A + k0, p.K, t.rows, Bm + (size_t)t.n0 * p.K + k0, p.K, t.cols, k1 - k0, L,
+           nullptr, p.a_map + t.row0, p.a_src_rows);
   } else {
-    const bf16* A = p.A + (size_t)row0 * p.K;
+    const bf16* A = p.A + (size_t)t.row0 * p.K + k0;
     if (B_K) {
-      tg.run(A, p.K, rows, Bm + (size_t)n0 * p.K, p.K, cols, p.K, L);
+      tg.run(A, p.K, t.rows, Bm + (size_t)t.n0 * p.K + k0, p.K, t.cols, k1 - k0, L);
     } else {
-      tg.run(A, p.K, rows, Bm + n0, p.N, cols, p.K, L);
+      tg.run(A, p.K, t.rows, Bm + (size_t)k0 * p.N + t.n0, p.N, t.cols, k1 - k0, L);
     }
   }
+  if (seg >= 0) {
+    store_partial(tg, p.partial + (size_t)(bid - sp.n_dp) * (BM * BN));
+    return;
+  }
   if constexpr (MAP == MAP_SCATTER_C) {
-    store_tile<EPI>(tg, L, p.C + n0, p.N, rows, cols, nullptr, 0, nullptr, p.c_map + row0);
+    store_tile<EPI>(tg, L, p.C + t.n0, p.N, t.rows, t.cols, nullptr, 0, nullptr,
+                    p.c_map + t.row0);
   } else {
-    store_tile<EPI>(tg, L, p.C + (size_t)row0 * p.N + n0, p.N, rows, cols,
-                    p.aux ? p.aux + (size_t)row0 * (p.N / 32) + n0 / 32 : nullptr, p.N / 32,
-                    p.bits_out ? p.bits_out + (size_t)row0 * (p.N / 8) + n0 / 8 : nullptr);
+    store_tile<EPI>(tg, L, p.C + (size_t)t.row0 * p.N + t.n0, p.N, t.rows, t.cols,
+                    p.aux ? p.aux + (size_t)t.row0 * (p.N / 32) + t.n0 / 32 : nullptr, p.N / 32,
+                    p.bits_out ? p.bits_out + (size_t)t.row0 * (p.N / 8) + t.n0 / 8 : nullptr);
+  }
+}
+
+// Sum of the split tail's partial tiles (segment order) and the epilogue of
+// rows_gemm_kernel on it: ReLU + keep bits, plain store, or the ReLU mask,
+// bf16 rounding to nearest even, to the same destination rows.  Tail tile b
+// is spread over fixup_parts(BM, BN) workgroups of kGemmThreads / (BN / 8)
+// rows each; a thread takes 8 consecutive columns of one row and issues the
+// loads of four segments ahead of their (in-order) sums.
+constexpr int kFixupTiles = kMaxSplitUnits / 2;  // a split tail has <= this many tiles
+constexpr int fixup_parts(int BM, int BN) { return BM / (kGemmThreads / (BN / 8)); }
+template <int BM, int BN, int EPI, int MAP>
+__global__ void __launch_bounds__(kGemmThreads)
+rows_fixup_kernel(RowsArgs p) {
+  constexpr int kFixupRows = kGemmThreads / (BN / 8);
+  constexpr int kParts = fixup_parts(BM, BN);
+  static_assert(kParts * kFixupRows == BM, "whole rows per workgroup");
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_tstart[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_scratch[kGemmThreads / 64 + 1];
+  __shared__ int s_expert;
+  const int tb = blockIdx.x / kParts, part_rows = (blockIdx.x % kParts) * kFixupRows;
+  rows_scan<BM>(p, s_off, s_tstart, s_scratch);
+  const int NT = (p.N + BN - 1) / BN;
+  const SplitPlan sp = split_plan(s_tstart[p.E] * NT, p.K / kBK, p.cus, true);
+  if (tb >= sp.tail) return;
+  const RowTile t = find_tile<BM, BN>(sp.n_dp + tb, NT, p.N, p.E, s_off, s_tstart, &s_expert);
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  const float* part = p.partial + (size_t)tb * sp.s * (BM * BN);
+  {
+    const int g = threadIdx.x;
+    const int m = part_rows + g / (BN / 8), n = (g % (BN / 8)) * 8;
+    if (m >= t.rows || n >= t.cols) return;
+    const int wm = m / WM, j = (m % WM) / 32, ml = m % 32;
+    const int wn = n / WN, i = (n % WN) / 32, pq = (n % 32) / 8;
+    const size_t blk = ((size_t)((wm * 2 + wn) * FN + i) * FM + j) * 1024;
+    const size_t o0 = blk + ml * 16 + 4 * pq, o1 = blk + (ml + 32) * 16 + 4 * pq;
+    float v[8];  // -0 is the identity of +, so v becomes exactly segment 0 first
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = -0.f;
+    for (int s0 = 0; s0 < sp.s; s0 += 4) {
+      f32x4 a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (s0 + u < sp.s) {
+          const float* ps = part + (size_t)(s0 + u) * (BM * BN);
+          a[u] = *reinterpret_cast<const f32x4*>(ps + o0);
+          b[u] = *reinterpret_cast<const f32x4*>(ps + o1);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (s0 + u < sp.s) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[q] += a[u][q];
+            v[4 + q] += b[u][q];
+          }
+        }
+      }
+    }
+    const int row = t.row0 + m, col = t.n0 + n;
+    const size_t orow = MAP == MAP_SCATTER_C ? (size_t)p.c_map[row] : (size_t)row;
+    bf16x8 o;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = (bf16)(EPI == EPI_RELU ? fmaxf(v[q], 0.f) : v[q]);
+    if constexpr (EPI == EPI_MASK) {
+      const uint32_t keep = p.aux[(size_t)row * (p.N / 32) + col / 32] >> (col % 32);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (!((keep >> q) & 1u)) o[q] = __builtin_bit_cast(bf16, (uint16_t)0);
+    }
+    *reinterpret_cast<bf16x8*>(p.C + orow * p.N + col) = o;
+    if constexpr (EPI == EPI_RELU) {
+      if (p.bits_out != nullptr) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) b |= ((float)o[q] > 0.f ? 1u : 0u) << q;
+        p.bits_out[(size_t)row * (p.N / 8) + col / 8] = (uint8_t)b;
+      }
+    }
   }
 }
 
@@ -872,37 +1047,74 @@ f32_wgrad_kernel(const float* __restrict__ X1, const float* __restrict__ X2, flo
   template __global__ void rows_gemm_kernel<BM, BN, false, EPI_STORE, MAP_NONE>(RowsArgs);     \
   template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_GATHER_A>(RowsArgs);   \
   template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_SCATTER_C>(RowsArgs); \
-  template __global__ void wgrad_kernel<BM, BN, false>(WgradArgs);                             \
+  template __global__ void rows_fixup_kernel<BM, BN, EPI_RELU, MAP_NONE>(RowsArgs);            \
+  template __global__ void rows_fixup_kernel<BM, BN, EPI_STORE, MAP_NONE>(RowsArgs);           \
+  template __global__ void rows_fixup_kernel<BM, BN, EPI_MASK, MAP_NONE>(RowsArgs);            \
+  template __global__ void rows_fixup_kernel<BM, BN, EPI_RELU, MAP_GATHER_A>(RowsArgs);        \
+  template __global__ void rows_fixup_kernel<BM, BN, EPI_STORE, MAP_SCATTER_C>(RowsArgs);
+#define MOE_WGRAD_VARIANTS(BM, BN)                                   \
+  template __global__ void wgrad_kernel<BM, BN, false>(WgradArgs);   \
   template __global__ void wgrad_kernel<BM, BN, true>(WgradArgs);
-MOE_ROWS_VARIANTS(256, 256)
+// (a 256 x 256 row tile holds 256 accumulators per lane and would spill)
 MOE_ROWS_VARIANTS(256, 128)
 MOE_ROWS_VARIANTS(128, 256)
 MOE_ROWS_VARIANTS(128, 128)
+MOE_WGRAD_VARIANTS(256, 256)
+MOE_WGRAD_VARIANTS(256, 128)
+MOE_WGRAD_VARIANTS(128, 256)
+MOE_WGRAD_VARIANTS(128, 128)
 #undef MOE_ROWS_VARIANTS
+#undef MOE_WGRAD_VARIANTS
 
 // ---------------------------------------------------------------------------
 // launchers
 
+#define MOE_TRY(expr)                         \
+  do {                                        \
+    hipError_t _e = (expr);                   \
+    if (_e != hipSuccess) return _e;          \
+  } while (0)
+
+// Compute units of the current device (tiles per full round), cached per
+// device.
+static int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
 // Tile shape per product.  Row-grouped products: a small cost model, time ~
 // (rounds of one tile per CU) x (tile area) / (relative speed of the shape on
 // random bf16 data: 128x256 and 256x128 tiles do the most work per cycle,
-// 128x128 the least), with the row tiles estimated as an even spread of
-// S_max rows plus half a ragged tile per expert.  Weight gradients: the
-// largest tiles that still give every CU two.
+// 128x128 the least; 256x256 is left out, its accumulators leave too few
+// registers), with the row tiles estimated as an even spread of
+// S_max rows plus half a ragged tile per expert, and a split last round
+// costing 1/s of a round plus the fixup.  Weight gradients: the largest
+// tiles that still give every CU two.
 struct Shape2 {
   int bm, bn;
 };
-static Shape2 pick_rows_tile(int S_max, int E, int N) {
+static Shape2 pick_rows_tile(int S_max, int E, int K, int N, int cus, bool split) {
   struct C {
     int bm, bn;
     double speed;
   };
-  const C cand[] = {{128, 256, 1.15}, {256, 128, 1.12}, {256, 256, 1.0}, {128, 128, 0.95}};
+  const C cand[] = {{128, 256, 1.15}, {256, 128, 1.12}, {128, 128, 0.95}};
   Shape2 best{128, 128};
   double best_t = 1e300;
   for (const C& c : cand) {
-    const double tiles = (double)((S_max + c.bm - 1) / c.bm + E / 2) * ((N + c.bn - 1) / c.bn);
-    const double rounds = std::ceil(tiles / 256.0);
+    const int tiles = ((S_max + c.bm - 1) / c.bm + E / 2) * ((N + c.bn - 1) / c.bn);
+    const SplitPlan sp = split_plan(tiles, K / kBK, cus, split);
+    const double rounds = sp.s > 1 ? sp.n_dp / cus + 1.0 / sp.s + 0.1
+                                   : std::ceil((double)tiles / cus);
     const double t = rounds * c.bm * c.bn / c.speed;
     if (t < best_t) {
       best_t = t;
@@ -925,25 +1137,31 @@ static Shape2 pick_tile(MT mt, int N) {
 template <int BM, int BN, bool B_K, int EPI, int MAP>
 static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
   // worst case: sum over experts of ceil(rows_e / BM) <= S_max / BM + E
+  // tiles, plus up to kMaxSplitUnits segments replacing the split tail
   const long long mt_max = (S_max + BM - 1) / BM + p.E;
   const long long nt = (p.N + BN - 1) / BN;
-  const long long grid = mt_max * nt;
+  const long long grid = mt_max * nt + (p.partial != nullptr ? kMaxSplitUnits : 0);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI, MAP>), dim3((unsigned)grid),
                      dim3(kGemmThreads), 0, s, p);
+  if (p.partial != nullptr) {
+    MOE_TRY(hipGetLastError());
+    hipLaunchKernelGGL((rows_fixup_kernel<BM, BN, EPI, MAP>),
+                       dim3(kFixupTiles * fixup_parts(BM, BN)), dim3(kGemmThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
 template <bool B_K, int EPI, int MAP = MAP_NONE>
 static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const uint32_t* aux,
                               const int32_t* offsets, long long b_stride, int K, int N, int E,
-                              int S_max, hipStream_t s, uint32_t* bits_out = nullptr,
-                              const int32_t* a_map = nullptr, const int32_t* c_map = nullptr,
-                              int a_src_rows = 0) {
+                              int S_max, float* partial, hipStream_t s,
+                              uint32_t* bits_out = nullptr, const int32_t* a_map = nullptr,
+                              const int32_t* c_map = nullptr, int a_src_rows = 0) {
+  const int cus = device_cus();
   RowsArgs p{A, B, C, aux, reinterpret_cast<uint8_t*>(bits_out), offsets, a_map, c_map,
-             b_stride, K, N, E, a_src_rows};
-  const Shape2 t = pick_rows_tile(S_max, E, N);
-  if (t.bm == 256 && t.bn == 256) return launch_rows_t<256, 256, B_K, EPI, MAP>(p, S_max, s);
+             partial, b_stride, K, N, E, a_src_rows, cus};
+  const Shape2 t = pick_rows_tile(S_max, E, K, N, cus, partial != nullptr);
   if (t.bm == 256 && t.bn == 128) return launch_rows_t<256, 128, B_K, EPI, MAP>(p, S_max, s);
   if (t.bm == 128 && t.bn == 256) return launch_rows_t<128, 256, B_K, EPI, MAP>(p, S_max, s);
   return launch_rows_t<128, 128, B_K, EPI, MAP>(p, S_max, s);
@@ -970,22 +1188,22 @@ static hipError_t launch_wgrad(const bf16* X1, const bf16* X2, float* C, const i
   return launch_wgrad_t<128, 128, GATE>(p, s);
 }
 
-#define MOE_TRY(expr)                         \
-  do {                                        \
-    hipError_t _e = (expr);                   \
-    if (_e != hipSuccess) return _e;          \
-  } while (0)
+// Bytes of float32 partial tiles a row-grouped launch may use: the split
+// tail never holds more than kMaxSplitUnits tiles of the largest shape.
+size_t rows_partial_bytes(int act) {
+  return act == MOE_BF16 ? (size_t)kMaxSplitUnits * 256 * 256 * sizeof(float) : 0;
+}
 
 hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets, const void* w1,
                              const void* w2, void* h, void* out_perm, uint32_t* relu_bits,
-                             int S_max, int d, int F, int E, hipStream_t s) {
+                             float* partial, int S_max, int d, int F, int E, hipStream_t s) {
   if (act == MOE_BF16) {
     MOE_TRY((launch_rows<true, EPI_RELU>((const bf16*)x_perm, (const bf16*)w1, (bf16*)h, nullptr,
-                                         offsets, (long long)F * d, d, F, E, S_max, s,
+                                         offsets, (long long)F * d, d, F, E, S_max, partial, s,
                                          relu_bits)));
     MOE_TRY((launch_rows<true, EPI_STORE>((const bf16*)h, (const bf16*)w2, (bf16*)out_perm,
                                           nullptr, offsets, (long long)d * F, F, d, E, S_max,
-                                          s)));
+                                          partial, s)));
     return hipSuccess;
   }
   dim3 b(256);
@@ -1004,16 +1222,16 @@ hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets
 hipError_t launch_expert_fwd_fused(int act, const void* x, const int32_t* row_token, int T,
                                    const int32_t* offsets, const int32_t* row_slot,
                                    const void* w1, const void* w2, void* h, void* out_slot,
-                                   uint32_t* relu_bits, int S_max, int d, int F, int E,
-                                   hipStream_t s) {
+                                   uint32_t* relu_bits, float* partial, int S_max, int d, int F,
+                                   int E, hipStream_t s) {
   if (act == MOE_BF16) {
     // FC1 reads token rows x[row_token[r]]; FC2 stores row r at slot row_slot[r]
     MOE_TRY((launch_rows<true, EPI_RELU, MAP_GATHER_A>(
         (const bf16*)x, (const bf16*)w1, (bf16*)h, nullptr, offsets, (long long)F * d, d, F, E,
-        S_max, s, relu_bits, row_token, nullptr, T)));
+        S_max, partial, s, relu_bits, row_token, nullptr, T)));
     MOE_TRY((launch_rows<true, EPI_STORE, MAP_SCATTER_C>(
         (const bf16*)h, (const bf16*)w2, (bf16*)out_slot, nullptr, offsets, (long long)d * F, F,
-        d, E, S_max, s, nullptr, nullptr, row_slot, 0)));
+        d, E, S_max, partial, s, nullptr, nullptr, row_slot, 0)));
     return hipSuccess;
   }
   dim3 b(256);
@@ -1033,8 +1251,8 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
                              const int32_t* offsets, const void* w1, const void* w2, void* dz,
                              void* dx_perm, float* dw1, float* dw2, const float* dsel_perm,
                              float* dw_gate, float* db_gate, const uint32_t* relu_bits_in,
-                             uint32_t* relu_bits_ws, int S_max, int d, int F, int E,
-                             hipStream_t s) {
+                             uint32_t* relu_bits_ws, float* partial, int S_max, int d, int F,
+                             int E, hipStream_t s) {
   if (act == MOE_BF16) {
     // keep bits of the ReLU (unless the forward kept them), then
     // dz = (dO W2[e]) * [h > 0]: A = dO [rows][d], B = W2[e] as [K=d][N=F]
@@ -1049,14 +1267,14 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
     }
     MOE_TRY((launch_rows<false, EPI_MASK>((const bf16*)d_out, (const bf16*)w2, (bf16*)dz,
                                           relu_bits, offsets, (long long)d * F, d, F, E, S_max,
-                                          s)));
+                                          partial, s)));
     // dW2[e] = dO^T h  ([d][F])
     MOE_TRY((launch_wgrad<false>((const bf16*)d_out, (const bf16*)h, dw2, offsets, nullptr,
                                  nullptr, nullptr, d, F, E, s)));
     // dx_perm = dz W1[e]: A = dz [rows][F], B = W1[e] as [K=F][N=d]  (may reuse dO's memory)
     MOE_TRY((launch_rows<false, EPI_STORE>((const bf16*)dz, (const bf16*)w1, (bf16*)dx_perm,
                                            nullptr, offsets, (long long)F * d, F, d, E, S_max,
-                                           s)));
+                                           partial, s)));
     // dW1[e] = dz^T x_perm  ([F][d]), with the gate's dW_gate / db over the kept rows
     MOE_TRY((launch_wgrad<true>((const bf16*)dz, (const bf16*)x_perm, dw1, offsets, dsel_perm,
                                 dw_gate, db_gate, F, d, E, s)));

@@ -98,12 +98,14 @@ struct BwdWs {
   float* dsel_perm; // [S]     the same per packed row
   float* w_gate_t;  // [E][d]
   uint32_t* relu_bits;  // [S][F/32] keep bits of the ReLU (bf16 path)
+  float* partial;       // split-tail partial tiles of the row-grouped GEMMs
 };
 
 size_t bwd_ws_bytes(const moe_shape* s) {
   const size_t S = (size_t)slots(s), a = act_bytes(s);
   return align_up(S * s->d_model * a) + align_up(S * s->d_ff * a) + 2 * align_up(S * 4) +
-         align_up((size_t)s->E * s->d_model * 4) + align_up(S * (size_t)s->d_ff / 8);
+         align_up((size_t)s->E * s->d_model * 4) + align_up(S * (size_t)s->d_ff / 8) +
+         rows_partial_bytes(s->act_dtype);
 }
 
 BwdWs carve_bwd(const moe_shape* s, void* ws) {
@@ -121,7 +123,21 @@ BwdWs carve_bwd(const moe_shape* s, void* ws) {
   w.w_gate_t = reinterpret_cast<float*>(p);
   p += align_up((size_t)s->E * s->d_model * 4);
   w.relu_bits = reinterpret_cast<uint32_t*>(p);
+  p += align_up(S * (size_t)s->d_ff / 8);
+  w.partial = rows_partial_bytes(s->act_dtype) ? reinterpret_cast<float*>(p) : nullptr;
   return w;
+}
+
+// Forward workspaces: the routing/permutation part, [row_slot [S] for the
+// fused forward], then the GEMMs' split-tail partial tiles.
+size_t fwd_ws_bytes(const moe_shape* s, bool fused) {
+  return perm_ws_bytes(s) + (fused ? align_up((size_t)slots(s) * 4) : 0) +
+         rows_partial_bytes(s->act_dtype);
+}
+float* fwd_partial(const moe_shape* s, void* ws, bool fused) {
+  if (rows_partial_bytes(s->act_dtype) == 0) return nullptr;
+  return reinterpret_cast<float*>(static_cast<char*>(ws) + perm_ws_bytes(s) +
+                                  (fused ? align_up((size_t)slots(s) * 4) : 0));
 }
 
 moe_status check_ws(const moe_shape* s, int op, const void* ws, size_t bytes) {
@@ -175,15 +191,17 @@ size_t moe_workspace_bytes(const moe_shape* s, int32_t op) {
   switch (op) {
     case MOE_OP_ROUTE:
     case MOE_OP_PERMUTE:
-    case MOE_OP_FORWARD:
       return perm_ws_bytes(s);
+    case MOE_OP_FORWARD:
+      return fwd_ws_bytes(s, false);
+    case MOE_OP_FORWARD_FUSED:
+      return fwd_ws_bytes(s, true);
     case MOE_OP_EXPERT_FFN:
+      return rows_partial_bytes(s->act_dtype);
     case MOE_OP_COMBINE:
       return 0;
     case MOE_OP_BACKWARD:
       return bwd_ws_bytes(s);
-    case MOE_OP_FORWARD_FUSED:  // + row_slot [S]
-      return perm_ws_bytes(s) + align_up((size_t)slots(s) * 4);
     default:
       return 0;
   }
@@ -259,14 +277,15 @@ moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_id
 moe_status moe_expert_ffn(const moe_shape* s, const void* x_perm, const int32_t* offsets,
                           const void* w1, const void* w2, void* h, void* out_perm,
                           uint32_t* relu_bits, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!ptrs_ok(x_perm, offsets, w1, w2, h, out_perm) || !opt_ok(relu_bits))
     return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_EXPERT_FFN, ws, ws_bytes)) != MOE_OK) return st;
+  float* partial = rows_partial_bytes(s->act_dtype) ? static_cast<float*>(ws) : nullptr;
   MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, relu_bits,
-                            (int)slots(s), s->d_model, s->d_ff, s->E, as_stream(stream)));
+                            partial, (int)slots(s), s->d_model, s->d_ff, s->E,
+                            as_stream(stream)));
   return MOE_OK;
 }
 
@@ -305,7 +324,8 @@ moe_status moe_forward(const moe_shape* s, const void* x, const float* w_gate,
                         s->capacity_priority == MOE_PRIORITY_CHOICE, offsets, slot_row, row_token,
                         x_perm, stream_));
   MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, relu_bits,
-                            (int)slots(s), s->d_model, s->d_ff, s->E, stream_));
+                            fwd_partial(s, ws, false), (int)slots(s), s->d_model, s->d_ff, s->E,
+                            stream_));
   MOE_HIP(launch_combine(s->act_dtype, out_perm, topk_w, slot_row, y, s->T, s->d_model, s->k,
                          stream_));
   return MOE_OK;
@@ -336,8 +356,8 @@ moe_status moe_forward_fused(const moe_shape* s, const void* x, const float* w_g
                        s->capacity_priority == MOE_PRIORITY_CHOICE, offsets, slot_row, row_token,
                        row_slot, stream_));
   MOE_HIP(launch_expert_fwd_fused(s->act_dtype, x, row_token, s->T, offsets, row_slot, w1, w2, h,
-                                  out_slot, relu_bits, (int)slots(s), s->d_model, s->d_ff, s->E,
-                                  stream_));
+                                  out_slot, relu_bits, fwd_partial(s, ws, true), (int)slots(s),
+                                  s->d_model, s->d_ff, s->E, stream_));
   MOE_HIP(launch_combine(s->act_dtype, out_slot, topk_w, slot_row, y, s->T, s->d_model, s->k,
                          stream_, true));
   return MOE_OK;
@@ -367,7 +387,7 @@ moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const
   // the last reader of d_out.  For bf16 the FC1 wgrad also writes dW_gate and
   // db over the kept rows.
   MOE_HIP(launch_expert_bwd(act, bw.d_out, x_perm, h, offsets, w1, w2, bw.dz, bw.d_out, dw1, dw2,
-                            bw.dsel_perm, dw_gate, db_gate, relu_bits, bw.relu_bits,
+                            bw.dsel_perm, dw_gate, db_gate, relu_bits, bw.relu_bits, bw.partial,
                             (int)slots(s), s->d_model, s->d_ff, s->E, stream_));
   if (act != MOE_BF16)
     MOE_HIP(launch_gate_rows(act, x_perm, bw.dsel_perm, offsets, dw_gate, db_gate, s->d_model,

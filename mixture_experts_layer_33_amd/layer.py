@@ -107,9 +107,12 @@ class MoeLayer:
                     self.slot_row, self.row_token, self.x_perm, self.ws_fwd, stream)
 
     def expert_ffn(self, w1, w2, x_perm=None, offsets=None, stream=None):
+        if getattr(self, "ws_ffn", None) is None:
+            nb = max(moe_workspace_bytes(self.shape, "expert_ffn"), 256)
+            self.ws_ffn = torch.empty(nb, dtype=torch.uint8, device=self.device)
         moe_expert_ffn(self.shape, self.x_perm if x_perm is None else x_perm,
                        self.offsets if offsets is None else offsets, w1, w2, self.h,
-                       self.out_perm, self.relu_bits, None, stream)
+                       self.out_perm, self.relu_bits, self.ws_ffn, stream)
 
     def combine(self, out_perm=None, topk_w=None, slot_row=None, stream=None):
         moe_combine(self.shape, self.out_perm if out_perm is None else out_perm,

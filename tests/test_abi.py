@@ -74,7 +74,9 @@ def test_workspace_sizes():
     s = shape()
     for op in ("route", "permute", "forward"):
         assert moe.moe_workspace_bytes(s, op) > 0
-    assert moe.moe_workspace_bytes(s, "expert_ffn") == 0
+    # bf16 expert GEMMs keep float32 partial tiles of a split last round
+    assert moe.moe_workspace_bytes(s, "expert_ffn") > 0
+    assert moe.moe_workspace_bytes(shape(act=moe.MOE_F32), "expert_ffn") == 0
     assert moe.moe_workspace_bytes(s, "combine") == 0
     # backward keeps dO, dz and the per-slot gate gradients at least
     S = s.T * s.k
@@ -105,11 +107,15 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.moe_expert_ffn(bs, P, P, P, P, None, P, None, None, 0, None) == -1
     # optional relu_bits must still be 16-byte aligned
     assert L.moe_expert_ffn(bs, P, P, P, P, P, P, P + 4, None, 0, None) == -1
+    ffn = moe.moe_workspace_bytes(s, "expert_ffn")
+    assert L.moe_expert_ffn(bs, P, P, P, P, P, P, None, None, 0, None) == -3
+    assert L.moe_expert_ffn(bs, P, P, P, P, P, P, None, P, ffn - 1, None) == -3
     assert L.moe_combine(bs, P, P, P, None, None) == -1
     # misaligned pointer
     assert L.moe_combine(bs, P, P, P + 4, P, None) == -1
     # workspace too small / missing / misaligned
-    assert L.moe_route(bs, P, P, P, None, None, P, P, P, P, ws - 1, None) == -3
+    rws = moe.moe_workspace_bytes(s, "route")
+    assert L.moe_route(bs, P, P, P, None, None, P, P, P, P, rws - 1, None) == -3
     assert L.moe_permute(bs, P, P, None, P, P, P, P, P, None, ws, None) == -3
     assert L.moe_forward(bs, P, P, P, P, P, P, None, P, P, None, P, P, P, P, P, P, P, None,
                          P + 16, ws, None) == -3
