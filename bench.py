@@ -68,6 +68,7 @@ def parse():
 
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_33_amd", "csrc", "gemm.hip")
 GEMM_KERNEL = "rows_gemm_kernel"
+FIXUP_KERNEL = "rows_fixup_kernel"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30
 
@@ -103,10 +104,16 @@ def summarize_traffic(args):
             raise SystemExit(f"{path}: no 1 GiB copy dispatch (run with --copy-calibration)")
         scale = (COPY_BYTES / 1024) / (sum(copies) / len(copies))
         per_kernel = {}
-        for r in rows:
-            # forward launches: K-contiguous weights, epilogue ReLU (FC1) or store (FC2)
-            if re.search(GEMM_KERNEL + r"<\d+, \d+, true, [01]>", r["Kernel_Name"]):
-                per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        for i, r in enumerate(rows):
+            # forward launches: K-contiguous weights, epilogue ReLU (FC1) or store
+            # (FC2), packed rows; a split-tail fixup dispatched right after one
+            # belongs to that launch
+            if re.search(GEMM_KERNEL + r"<\d+, \d+, true, [01], 0>", r["Kernel_Name"]):
+                v = float(r["Counter_Value"])
+                if i + 1 < len(rows) and FIXUP_KERNEL in rows[i + 1]["Kernel_Name"]:
+                    v += float(rows[i + 1]["Counter_Value"])
+                per_kernel.setdefault(r["Kernel_Name"], []).append(v)
         if len(per_kernel) != 2:
             raise SystemExit(f"{path}: expected the FC1 and FC2 forward GEMM kernels, "
                              f"found {sorted(per_kernel)}")
@@ -134,8 +141,9 @@ def summarize_traffic(args):
     lines.append(args.command.strip() or "(not recorded)")
     lines.append("```")
     lines.append("")
-    lines.append("Counters are KiB per dispatch, averaged over the dispatches of each kernel; "
-                 "each is scaled by 1 GiB / (the same counter's reading for the 1 GiB "
+    lines.append("Counters are KiB per launch (the GEMM dispatch plus the split-tail fixup "
+                 "dispatched right after it, if any), averaged over the launches of each "
+                 "kernel; each is scaled by 1 GiB / (the same counter's reading for the 1 GiB "
                  f"device copy `{COPY_KERNEL}`).")
     lines.append("")
     lines.append("| counter | copy reading (KiB) | scale |")

@@ -657,6 +657,10 @@ constexpr int kMaxSplit = 16;
 // 16-step tiles cost more in the fixup than they save).
 constexpr int kMinSplit = 4;
 constexpr int kMinSplitSteps = 4;    // k steps (of kBK) per segment, at least
+// Products with a shorter K are never split, so they launch no fixup (a
+// launch costs ~5 us even when it finds nothing to do; a tile of K < 2048 is
+// too short for a split to win that back).
+constexpr int kMinSplitK = 2048;
 struct SplitPlan {
   int n_dp, tail, s;
 };
@@ -815,33 +819,35 @@ rows_gemm_kernel(RowsArgs p) {
 // Sum of the split tail's partial tiles (segment order) and the epilogue of
 // rows_gemm_kernel on it: ReLU + keep bits, plain store, or the ReLU mask,
 // bf16 rounding to nearest even, to the same destination rows.  Tail tile b
-// is spread over fixup_parts(BM, BN) workgroups of kGemmThreads / (BN / 8)
-// rows each; a thread takes 8 consecutive columns of one row and issues the
-// loads of four segments ahead of their (in-order) sums.
-constexpr int kFixupTiles = kMaxSplitUnits / 2;  // a split tail has <= this many tiles
+// is cut into fixup_parts(BM, BN) items of kGemmThreads / (BN / 8) rows each,
+// dealt to the workgroups in turn; a thread takes 8 consecutive columns of
+// one row and issues the loads of four segments ahead of their (in-order)
+// sums.  One workgroup per CU: the launch follows every split-capable GEMM
+// launch and must cost little when the device-side plan has no split.
+constexpr int kFixupBlocks = 256;
 constexpr int fixup_parts(int BM, int BN) { return BM / (kGemmThreads / (BN / 8)); }
 template <int BM, int BN, int EPI, int MAP>
 __global__ void __launch_bounds__(kGemmThreads)
 rows_fixup_kernel(RowsArgs p) {
   constexpr int kFixupRows = kGemmThreads / (BN / 8);
   constexpr int kParts = fixup_parts(BM, BN);
-  static_assert(kParts * kFixupRows == BM, "whole rows per workgroup");
+  static_assert(kParts * kFixupRows == BM, "whole rows per item");
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int s_tstart[MOE_MAX_EXPERTS + 1];
   __shared__ int s_scratch[kGemmThreads / 64 + 1];
   __shared__ int s_expert;
-  const int tb = blockIdx.x / kParts, part_rows = (blockIdx.x % kParts) * kFixupRows;
   rows_scan<BM>(p, s_off, s_tstart, s_scratch);
   const int NT = (p.N + BN - 1) / BN;
   const SplitPlan sp = split_plan(s_tstart[p.E] * NT, p.K / kBK, p.cus, true);
-  if (tb >= sp.tail) return;
-  const RowTile t = find_tile<BM, BN>(sp.n_dp + tb, NT, p.N, p.E, s_off, s_tstart, &s_expert);
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  const float* part = p.partial + (size_t)tb * sp.s * (BM * BN);
-  {
+  for (int item = blockIdx.x; item < sp.tail * kParts; item += gridDim.x) {
+    const int tb = item / kParts, part_rows = (item % kParts) * kFixupRows;
+    const RowTile t = find_tile<BM, BN>(sp.n_dp + tb, NT, p.N, p.E, s_off, s_tstart, &s_expert);
+    __syncthreads();  // every thread has read s_expert before the next item rewrites it
+    const float* part = p.partial + (size_t)tb * sp.s * (BM * BN);
     const int g = threadIdx.x;
     const int m = part_rows + g / (BN / 8), n = (g % (BN / 8)) * 8;
-    if (m >= t.rows || n >= t.cols) return;
+    if (m >= t.rows || n >= t.cols) continue;
     const int wm = m / WM, j = (m % WM) / 32, ml = m % 32;
     const int wn = n / WN, i = (n % WN) / 32, pq = (n % 32) / 8;
     const size_t blk = ((size_t)((wm * 2 + wn) * FN + i) * FM + j) * 1024;
@@ -1147,7 +1153,7 @@ static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
   if (p.partial != nullptr) {
     MOE_TRY(hipGetLastError());
     hipLaunchKernelGGL((rows_fixup_kernel<BM, BN, EPI, MAP>),
-                       dim3(kFixupTiles * fixup_parts(BM, BN)), dim3(kGemmThreads), 0, s, p);
+                       dim3(kFixupBlocks), dim3(kGemmThreads), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -1159,6 +1165,7 @@ static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const uint3
                               uint32_t* bits_out = nullptr, const int32_t* a_map = nullptr,
                               const int32_t* c_map = nullptr, int a_src_rows = 0) {
   const int cus = device_cus();
+  if (K < kMinSplitK) partial = nullptr;
   RowsArgs p{A, B, C, aux, reinterpret_cast<uint8_t*>(bits_out), offsets, a_map, c_map,
              partial, b_stride, K, N, E, a_src_rows, cus};
   const Shape2 t = pick_rows_tile(S_max, E, K, N, cus, partial != nullptr);

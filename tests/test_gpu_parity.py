@@ -47,11 +47,10 @@ SMALL = {
     "uniform_top1_cf100": workloads.scaled(WL["uniform_cf125"], T=1000, d=256, F=320, k=1,
                                            capacity_factor=1.0),
     "skewed_top1": workloads.scaled(WL["skewed_zipf12"], T=1500, d=128, F=192, k=1),
-    # K = 1024 (d or F) with a partly filled last round of GEMM tiles: the
-    # second expert GEMM and the input-gradient GEMM split that round's tiles
-    # along K
-    "skewed_split_tail": workloads.scaled(WL["skewed_zipf12"], T=700, d=512, F=1024),
-    "uniform_cf100_split_tail": workloads.scaled(WL["uniform_cf125"], T=900, d=512, F=1024,
+    # K = F = 2048 with a partly filled last round of GEMM tiles: the second
+    # expert GEMM and the input-gradient GEMM split that round's tiles along K
+    "skewed_split_tail": workloads.scaled(WL["skewed_zipf12"], T=700, d=512, F=2048),
+    "uniform_cf100_split_tail": workloads.scaled(WL["uniform_cf125"], T=900, d=512, F=2048,
                                                  capacity_factor=1.0),
 }
 
