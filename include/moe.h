@@ -159,7 +159,7 @@ moe_status moe_permute(const moe_shape* shape, const void* x, const int32_t* top
  * words, bit (f % 32) of word [r][f / 32] set iff h[r][f] > 0, over rows
  * [0, offsets[E]); moe_backward can take it instead of deriving the ReLU
  * mask from h.  Ignored for MOE_F32.
- * Workspace: MOE_OP_EXPERT_FFN: bf16 needs 64 MiB of scratch for float32
+ * Workspace: MOE_OP_EXPERT_FFN: bf16 needs 32 MiB of scratch for float32
  * partial tiles (when the last round of GEMM tiles would leave compute
  * units idle, its tiles are split along the reduction dimension and summed
  * in a fixed order, so results are deterministic); MOE_F32 needs none (the

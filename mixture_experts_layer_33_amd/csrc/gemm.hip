@@ -651,6 +651,7 @@ enum RowMap { MAP_NONE = 0, MAP_GATHER_A = 1, MAP_SCATTER_C = 2 };
 // segment order and applies the epilogue.  Deterministic: the plan depends
 // only on the tile count, K and the CU count.
 constexpr int kMaxSplitUnits = 256;  // partial tiles the workspace holds
+constexpr int kMaxRowTileArea = 256 * 128;  // largest row tile (256 x 128, 128 x 256)
 constexpr int kMaxSplit = 16;
 // A split pays only when it cuts the last round to a quarter or less: the
 // fixup reads s partial tiles per tail tile (measured: 2-way splits of
@@ -1142,6 +1143,7 @@ static Shape2 pick_tile(MT mt, int N) {
 
 template <int BM, int BN, bool B_K, int EPI, int MAP>
 static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
+  static_assert(BM * BN <= kMaxRowTileArea, "partial tiles must fit the workspace");
   // worst case: sum over experts of ceil(rows_e / BM) <= S_max / BM + E
   // tiles, plus up to kMaxSplitUnits segments replacing the split tail
   const long long mt_max = (S_max + BM - 1) / BM + p.E;
@@ -1196,9 +1198,9 @@ static hipError_t launch_wgrad(const bf16* X1, const bf16* X2, float* C, const i
 }
 
 // Bytes of float32 partial tiles a row-grouped launch may use: the split
-// tail never holds more than kMaxSplitUnits tiles of the largest shape.
+// tail never holds more than kMaxSplitUnits tiles of the largest row tile.
 size_t rows_partial_bytes(int act) {
-  return act == MOE_BF16 ? (size_t)kMaxSplitUnits * 256 * 256 * sizeof(float) : 0;
+  return act == MOE_BF16 ? (size_t)kMaxSplitUnits * kMaxRowTileArea * sizeof(float) : 0;
 }
 
 hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets, const void* w1,
