@@ -1280,13 +1280,15 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
     // dW2[e] = dO^T h  ([d][F])
     MOE_TRY((launch_wgrad<false>((const bf16*)d_out, (const bf16*)h, dw2, offsets, nullptr,
                                  nullptr, nullptr, d, F, E, s)));
-    // dx_perm = dz W1[e]: A = dz [rows][F], B = W1[e] as [K=F][N=d]  (may reuse dO's memory)
-    MOE_TRY((launch_rows<false, EPI_STORE>((const bf16*)dz, (const bf16*)w1, (bf16*)dx_perm,
-                                           nullptr, offsets, (long long)F * d, F, d, E, S_max,
-                                           partial, s)));
     // dW1[e] = dz^T x_perm  ([F][d]), with the gate's dW_gate / db over the kept rows
     MOE_TRY((launch_wgrad<true>((const bf16*)dz, (const bf16*)x_perm, dw1, offsets, dsel_perm,
                                 dw_gate, db_gate, F, d, E, s)));
+    // dx_perm = dz W1[e]: A = dz [rows][F], B = W1[e] as [K=F][N=d]  (may reuse dO's
+    // memory: it runs after the last reader of dO).  Last of the four, so the
+    // decode of dX that follows reads dx_perm while it is still cached.
+    MOE_TRY((launch_rows<false, EPI_STORE>((const bf16*)dz, (const bf16*)w1, (bf16*)dx_perm,
+                                           nullptr, offsets, (long long)F * d, F, d, E, S_max,
+                                           partial, s)));
     return hipSuccess;
   }
   dim3 b(256);
