@@ -101,6 +101,19 @@ def test_fused_forward_matches_forward_and_reference(name):
     _check_against_reference(w, inp, layer)
 
 
+@pytest.mark.parametrize("name", ["single_expert", "max_E_and_k", "one_token",
+                                  "three_tokens_fp32", "heavy_drops_k3_choice", "wide_F_ragged"])
+def test_fused_forward_edge_cases(name):
+    """The edge shapes of the end-to-end edge tests: one expert, E = 256 with
+    k = 8, one and three tokens, heavy drops under choice-major priority, a
+    ragged wide F."""
+    from test_gpu_edges import EDGES
+    w = EDGES[name]
+    inp, layer, ref, out_perm = _run(w)
+    _check_against_unfused(w, layer, ref, out_perm)
+    _check_against_reference(w, inp, layer)
+
+
 @pytest.mark.parametrize("name", ["uniform_cf125", "fine_grained"])
 def test_fused_forward_full_size_matches_forward(name):
     """At full size (the launch shapes bench.py times), bit for bit against
