@@ -69,4 +69,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   return excl;
 }
 
+// a compile-time int as a value (selects an unrolled step's buffers)
+template <int V>
+struct Ic {
+  static constexpr int value = V;
+};
+
 }  // namespace moe

@@ -244,11 +244,6 @@ __device__ __forceinline__ void interleave() {
   if constexpr (m2 > b) __builtin_amdgcn_sched_group_barrier(0x008, m2 - b, 0);
 }
 
-template <int V>
-struct Ic {
-  static constexpr int value = V;
-};
-
 // The LDS stage buffers of a tile, each its own LDS object: the compiler can
 // then tell that the buffer being read is not the one the copies are filling
 // (with one shared array it waits for every copy before each transposed

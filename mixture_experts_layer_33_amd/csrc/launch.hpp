@@ -9,13 +9,12 @@ namespace moe {
 // ---- gate routing (route.hip)
 // logits = x * w_gate + b (float32); top-k with lowest-index ties; weights =
 // softmax over the selected logits.
-// bf16 without logits_in runs the router on MFMA and needs `wsplit`
-// (route_split_bytes) for the split copy of W_gate.
+// bf16 without logits_in runs the router on MFMA (W_gate split into three
+// exact bf16 parts as it is staged).
 hipError_t launch_route(int act, const void* x, const float* w_gate, const float* b_gate,
                         const float* logits_in, float* logits_out, int32_t* topk_idx,
-                        float* topk_w, int T, int d, int E, int k, void* wsplit, hipStream_t s);
+                        float* topk_w, int T, int d, int E, int k, hipStream_t s);
 int route_padded_experts(int E);
-size_t route_split_bytes(int d, int E);
 
 // ---- input encode (permute.hip)
 // Per tile of kRankTile slots: stable rank of each slot among the tile's

@@ -61,14 +61,12 @@ struct PermWs {
   int32_t* tile_base;   // [E][n_tiles]
   int32_t* raw_tmp;     // [E] raw counts when the caller passes none
   int32_t* kept_tmp;    // [E] kept counts when the caller passes none
-  void* wsplit;         // [3][EP][d] bf16 split router weights (bf16 only)
 };
 
 size_t perm_ws_bytes(const moe_shape* s) {
   const size_t S = (size_t)slots(s);
   const size_t nt = (size_t)rank_tiles(s) * (size_t)s->E;
   size_t b = align_up(S * 4) + 2 * align_up(nt * 4) + 2 * align_up((size_t)s->E * 4);
-  if (s->act_dtype == MOE_BF16) b += align_up(route_split_bytes(s->d_model, s->E));
   return b;
 }
 
@@ -87,7 +85,6 @@ PermWs carve_perm(const moe_shape* s, void* ws) {
   p += align_up((size_t)s->E * 4);
   w.kept_tmp = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)s->E * 4);
-  w.wsplit = (s->act_dtype == MOE_BF16) ? p : nullptr;
   return w;
 }
 
@@ -171,7 +168,7 @@ moe_status do_route(const moe_shape* s, const void* x, const float* w_gate, cons
                     const float* logits_in, float* logits_out, int32_t* idx, float* w,
                     int32_t* counts_raw, int32_t* counts_kept, const PermWs& pw, hipStream_t st) {
   MOE_HIP(launch_route(s->act_dtype, x, w_gate, b_gate, logits_in, logits_out, idx, w, s->T,
-                       s->d_model, s->E, s->k, pw.wsplit, st));
+                       s->d_model, s->E, s->k, st));
   const int nt = rank_tiles(s);
   MOE_HIP(launch_rank_hist(idx, s->T, s->k, s->capacity_priority == MOE_PRIORITY_CHOICE, s->E,
                            pw.local_rank, pw.hist, nt, st));
@@ -242,7 +239,7 @@ moe_status moe_route(const moe_shape* s, const void* x, const float* w_gate, con
   PermWs pw = carve_perm(s, ws);
   if (counts_raw == nullptr) {  // routing only; moe_permute counts
     MOE_HIP(launch_route(s->act_dtype, x, w_gate, b_gate, logits_in, logits_out, topk_idx,
-                         topk_w, s->T, s->d_model, s->E, s->k, pw.wsplit, as_stream(stream)));
+                         topk_w, s->T, s->d_model, s->E, s->k, as_stream(stream)));
     return MOE_OK;
   }
   return do_route(s, x, w_gate, b_gate, logits_in, logits_out, topk_idx, topk_w, counts_raw,

@@ -128,34 +128,16 @@ route_kernel(const ActT* __restrict__ x, const float* __restrict__ w_gate,
 // ---------------------------------------------------------------------------
 // bf16 activations: the router product on MFMA.  W_gate (float32) is split
 // exactly into three bf16 parts, W = hi + mid + lo (each part takes the next
-// 8 bits of the 24-bit significand), stored transposed as [3][EP][d] with
-// EP = E rounded up to 16 (extra rows zero).  bf16 x times each bf16 part is
-// exact in float32, so logits = sum over the three parts of x W_p with
-// float32 accumulation: float32 accuracy at matrix-core rate.
-__global__ void split_gate_kernel(const float* __restrict__ w_gate, bf16* __restrict__ wsplit,
-                                  int d, int E, int EP) {
-  __shared__ float tile[32][33];
-  const int i0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int r = ty; r < 32; r += 8) {
-    const int i = i0 + r, e = e0 + tx;
-    tile[r][tx] = (i < d && e < E) ? w_gate[(size_t)i * E + e] : 0.f;
-  }
-  __syncthreads();
-  for (int r = ty; r < 32; r += 8) {
-    const int e = e0 + r, i = i0 + tx;
-    if (e < EP && i < d) {
-      const float v = tile[tx][r];
-      const bf16 hi = (bf16)v;
-      const float r1 = v - (float)hi;
-      const bf16 mid = (bf16)r1;
-      const bf16 lo = (bf16)(r1 - (float)mid);
-      const size_t plane = (size_t)EP * d;
-      wsplit[(size_t)e * d + i] = hi;
-      wsplit[plane + (size_t)e * d + i] = mid;
-      wsplit[2 * plane + (size_t)e * d + i] = lo;
-    }
-  }
+// 8 bits of the 24-bit significand); bf16 x times each bf16 part is exact in
+// float32, so logits = sum over the three parts of x W_p with float32
+// accumulation: float32 accuracy at matrix-core rate.  The split happens
+// while W_gate is staged into LDS, as [3][EP][SW] (EP = E rounded up to 16,
+// extra rows zero), so there is no separate pass over W_gate.
+__device__ __forceinline__ void split3(float v, bf16& hi, bf16& mid, bf16& lo) {
+  hi = (bf16)v;
+  const float r1 = v - (float)hi;
+  mid = (bf16)r1;
+  lo = (bf16)(r1 - (float)mid);
 }
 
 // LDS row of SW bf16 (SW/8 16-byte chunks), chunks XOR-swizzled by the low
@@ -168,14 +150,16 @@ __device__ __forceinline__ int rswz(int row, int kc) {
 }
 
 // Router logits on MFMA (v_mfma_f32_16x16x32_bf16, 16 tokens x 16 experts per
-// block).  Four wavefronts; KS of them share one group of 16 tokens and split
+// block).  Four wavefronts; KS of them share TG groups of 16 tokens and split
 // the k range of every LDS stage between them, their partial logits summed
-// in LDS in a fixed order, so a workgroup covers 64 / KS tokens (KS > 1 gives
-// small batches enough workgroups).  The three bf16 parts of W_gate go
-// through LDS; x fragments are read straight from memory one stage ahead.
-template <int EP, int KS>
+// in LDS in a fixed order, so a workgroup covers 64 TG / KS tokens (KS > 1
+// gives small batches enough workgroups; TG > 1 reuses each staged W_gate
+// slice for more tokens when experts are many).  Loads run two stages ahead:
+// W_gate through registers into LDS (split on the way), x fragments straight
+// into registers.
+template <int EP, int KS, int TG>
 __global__ void __launch_bounds__(256)
-route_mfma_kernel(const bf16* __restrict__ x, const bf16* __restrict__ wsplit,
+route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
                   const float* __restrict__ b_gate, float* __restrict__ logits_out,
                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int d, int E,
                   int k) {
@@ -183,56 +167,76 @@ route_mfma_kernel(const bf16* __restrict__ x, const bf16* __restrict__ wsplit,
   constexpr int SW = KS * BK;                     // k per stage
   constexpr int FN = EP / 16;
   constexpr int ROWS = 3 * EP;                    // LDS rows per stage
-  constexpr int CPR = SW / 8;                     // chunks per row
-  constexpr int NQ = ROWS * CPR;                  // chunks per stage
-  constexpr int NCH = (NQ + 255) / 256;           // chunks per thread
-  constexpr int TPW = 64 / KS;                    // tokens per workgroup
+  constexpr int CPR = SW / 8;                     // 8-k chunks per row
+  constexpr int NQ = EP * CPR;                    // (expert, chunk) pairs per stage
+  constexpr int NCH = (NQ + 255) / 256;           // pairs per thread
+  constexpr int TPW = 64 / KS * TG;               // tokens per workgroup
   constexpr int NS = BK / 32;                     // MFMA k slices per wavefront per stage
   __shared__ __attribute__((aligned(16))) bf16 lds[2][ROWS * SW];
-  __shared__ f32x4 red[KS > 1 ? 4 : 1][KS > 1 ? 64 * FN : 1];
+  __shared__ f32x4 red[KS > 1 ? 4 : 1][KS > 1 ? 64 * FN * TG : 1];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int grp = wid / KS, ks = wid % KS;
-  const int t0 = blockIdx.x * TPW + grp * 16;
-  const int ta = min(t0 + (lane & 15), T - 1);  // A-fragment row (clamped)
-  const bf16* xrow = x + (size_t)ta * d + ks * BK + (lane >> 4) * 8;
-  f32x4 acc[FN];
+  const int t0 = blockIdx.x * TPW + grp * 16 * TG;
+  const bf16* xrow[TG];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < TG; ++g) {
+    const int ta = min(t0 + g * 16 + (lane & 15), T - 1);  // A-fragment row (clamped)
+    xrow[g] = x + (size_t)ta * d + ks * BK + (lane >> 4) * 8;
+  }
+  f32x4 acc[TG][FN];
+#pragma unroll
+  for (int g = 0; g < TG; ++g)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  i32x4 stage[NCH];
-  auto load_stage = [&](int k0) {
+  float wr[2][NCH][8];      // W_gate of the stages ahead (two register sets)
+  bf16x8 xr[2][TG][NS];     // x fragments of the stages ahead
+  auto load_w = [&](int kt, float(&dst)[NCH][8]) {
+    const int k0 = kt * SW;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int q = tid + c * 256, row = q / CPR, kc = q % CPR;
-      if (NQ % 256 == 0 || q < NQ)
-        stage[c] = *reinterpret_cast<const i32x4*>(wsplit + (size_t)row * d + k0 + kc * 8);
+      const int q = tid + c * 256, e = q % EP, kc = q / EP;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dst[c][i] = ((NQ % 256 == 0 || q < NQ) && e < E)
+                        ? w_gate[(size_t)(k0 + kc * 8 + i) * E + e] : 0.f;
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_w = [&](int buf, const float(&src)[NCH][8]) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int q = tid + c * 256, row = q / CPR, kc = q % CPR;
-      if (NQ % 256 == 0 || q < NQ)
-        *reinterpret_cast<i32x4*>(&lds[buf][rswz<SW>(row, kc)]) = stage[c];
+      const int q = tid + c * 256, e = q % EP, kc = q / EP;
+      if (NQ % 256 == 0 || q < NQ) {
+        bf16x8 hi, mid, lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          bf16 h, m, l;
+          split3(src[c][i], h, m, l);
+          hi[i] = h;
+          mid[i] = m;
+          lo[i] = l;
+        }
+        *reinterpret_cast<bf16x8*>(&lds[buf][rswz<SW>(e, kc)]) = hi;
+        *reinterpret_cast<bf16x8*>(&lds[buf][rswz<SW>(EP + e, kc)]) = mid;
+        *reinterpret_cast<bf16x8*>(&lds[buf][rswz<SW>(2 * EP + e, kc)]) = lo;
+      }
     }
   };
-  bf16x8 xc[NS], xn[NS];
-  auto load_x = [&](int kt, bf16x8(&dst)[NS]) {
+  auto load_x = [&](int kt, bf16x8(&dst)[TG][NS]) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      dst[s] = *reinterpret_cast<const bf16x8*>(xrow + (size_t)kt * SW + s * 32);
+    for (int g = 0; g < TG; ++g)
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        dst[g][s] = *reinterpret_cast<const bf16x8*>(xrow[g] + (size_t)kt * SW + s * 32);
   };
   const int nk = d / SW;
-  load_stage(0);
-  load_x(0, xc);
-  store_stage(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      load_stage((kt + 1) * SW);
-      load_x(kt + 1, xn);
-    }
+  // step kt on LDS buffer P = kt % 2 with x in xr[P]; issues the W_gate loads
+  // of stage kt + 2 into wr[P] (stage kt is already in LDS), stores stage
+  // kt + 1 (loaded a step earlier) into the other buffer, then loads the x
+  // fragments of stage kt + 2 into xr[P]
+  auto step = [&](auto P_, int kt) {
+    constexpr int P = decltype(P_)::value;
+    if (kt + 2 < nk) load_w(kt + 2, wr[P]);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int kc = ks * (BK / 8) + s * 4 + (lane >> 4);
@@ -241,18 +245,30 @@ route_mfma_kernel(const bf16* __restrict__ x, const bf16* __restrict__ wsplit,
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int row = p * EP + j * 16 + (lane & 15);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&lds[cur][rswz<SW>(row, kc)]);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xc[s], b, acc[j], 0, 0, 0);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&lds[P][rswz<SW>(row, kc)]);
+#pragma unroll
+          for (int g = 0; g < TG; ++g)
+            acc[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[P][g][s], b, acc[g][j], 0, 0,
+                                                                0);
         }
     }
-    if (kt + 1 < nk) store_stage(cur ^ 1);
+    if (kt + 1 < nk) store_w(P ^ 1, wr[P ^ 1]);
+    if (kt + 2 < nk) load_x(kt + 2, xr[P]);
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) xc[s] = xn[s];
+  };
+  load_w(0, wr[0]);
+  if (nk > 1) load_w(1, wr[1]);
+  load_x(0, xr[0]);
+  if (nk > 1) load_x(1, xr[1]);
+  store_w(0, wr[0]);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(Ic<0>{}, kt);
+    if (kt + 1 < nk) step(Ic<1>{}, kt + 1);
   }
   if constexpr (KS > 1) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) red[wid][lane * FN + j] = acc[j];
+    for (int j = 0; j < FN; ++j) red[wid][lane * FN + j] = acc[0][j];
     __syncthreads();
     if (ks != 0) return;
 #pragma unroll
@@ -264,72 +280,74 @@ route_mfma_kernel(const bf16* __restrict__ x, const bf16* __restrict__ wsplit,
 #pragma unroll
         for (int i = 0; i < 4; ++i) sum[i] += o[i];
       }
-      acc[j] = sum;
+      acc[0][j] = sum;
     }
   }
 
-  // lane holds tokens t0 + (lane/16)*4 + i (i < 4), experts j*16 + lane%16
-  const int g = lane & 15;
+  // lane holds tokens t0 + 16 g + (lane/16)*4 + i (i < 4), experts j*16 + lane%16
+  const int gl = lane & 15;
   float bias[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int e = j * 16 + g;
+    const int e = j * 16 + gl;
     bias[j] = (e < E) ? b_gate[e] : 0.f;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + (lane >> 4) * 4 + i;
-    float v[FN];
+  for (int g = 0; g < TG; ++g)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) v[j] = acc[j][i] + bias[j];
-    if (logits_out != nullptr && t < T) {
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + g * 16 + (lane >> 4) * 4 + i;
+      float v[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int e = j * 16 + g;
-        if (e < E) logits_out[(size_t)t * E + e] = v[j];
-      }
-    }
-    unsigned taken = 0;
-    float sv[MOE_MAX_TOPK];
-    int si[MOE_MAX_TOPK];
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+      for (int j = 0; j < FN; ++j) v[j] = acc[g][j][i] + bias[j];
+      if (logits_out != nullptr && t < T) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int e = j * 16 + g;
-        if (e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
-          bv = v[j];
-          bi = e;
+        for (int j = 0; j < FN; ++j) {
+          const int e = j * 16 + gl;
+          if (e < E) logits_out[(size_t)t * E + e] = v[j];
         }
       }
+      unsigned taken = 0;
+      float sv[MOE_MAX_TOPK];
+      int si[MOE_MAX_TOPK];
+      for (int r = 0; r < k; ++r) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
 #pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
+        for (int j = 0; j < FN; ++j) {
+          const int e = j * 16 + gl;
+          if (e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
+            bv = v[j];
+            bi = e;
+          }
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+          const float ov = __shfl_xor(bv, o, 64);
+          const int oi = __shfl_xor(bi, o, 64);
+          if (better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        if ((bi & 15) == gl) taken |= 1u << (bi >> 4);
+        sv[r] = bv;
+        si[r] = bi;
+      }
+      if (gl == 0 && t < T) {
+        float pr[MOE_MAX_TOPK];
+        float sum = 0.f;
+        for (int r = 0; r < k; ++r) {
+          pr[r] = expf(sv[r] - sv[0]);
+          sum += pr[r];
+        }
+        const float inv = 1.0f / sum;
+        for (int r = 0; r < k; ++r) {
+          topk_idx[(size_t)t * k + r] = si[r];
+          topk_w[(size_t)t * k + r] = pr[r] * inv;
         }
       }
-      if ((bi & 15) == g) taken |= 1u << (bi >> 4);
-      sv[r] = bv;
-      si[r] = bi;
     }
-    if (g == 0 && t < T) {
-      float pr[MOE_MAX_TOPK];
-      float sum = 0.f;
-      for (int r = 0; r < k; ++r) {
-        pr[r] = expf(sv[r] - sv[0]);
-        sum += pr[r];
-      }
-      const float inv = 1.0f / sum;
-      for (int r = 0; r < k; ++r) {
-        topk_idx[(size_t)t * k + r] = si[r];
-        topk_w[(size_t)t * k + r] = pr[r] * inv;
-      }
-    }
-  }
 }
 
 int route_padded_experts(int E) {
@@ -338,42 +356,47 @@ int route_padded_experts(int E) {
   return ep;
 }
 
-size_t route_split_bytes(int d, int E) {
-  return (size_t)3 * route_padded_experts(E) * d * sizeof(bf16);
-}
-
 hipError_t launch_route(int act, const void* x, const float* w_gate, const float* b_gate,
                         const float* logits_in, float* logits_out, int32_t* topk_idx,
-                        float* topk_w, int T, int d, int E, int k, void* wsplit, hipStream_t s) {
+                        float* topk_w, int T, int d, int E, int k, hipStream_t s) {
   if (act == MOE_BF16 && logits_in == nullptr) {
     const int EP = route_padded_experts(E);
-    hipLaunchKernelGGL(split_gate_kernel, dim3((d + 31) / 32, (EP + 31) / 32), dim3(256), 0, s,
-                       w_gate, (bf16*)wsplit, d, E, EP);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    // split each stage's k range over KS wavefronts when the batch is too
-    // small to give every CU two workgroups of 64 tokens (LDS and d permitting)
-    int ks = 1;
+    // Token groups per wavefront (TG): as many as keep one workgroup per CU
+    // (and the registers unspilled); then, for batches too
+    // small for that, split each stage's k range over KS wavefronts (LDS
+    // and d permitting).
     const int bk = EP > 128 ? 32 : 64;
+    const int max_tg = EP <= 64 ? 4 : EP == 128 ? 2 : 1;  // more would spill
     const int max_ks = EP <= 32 ? 4 : EP == 64 ? 2 : 1;
-    while (ks < max_ks && (T + 64 / ks - 1) / (64 / ks) < 512 && d % (2 * ks * bk) == 0) ks *= 2;
-    dim3 grid((T + 64 / ks - 1) / (64 / ks)), block(256);
+    int tg = 1, ks = 1;
+    while (tg < max_tg && (T + 64 * 2 * tg - 1) / (64 * 2 * tg) >= 256) tg *= 2;
+    if (tg == 1)
+      while (ks < max_ks && (T + 64 / ks - 1) / (64 / ks) < 256 && d % (2 * ks * bk) == 0)
+        ks *= 2;
+    const int tpw = 64 / ks * tg;
+    dim3 grid((T + tpw - 1) / tpw), block(256);
     const bf16* xs = (const bf16*)x;
-    const bf16* wsp = (const bf16*)wsplit;
-#define MOE_ROUTE(EPV, KSV)                                                                 \
-  hipLaunchKernelGGL((route_mfma_kernel<EPV, KSV>), grid, block, 0, s, xs, wsp, b_gate,      \
-                     logits_out, topk_idx, topk_w, T, d, E, k)
-    switch (EP * 8 + ks) {
-      case 16 * 8 + 4: MOE_ROUTE(16, 4); break;
-      case 16 * 8 + 2: MOE_ROUTE(16, 2); break;
-      case 16 * 8 + 1: MOE_ROUTE(16, 1); break;
-      case 32 * 8 + 4: MOE_ROUTE(32, 4); break;
-      case 32 * 8 + 2: MOE_ROUTE(32, 2); break;
-      case 32 * 8 + 1: MOE_ROUTE(32, 1); break;
-      case 64 * 8 + 2: MOE_ROUTE(64, 2); break;
-      case 64 * 8 + 1: MOE_ROUTE(64, 1); break;
-      case 128 * 8 + 1: MOE_ROUTE(128, 1); break;
-      default: MOE_ROUTE(256, 1); break;
+#define MOE_ROUTE(EPV, KSV, TGV)                                                              \
+  hipLaunchKernelGGL((route_mfma_kernel<EPV, KSV, TGV>), grid, block, 0, s, xs, w_gate,        \
+                     b_gate, logits_out, topk_idx, topk_w, T, d, E, k)
+    switch ((EP * 8 + ks) * 8 + tg) {
+      case (16 * 8 + 4) * 8 + 1: MOE_ROUTE(16, 4, 1); break;
+      case (16 * 8 + 2) * 8 + 1: MOE_ROUTE(16, 2, 1); break;
+      case (16 * 8 + 1) * 8 + 1: MOE_ROUTE(16, 1, 1); break;
+      case (16 * 8 + 1) * 8 + 2: MOE_ROUTE(16, 1, 2); break;
+      case (16 * 8 + 1) * 8 + 4: MOE_ROUTE(16, 1, 4); break;
+      case (32 * 8 + 4) * 8 + 1: MOE_ROUTE(32, 4, 1); break;
+      case (32 * 8 + 2) * 8 + 1: MOE_ROUTE(32, 2, 1); break;
+      case (32 * 8 + 1) * 8 + 1: MOE_ROUTE(32, 1, 1); break;
+      case (32 * 8 + 1) * 8 + 2: MOE_ROUTE(32, 1, 2); break;
+      case (32 * 8 + 1) * 8 + 4: MOE_ROUTE(32, 1, 4); break;
+      case (64 * 8 + 2) * 8 + 1: MOE_ROUTE(64, 2, 1); break;
+      case (64 * 8 + 1) * 8 + 1: MOE_ROUTE(64, 1, 1); break;
+      case (64 * 8 + 1) * 8 + 2: MOE_ROUTE(64, 1, 2); break;
+      case (64 * 8 + 1) * 8 + 4: MOE_ROUTE(64, 1, 4); break;
+      case (128 * 8 + 1) * 8 + 1: MOE_ROUTE(128, 1, 1); break;
+      case (128 * 8 + 1) * 8 + 2: MOE_ROUTE(128, 1, 2); break;
+      default: MOE_ROUTE(256, 1, 1); break;
     }
 #undef MOE_ROUTE
     return hipGetLastError();
