@@ -751,7 +751,9 @@ __device__ __forceinline__ void store_partial(const TG& tg, float* dst) {
     }
 }
 
-template <int BM, int BN, bool B_K, int EPI, int MAP>
+// PERSIST (no split tail, p.partial null): one workgroup per CU walks its
+// XCD's tiles; otherwise one workgroup per tile or split unit.
+template <int BM, int BN, bool B_K, int EPI, int MAP, bool PERSIST>
 __global__ void __launch_bounds__(kGemmThreads)
 rows_gemm_kernel(RowsArgs p) {
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
@@ -763,52 +765,68 @@ rows_gemm_kernel(RowsArgs p) {
   const int NT = (p.N + BN - 1) / BN;
   const int total = MT * NT;
   const int nk = p.K / kBK;
-  const SplitPlan sp = split_plan(total, nk, p.cus, p.partial != nullptr);
-  const int bid = blockIdx.x;
-  int logical, seg = -1;
-  if (bid < sp.n_dp) {
-    // XCD-contiguous ranges: workgroup bid runs on XCD bid % 8.
-    const int x = bid % kXcds, i = bid / kXcds;
-    const int q = sp.n_dp / kXcds, rmd = sp.n_dp % kXcds;
-    logical = x * q + min(x, rmd) + i;
-  } else {
-    const int u = bid - sp.n_dp;  // split unit: tile n_dp + u / s, segment u % s
-    if (u >= sp.tail * sp.s) return;
-    logical = sp.n_dp + u / sp.s;
-    seg = u % sp.s;
-  }
-  const RowTile t = find_tile<BM, BN>(logical, NT, p.N, p.E, s_off, s_tstart, &s_expert);
-  // k range of this workgroup (whole K unless a segment of a split tile)
-  const int k0 = seg < 0 ? 0 : (seg * nk / sp.s) * kBK;
-  const int k1 = seg < 0 ? p.K : ((seg + 1) * nk / sp.s) * kBK;
-
   using TG = TileGemm<BM, BN, true, B_K>;
-  TG tg;
   const StageBufs L = tile_lds<TG>();
-  const bf16* Bm = p.B + (size_t)t.e * p.b_stride;
-  if constexpr (MAP == MAP_GATHER_A) {
-    static_assert(B_K, "gathered rows are a forward (NT) product");
-    tg.run(p.A + k0, p.K, t.rows, Bm + (size_t)t.n0 * p.K + k0, p.K, t.cols, k1 - k0, L,
-           nullptr, p.a_map + t.row0, p.a_src_rows);
-  } else {
-    const bf16* A = p.A + (size_t)t.row0 * p.K + k0;
-    if (B_K) {
-      tg.run(A, p.K, t.rows, Bm + (size_t)t.n0 * p.K + k0, p.K, t.cols, k1 - k0, L);
+  // one tile; seg >= 0: that K segment of a split tail tile, stored as a
+  // partial tile (unit u)
+  auto do_tile = [&](int logical, int seg, int s_parts, int u) {
+    const RowTile t = find_tile<BM, BN>(logical, NT, p.N, p.E, s_off, s_tstart, &s_expert);
+    const int k0 = seg < 0 ? 0 : (seg * nk / s_parts) * kBK;
+    const int k1 = seg < 0 ? p.K : ((seg + 1) * nk / s_parts) * kBK;
+    TG tg;
+    const bf16* Bm = p.B + (size_t)t.e * p.b_stride;
+    if constexpr (MAP == MAP_GATHER_A) {
+      static_assert(B_K, "gathered rows are a forward (NT) product");
+      tg.run(p.A + k0, p.K, t.rows, Bm + (size_t)t.n0 * p.K + k0, p.K, t.cols, k1 - k0, L,
+             nullptr, p.a_map + t.row0, p.a_src_rows);
     } else {
-      tg.run(A, p.K, t.rows, Bm + (size_t)k0 * p.N + t.n0, p.N, t.cols, k1 - k0, L);
+      const bf16* A = p.A + (size_t)t.row0 * p.K + k0;
+      if (B_K) {
+        tg.run(A, p.K, t.rows, Bm + (size_t)t.n0 * p.K + k0, p.K, t.cols, k1 - k0, L);
+      } else {
+        tg.run(A, p.K, t.rows, Bm + (size_t)k0 * p.N + t.n0, p.N, t.cols, k1 - k0, L);
+      }
     }
-  }
-  if (seg >= 0) {
-    store_partial(tg, p.partial + (size_t)(bid - sp.n_dp) * (BM * BN));
-    return;
-  }
-  if constexpr (MAP == MAP_SCATTER_C) {
-    store_tile<EPI>(tg, L, p.C + t.n0, p.N, t.rows, t.cols, nullptr, 0, nullptr,
-                    p.c_map + t.row0);
+    if (seg >= 0) {
+      store_partial(tg, p.partial + (size_t)u * (BM * BN));
+      return;
+    }
+    if constexpr (MAP == MAP_SCATTER_C) {
+      store_tile<EPI>(tg, L, p.C + t.n0, p.N, t.rows, t.cols, nullptr, 0, nullptr,
+                      p.c_map + t.row0);
+    } else {
+      store_tile<EPI>(tg, L, p.C + (size_t)t.row0 * p.N + t.n0, p.N, t.rows, t.cols,
+                      p.aux ? p.aux + (size_t)t.row0 * (p.N / 32) + t.n0 / 32 : nullptr, p.N / 32,
+                      p.bits_out ? p.bits_out + (size_t)t.row0 * (p.N / 8) + t.n0 / 8 : nullptr);
+    }
+  };
+  if constexpr (PERSIST) {
+    // Persistent: workgroup b (on XCD b % 8) runs every (workgroups on its
+    // XCD)-th tile of that XCD's contiguous range, so consecutive tiles of
+    // one CU need no new workgroup and one XCD's L2 serves one expert group.
+    const int G = gridDim.x, x = blockIdx.x % kXcds, w = blockIdx.x / kXcds;
+    const int per_x = G / kXcds + (x < G % kXcds ? 1 : 0);
+    const int q = total / kXcds, rmd = total % kXcds;
+    const int lo = x * q + min(x, rmd), hi = lo + q + (x < rmd ? 1 : 0);
+    for (int logical = lo + w; logical < hi; logical += per_x) {
+      do_tile(logical, -1, 1, 0);
+      // every wave has read its epilogue strip before the next tile's copies
+      // reuse the stage buffers (LDS only: the stores may stay in flight)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
   } else {
-    store_tile<EPI>(tg, L, p.C + (size_t)t.row0 * p.N + t.n0, p.N, t.rows, t.cols,
-                    p.aux ? p.aux + (size_t)t.row0 * (p.N / 32) + t.n0 / 32 : nullptr, p.N / 32,
-                    p.bits_out ? p.bits_out + (size_t)t.row0 * (p.N / 8) + t.n0 / 8 : nullptr);
+    const SplitPlan sp = split_plan(total, nk, p.cus, p.partial != nullptr);
+    const int bid = blockIdx.x;
+    if (bid < sp.n_dp) {
+      // XCD-contiguous ranges: workgroup bid runs on XCD bid % 8.
+      const int x = bid % kXcds, i = bid / kXcds;
+      const int q = sp.n_dp / kXcds, rmd = sp.n_dp % kXcds;
+      do_tile(x * q + min(x, rmd) + i, -1, 1, 0);
+    } else {
+      const int u = bid - sp.n_dp;  // split unit: tile n_dp + u / s, segment u % s
+      if (u >= sp.tail * sp.s) return;
+      do_tile(sp.n_dp + u / sp.s, u % sp.s, sp.s, u);
+    }
   }
 }
 
@@ -1042,13 +1060,16 @@ f32_wgrad_kernel(const float* __restrict__ X1, const float* __restrict__ X2, flo
 
 // Every kernel variant the launchers can pick, instantiated explicitly (so
 // each is emitted whatever order the launchers reference them in).
+#define MOE_ROWS_PERSIST(BM, BN, P)                                                            \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_NONE, P>(RowsArgs);     \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_NONE, P>(RowsArgs);    \
+  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_MASK, MAP_NONE, P>(RowsArgs);    \
+  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_STORE, MAP_NONE, P>(RowsArgs);   \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_GATHER_A, P>(RowsArgs); \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_SCATTER_C, P>(RowsArgs);
 #define MOE_ROWS_VARIANTS(BM, BN)                                                      \
-  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_NONE>(RowsArgs);       \
-  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_NONE>(RowsArgs);      \
-  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_MASK, MAP_NONE>(RowsArgs);      \
-  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_STORE, MAP_NONE>(RowsArgs);     \
-  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_GATHER_A>(RowsArgs);   \
-  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_SCATTER_C>(RowsArgs); \
+  MOE_ROWS_PERSIST(BM, BN, true)                                                               \
+  MOE_ROWS_PERSIST(BM, BN, false)                                                              \
   template __global__ void rows_fixup_kernel<BM, BN, EPI_RELU, MAP_NONE>(RowsArgs);            \
   template __global__ void rows_fixup_kernel<BM, BN, EPI_STORE, MAP_NONE>(RowsArgs);           \
   template __global__ void rows_fixup_kernel<BM, BN, EPI_MASK, MAP_NONE>(RowsArgs);            \
@@ -1066,6 +1087,7 @@ MOE_WGRAD_VARIANTS(256, 128)
 MOE_WGRAD_VARIANTS(128, 256)
 MOE_WGRAD_VARIANTS(128, 128)
 #undef MOE_ROWS_VARIANTS
+#undef MOE_ROWS_PERSIST
 #undef MOE_WGRAD_VARIANTS
 
 // ---------------------------------------------------------------------------
@@ -1143,10 +1165,16 @@ static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
   // tiles, plus up to kMaxSplitUnits segments replacing the split tail
   const long long mt_max = (S_max + BM - 1) / BM + p.E;
   const long long nt = (p.N + BN - 1) / BN;
-  const long long grid = mt_max * nt + (p.partial != nullptr ? kMaxSplitUnits : 0);
+  // without a split tail the kernel is persistent: one workgroup per CU
+  const long long grid = p.partial != nullptr ? mt_max * nt + kMaxSplitUnits
+                                              : std::min<long long>(mt_max * nt, p.cus);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI, MAP>), dim3((unsigned)grid),
-                     dim3(kGemmThreads), 0, s, p);
+  if (p.partial != nullptr)
+    hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI, MAP, false>), dim3((unsigned)grid),
+                       dim3(kGemmThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI, MAP, true>), dim3((unsigned)grid),
+                       dim3(kGemmThreads), 0, s, p);
   if (p.partial != nullptr) {
     MOE_TRY(hipGetLastError());
     hipLaunchKernelGGL((rows_fixup_kernel<BM, BN, EPI, MAP>),
