@@ -109,7 +109,8 @@ def summarize_traffic(args):
             # forward launches: K-contiguous weights, epilogue ReLU (FC1) or store
             # (FC2), packed rows; a split-tail fixup dispatched right after one
             # belongs to that launch
-            if re.search(GEMM_KERNEL + r"<\d+, \d+, true, [01], 0>", r["Kernel_Name"]):
+            if re.search(GEMM_KERNEL + r"<\d+, \d+, true, [01], 0, (?:true|false)>",
+                         r["Kernel_Name"]):
                 v = float(r["Counter_Value"])
                 if i + 1 < len(rows) and FIXUP_KERNEL in rows[i + 1]["Kernel_Name"]:
                     v += float(rows[i + 1]["Counter_Value"])
