@@ -122,8 +122,33 @@ ep_plan_kernel(int E, int R, int extra, const int32_t* __restrict__ offsets,
   }
   __syncthreads();
 
-  // 5. least-loaded placement: lane = rank
-  if (tid < 64) {
+  // 5. least-loaded placement.  Up to 16 ranks: one lane, loads in
+  // registers (a short scan per copy); more: lane = rank, wave argmin.
+  if (R <= 16) {
+    if (tid == 0) {
+      int load[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) load[q] = 0;
+      for (int j = 0; j < P; ++j) {
+        const int p = s_order[j];
+        int bq = 0, bl = load[0];
+#pragma unroll
+        for (int q = 1; q < 16; ++q)
+          if (q < R && load[q] < bl) {
+            bl = load[q];
+            bq = q;
+          }
+        const int rows = s_rows[p];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (q == bq) load[q] += rows;
+        replica_rank[p] = bq;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (q < R) rank_rows[q] = load[q];
+    }
+  } else if (tid < 64) {
     int load = lane < R ? 0 : 0x7fffffff;
     for (int j = 0; j < P; ++j) {
       const int p = s_order[j];
