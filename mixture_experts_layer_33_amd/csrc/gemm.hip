@@ -588,7 +588,8 @@ __device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, voi
       const int r = t * RPI + lane / CPR, c = (lane % CPR) * (16 / ES);
       const i32x4 v = *reinterpret_cast<const i32x4*>(strip + r * PITCH + c * ES);
       const int m = m0 + r, n = n0 + c;
-      if (m < rows && n < cols) {
+      const bool ok = m < rows && n < cols;
+      if (ok) {
         const size_t at = (size_t)cr[j * IT + t] * ldc + n;
         if constexpr (EPI == EPI_MASK) {
           const uint32_t keep = mw[j * IT + t] >> (n & 31);
@@ -600,15 +601,23 @@ __device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, voi
           *reinterpret_cast<i32x4*>(reinterpret_cast<bf16*>(C) + at) = o;
         } else {
           *reinterpret_cast<i32x4*>(reinterpret_cast<OutT*>(C) + at) = v;
-          if constexpr (EPI == EPI_RELU) {
-            if (bits_out != nullptr) {  // byte n/8 of row m: bit q <=> element n + q > 0
-              const bf16x8 hv = __builtin_bit_cast(bf16x8, v);
-              uint32_t b = 0;
+        }
+      }
+      if constexpr (EPI == EPI_RELU) {
+        if (bits_out != nullptr) {
+          // byte n/8 of row m: bit q <=> element n + q > 0.  Four consecutive
+          // lanes hold 32 consecutive columns of one row (CPR is a multiple
+          // of 4); the first of them stores the four bytes as one word.
+          static_assert(CPR % 4 == 0, "a lane quad stays in one row");
+          const bf16x8 hv = __builtin_bit_cast(bf16x8, v);
+          uint32_t b = 0;
 #pragma unroll
-              for (int q = 0; q < 8; ++q) b |= ((float)hv[q] > 0.f ? 1u : 0u) << q;
-              bits_out[(size_t)m * (ldc / 8) + n / 8] = (uint8_t)b;
-            }
-          }
+          for (int q = 0; q < 8; ++q) b |= ((float)hv[q] > 0.f ? 1u : 0u) << q;
+          const uint32_t b1 = __shfl_down(b, 1, 64), b2 = __shfl_down(b, 2, 64),
+                         b3 = __shfl_down(b, 3, 64);
+          if (ok && (lane & 3) == 0)
+            *reinterpret_cast<uint32_t*>(bits_out + (size_t)m * (ldc / 8) + n / 8) =
+                b | (b1 << 8) | (b2 << 16) | (b3 << 24);
         }
       }
     }
