@@ -57,6 +57,8 @@ def parse():
                    help="capacity priority (default: the workload's)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-reps", type=int, default=20)
+    p.add_argument("--cold-reps", type=int, default=20,
+                   help="repetitions of the cache-flushed forward / backward timings")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -253,6 +255,14 @@ def main():
     x, dy = up(inp["x"]), up(inp["dy"])
     w_gate, b_gate = up(inp["w_gate"], False), up(inp["b_gate"], False)
     w1, w2 = up(inp["w1"]), up(inp["w2"])
+    # a drifting workload cycles through its iterations' tokens, output
+    # gradients and gate biases (the weights stay fixed)
+    per_iter = [(x, dy, b_gate)]
+    for it in range(1, w.iters):
+        nxt = workloads.make_inputs(w, it, with_weights=False, with_dy=True)
+        per_iter.append((up(nxt["x"]), up(nxt["dy"]), up(nxt["b_gate"], False)))
+    if w.iters > 1:
+        log(f"{w.iters} drifting iterations resident")
     act = moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32
     layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, w.capacity_factor, act, window=w.window,
                      priority=w.priority)
@@ -262,8 +272,9 @@ def main():
     ev = []  # (before, after) moe_expert_ffn in each timed step
 
     def step(mark=None):
-        layer.route(x, w_gate, b_gate, logits_out=False, counts=False)
-        layer.permute(x)
+        xi, dyi, bi = per_iter[it_counter[0] % len(per_iter)]
+        layer.route(xi, w_gate, bi, logits_out=False, counts=False)
+        layer.permute(xi)
         if mark is not None:
             mark[0].record(stream)
         layer.expert_ffn(w1, w2)
@@ -271,7 +282,7 @@ def main():
             mark[1].record(stream)
         layer.combine()
         layer.popularity(it_counter[0])
-        layer.backward(dy, x, w_gate, w1, w2, dlogits=False)
+        layer.backward(dyi, xi, w_gate, w1, w2, dlogits=False)
         it_counter[0] += 1
 
     log(f"warmup {args.warmup} steps")
@@ -315,6 +326,9 @@ def main():
     t_bwd = time_it(lambda: layer.backward(dy, x, w_gate, w1, w2, dlogits=False), reps)
     t_ffn = time_it(lambda: layer.expert_ffn(w1, w2), reps)
     t_comb = time_it(lambda: layer.combine(), reps)
+    t_route = time_it(lambda: layer.route(x, w_gate, b_gate, logits_out=False, counts=False),
+                      reps)
+    t_perm = time_it(lambda: layer.permute(x), reps)
     # the gather/scatter-fused forward (same y, no packed token copy)
     t_fused = time_it(lambda: layer.forward_fused(x, w_gate, b_gate, w1, w2, logits_out=False),
                       reps)
@@ -354,6 +368,42 @@ def main():
         f"({achieved:.1f} TFLOP/s), combine {t_comb*1e3:.1f} us "
         f"({comb_bytes / (t_comb / 1e3) / 1e9:.0f} GB/s)")
 
+    # HBM-bound steps against their algorithmic bytes (route: E <= 16 only is
+    # HBM-bound; beyond, its MFMA work dominates)
+    sx = 2 if w.dtype == "bf16" else 4
+    hbm_bytes = {"route": w.T * w.d * sx + 4 * w.d * w.E + 8 * w.T * w.k,
+                 "permute": w.T * w.d * sx + s_kept * w.d * sx + 12 * w.T * w.k,
+                 "combine": s_kept * w.d * sx + w.T * w.d * sx + 8 * w.T * w.k}
+    hbm = {}
+    for name, t in (("route", t_route), ("permute", t_perm), ("combine", t_comb)):
+        gbs = hbm_bytes[name] / (t / 1e3) / 1e9
+        hbm[name] = {"ms": t, "bytes": hbm_bytes[name], "GB/s": gbs,
+                     "frac": gbs / PEAK_HBM_GBS}
+
+    # cold cache: 512 MiB written before each repetition (evicts the 256 MB
+    # last-level cache), median / p10 / p90 of the forward and the backward
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def cold(fn, reps=args.cold_reps):
+        ts = []
+        for r in range(reps):
+            flush.fill_(r & 255)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        q = np.percentile(ts, [10, 50, 90])
+        return {"median": float(q[1]), "p10": float(q[0]), "p90": float(q[2])}
+
+    cold_ms = {"forward": cold(lambda: layer.forward(x, w_gate, b_gate, w1, w2,
+                                                     logits_out=False)),
+               "backward": cold(lambda: layer.backward(dy, x, w_gate, w1, w2, dlogits=False))}
+    del flush
+    log(f"cold cache: forward {cold_ms['forward']['median']:.3f} ms, backward "
+        f"{cold_ms['backward']['median']:.3f} ms (medians)")
+
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
         b = torch.empty_like(a)
@@ -371,7 +421,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d_model": w.d, "d_ff": w.F, "E": w.E,
                    "k": w.k, "capacity_factor": w.capacity_factor,
                    "capacity_priority": w.priority,
-                   "step": "forward + popularity window + backward", "S_kept": s_kept},
+                   "step": "forward + popularity window + backward", "S_kept": s_kept,
+                   "iterations": w.iters},
         "roofline": {"bound": "mfma",
                      "kernel": "rows_gemm_kernel (grouped expert GEMM, FC1 and FC2 launches)",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
@@ -383,6 +434,8 @@ def main():
                      "cooccurrence_update": t_co, "predict_popularity": t_pred},
         "ep_plan": {"ranks": R_plan, "extra_copies": extra_plan,
                     "max_over_mean_rank_rows": plan_balance},
+        "hbm_parts": hbm,
+        "cold_ms": cold_ms,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (CPU reference) ...")
