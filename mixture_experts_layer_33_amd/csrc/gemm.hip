@@ -599,6 +599,10 @@ __device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, voi
             o[q] &= (int)(((keep >> (2 * q)) & 1u ? 0x0000ffffu : 0u) |
                           ((keep >> (2 * q + 1)) & 1u ? 0xffff0000u : 0u));
           *reinterpret_cast<i32x4*>(reinterpret_cast<bf16*>(C) + at) = o;
+        } else if constexpr (EPI == EPI_F32) {
+          // weight gradients are written once and not read back here:
+          // streaming stores keep them from evicting the operands
+          __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(reinterpret_cast<OutT*>(C) + at));
         } else {
           *reinterpret_cast<i32x4*>(reinterpret_cast<OutT*>(C) + at) = v;
         }
