@@ -20,7 +20,14 @@ cpu_baseline = the CPU reference on a bounded sample of the same workload
     python bench.py --summarize-traffic FETCH_CSV WRITE_CSV [--workload NAME]
 
 (no GPU) turns the counter files of two rocprofv3 --pmc runs of
-``bench.py --copy-calibration`` into that traffic summary.
+``bench.py --copy-calibration`` into that traffic summary, and
+
+    python bench.py --summarize-mfma COUNTER_CSV AGENT_CSV BENCH_JSON [--workload NAME]
+
+(no GPU) turns one rocprofv3 --pmc run of bench.py with the MFMA counters
+(SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE; its
+JSON line saved as BENCH_JSON) into the per-kernel MFMA utilization of the six
+expert GEMM launches of a step.
 """
 from __future__ import annotations
 
@@ -63,6 +70,8 @@ def parse():
                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the HBM traffic summary from two counter runs (no GPU)")
+    p.add_argument("--summarize-mfma", nargs=3, metavar=("COUNTER_CSV", "AGENT_CSV", "BENCH_JSON"),
+                   help="write the MFMA utilization summary from one counter run (no GPU)")
     p.add_argument("--command", default="",
                    help="the command lines that produced the counter files (recorded)")
     return p.parse_args()
@@ -172,6 +181,99 @@ def summarize_traffic(args):
     print(traffic_path(w.name))
 
 
+# the expert GEMM launches of one step: kernel-name pattern -> product
+GEMM_ROLES = [
+    (GEMM_KERNEL + r"<\d+, \d+, true, 0, 0, (?:true|false)>", "FC1 forward (ReLU)"),
+    (GEMM_KERNEL + r"<\d+, \d+, true, 1, 0, (?:true|false)>", "FC2 forward"),
+    (GEMM_KERNEL + r"<\d+, \d+, false, 2, 0, (?:true|false)>", "FC2 input gradient (masked)"),
+    (GEMM_KERNEL + r"<\d+, \d+, false, 1, 0, (?:true|false)>", "FC1 input gradient"),
+    (r"wgrad_kernel<\d+, \d+, false>", "FC2 weight gradient"),
+    (r"wgrad_kernel<\d+, \d+, true>", "FC1 weight gradient (+ gate)"),
+]
+
+
+def mfma_path(name):
+    return os.path.join(ROOT, "profiles", f"expert_gemms_{name}_mfma_utilization.md")
+
+
+def summarize_mfma(args):
+    """MFMA busy fraction, clock and executed flops per expert GEMM launch.
+
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over every SIMD; GRBM_GUI_ACTIVE over
+    the XCDs, so busy / (SIMDs * GRBM_GUI_ACTIVE / XCDs) is the fraction of
+    SIMD cycles the matrix pipe was busy, and GRBM_GUI_ACTIVE / XCDs over the
+    dispatch's duration the average clock.  SQ_INSTS_VALU_MFMA_MOPS_BF16
+    counts units of 512 flops."""
+    import csv
+    w = workloads.workloads()[args.workload]
+    cpath, apath, bpath = args.summarize_mfma
+    with open(apath, newline="") as f:
+        agents = [r for r in csv.DictReader(f) if r.get("Name", "").startswith("gfx")]
+    if not agents:
+        raise SystemExit(f"{apath}: no GPU agent")
+    simds, xcds = int(agents[0]["Simd_Count"]), int(agents[0]["Num_Xcc"])
+    disp = {}
+    with open(cpath, newline="") as f:
+        for r in csv.DictReader(f):
+            d = disp.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "c": {},
+                                                   "ns": int(r["End_Timestamp"]) -
+                                                   int(r["Start_Timestamp"])})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + \
+                float(r["Counter_Value"])
+    need = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
+    with open(bpath) as f:
+        cfg = json.loads(f.read().strip().splitlines()[-1])["config"]
+    if cfg["workload"] != w.name:
+        raise SystemExit(f"{bpath}: workload {cfg['workload']}, not {w.name}")
+    alg = 2.0 * cfg["d_model"] * cfg["d_ff"] * cfg["S_kept"]
+    rows = []
+    for pat, role in GEMM_ROLES:
+        ds = [d for d in disp.values() if re.search(pat, d["name"])]
+        if not ds:
+            continue
+        for d in ds:
+            missing = [c for c in need if c not in d["c"]]
+            if missing:
+                raise SystemExit(f"{cpath}: {d['name']} lacks {missing}")
+        n = len(ds)
+        us = sum(d["ns"] for d in ds) / n / 1e3
+        busy = sum(d["c"][need[0]] for d in ds) / n
+        flops = sum(d["c"][need[1]] for d in ds) / n * 512
+        gui = sum(d["c"][need[2]] for d in ds) / n
+        cyc = gui / xcds
+        rows.append({"role": role, "kernel": ds[0]["name"], "dispatches": n, "us": us,
+                     "busy": busy / (simds * cyc), "ghz": cyc / (us * 1e3),
+                     "flops": flops, "alg": alg})
+    if len(rows) != len(GEMM_ROLES):
+        raise SystemExit(f"{cpath}: found {[r['role'] for r in rows]}, expected all six products")
+    L = [f"# MFMA utilization of the expert GEMMs, {w.name}", "",
+         f"Workload: {w.description}.", "",
+         "Commands (run from the repository root on one MI355X):", "", "```",
+         args.command.strip() or "(not recorded)", "```", "",
+         f"Counters per dispatch, averaged over each kernel's dispatches ({simds} SIMDs, "
+         f"{xcds} XCDs).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x "
+         "GRBM_GUI_ACTIVE / XCDs): the share of SIMD cycles the matrix pipe was busy, at "
+         "the clock the dispatch ran at (GRBM_GUI_ACTIVE / XCDs / duration).  Executed "
+         "flops = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 (rows padded up to whole tiles "
+         f"included); algorithmic = 2 d F S_kept = {alg / 1e9:.1f} GFLOP per product.  "
+         "Durations are from the counter run (dispatches serialized), so they run a "
+         "little longer than in the timed steps.", "",
+         "| product | kernel | dispatches | µs | MFMA busy | clock GHz | executed / algorithmic "
+         "flops | algorithmic TFLOP/s |",
+         "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        L.append(f"| {r['role']} | `{r['kernel'][:70]}` | {r['dispatches']} | {r['us']:.1f} | "
+                 f"{r['busy']:.1%} | {r['ghz']:.2f} | {r['flops'] / r['alg']:.3f} | "
+                 f"{r['alg'] / (r['us'] * 1e-6) / 1e12:.0f} |")
+    L.append("")
+    L.append("mfma-json: " + json.dumps({"workload": w.name, "gemm_source_sha256":
+                                         gemm_source_hash(), "rows": rows}))
+    os.makedirs(os.path.dirname(mfma_path(w.name)), exist_ok=True)
+    with open(mfma_path(w.name), "w") as f:
+        f.write("\n".join(L) + "\n")
+    print(mfma_path(w.name))
+
+
 def load_traffic(name):
     """Bytes per launch from the committed counter summary, or None when there
     is none or the GEMM source has changed since it was taken."""
@@ -228,6 +330,9 @@ def main():
     args = parse()
     if args.summarize_traffic:
         summarize_traffic(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
