@@ -52,6 +52,14 @@ SMALL = {
     "skewed_split_tail": workloads.scaled(WL["skewed_zipf12"], T=700, d=512, F=2048),
     "uniform_cf100_split_tail": workloads.scaled(WL["uniform_cf125"], T=900, d=512, F=2048,
                                                  capacity_factor=1.0),
+    # more row tiles than CUs with K = d < 2048: the first GEMM and the masked
+    # input gradient walk several tiles per workgroup, each tile's last steps
+    # copying the next tile's first stages (1, 2, 3 and 16 k-steps of 64)
+    "uniform_walk_k64": workloads.scaled(WL["uniform_cf125"], T=4096, d=64, F=2048),
+    "uniform_walk_k128": workloads.scaled(WL["uniform_cf125"], T=4096, d=128, F=1024),
+    "uniform_walk_k192": workloads.scaled(WL["uniform_cf125"], T=3000, d=192, F=2048,
+                                          capacity_factor=1.0),
+    "skewed_walk_k1024": workloads.scaled(WL["skewed_zipf12"], T=2048, d=1024, F=2048),
 }
 
 
@@ -200,7 +208,7 @@ def test_forward_backward_end_to_end(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "skewed_zipf12", "uniform_cf050",
-                                  "skewed_split_tail"])
+                                  "skewed_split_tail", "uniform_walk_k128"])
 def test_bitwise_repeatable(name):
     w, inp, dev, layer = _setup(name)
     outs = []
