@@ -303,54 +303,13 @@ struct TileGemm {
   f32x16 acc[FN][FM];  // acc[i][j]: n-block i, m-block j
   float gacc[8];
   float gdb;
-  TA ta;  // operands whose stages the copies fill
-  TB tb;
-
-  // The next tile of a persistent walk (same K, lda and ldb; no row gather).
-  struct Next {
-    const bf16* A;
-    const bf16* B;
-    int a_rows, b_rows;
-    bool valid;
-  };
 
   // A: rows [0, a_rows) (K-contiguous) or columns [0, a_rows) over k rows
   // [0, K) (MN-contiguous); likewise B.  With a_idx (K-contiguous A only),
   // tile row r is row a_idx[r] of A ([a_src_rows][lda]).
-  __device__ __forceinline__ void prepare(const bf16* A, int lda, int a_rows, const bf16* B,
-                                          int ldb, int b_rows, int K,
-                                          const int32_t* a_idx = nullptr, int a_src_rows = 0) {
-    const int wid = (int)uniform(threadIdx.x >> 6);
-    if constexpr (A_K) {
-      if (a_idx != nullptr)
-        ta.init_gather(A, lda, a_rows, a_src_rows, a_idx, wid);
-      else
-        ta.init(A, lda, a_rows, K, wid);
-    } else {
-      ta.init(A, lda, a_rows, K, wid);
-    }
-    tb.init(B, ldb, b_rows, K, wid);
-  }
-
   __device__ void run(const bf16* A, int lda, int a_rows, const bf16* B, int ldb, int b_rows,
                       int K, const StageBufs& L, const float* gsel = nullptr,
                       const int32_t* a_idx = nullptr, int a_src_rows = 0) {
-    prepare(A, lda, a_rows, B, ldb, b_rows, K, a_idx, a_src_rows);
-    run_staged<0>(K, lda, ldb, L, gsel, Next{nullptr, nullptr, 0, 0, false}, false);
-  }
-
-  // Whether a tile of nk k-steps hands its last copies to the next tile: the
-  // next tile's first stages - 1 stages are then copied by its last steps.
-  __device__ static bool hands_over(int nk) { return nk >= kStages - 1; }
-
-  // The k loop on prepared operands, stage kt in LDS buffer (START + kt) %
-  // kStages.  With nx.valid (and hands_over(nk)), the copies past this
-  // tile's end fetch the first stages of nx instead (ta and tb switch to it
-  // once this tile's copies are all issued), so the next tile can start
-  // with `prefetched` at buffer (START + nk) % kStages.
-  template <int START>
-  __device__ __forceinline__ void run_staged(int K, int lda, int ldb, const StageBufs& L,
-                                             const float* gsel, const Next nx, bool prefetched) {
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -364,7 +323,17 @@ struct TileGemm {
     if (nk == 0) return;
     const int wid = (int)uniform(threadIdx.x >> 6);
     const int wm = wid >> 1, wn = wid & 1;
-    const bool pass_on = nx.valid && hands_over(nk);
+    TA ta;
+    TB tb;
+    if constexpr (A_K) {
+      if (a_idx != nullptr)
+        ta.init_gather(A, lda, a_rows, a_src_rows, a_idx, wid);
+      else
+        ta.init(A, lda, a_rows, K, wid);
+    } else {
+      ta.init(A, lda, a_rows, K, wid);
+    }
+    tb.init(B, ldb, b_rows, K, wid);
     uint32_t alo[TA::NLO], blo[TB::NLO];
     TA::lane_offsets(alo);
     TB::lane_offsets(blo);
@@ -444,18 +413,9 @@ struct TileGemm {
       char* const ad = L.a[SD];
       char* const bd = L.b[SD];
       const int kd = kt + kStages - 1;
-      bool live = kd < nk;
-      int kc = kd;  // k stage the copies fetch
-      if (!live && pass_on) {
-        if (kd == nk) {  // this tile's copies are all issued
-          ta.init(nx.A, lda, nx.a_rows, K, wid);
-          tb.init(nx.B, ldb, nx.b_rows, K, wid);
-        }
-        kc = kd - nk;
-        live = true;
-      }
+      const bool live = kd < nk;
       const Rsrc ra = ta.rsrc(live), rb = tb.rsrc(live);
-      const uint32_t sa = ta.soff(kc * kBK), sb = tb.soff(kc * kBK);
+      const uint32_t sa = ta.soff(kd * kBK), sb = tb.soff(kd * kBK);
       constexpr int NM = FM * FN;
       load_gate(kt);
       __builtin_amdgcn_sched_barrier(0);
@@ -491,37 +451,32 @@ struct TileGemm {
       sync();
     };
 
-    // prologue: stages 0 .. stages-2 in flight, wait for stage 0 (a
-    // prefetched tile's are in LDS already: the previous tile ended with a
-    // full wait and a barrier)
-    constexpr int S0 = START % kStages, S1 = (START + 1) % kStages, S2 = (START + 2) % kStages;
-    if (!prefetched) {
-      issue_all(0, L.a[S0], L.b[S0]);
-      if constexpr (kStages == 3) issue_all(1, L.a[S1], L.b[S1]);
-      sync();
-    }
-    step(Ic<S0>{}, Ic<1>{}, 0);
+    // prologue: stages 0 .. stages-2 in flight, wait for stage 0
+    issue_all(0, L.a[0], L.b[0]);
+    if constexpr (kStages == 3) issue_all(1, L.a[1], L.b[1]);
+    sync();
+    step(Ic<0>{}, Ic<1>{}, 0);
     // whole rounds of `stages` steps, then the rest (one loop exit)
     int kt = 1;
     for (; kt + kStages <= nk; kt += kStages) {
-      step(Ic<S1>{}, Ic<0>{}, kt);
+      step(Ic<1 % kStages>{}, Ic<0>{}, kt);
       if constexpr (kStages == 3) {
-        step(Ic<S2>{}, Ic<0>{}, kt + 1);
-        step(Ic<S0>{}, Ic<0>{}, kt + 2);
+        step(Ic<2>{}, Ic<0>{}, kt + 1);
+        step(Ic<0>{}, Ic<0>{}, kt + 2);
       } else {
-        step(Ic<S0>{}, Ic<0>{}, kt + 1);
+        step(Ic<0>{}, Ic<0>{}, kt + 1);
       }
     }
     if (kt < nk) {
-      step(Ic<S1>{}, Ic<0>{}, kt);
+      step(Ic<1 % kStages>{}, Ic<0>{}, kt);
       if constexpr (kStages == 3) {
-        if (kt + 1 < nk) step(Ic<S2>{}, Ic<0>{}, kt + 1);
+        if (kt + 1 < nk) step(Ic<2>{}, Ic<0>{}, kt + 1);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     mma(a1, b1);
-    // copies past the end (or the next tile's first stages) are still in
-    // flight: let them land before the caller reuses LDS
+    // copies past the end are still in flight: let them land before the
+    // caller reuses LDS
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
@@ -561,10 +516,8 @@ struct TileGemm {
 // of the tile (cols is a multiple of 8).  Call after run(); uses the stage
 // buffers.
 // With crow, tile row m is stored at row crow[m] of C (C then points at the
-// tile's first column of row 0).  FREE >= 0: the four strips share the A
-// and B buffers of stage FREE (the others may hold the next tile's first
-// stages); otherwise they take a[0], a[1], b[0] and b[1].
-template <int EPI, int FREE = -1, class TG>
+// tile's first column of row 0).
+template <int EPI, class TG>
 __device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, void* C, int ldc,
                                            int rows, int cols, const uint32_t* aux, int ld_aux,
                                            uint8_t* bits_out = nullptr,
@@ -579,17 +532,8 @@ __device__ __forceinline__ void store_tile(const TG& tg, const StageBufs& L, voi
                 "a wave's strip must fit in one stage buffer");
   const int lane = threadIdx.x & 63, wid = (int)uniform(threadIdx.x >> 6);
   const int wm = wid >> 1, wn = wid & 1;
-  char* strip;
-  if constexpr (FREE >= 0) {
-    constexpr int STRIP = 32 * PITCH;
-    constexpr int NA = TG::TA::kBytes / STRIP < 4 ? TG::TA::kBytes / STRIP : 4;
-    static_assert(FREE < TG::kStages, "a stage of the tile");
-    static_assert(NA + TG::TB::kBytes / STRIP >= 4, "four strips must fit in one stage");
-    strip = wid < NA ? L.a[FREE] + wid * STRIP : L.b[FREE] + (wid - NA) * STRIP;
-  } else {
-    // wave w stages in a[0], a[1], b[0], b[1]
-    strip = wid == 0 ? L.a[0] : wid == 1 ? L.a[1] : wid == 2 ? L.b[0] : L.b[1];
-  }
+  // wave w stages in a[0], a[1], b[0], b[1]
+  char* const strip = wid == 0 ? L.a[0] : wid == 1 ? L.a[1] : wid == 2 ? L.b[0] : L.b[1];
   const int n0 = wn * WN;
   constexpr int IT = 32 / RPI;  // row-phase iterations per strip
   uint32_t mw[EPI == EPI_MASK ? TG::FM * IT : 1];
@@ -828,7 +772,7 @@ rows_gemm_kernel(RowsArgs p) {
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int s_tstart[MOE_MAX_EXPERTS + 1];
   __shared__ int s_scratch[kGemmThreads / 64 + 1];
-  __shared__ int s_expert, s_expert_next;
+  __shared__ int s_expert;
   rows_scan<BM>(p, s_off, s_tstart, s_scratch);
   const int MT = s_tstart[p.E];
   const int NT = (p.N + BN - 1) / BN;
@@ -873,67 +817,14 @@ rows_gemm_kernel(RowsArgs p) {
     // Persistent: workgroup b (on XCD b % 8) runs every (workgroups on its
     // XCD)-th tile of that XCD's contiguous range, so consecutive tiles of
     // one CU need no new workgroup and one XCD's L2 serves one expert group.
-    // Each tile's last steps copy the first stages of the CU's next tile
-    // (the stage buffers rotate from tile to tile), so a tile starts without
-    // waiting for memory.
     const int G = gridDim.x, x = blockIdx.x % kXcds, w = blockIdx.x / kXcds;
     const int per_x = G / kXcds + (x < G % kXcds ? 1 : 0);
     const int q = total / kXcds, rmd = total % kXcds;
     const int lo = x * q + min(x, rmd), hi = lo + q + (x < rmd ? 1 : 0);
-    constexpr int KS = TG::kStages;
-    TG tg;
-    int start = 0;        // LDS buffer of the tile's stage 0
-    bool ready = false;   // its first stages were copied by the previous tile
     for (int logical = lo + w; logical < hi; logical += per_x) {
-      const RowTile t = find_tile<BM, BN>(logical, NT, p.N, p.E, s_off, s_tstart, &s_expert);
-      const bf16* Bm = p.B + (size_t)t.e * p.b_stride;
-      const bf16* A = p.A + (size_t)t.row0 * p.K;
-      const bf16* Bt = B_K ? Bm + (size_t)t.n0 * p.K : Bm + t.n0;
-      const int ldb = B_K ? p.K : p.N;
-      typename TG::Next nx{nullptr, nullptr, 0, 0, false};
-      if (MAP != MAP_GATHER_A && logical + per_x < hi) {
-        const RowTile u =
-            find_tile<BM, BN>(logical + per_x, NT, p.N, p.E, s_off, s_tstart, &s_expert_next);
-        const bf16* Bu = p.B + (size_t)u.e * p.b_stride;
-        nx = {p.A + (size_t)u.row0 * p.K, B_K ? Bu + (size_t)u.n0 * p.K : Bu + u.n0, u.rows,
-              u.cols, true};
-      }
-      if (!ready) {
-        if constexpr (MAP == MAP_GATHER_A)
-          tg.prepare(p.A, p.K, t.rows, Bt, ldb, t.cols, p.K, p.a_map + t.row0, p.a_src_rows);
-        else
-          tg.prepare(A, p.K, t.rows, Bt, ldb, t.cols, p.K);
-      }
-      if (start == 0)
-        tg.template run_staged<0>(p.K, p.K, ldb, L, nullptr, nx, ready);
-      else if (start == 1)
-        tg.template run_staged<1 % KS>(p.K, p.K, ldb, L, nullptr, nx, ready);
-      else
-        tg.template run_staged<2 % KS>(p.K, p.K, ldb, L, nullptr, nx, ready);
-      // the epilogue stages through the buffers only the last step read
-      auto store = [&](auto FREE_) {
-        constexpr int FREE = decltype(FREE_)::value;
-        if constexpr (MAP == MAP_SCATTER_C) {
-          store_tile<EPI, FREE>(tg, L, p.C + t.n0, p.N, t.rows, t.cols, nullptr, 0, nullptr,
-                                p.c_map + t.row0);
-        } else {
-          store_tile<EPI, FREE>(
-              tg, L, p.C + (size_t)t.row0 * p.N + t.n0, p.N, t.rows, t.cols,
-              p.aux ? p.aux + (size_t)t.row0 * (p.N / 32) + t.n0 / 32 : nullptr, p.N / 32,
-              p.bits_out ? p.bits_out + (size_t)t.row0 * (p.N / 8) + t.n0 / 8 : nullptr);
-        }
-      };
-      const int free_stage = (start + nk - 1) % KS;
-      if (free_stage == 0)
-        store(Ic<0>{});
-      else if (free_stage == 1)
-        store(Ic<1 % KS>{});
-      else
-        store(Ic<2 % KS>{});
-      ready = nx.valid && TG::hands_over(nk);
-      start = ready ? (start + nk) % KS : 0;
+      do_tile(logical, -1, 1, 0);
       // every wave has read its epilogue strip before the next tile's copies
-      // reuse that buffer (LDS only: the stores may stay in flight)
+      // reuse the stage buffers (LDS only: the stores may stay in flight)
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
   } else {

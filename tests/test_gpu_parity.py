@@ -53,8 +53,8 @@ SMALL = {
     "uniform_cf100_split_tail": workloads.scaled(WL["uniform_cf125"], T=900, d=512, F=2048,
                                                  capacity_factor=1.0),
     # more row tiles than CUs with K = d < 2048: the first GEMM and the masked
-    # input gradient walk several tiles per workgroup, each tile's last steps
-    # copying the next tile's first stages (1, 2, 3 and 16 k-steps of 64)
+    # input gradient walk several tiles per workgroup (1, 2, 3 and 16 k-steps
+    # of 64 per tile)
     "uniform_walk_k64": workloads.scaled(WL["uniform_cf125"], T=4096, d=64, F=2048),
     "uniform_walk_k128": workloads.scaled(WL["uniform_cf125"], T=4096, d=128, F=1024),
     "uniform_walk_k192": workloads.scaled(WL["uniform_cf125"], T=3000, d=192, F=2048,
