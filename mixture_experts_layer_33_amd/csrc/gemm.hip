@@ -57,10 +57,14 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0,
                                            (int)uniform(bytes), kRsrcWord3);
 }
+// Cache-policy field of a buffer load: the non-temporal (streaming) hint.
+constexpr int kNonTemporal = 2;
+
 // 16 bytes per lane from r at (voff + soff) to LDS at dst + 16 * lane
+template <int AUX = 0>
 __device__ __forceinline__ void copy16(Rsrc r, char* dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
-                                           voff, soff, 0, 0);
+                                           voff, soff, 0, AUX);
 }
 
 // ---------------------------------------------------------------------------
@@ -109,11 +113,11 @@ struct TileK {
   // resource and stage offset for the stage starting at k0 (dead: zeros)
   __device__ Rsrc rsrc(bool live) const { return make_rsrc(base, live ? bytes : 0u); }
   __device__ static uint32_t soff(int k0) { return (uint32_t)k0 * 2u; }
-  template <int Q, int NQ>
+  template <int Q, int NQ, int AUX = 0>
   __device__ void issue(Rsrc r, uint32_t so, char* stage, int wid) const {
 #pragma unroll
     for (int i = 0; i < N; ++i)
-      if (i % NQ == Q) copy16(r, stage + (i * 4 + wid) * 1024, off[i], so);
+      if (i % NQ == Q) copy16<AUX>(r, stage + (i * 4 + wid) * 1024, off[i], so);
   }
   static constexpr int issued(int Q, int NQ) {
     int n = 0;
@@ -173,11 +177,11 @@ struct TileMN {
   }
   __device__ Rsrc rsrc(bool live) const { return make_rsrc(base, live ? bytes : 0u); }
   __device__ uint32_t soff(int k0) const { return (uint32_t)k0 * ld2; }
-  template <int Q, int NQ>
+  template <int Q, int NQ, int AUX = 0>
   __device__ void issue(Rsrc r, uint32_t so, char* stage, int wid) const {
 #pragma unroll
     for (int i = 0; i < N; ++i)
-      if (i % NQ == Q) copy16(r, stage + (i * 4 + wid) * 1024, off[i], so);
+      if (i % NQ == Q) copy16<AUX>(r, stage + (i * 4 + wid) * 1024, off[i], so);
   }
   static constexpr int issued(int Q, int NQ) {
     int n = 0;
@@ -299,6 +303,10 @@ struct TileGemm {
   static constexpr int kStages =
       STAGES != 0 ? STAGES : (3 * kStageBytes + 4096 <= 160 * 1024 ? 3 : 2);
   static constexpr int kStageOps = TA::N + TB::N;
+  // In the row-grouped products (A K-contiguous) B is an expert's weight
+  // matrix: copied with the streaming hint, so that the weights, read once
+  // per launch, leave the caches to the activations later launches re-read.
+  static constexpr int kBAux = A_K ? kNonTemporal : 0;
   static constexpr int kReads = FM * TA::kReads + FN * TB::kReads;  // LDS reads per slice
   f32x16 acc[FN][FM];  // acc[i][j]: n-block i, m-block j
   float gacc[8];
@@ -357,7 +365,7 @@ struct TileGemm {
       const Rsrc ra = ta.rsrc(live), rb = tb.rsrc(live);
       const uint32_t sa = ta.soff(kt * kBK), sb = tb.soff(kt * kBK);
       ta.template issue<0, 1>(ra, sa, ad, wid);
-      tb.template issue<0, 1>(rb, sb, bd, wid);
+      tb.template issue<0, 1, kBAux>(rb, sb, bd, wid);
     };
     constexpr int kGateRows = GATE ? kBK * (BN / 8) / kGemmThreads : 1;
     float gv[kGateRows];
@@ -422,28 +430,28 @@ struct TileGemm {
       // region 0: slice 0 -> set 0; finish slice 3 of step kt-1 (set 1)
       load(as, bs, 0, a0, b0);
       ta.template issue<0, 4>(ra, sa, ad, wid);
-      tb.template issue<0, 4>(rb, sb, bd, wid);
+      tb.template issue<0, 4, kBAux>(rb, sb, bd, wid);
       if constexpr (!FIRST) mma(a1, b1);
       interleave<FIRST ? 0 : NM, kReads, TA::issued(0, 4) + TB::issued(0, 4)>();
       __builtin_amdgcn_sched_barrier(0);
       // region 1: slice 1 -> set 1; slice 0
       load(as, bs, 1, a1, b1);
       ta.template issue<1, 4>(ra, sa, ad, wid);
-      tb.template issue<1, 4>(rb, sb, bd, wid);
+      tb.template issue<1, 4, kBAux>(rb, sb, bd, wid);
       mma(a0, b0);
       interleave<NM, kReads, TA::issued(1, 4) + TB::issued(1, 4)>();
       __builtin_amdgcn_sched_barrier(0);
       // region 2: slice 2 -> set 0; slice 1
       load(as, bs, 2, a0, b0);
       ta.template issue<2, 4>(ra, sa, ad, wid);
-      tb.template issue<2, 4>(rb, sb, bd, wid);
+      tb.template issue<2, 4, kBAux>(rb, sb, bd, wid);
       mma(a1, b1);
       interleave<NM, kReads, TA::issued(2, 4) + TB::issued(2, 4)>();
       __builtin_amdgcn_sched_barrier(0);
       // region 3: slice 3 -> set 1; slice 2
       load(as, bs, 3, a1, b1);
       ta.template issue<3, 4>(ra, sa, ad, wid);
-      tb.template issue<3, 4>(rb, sb, bd, wid);
+      tb.template issue<3, 4, kBAux>(rb, sb, bd, wid);
       mma(a0, b0);
       interleave<NM, kReads, TA::issued(3, 4) + TB::issued(3, 4)>();
       __builtin_amdgcn_sched_barrier(0);
