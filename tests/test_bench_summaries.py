@@ -1,6 +1,7 @@
-"""bench.py's counter summaries on synthetic rocprofv3 CSV files (no GPU): the
-HBM-traffic scaling by the calibration copy, and the MFMA utilization
-arithmetic (busy share of SIMD cycles, clock, executed flops)."""
+"""bench.py without a GPU: its counter summaries on synthetic rocprofv3 CSV
+files (the HBM-traffic scaling by the calibration copy, the MFMA utilization
+arithmetic: busy share of SIMD cycles, clock, executed flops), and the
+refusal of more than one GPU."""
 import csv
 import json
 import types
@@ -124,3 +125,12 @@ def test_traffic_summary_scales_by_the_copy(tmp_path, out_root):
     assert rec["traffic_bytes_per_launch"] == pytest.approx((b1 + b2) / 2)
     assert rec["gemm_source_sha256"] == bench.gemm_source_hash()
     assert bench.load_traffic("uniform_cf125") == pytest.approx((b1 + b2) / 2)
+
+
+def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    line = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
