@@ -84,6 +84,11 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30
 
 
+def _rows_kernel(b_k, epi, row_map):
+    """rows_gemm_kernel<BM, BN, B_K, EPI, MAP, PERSIST, STREAM_B> of one product"""
+    return GEMM_KERNEL + rf"<\d+, \d+, {b_k}, {epi}, {row_map}, (?:true|false), (?:true|false)>"
+
+
 def traffic_path(name):
     return os.path.join(ROOT, "profiles", f"rows_gemm_{name}_hbm_traffic.md")
 
@@ -120,8 +125,7 @@ def summarize_traffic(args):
             # forward launches: K-contiguous weights, epilogue ReLU (FC1) or store
             # (FC2), packed rows; a split-tail fixup dispatched right after one
             # belongs to that launch
-            if re.search(GEMM_KERNEL + r"<\d+, \d+, true, [01], 0, (?:true|false)>",
-                         r["Kernel_Name"]):
+            if re.search(_rows_kernel("true", "[01]", 0), r["Kernel_Name"]):
                 v = float(r["Counter_Value"])
                 if i + 1 < len(rows) and FIXUP_KERNEL in rows[i + 1]["Kernel_Name"]:
                     v += float(rows[i + 1]["Counter_Value"])
@@ -183,10 +187,10 @@ def summarize_traffic(args):
 
 # the expert GEMM launches of one step: kernel-name pattern -> product
 GEMM_ROLES = [
-    (GEMM_KERNEL + r"<\d+, \d+, true, 0, 0, (?:true|false)>", "FC1 forward (ReLU)"),
-    (GEMM_KERNEL + r"<\d+, \d+, true, 1, 0, (?:true|false)>", "FC2 forward"),
-    (GEMM_KERNEL + r"<\d+, \d+, false, 2, 0, (?:true|false)>", "FC2 input gradient (masked)"),
-    (GEMM_KERNEL + r"<\d+, \d+, false, 1, 0, (?:true|false)>", "FC1 input gradient"),
+    (_rows_kernel("true", 0, 0), "FC1 forward (ReLU)"),
+    (_rows_kernel("true", 1, 0), "FC2 forward"),
+    (_rows_kernel("false", 2, 0), "FC2 input gradient (masked)"),
+    (_rows_kernel("false", 1, 0), "FC1 input gradient"),
     (r"wgrad_kernel<\d+, \d+, false>", "FC2 weight gradient"),
     (r"wgrad_kernel<\d+, \d+, true>", "FC1 weight gradient (+ gate)"),
 ]

@@ -292,7 +292,8 @@ __device__ __forceinline__ StageBufs tile_lds() {
 // g[n] = sum_k gsel[k] B(n, k) for its columns from the LDS stages (gacc: per
 // thread, 8 columns over its share of the rows) and sum_k gsel[k] (gdb);
 // see gate_reduce().
-template <int BM, int BN, bool A_K, bool B_K, bool GATE = false, int STAGES = 0>
+template <int BM, int BN, bool A_K, bool B_K, bool GATE = false, int STAGES = 0,
+          int B_AUX = 0>
 struct TileGemm {
   using TA = Tile<A_K, BM>;
   using TB = Tile<B_K, BN>;
@@ -303,10 +304,7 @@ struct TileGemm {
   static constexpr int kStages =
       STAGES != 0 ? STAGES : (3 * kStageBytes + 4096 <= 160 * 1024 ? 3 : 2);
   static constexpr int kStageOps = TA::N + TB::N;
-  // In the row-grouped products (A K-contiguous) B is an expert's weight
-  // matrix: copied with the streaming hint, so that the weights, read once
-  // per launch, leave the caches to the activations later launches re-read.
-  static constexpr int kBAux = A_K ? kNonTemporal : 0;
+  static constexpr int kBAux = B_AUX;  // cache policy of B's copies
   static constexpr int kReads = FM * TA::kReads + FN * TB::kReads;  // LDS reads per slice
   f32x16 acc[FN][FM];  // acc[i][j]: n-block i, m-block j
   float gacc[8];
@@ -724,6 +722,10 @@ struct RowTile {
 // groups of up to 8 m-tiles, n walked column by column inside a group.  A
 // group never mixes experts, so the workgroups running together on one XCD
 // share one expert's weights.
+// Row tiles of one expert run in groups of this many m-tiles, each group
+// sweeping the n-tiles, so concurrent tiles share the expert's weight tiles.
+constexpr int kGroupM = 8;
+
 template <int BM, int BN>
 __device__ __forceinline__ RowTile find_tile(int logical, int NT, int N, int E, const int* s_off,
                                              const int* s_tstart, int* s_expert) {
@@ -733,7 +735,7 @@ __device__ __forceinline__ RowTile find_tile(int logical, int NT, int N, int E, 
   __syncthreads();
   RowTile t;
   t.e = *s_expert;
-  constexpr int G = 8;
+  constexpr int G = kGroupM;
   const int mte = s_tstart[t.e + 1] - s_tstart[t.e];
   const int j = logical - s_tstart[t.e] * NT;
   const int grp = j / (G * NT);
@@ -773,8 +775,9 @@ __device__ __forceinline__ void store_partial(const TG& tg, float* dst) {
 }
 
 // PERSIST (no split tail, p.partial null): one workgroup per CU walks its
-// XCD's tiles; otherwise one workgroup per tile or split unit.
-template <int BM, int BN, bool B_K, int EPI, int MAP, bool PERSIST>
+// XCD's tiles; otherwise one workgroup per tile or split unit.  STREAM_B:
+// the expert weights (B) are copied with the non-temporal hint.
+template <int BM, int BN, bool B_K, int EPI, int MAP, bool PERSIST, bool STREAM_B>
 __global__ void __launch_bounds__(kGemmThreads)
 rows_gemm_kernel(RowsArgs p) {
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
@@ -786,7 +789,7 @@ rows_gemm_kernel(RowsArgs p) {
   const int NT = (p.N + BN - 1) / BN;
   const int total = MT * NT;
   const int nk = p.K / kBK;
-  using TG = TileGemm<BM, BN, true, B_K>;
+  using TG = TileGemm<BM, BN, true, B_K, false, 0, STREAM_B ? kNonTemporal : 0>;
   const StageBufs L = tile_lds<TG>();
   // one tile; seg >= 0: that K segment of a split tail tile, stored as a
   // partial tile (unit u)
@@ -1081,16 +1084,18 @@ f32_wgrad_kernel(const float* __restrict__ X1, const float* __restrict__ X2, flo
 
 // Every kernel variant the launchers can pick, instantiated explicitly (so
 // each is emitted whatever order the launchers reference them in).
-#define MOE_ROWS_PERSIST(BM, BN, P)                                                            \
-  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_NONE, P>(RowsArgs);     \
-  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_NONE, P>(RowsArgs);    \
-  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_MASK, MAP_NONE, P>(RowsArgs);    \
-  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_STORE, MAP_NONE, P>(RowsArgs);   \
-  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_GATHER_A, P>(RowsArgs); \
-  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_SCATTER_C, P>(RowsArgs);
+#define MOE_ROWS_PERSIST(BM, BN, P, W)                                                           \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_NONE, P, W>(RowsArgs);     \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_NONE, P, W>(RowsArgs);    \
+  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_MASK, MAP_NONE, P, W>(RowsArgs);    \
+  template __global__ void rows_gemm_kernel<BM, BN, false, EPI_STORE, MAP_NONE, P, W>(RowsArgs);   \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_RELU, MAP_GATHER_A, P, W>(RowsArgs); \
+  template __global__ void rows_gemm_kernel<BM, BN, true, EPI_STORE, MAP_SCATTER_C, P, W>(RowsArgs);
 #define MOE_ROWS_VARIANTS(BM, BN)                                                      \
-  MOE_ROWS_PERSIST(BM, BN, true)                                                               \
-  MOE_ROWS_PERSIST(BM, BN, false)                                                              \
+  MOE_ROWS_PERSIST(BM, BN, true, false)                                                        \
+  MOE_ROWS_PERSIST(BM, BN, false, false)                                                       \
+  MOE_ROWS_PERSIST(BM, BN, true, true)                                                         \
+  MOE_ROWS_PERSIST(BM, BN, false, true)                                                        \
   template __global__ void rows_fixup_kernel<BM, BN, EPI_RELU, MAP_NONE>(RowsArgs);            \
   template __global__ void rows_fixup_kernel<BM, BN, EPI_STORE, MAP_NONE>(RowsArgs);           \
   template __global__ void rows_fixup_kernel<BM, BN, EPI_MASK, MAP_NONE>(RowsArgs);            \
@@ -1179,7 +1184,7 @@ static Shape2 pick_tile(MT mt, int N) {
   return {128, 128};
 }
 
-template <int BM, int BN, bool B_K, int EPI, int MAP>
+template <int BM, int BN, bool B_K, int EPI, int MAP, bool STREAM_B>
 static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
   static_assert(BM * BN <= kMaxRowTileArea, "partial tiles must fit the workspace");
   // worst case: sum over experts of ceil(rows_e / BM) <= S_max / BM + E
@@ -1191,11 +1196,11 @@ static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
                                               : std::min<long long>(mt_max * nt, p.cus);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (p.partial != nullptr)
-    hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI, MAP, false>), dim3((unsigned)grid),
-                       dim3(kGemmThreads), 0, s, p);
+    hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI, MAP, false, STREAM_B>),
+                       dim3((unsigned)grid), dim3(kGemmThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI, MAP, true>), dim3((unsigned)grid),
-                       dim3(kGemmThreads), 0, s, p);
+    hipLaunchKernelGGL((rows_gemm_kernel<BM, BN, B_K, EPI, MAP, true, STREAM_B>),
+                       dim3((unsigned)grid), dim3(kGemmThreads), 0, s, p);
   if (p.partial != nullptr) {
     MOE_TRY(hipGetLastError());
     hipLaunchKernelGGL((rows_fixup_kernel<BM, BN, EPI, MAP>),
@@ -1204,10 +1209,22 @@ static hipError_t launch_rows_t(const RowsArgs& p, int S_max, hipStream_t s) {
   return hipGetLastError();
 }
 
+// max_rows: the most rows one expert can hold (its capacity).  When no
+// expert can need more than one group of m-tiles, the tiles that share a
+// weight tile all run together, so the weights are read once per launch and
+// are copied with the streaming hint (they then leave the caches to the
+// activations that later launches re-read).  With more m-tiles per expert
+// the later groups re-read the weight tiles, which must stay cached.
+template <bool B_K, int EPI, int MAP, int BM, int BN>
+static hipError_t launch_rows_s(const RowsArgs& p, int S_max, int max_rows, hipStream_t s) {
+  if ((max_rows + BM - 1) / BM <= kGroupM)
+    return launch_rows_t<BM, BN, B_K, EPI, MAP, true>(p, S_max, s);
+  return launch_rows_t<BM, BN, B_K, EPI, MAP, false>(p, S_max, s);
+}
 template <bool B_K, int EPI, int MAP = MAP_NONE>
 static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const uint32_t* aux,
                               const int32_t* offsets, long long b_stride, int K, int N, int E,
-                              int S_max, float* partial, hipStream_t s,
+                              int S_max, int max_rows, float* partial, hipStream_t s,
                               uint32_t* bits_out = nullptr, const int32_t* a_map = nullptr,
                               const int32_t* c_map = nullptr, int a_src_rows = 0) {
   const int cus = device_cus();
@@ -1215,9 +1232,11 @@ static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const uint3
   RowsArgs p{A, B, C, aux, reinterpret_cast<uint8_t*>(bits_out), offsets, a_map, c_map,
              partial, b_stride, K, N, E, a_src_rows, cus};
   const Shape2 t = pick_rows_tile(S_max, E, K, N, cus, partial != nullptr);
-  if (t.bm == 256 && t.bn == 128) return launch_rows_t<256, 128, B_K, EPI, MAP>(p, S_max, s);
-  if (t.bm == 128 && t.bn == 256) return launch_rows_t<128, 256, B_K, EPI, MAP>(p, S_max, s);
-  return launch_rows_t<128, 128, B_K, EPI, MAP>(p, S_max, s);
+  if (t.bm == 256 && t.bn == 128)
+    return launch_rows_s<B_K, EPI, MAP, 256, 128>(p, S_max, max_rows, s);
+  if (t.bm == 128 && t.bn == 256)
+    return launch_rows_s<B_K, EPI, MAP, 128, 256>(p, S_max, max_rows, s);
+  return launch_rows_s<B_K, EPI, MAP, 128, 128>(p, S_max, max_rows, s);
 }
 
 template <int BM, int BN, bool GATE>
@@ -1249,14 +1268,15 @@ size_t rows_partial_bytes(int act) {
 
 hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets, const void* w1,
                              const void* w2, void* h, void* out_perm, uint32_t* relu_bits,
-                             float* partial, int S_max, int d, int F, int E, hipStream_t s) {
+                             float* partial, int S_max, int max_rows, int d, int F, int E,
+                             hipStream_t s) {
   if (act == MOE_BF16) {
     MOE_TRY((launch_rows<true, EPI_RELU>((const bf16*)x_perm, (const bf16*)w1, (bf16*)h, nullptr,
-                                         offsets, (long long)F * d, d, F, E, S_max, partial, s,
-                                         relu_bits)));
+                                         offsets, (long long)F * d, d, F, E, S_max, max_rows,
+                                         partial, s, relu_bits)));
     MOE_TRY((launch_rows<true, EPI_STORE>((const bf16*)h, (const bf16*)w2, (bf16*)out_perm,
                                           nullptr, offsets, (long long)d * F, F, d, E, S_max,
-                                          partial, s)));
+                                          max_rows, partial, s)));
     return hipSuccess;
   }
   dim3 b(256);
@@ -1275,16 +1295,16 @@ hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets
 hipError_t launch_expert_fwd_fused(int act, const void* x, const int32_t* row_token, int T,
                                    const int32_t* offsets, const int32_t* row_slot,
                                    const void* w1, const void* w2, void* h, void* out_slot,
-                                   uint32_t* relu_bits, float* partial, int S_max, int d, int F,
-                                   int E, hipStream_t s) {
+                                   uint32_t* relu_bits, float* partial, int S_max, int max_rows,
+                                   int d, int F, int E, hipStream_t s) {
   if (act == MOE_BF16) {
     // FC1 reads token rows x[row_token[r]]; FC2 stores row r at slot row_slot[r]
     MOE_TRY((launch_rows<true, EPI_RELU, MAP_GATHER_A>(
         (const bf16*)x, (const bf16*)w1, (bf16*)h, nullptr, offsets, (long long)F * d, d, F, E,
-        S_max, partial, s, relu_bits, row_token, nullptr, T)));
+        S_max, max_rows, partial, s, relu_bits, row_token, nullptr, T)));
     MOE_TRY((launch_rows<true, EPI_STORE, MAP_SCATTER_C>(
         (const bf16*)h, (const bf16*)w2, (bf16*)out_slot, nullptr, offsets, (long long)d * F, F,
-        d, E, S_max, partial, s, nullptr, nullptr, row_slot, 0)));
+        d, E, S_max, max_rows, partial, s, nullptr, nullptr, row_slot, 0)));
     return hipSuccess;
   }
   dim3 b(256);
@@ -1304,8 +1324,8 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
                              const int32_t* offsets, const void* w1, const void* w2, void* dz,
                              void* dx_perm, float* dw1, float* dw2, const float* dsel_perm,
                              float* dw_gate, float* db_gate, const uint32_t* relu_bits_in,
-                             uint32_t* relu_bits_ws, float* partial, int S_max, int d, int F,
-                             int E, hipStream_t s) {
+                             uint32_t* relu_bits_ws, float* partial, int S_max, int max_rows,
+                             int d, int F, int E, hipStream_t s) {
   if (act == MOE_BF16) {
     // keep bits of the ReLU (unless the forward kept them), then
     // dz = (dO W2[e]) * [h > 0]: A = dO [rows][d], B = W2[e] as [K=d][N=F]
@@ -1320,7 +1340,7 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
     }
     MOE_TRY((launch_rows<false, EPI_MASK>((const bf16*)d_out, (const bf16*)w2, (bf16*)dz,
                                           relu_bits, offsets, (long long)d * F, d, F, E, S_max,
-                                          partial, s)));
+                                          max_rows, partial, s)));
     // dW2[e] = dO^T h  ([d][F])
     MOE_TRY((launch_wgrad<false>((const bf16*)d_out, (const bf16*)h, dw2, offsets, nullptr,
                                  nullptr, nullptr, d, F, E, s)));
@@ -1332,7 +1352,7 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
     // decode of dX that follows reads dx_perm while it is still cached.
     MOE_TRY((launch_rows<false, EPI_STORE>((const bf16*)dz, (const bf16*)w1, (bf16*)dx_perm,
                                            nullptr, offsets, (long long)F * d, F, d, E, S_max,
-                                           partial, s)));
+                                           max_rows, partial, s)));
     return hipSuccess;
   }
   dim3 b(256);

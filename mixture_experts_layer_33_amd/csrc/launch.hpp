@@ -71,19 +71,20 @@ hipError_t launch_popularity(int E, int window, int64_t iter, const int32_t* cou
 // Forward: h = ReLU(x_perm W1[e]^T), out = h W2[e]^T over each expert's rows.
 // relu_bits (bf16, optional): keep bits [h > 0] written by FC1's epilogue.
 // partial (bf16; rows_partial_bytes, or null): scratch for splitting the
-// last round of tiles along K.
+// last round of tiles along K.  max_rows: the most rows one expert can hold
+// (the capacity; T when dropless), which picks the weights' cache policy.
 size_t rows_partial_bytes(int act);
 hipError_t launch_expert_fwd(int act, const void* x_perm, const int32_t* offsets,
                              const void* w1, const void* w2, void* h, void* out_perm,
-                             uint32_t* relu_bits, float* partial, int S_max, int d, int F, int E,
-                             hipStream_t s);
+                             uint32_t* relu_bits, float* partial, int S_max, int max_rows, int d,
+                             int F, int E, hipStream_t s);
 // Gather/scatter-fused forward: FC1 reads token rows x[row_token[r]] ([T][d]);
 // FC2 stores packed row r at row row_slot[r] of out_slot ([T*k][d]).
 hipError_t launch_expert_fwd_fused(int act, const void* x, const int32_t* row_token, int T,
                                    const int32_t* offsets, const int32_t* row_slot,
                                    const void* w1, const void* w2, void* h, void* out_slot,
-                                   uint32_t* relu_bits, float* partial, int S_max, int d, int F,
-                                   int E, hipStream_t s);
+                                   uint32_t* relu_bits, float* partial, int S_max, int max_rows,
+                                   int d, int F, int E, hipStream_t s);
 // Backward GEMMs: dz = (dO W2[e]) * [h > 0]; dW2[e] = dO^T h;
 // dx_perm = dz W1[e]; dW1[e] = dz^T x_perm.
 // bf16 also folds dW_gate / db over the kept rows into the FC1 wgrad and
@@ -94,7 +95,7 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
                              void* dz, void* dx_perm, float* dw1, float* dw2,
                              const float* dsel_perm, float* dw_gate, float* db_gate,
                              const uint32_t* relu_bits_in, uint32_t* relu_bits_ws,
-                             float* partial, int S_max,
+                             float* partial, int S_max, int max_rows,
                              int d, int F, int E, hipStream_t s);
 
 // ---- expert-parallel dispatch plan (plan.hip)

@@ -281,7 +281,7 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x_perm, const int32_t*
   if ((st = check_ws(s, MOE_OP_EXPERT_FFN, ws, ws_bytes)) != MOE_OK) return st;
   float* partial = rows_partial_bytes(s->act_dtype) ? static_cast<float*>(ws) : nullptr;
   MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, relu_bits,
-                            partial, (int)slots(s), s->d_model, s->d_ff, s->E,
+                            partial, (int)slots(s), capacity_of(s), s->d_model, s->d_ff, s->E,
                             as_stream(stream)));
   return MOE_OK;
 }
@@ -321,8 +321,8 @@ moe_status moe_forward(const moe_shape* s, const void* x, const float* w_gate,
                         s->capacity_priority == MOE_PRIORITY_CHOICE, offsets, slot_row, row_token,
                         x_perm, stream_));
   MOE_HIP(launch_expert_fwd(s->act_dtype, x_perm, offsets, w1, w2, h, out_perm, relu_bits,
-                            fwd_partial(s, ws, false), (int)slots(s), s->d_model, s->d_ff, s->E,
-                            stream_));
+                            fwd_partial(s, ws, false), (int)slots(s), capacity_of(s), s->d_model,
+                            s->d_ff, s->E, stream_));
   MOE_HIP(launch_combine(s->act_dtype, out_perm, topk_w, slot_row, y, s->T, s->d_model, s->k,
                          stream_));
   return MOE_OK;
@@ -354,7 +354,7 @@ moe_status moe_forward_fused(const moe_shape* s, const void* x, const float* w_g
                        row_slot, stream_));
   MOE_HIP(launch_expert_fwd_fused(s->act_dtype, x, row_token, s->T, offsets, row_slot, w1, w2, h,
                                   out_slot, relu_bits, fwd_partial(s, ws, true), (int)slots(s),
-                                  s->d_model, s->d_ff, s->E, stream_));
+                                  capacity_of(s), s->d_model, s->d_ff, s->E, stream_));
   MOE_HIP(launch_combine(s->act_dtype, out_slot, topk_w, slot_row, y, s->T, s->d_model, s->k,
                          stream_, true));
   return MOE_OK;
@@ -385,7 +385,7 @@ moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const
   // db over the kept rows.
   MOE_HIP(launch_expert_bwd(act, bw.d_out, x_perm, h, offsets, w1, w2, bw.dz, bw.d_out, dw1, dw2,
                             bw.dsel_perm, dw_gate, db_gate, relu_bits, bw.relu_bits, bw.partial,
-                            (int)slots(s), s->d_model, s->d_ff, s->E, stream_));
+                            (int)slots(s), capacity_of(s), s->d_model, s->d_ff, s->E, stream_));
   if (act != MOE_BF16)
     MOE_HIP(launch_gate_rows(act, x_perm, bw.dsel_perm, offsets, dw_gate, db_gate, s->d_model,
                              s->E, stream_));

@@ -17,10 +17,10 @@ COUNTER_FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Proc
                   "End_Timestamp"]
 
 KERNELS = [
-    "void moe::rows_gemm_kernel<128, 256, true, 0, 0, true>(moe::RowsArgs)",
-    "void moe::rows_gemm_kernel<128, 256, true, 1, 0, false>(moe::RowsArgs)",
-    "void moe::rows_gemm_kernel<128, 256, false, 2, 0, true>(moe::RowsArgs)",
-    "void moe::rows_gemm_kernel<128, 256, false, 1, 0, false>(moe::RowsArgs)",
+    "void moe::rows_gemm_kernel<128, 256, true, 0, 0, true, true>(moe::RowsArgs)",
+    "void moe::rows_gemm_kernel<128, 256, true, 1, 0, false, true>(moe::RowsArgs)",
+    "void moe::rows_gemm_kernel<128, 256, false, 2, 0, true, false>(moe::RowsArgs)",
+    "void moe::rows_gemm_kernel<128, 256, false, 1, 0, false, false>(moe::RowsArgs)",
     "void moe::wgrad_kernel<256, 256, false>(moe::WgradArgs)",
     "void moe::wgrad_kernel<256, 256, true>(moe::WgradArgs)",
 ]
@@ -59,7 +59,7 @@ def test_mfma_summary_arithmetic(tmp_path, out_root):
              "SQ_INSTS_VALU_MFMA_MOPS_BF16": 0.0}
     # the gather/scatter-fused forward's launches must not be counted
     disp = [(k, ns, counters) for k in KERNELS for _ in range(2)]
-    disp.append(("void moe::rows_gemm_kernel<128, 256, true, 0, 1, true>(moe::RowsArgs)", 7, other))
+    disp.append(("void moe::rows_gemm_kernel<128, 256, true, 0, 1, true, true>(moe::RowsArgs)", 7, other))
     cpath, apath, bpath = tmp_path / "c.csv", tmp_path / "a.csv", tmp_path / "b.json"
     write_counters(cpath, disp)
     with open(apath, "w", newline="") as f:
