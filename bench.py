@@ -16,6 +16,9 @@ traffic      = HBM bytes per launch of that kernel from the FETCH_SIZE and
                WRITE_SIZE counters (profiles/rows_gemm_<workload>_hbm_traffic.md),
                or null when the GEMM source changed since they were taken
 cpu_baseline = the CPU reference on a bounded sample of the same workload
+warm_ms      = median, p10 and p90 of the timed steps and of single forward,
+               fused-forward and backward calls back to back; cold_ms the same
+               for forward and backward after writing 512 MiB (caches flushed)
 
     python bench.py --summarize-traffic FETCH_CSV WRITE_CSV [--workload NAME]
 
@@ -402,11 +405,13 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
         step(ev[i])
+        step_end[i].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -493,6 +498,33 @@ def main():
     # last-level cache), median / p10 / p90 of the forward and the backward
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
 
+    def pct(ts):
+        q = np.percentile(ts, [10, 50, 90])
+        return {"median": float(q[1]), "p10": float(q[0]), "p90": float(q[2])}
+
+    def warm(fn, reps=args.cold_reps):
+        """one call's time, calls back to back with caches warm"""
+        fn()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record(stream)
+        for r in range(reps):
+            fn()
+            evs[r + 1].record(stream)
+        torch.cuda.synchronize()
+        return pct([evs[r].elapsed_time(evs[r + 1]) for r in range(reps)])
+
+    step_ms = [(start if i == 0 else step_end[i - 1]).elapsed_time(step_end[i])
+               for i in range(args.steps)]
+    warm_ms = {"step": pct(step_ms),
+               "forward": warm(lambda: layer.forward(x, w_gate, b_gate, w1, w2, logits_out=False)),
+               "forward_fused": warm(lambda: layer.forward_fused(x, w_gate, b_gate, w1, w2,
+                                                                 logits_out=False)),
+               "backward": warm(lambda: layer.backward(dy, x, w_gate, w1, w2, dlogits=False))}
+    log(f"warm: step {warm_ms['step']['median']:.3f} ms, forward "
+        f"{warm_ms['forward']['median']:.3f} ms, backward {warm_ms['backward']['median']:.3f} ms "
+        f"(medians)")
+
     def cold(fn, reps=args.cold_reps):
         ts = []
         for r in range(reps):
@@ -503,8 +535,7 @@ def main():
             b.record(stream)
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b))
-        q = np.percentile(ts, [10, 50, 90])
-        return {"median": float(q[1]), "p10": float(q[0]), "p90": float(q[2])}
+        return pct(ts)
 
     cold_ms = {"forward": cold(lambda: layer.forward(x, w_gate, b_gate, w1, w2,
                                                      logits_out=False)),
@@ -544,6 +575,7 @@ def main():
         "ep_plan": {"ranks": R_plan, "extra_copies": extra_plan,
                     "max_over_mean_rank_rows": plan_balance},
         "hbm_parts": hbm,
+        "warm_ms": warm_ms,
         "cold_ms": cold_ms,
     }
     if not args.no_cpu_baseline:
