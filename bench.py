@@ -19,6 +19,8 @@ cpu_baseline = the CPU reference on a bounded sample of the same workload
 warm_ms      = median, p10 and p90 of the timed steps and of single forward,
                fused-forward and backward calls back to back; cold_ms the same
                for forward and backward after writing 512 MiB (caches flushed)
+probes       = a 1 GiB device copy and the vendor dense GEMM of the same flops,
+               measured in the same run, with the run's fractions of them
 
     python bench.py --summarize-traffic FETCH_CSV WRITE_CSV [--workload NAME]
 
@@ -544,6 +546,37 @@ def main():
     log(f"cold cache: forward {cold_ms['forward']['median']:.3f} ms, backward "
         f"{cold_ms['backward']['median']:.3f} ms (medians)")
 
+    # Probes measured on the same GPU in the same run: a plain 1 GiB device
+    # copy (read + write) and the vendor dense GEMM (torch.mm in bf16) with the
+    # first expert GEMM's flops (all kept rows times one expert's weights); the
+    # roofline and the HBM-bound steps are also given as fractions of them.
+    def probe_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    copy_gbs = 2.0 * (1 << 30) / (probe_ms(lambda: dst.copy_(src)) * 1e-3) / 1e9
+    del src, dst
+    probes = {"copy_1GiB_GB/s": copy_gbs,
+              "hbm_parts_frac_of_copy": {k: v["GB/s"] / copy_gbs for k, v in hbm.items()}}
+    if w.dtype == "bf16":
+        pa = torch.randn(s_kept, w.d, device="cuda").to(torch.bfloat16)
+        pb = (torch.randn(w.d, w.F, device="cuda") * 0.02).to(torch.bfloat16)
+        mm_tflops = flops_launch / (probe_ms(lambda: torch.mm(pa, pb)) * 1e-3) / 1e12
+        probes.update({"dense_gemm_shape": [s_kept, w.d, w.F], "dense_gemm_TFLOP/s": mm_tflops,
+                       "roofline_frac_of_dense_gemm": achieved / mm_tflops})
+        del pa, pb
+    log(f"probes: copy {copy_gbs:.0f} GB/s, dense GEMM "
+        f"{probes.get('dense_gemm_TFLOP/s', float('nan')):.0f} TFLOP/s")
+
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
         b = torch.empty_like(a)
@@ -577,6 +610,7 @@ def main():
         "hbm_parts": hbm,
         "warm_ms": warm_ms,
         "cold_ms": cold_ms,
+        "probes": probes,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (CPU reference) ...")
