@@ -60,6 +60,11 @@ SMALL = {
     "uniform_walk_k192": workloads.scaled(WL["uniform_cf125"], T=3000, d=192, F=2048,
                                           capacity_factor=1.0),
     "skewed_walk_k1024": workloads.scaled(WL["skewed_zipf12"], T=2048, d=1024, F=2048),
+    # tile shapes the cases above do not reach: 256 x 128 row tiles in the
+    # persistent walk (every product), and 128 x 256 persistent tiles next to
+    # 128 x 128 tiles with a split tail, all with the weights read plainly
+    "mixtral_tiles_256x128": workloads.scaled(WL["mixtral_shaped"], T=16384, d=128, F=128),
+    "skewed_tiles_mixed": workloads.scaled(WL["skewed_zipf12"], T=8192, d=256, F=2048),
 }
 
 
