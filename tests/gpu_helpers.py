@@ -54,6 +54,33 @@ def assert_close_per_expert(gpu, ref, tol, what=""):
             assert_close(gpu[e], ref[e], tol, f"{what}[{e}]")
 
 
+def relu_kink_flips(h_gpu, h_ref, x_perm_ref, w1, rows_gpu, rows_ref, experts):
+    """ReLU mask disagreements between the two sides' stored h.
+
+    Each side masks the FC2 input gradient with its own h > 0.  A
+    pre-activation within float32 rounding of zero can be kept by one side
+    (float64 sum slightly positive) and not by the other (float32 sum zero or
+    negative): that flips one element of dz, hence one row of FC1's weight
+    gradient and one token's dX.  Every disagreement must be such a near-kink:
+    |z| within the float32 summation bound (d + 2) * 2^-23 * sum_i |x_i w_i|.
+    Returns the flipped (expert, F index) pairs and the reference rows."""
+    w1 = np.asarray(w1, dtype=np.float64)
+    pairs, rows = set(), []
+    for e in experts:
+        (ag, bg), (ar, br) = rows_gpu[e], rows_ref[e]
+        assert bg - ag == br - ar, f"expert {e}: row counts differ"
+        flip = (h_gpu[ag:bg] > 0) != (h_ref[ar:br] > 0)
+        for i, c in zip(*np.nonzero(flip)):
+            xr = np.asarray(x_perm_ref[ar + i], dtype=np.float64)
+            terms = xr * w1[e, c]
+            bound = (xr.size + 2) * 2.0 ** -23 * np.abs(terms).sum()
+            assert abs(terms.sum()) <= bound, (
+                f"ReLU mask differs away from a kink: expert {e} row {ar + i} column {c}")
+            pairs.add((int(e), int(c)))
+            rows.append(int(ar + i))
+    return pairs, rows
+
+
 def make_case(w: workloads.Workload, it: int = 0, with_dy: bool = True):
     inp = workloads.make_inputs(w, it, with_weights=True, with_dy=with_dy)
     return inp

@@ -58,7 +58,7 @@ def run_case(w, b_override=None):
 def test_edge_end_to_end(name):
     w = EDGES[name]
     inp, layer, fwd, bwd = run_case(w)
-    mism = compare_end_to_end(w, layer, fwd, bwd)
+    mism = compare_end_to_end(w, layer, fwd, bwd, inp["w1"])
     assert mism.size == 0
     if name.startswith("heavy_drops") or name.endswith("_choice"):
         assert fwd["drops"] > 0
@@ -75,7 +75,7 @@ def test_empty_experts_get_zero_weight_gradients():
     b[::3] = -1e4  # experts 0, 3, 6, 9 are never chosen
     inp, layer, fwd, bwd = run_case(w, b)
     assert (fwd["counts_raw"][::3] == 0).all()
-    mism = compare_end_to_end(w, layer, fwd, bwd)
+    mism = compare_end_to_end(w, layer, fwd, bwd, inp["w1"])
     assert mism.size == 0
     dw1, dw2 = down(layer.dw1), down(layer.dw2)
     assert not np.any(dw1[::3]) and not np.any(dw2[::3])
