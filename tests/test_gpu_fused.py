@@ -40,6 +40,9 @@ CASES = {
                                            capacity_factor=1.0),
     "mixtral_shaped": workloads.scaled(WL["mixtral_shaped"], T=1200, d=256, F=448),
     "fine_grained": workloads.scaled(WL["fine_grained"], T=2100, d=256, F=128),
+    # K = d = F = 2048: the gathered FC1 and the scattered FC2 both split
+    # their last round of tiles along K
+    "skewed_split_both": workloads.scaled(WL["skewed_zipf12"], T=700, d=2048, F=2048),
 }
 NAMES = ("y", "logits", "topk_idx", "topk_w", "counts_raw", "counts_kept", "offsets",
          "slot_row", "row_token", "h", "relu_bits")
