@@ -89,6 +89,38 @@ def test_router_logits(name):
     assert_close(down(layer.logits), ref, 1e-5, "logits")
 
 
+# (T, d, E, k) reaching each MFMA router launch shape (padded E, k-split over
+# wavefronts, 16-token groups per wavefront) that the scaled workloads do not
+ROUTER_SHAPES = {
+    "E16_tg2": (32768, 64, 16, 2),
+    "E16_tg4": (65536, 64, 16, 2),
+    "E32_ks1": (20000, 64, 32, 2),
+    "E32_tg2": (32768, 64, 32, 2),
+    "E32_tg4": (65536, 64, 32, 4),
+    "E64_ks2": (4000, 128, 64, 2),
+    "E64_ks1": (20000, 64, 64, 1),
+    "E64_tg2": (32768, 64, 64, 2),
+    "E48_tg4": (65536, 64, 48, 3),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTER_SHAPES))
+def test_router_launch_shapes(name):
+    """Logits against the reference, and the kernel's own top-k and weights
+    against the reference's top-k of those same float32 logits."""
+    T, d, E, k = ROUTER_SHAPES[name]
+    w = workloads.scaled(WL["skewed_zipf12"], T=T, d=d, F=64, E=E, k=k)
+    inp = workloads.make_inputs(w, 0, with_weights=False)
+    layer = MoeLayer(T, d, 64, E, k, 0.0, act_code("bf16"), backward=False)
+    layer.route(up(inp["x"], "bf16"), up(inp["w_gate"]), up(inp["b_gate"]))
+    torch.cuda.synchronize()
+    L = down(layer.logits)
+    assert_close(L, orc.router_logits(inp["x"], inp["w_gate"], inp["b_gate"]), 1e-5, "logits")
+    idx, wt = orc.topk_gate(L, k)
+    np.testing.assert_array_equal(down(layer.topk_idx), idx)
+    assert_close(down(layer.topk_w), wt, 1e-5, "topk_w")
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_route_bitexact_on_shared_logits(name):
     w, inp, dev, layer = _setup(name)
