@@ -68,6 +68,9 @@ SMALL = {
     "skewed_tiles_mixed": workloads.scaled(WL["skewed_zipf12"], T=8192, d=256, F=2048),
     # narrow d, wide F: FC1's weight gradient takes 128 x 256 tiles
     "mixtral_wgrad_128x256": workloads.scaled(WL["mixtral_shaped"], T=2048, d=128, F=8192),
+    # K = d = 2048: FC1 (ReLU and keep bits) and the masked input gradient
+    # split their last round along K, so their fixups apply those epilogues
+    "skewed_split_fc1": workloads.scaled(WL["skewed_zipf12"], T=700, d=2048, F=512),
 }
 
 
@@ -305,7 +308,7 @@ def test_forward_equals_its_entry_points(name):
         assert torch.equal(a, b), n
 
 
-@pytest.mark.parametrize("name", ["skewed_zipf12", "uniform_cf050"])
+@pytest.mark.parametrize("name", ["skewed_zipf12", "uniform_cf050", "skewed_split_fc1"])
 def test_forward_relu_bits_and_backward_with_or_without_them(name):
     """The keep bits the forward writes are exactly [h > 0] over the kept
     rows, and the backward gives bit-for-bit the same results whether it is
