@@ -717,15 +717,15 @@ __device__ __forceinline__ void rows_scan(const RowsArgs& p, int* s_off, int* s_
 struct RowTile {
   int e, row0, rows, n0, cols;
 };
-// Tile `logical` (whole block, uniform): expert by expert (tiles of expert e
-// are logical [s_tstart[e] * NT, s_tstart[e+1] * NT)); inside an expert,
-// groups of up to 8 m-tiles, n walked column by column inside a group.  A
-// group never mixes experts, so the workgroups running together on one XCD
-// share one expert's weights.
 // Row tiles of one expert run in groups of this many m-tiles, each group
 // sweeping the n-tiles, so concurrent tiles share the expert's weight tiles.
 constexpr int kGroupM = 8;
 
+// Tile `logical` (whole block, uniform): expert by expert (tiles of expert e
+// are logical [s_tstart[e] * NT, s_tstart[e+1] * NT)); inside an expert,
+// groups of up to kGroupM m-tiles, n walked column by column inside a group.
+// A group never mixes experts, so the workgroups running together on one XCD
+// share one expert's weights.
 template <int BM, int BN>
 __device__ __forceinline__ RowTile find_tile(int logical, int NT, int N, int E, const int* s_off,
                                              const int* s_tstart, int* s_expert) {
