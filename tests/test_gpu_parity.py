@@ -31,6 +31,8 @@ WL = workloads.workloads()
 # tiles, F not a multiple of the 128-column GEMM tiles
 SMALL = {
     "tiny_fp32": WL["tiny_fp32"],
+    # float32 throughout at a size that spans many row blocks, with drops
+    "fp32_cf100": workloads.scaled(WL["tiny_fp32"], T=1000, d=128, F=320, capacity_factor=1.0),
     "uniform_cf125": workloads.scaled(WL["uniform_cf125"], T=1000, d=256, F=320),
     "uniform_cf100": workloads.scaled(WL["uniform_cf125"], T=1000, d=256, F=320,
                                       capacity_factor=1.0),
