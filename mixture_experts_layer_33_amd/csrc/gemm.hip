@@ -282,8 +282,9 @@ __device__ __forceinline__ StageBufs tile_lds() {
 // Pipeline: 3 LDS stages (2 where 3 do not fit), one barrier per 64-deep k
 // step.  Step kt reads stage kt in four 16-deep slices, software-pipelined
 // over two register sets, and copies stage kt + stages - 1 into the buffer
-// stage kt - 1 used; the copies and the reads of the next slice are spread
-// between the MFMAs.  The last slice's MFMAs run after the barrier, covering
+// stage kt - 1 used; the copies (all at the step's start with two stages)
+// and the reads of the next slice are spread between the MFMAs.  The last
+// slice's MFMAs run after the barrier, covering
 // the latency of the first reads of the next stage.  Every step issues a full
 // stage of copies (past the end of K they are out of range and read nothing),
 // so a wave's outstanding-copy count is the same at every barrier.
@@ -425,33 +426,36 @@ struct TileGemm {
       constexpr int NM = FM * FN;
       load_gate(kt);
       __builtin_amdgcn_sched_barrier(0);
-      // region 0: slice 0 -> set 0; finish slice 3 of step kt-1 (set 1)
+      // region 0: slice 0 -> set 0; finish slice 3 of step kt-1 (set 1).
+      // With two stages the next stage must land within this step, so all of
+      // its copies go out here; with three they are spread over the regions.
+      constexpr int NQ = kStages == 2 ? 1 : 4;
       load(as, bs, 0, a0, b0);
-      ta.template issue<0, 4>(ra, sa, ad, wid);
-      tb.template issue<0, 4, kBAux>(rb, sb, bd, wid);
+      ta.template issue<0, NQ>(ra, sa, ad, wid);
+      tb.template issue<0, NQ, kBAux>(rb, sb, bd, wid);
       if constexpr (!FIRST) mma(a1, b1);
-      interleave<FIRST ? 0 : NM, kReads, TA::issued(0, 4) + TB::issued(0, 4)>();
+      interleave<FIRST ? 0 : NM, kReads, TA::issued(0, NQ) + TB::issued(0, NQ)>();
       __builtin_amdgcn_sched_barrier(0);
       // region 1: slice 1 -> set 1; slice 0
       load(as, bs, 1, a1, b1);
-      ta.template issue<1, 4>(ra, sa, ad, wid);
-      tb.template issue<1, 4, kBAux>(rb, sb, bd, wid);
+      ta.template issue<1, NQ>(ra, sa, ad, wid);
+      tb.template issue<1, NQ, kBAux>(rb, sb, bd, wid);
       mma(a0, b0);
-      interleave<NM, kReads, TA::issued(1, 4) + TB::issued(1, 4)>();
+      interleave<NM, kReads, TA::issued(1, NQ) + TB::issued(1, NQ)>();
       __builtin_amdgcn_sched_barrier(0);
       // region 2: slice 2 -> set 0; slice 1
       load(as, bs, 2, a0, b0);
-      ta.template issue<2, 4>(ra, sa, ad, wid);
-      tb.template issue<2, 4, kBAux>(rb, sb, bd, wid);
+      ta.template issue<2, NQ>(ra, sa, ad, wid);
+      tb.template issue<2, NQ, kBAux>(rb, sb, bd, wid);
       mma(a1, b1);
-      interleave<NM, kReads, TA::issued(2, 4) + TB::issued(2, 4)>();
+      interleave<NM, kReads, TA::issued(2, NQ) + TB::issued(2, NQ)>();
       __builtin_amdgcn_sched_barrier(0);
       // region 3: slice 3 -> set 1; slice 2
       load(as, bs, 3, a1, b1);
-      ta.template issue<3, 4>(ra, sa, ad, wid);
-      tb.template issue<3, 4, kBAux>(rb, sb, bd, wid);
+      ta.template issue<3, NQ>(ra, sa, ad, wid);
+      tb.template issue<3, NQ, kBAux>(rb, sb, bd, wid);
       mma(a0, b0);
-      interleave<NM, kReads, TA::issued(3, 4) + TB::issued(3, 4)>();
+      interleave<NM, kReads, TA::issued(3, NQ) + TB::issued(3, NQ)>();
       __builtin_amdgcn_sched_barrier(0);
       gate_stage(bs);
       sync();
