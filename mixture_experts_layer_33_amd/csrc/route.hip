@@ -9,6 +9,8 @@
 // passes the logits, a float32 FMA kernel with W_gate staged through LDS.  In
 // both, each token's logits sit in one 16-lane group, which selects the top k
 // by k rounds of a 16-lane (value, index) max reduction.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -140,6 +142,15 @@ __device__ __forceinline__ void split3(float v, bf16& hi, bf16& mid, bf16& lo) {
   lo = (bf16)(r1 - (float)mid);
 }
 
+// f(Ic<P>{}) for P = P0 .. N - 1, unrolled at compile time
+template <int P0, int N, class F>
+__device__ __forceinline__ void unroll_stages(F&& f) {
+  if constexpr (P0 < N) {
+    f(Ic<P0>{});
+    unroll_stages<P0 + 1, N>(f);
+  }
+}
+
 // LDS row of SW bf16 (SW/8 16-byte chunks), chunks XOR-swizzled by the low
 // row bits so that the 16 rows of an MFMA operand read fall in different
 // banks.
@@ -154,10 +165,12 @@ __device__ __forceinline__ int rswz(int row, int kc) {
 // the k range of every LDS stage between them, their partial logits summed
 // in LDS in a fixed order, so a workgroup covers 64 TG / KS tokens (KS > 1
 // gives small batches enough workgroups; TG > 1 reuses each staged W_gate
-// slice for more tokens when experts are many).  Loads run two stages ahead:
-// W_gate through registers into LDS (split on the way), x fragments straight
-// into registers.
-template <int EP, int KS, int TG>
+// slice for more tokens when experts are many).  Loads run D stages ahead, in
+// D register sets: W_gate through registers into LDS (split on the way, two
+// LDS buffers), x fragments straight into registers.  With few experts each
+// stage holds little work, so the kernel is bound by how many bytes each CU
+// keeps in flight: D sets the depth of that queue.
+template <int EP, int KS, int TG, int D, int UW>
 __global__ void __launch_bounds__(256)
 route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
                   const float* __restrict__ b_gate, float* __restrict__ logits_out,
@@ -168,8 +181,9 @@ route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
   constexpr int FN = EP / 16;
   constexpr int ROWS = 3 * EP;                    // LDS rows per stage
   constexpr int CPR = SW / 8;                     // 8-k chunks per row
-  constexpr int NQ = EP * CPR;                    // (expert, chunk) pairs per stage
-  constexpr int NCH = (NQ + 255) / 256;           // pairs per thread
+  constexpr int EU = EP / UW;                     // expert groups of a copy unit
+  constexpr int NU = EU * CPR;                    // (group, chunk) copy units per stage
+  constexpr int NCH = (NU + 255) / 256;           // copy units per thread
   constexpr int TPW = 64 / KS * TG;               // tokens per workgroup
   constexpr int NS = BK / 32;                     // MFMA k slices per wavefront per stage
   __shared__ __attribute__((aligned(16))) bf16 lds[2][ROWS * SW];
@@ -189,33 +203,55 @@ route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float wr[2][NCH][8];      // W_gate of the stages ahead (two register sets)
-  bf16x8 xr[2][TG][NS];     // x fragments of the stages ahead
-  auto load_w = [&](int kt, float(&dst)[NCH][8]) {
-    const int k0 = kt * SW;
+  // A copy unit is 8 consecutive k rows of W_gate (one LDS chunk) for UW
+  // consecutive experts: eight 16-byte loads when UW = 4 (E a multiple of 4,
+  // so with W_gate 16-byte aligned every row is), eight 4-byte ones when
+  // UW = 1.  Wide units pay
+  // off only when there are enough of them to occupy every thread.  Experts
+  // from E up to EP read a real expert's weights instead (clamped address,
+  // no branch): their logit columns are never read, and each output column
+  // of the product depends only on its own W_gate column.
+  static_assert(UW == 1 || UW == 4, "copy units are 1 or 4 experts wide");
+  static_assert(D >= 2 && D % 2 == 0, "register sets alternate over the two LDS buffers");
+  using WV = std::conditional_t<UW == 4, f32x4, float>;
+  WV wr[D][NCH][8];         // W_gate of the stages ahead (D register sets)
+  bf16x8 xr[D][TG][NS];     // x fragments of the stages ahead
+  int woff[NCH];            // element offset of each unit's first W_gate entry
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int q = tid + c * 256, eu = q % EU, kc = q / EU;
+    woff[c] = kc * 8 * E + min(UW * eu, E - UW);
+  }
+  auto load_w = [&](int kt, WV(&dst)[NCH][8]) {
+    const float* wk = w_gate + (size_t)kt * SW * E;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int q = tid + c * 256, e = q % EP, kc = q / EP;
+      if (NU % 256 != 0 && tid + c * 256 >= NU) continue;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        dst[c][i] = ((NQ % 256 == 0 || q < NQ) && e < E)
-                        ? w_gate[(size_t)(k0 + kc * 8 + i) * E + e] : 0.f;
+        dst[c][i] = *reinterpret_cast<const WV*>(wk + (size_t)i * E + woff[c]);
     }
   };
-  auto store_w = [&](int buf, const float(&src)[NCH][8]) {
+  auto store_w = [&](int buf, const WV(&src)[NCH][8]) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int q = tid + c * 256, e = q % EP, kc = q / EP;
-      if (NQ % 256 == 0 || q < NQ) {
+      const int q = tid + c * 256, eu = q % EU, kc = q / EU;
+      if (NU % 256 != 0 && q >= NU) continue;
+#pragma unroll
+      for (int u = 0; u < UW; ++u) {
         bf16x8 hi, mid, lo;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+          float v;
+          if constexpr (UW == 4) v = src[c][i][u];
+          else v = src[c][i];
           bf16 h, m, l;
-          split3(src[c][i], h, m, l);
+          split3(v, h, m, l);
           hi[i] = h;
           mid[i] = m;
           lo[i] = l;
         }
+        const int e = UW * eu + u;
         *reinterpret_cast<bf16x8*>(&lds[buf][rswz<SW>(e, kc)]) = hi;
         *reinterpret_cast<bf16x8*>(&lds[buf][rswz<SW>(EP + e, kc)]) = mid;
         *reinterpret_cast<bf16x8*>(&lds[buf][rswz<SW>(2 * EP + e, kc)]) = lo;
@@ -230,13 +266,14 @@ route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
         dst[g][s] = *reinterpret_cast<const bf16x8*>(xrow[g] + (size_t)kt * SW + s * 32);
   };
   const int nk = d / SW;
-  // step kt on LDS buffer P = kt % 2 with x in xr[P]; issues the W_gate loads
-  // of stage kt + 2 into wr[P] (stage kt is already in LDS), stores stage
-  // kt + 1 (loaded a step earlier) into the other buffer, then loads the x
-  // fragments of stage kt + 2 into xr[P]
+  // step kt: register set P = kt % D, LDS buffer kt % 2.  Stage kt's W_gate
+  // is already in LDS, so wr[P] takes the loads of stage kt + D; after the
+  // MFMAs, stage kt + 1 (loaded D - 1 steps earlier) goes into the other LDS
+  // buffer, and xr[P] takes the x fragments of stage kt + D
   auto step = [&](auto P_, int kt) {
     constexpr int P = decltype(P_)::value;
-    if (kt + 2 < nk) load_w(kt + 2, wr[P]);
+    constexpr int L = P % 2;
+    if (kt + D < nk) load_w(kt + D, wr[P]);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int kc = ks * (BK / 8) + s * 4 + (lane >> 4);
@@ -245,27 +282,30 @@ route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int row = p * EP + j * 16 + (lane & 15);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&lds[P][rswz<SW>(row, kc)]);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&lds[L][rswz<SW>(row, kc)]);
 #pragma unroll
           for (int g = 0; g < TG; ++g)
             acc[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[P][g][s], b, acc[g][j], 0, 0,
                                                                 0);
         }
     }
-    if (kt + 1 < nk) store_w(P ^ 1, wr[P ^ 1]);
-    if (kt + 2 < nk) load_x(kt + 2, xr[P]);
+    if (kt + 1 < nk) store_w(L ^ 1, wr[(P + 1) % D]);
+    if (kt + D < nk) load_x(kt + D, xr[P]);
     __syncthreads();
   };
-  load_w(0, wr[0]);
-  if (nk > 1) load_w(1, wr[1]);
-  load_x(0, xr[0]);
-  if (nk > 1) load_x(1, xr[1]);
+  unroll_stages<0, D>([&](auto P_) {
+    constexpr int P = decltype(P_)::value;
+    if (P < nk) {
+      load_w(P, wr[P]);
+      load_x(P, xr[P]);
+    }
+  });
   store_w(0, wr[0]);
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(Ic<0>{}, kt);
-    if (kt + 1 < nk) step(Ic<1>{}, kt + 1);
-  }
+  for (int kt = 0; kt < nk; kt += D)
+    unroll_stages<0, D>([&](auto P_) {
+      if (kt + decltype(P_)::value < nk) step(P_, kt + decltype(P_)::value);
+    });
   if constexpr (KS > 1) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) red[wid][lane * FN + j] = acc[0][j];
@@ -350,6 +390,13 @@ route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
     }
 }
 
+// Stages of loads in flight: deeper only where one wavefront covers a whole
+// stage's k range (the per-stage work is least there).
+constexpr int route_depth(int EP, int KS, int TG) { return KS == 1 && EP * TG < 128 ? 4 : 2; }
+
+// Experts per W_gate copy unit: 4 once that still leaves 256 units per stage.
+constexpr int route_unit(int EP, int KS) { return EP * KS * (EP > 128 ? 32 : 64) >= 8192 ? 4 : 1; }
+
 int route_padded_experts(int E) {
   int ep = 16;
   while (ep < E) ep *= 2;
@@ -376,9 +423,23 @@ hipError_t launch_route(int act, const void* x, const float* w_gate, const float
     const int tpw = 64 / ks * tg;
     dim3 grid((T + tpw - 1) / tpw), block(256);
     const bf16* xs = (const bf16*)x;
-#define MOE_ROUTE(EPV, KSV, TGV)                                                              \
-  hipLaunchKernelGGL((route_mfma_kernel<EPV, KSV, TGV>), grid, block, 0, s, xs, w_gate,        \
-                     b_gate, logits_out, topk_idx, topk_w, T, d, E, k)
+#define MOE_ROUTE_U(EPV, KSV, TGV, UWV)                                                      \
+  hipLaunchKernelGGL((route_mfma_kernel<EPV, KSV, TGV, route_depth(EPV, KSV, TGV), UWV>), grid, \
+                     block, 0, s, xs, w_gate, b_gate, logits_out, topk_idx, topk_w, T, d, E, k)
+#define MOE_ROUTE(EPV, KSV, TGV) MOE_ROUTE_U(EPV, KSV, TGV, route_unit(EPV, KSV))
+    if (route_unit(EP, ks) == 4 && E % 4 != 0) {
+      // rows of W_gate not 16-byte aligned: copied one expert at a time, one
+      // token group per wavefront
+      grid = dim3((T + 63) / 64);
+      switch (EP) {
+        case 16: MOE_ROUTE_U(16, 1, 1, 1); break;
+        case 32: MOE_ROUTE_U(32, 1, 1, 1); break;
+        case 64: MOE_ROUTE_U(64, 1, 1, 1); break;
+        case 128: MOE_ROUTE_U(128, 1, 1, 1); break;
+        default: MOE_ROUTE_U(256, 1, 1, 1); break;
+      }
+      return hipGetLastError();
+    }
     switch ((EP * 8 + ks) * 8 + tg) {
       case (16 * 8 + 4) * 8 + 1: MOE_ROUTE(16, 4, 1); break;
       case (16 * 8 + 2) * 8 + 1: MOE_ROUTE(16, 2, 1); break;
@@ -398,6 +459,7 @@ hipError_t launch_route(int act, const void* x, const float* w_gate, const float
       case (128 * 8 + 1) * 8 + 2: MOE_ROUTE(128, 1, 2); break;
       default: MOE_ROUTE(256, 1, 1); break;
     }
+#undef MOE_ROUTE_U
 #undef MOE_ROUTE
     return hipGetLastError();
   }

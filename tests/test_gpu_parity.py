@@ -106,7 +106,20 @@ ROUTER_SHAPES = {
     "E64_ks1": (20000, 64, 64, 1),
     "E64_tg2": (32768, 64, 64, 2),
     "E48_tg4": (65536, 64, 48, 3),
+    # W_gate copied one expert at a time where four-expert copies would
+    # otherwise run: E not a multiple of 4
+    "E33_ks2_single_copies": (4000, 256, 33, 2),
+    "E126_single_copies": (1000, 128, 126, 4),
+    "E250_single_copies": (700, 64, 250, 8),
 }
+
+
+def _router_case(T, d, E, k):
+    w = workloads.scaled(WL["skewed_zipf12"], T=T, d=d, F=64, E=E, k=k)
+    inp = workloads.make_inputs(w, 0, with_weights=False)
+    layer = MoeLayer(T, d, 64, E, k, 0.0, act_code("bf16"), backward=False)
+    layer.route(up(inp["x"], "bf16"), up(inp["w_gate"]), up(inp["b_gate"]))
+    return inp, layer
 
 
 @pytest.mark.parametrize("name", list(ROUTER_SHAPES))
@@ -114,10 +127,7 @@ def test_router_launch_shapes(name):
     """Logits against the reference, and the kernel's own top-k and weights
     against the reference's top-k of those same float32 logits."""
     T, d, E, k = ROUTER_SHAPES[name]
-    w = workloads.scaled(WL["skewed_zipf12"], T=T, d=d, F=64, E=E, k=k)
-    inp = workloads.make_inputs(w, 0, with_weights=False)
-    layer = MoeLayer(T, d, 64, E, k, 0.0, act_code("bf16"), backward=False)
-    layer.route(up(inp["x"], "bf16"), up(inp["w_gate"]), up(inp["b_gate"]))
+    inp, layer = _router_case(T, d, E, k)
     torch.cuda.synchronize()
     L = down(layer.logits)
     assert_close(L, orc.router_logits(inp["x"], inp["w_gate"], inp["b_gate"]), 1e-5, "logits")
