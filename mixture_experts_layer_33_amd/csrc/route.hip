@@ -431,8 +431,7 @@ hipError_t launch_route(int act, const void* x, const float* w_gate, const float
       // rows of W_gate not 16-byte aligned: copied one expert at a time, one
       // token group per wavefront
       grid = dim3((T + 63) / 64);
-      switch (EP) {
-        case 16: MOE_ROUTE_U(16, 1, 1, 1); break;
+      switch (EP) {  // four-expert units never run at EP = 16
         case 32: MOE_ROUTE_U(32, 1, 1, 1); break;
         case 64: MOE_ROUTE_U(64, 1, 1, 1); break;
         case 128: MOE_ROUTE_U(128, 1, 1, 1); break;
