@@ -25,6 +25,32 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// Keep the better of (bv, bi) and the pair that DPP control CTRL brings from
+// another lane of the same 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ void dpp_better(float& bv, int& bi) {
+  const int vb = __builtin_bit_cast(int, bv);
+  const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(vb, vb, CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, 0xF, 0xF, false);
+  if (better(ov, oi, bv, bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+// The best (value, index) pair of each row of 16 lanes, left in every lane of
+// the row, by register moves between lanes (no LDS): after the mirror
+// (lane i with 15 - i) and the half-row mirror (i with 7 - i in each half) the
+// four lanes of every quad hold four disjoint quarters of the row, which the
+// two quad swaps combine.  The order is total, so any pairing gives the same
+// winner.
+__device__ __forceinline__ void row16_best(float& bv, int& bi) {
+  dpp_better<0x140>(bv, bi);  // row_mirror
+  dpp_better<0x141>(bv, bi);  // row_half_mirror
+  dpp_better<0x4E>(bv, bi);   // quad_perm [2, 3, 0, 1]
+  dpp_better<0xB1>(bv, bi);   // quad_perm [1, 0, 3, 2]
+}
+
 template <typename ActT>
 __global__ void __launch_bounds__(kRouteThreads)
 route_kernel(const ActT* __restrict__ x, const float* __restrict__ w_gate,
@@ -361,15 +387,7 @@ route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
             bi = e;
           }
         }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-          const float ov = __shfl_xor(bv, o, 64);
-          const int oi = __shfl_xor(bi, o, 64);
-          if (better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-          }
-        }
+        row16_best(bv, bi);
         if ((bi & 15) == gl) taken |= 1u << (bi >> 4);
         sv[r] = bv;
         si[r] = bi;
