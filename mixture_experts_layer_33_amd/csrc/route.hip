@@ -228,6 +228,14 @@ route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
   for (int g = 0; g < TG; ++g)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the epilogue's gate bias (expert 16 j + lane % 16), loaded before the k
+  // loop so that its latency is hidden
+  float bias[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int e = j * 16 + (lane & 15);
+    bias[j] = (e < E) ? b_gate[e] : 0.f;
+  }
 
   // A copy unit is 8 consecutive k rows of W_gate (one LDS chunk) for UW
   // consecutive experts: eight 16-byte loads when UW = 4 (E a multiple of 4,
@@ -352,12 +360,6 @@ route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
 
   // lane holds tokens t0 + 16 g + (lane/16)*4 + i (i < 4), experts j*16 + lane%16
   const int gl = lane & 15;
-  float bias[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int e = j * 16 + gl;
-    bias[j] = (e < E) ? b_gate[e] : 0.f;
-  }
 #pragma unroll
   for (int g = 0; g < TG; ++g)
 #pragma unroll
