@@ -51,7 +51,8 @@ struct Chunk<float> {
   }
 };
 
-// Load token t's k (row, weight) pairs into every lane.
+// Load token t's k (row, weight) pairs into every lane (one token per
+// wavefront).
 __device__ __forceinline__ void token_slots(int t, int k, const int32_t* slot_row,
                                             const float* topk_w, int* rows, float* w) {
   const int lane = threadIdx.x & 63;
@@ -63,8 +64,8 @@ __device__ __forceinline__ void token_slots(int t, int k, const int32_t* slot_ro
   }
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    rows[j] = __shfl(r, j, 64);
-    w[j] = __shfl(wv, j, 64);
+    rows[j] = lane_value(r, j);
+    w[j] = lane_value(wv, j);
   }
 }
 
@@ -238,7 +239,7 @@ combine_bwd_kernel(const ActT* __restrict__ dy, const ActT* __restrict__ out_per
     int idx[MOE_MAX_TOPK];
     const int my = (lane < k) ? topk_idx[(size_t)t * k + lane] : -1;
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) idx[j] = __shfl(my, j, 64);
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) idx[j] = lane_value(my, j);
     for (int e = lane; e < E; e += 64) {
       float v = 0.f;
 #pragma unroll
@@ -284,9 +285,9 @@ dx_kernel(const ActT* __restrict__ dx_perm, const float* __restrict__ dsel,
     }
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      rows[j] = __shfl(r, j, 64);
-      idx[j] = __shfl(e, j, 64);
-      ds[j] = __shfl(v, j, 64);
+      rows[j] = lane_value(r, j);
+      idx[j] = lane_value(e, j);
+      ds[j] = lane_value(v, j);
     }
   }
   for (int c = lane * CK::N; c < d; c += 64 * CK::N) {

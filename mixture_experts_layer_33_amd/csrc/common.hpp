@@ -69,6 +69,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   return excl;
 }
 
+// Lane j's value of v (j wave-uniform), read into a scalar register: for
+// broadcasts within a wavefront that works on one token.
+__device__ __forceinline__ int lane_value(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
+__device__ __forceinline__ float lane_value(float v, int j) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+}
+
 // a compile-time int as a value (selects an unrolled step's buffers)
 template <int V>
 struct Ic {

@@ -161,7 +161,7 @@ gather_kernel(const ActT* __restrict__ x, const int32_t* __restrict__ topk_idx,
   }
   int rows[MOE_MAX_TOPK];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) rows[j] = __shfl(my_row, j, 64);
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) rows[j] = lane_value(my_row, j);
   // 16-byte chunks of the row
   const int nchunk = d * (int)sizeof(ActT) / 16;
   const i32x4* src = reinterpret_cast<const i32x4*>(x + (size_t)t * d);
