@@ -41,8 +41,19 @@
  *   same call may already be enqueued.
  * - Determinism: results are bitwise identical run to run (no float atomics;
  *   integer results never depend on thread order).
- * - Thread safety: the library keeps no state; concurrent calls need
- *   distinct outputs and workspaces.
+ * - Thread safety: the entry points with a workspace argument touch no
+ *   memory but their arguments; concurrent calls need distinct outputs and
+ *   workspaces.  The library keeps one host-side cache: the compute-unit
+ *   count of each device (read once), which sizes the expert GEMMs' last
+ *   round of tiles.  The float32 summation order of those tiles, and so the
+ *   exact bits of h, out_perm and the input gradients, depends on that count
+ *   (identical run to run on one device model).
+ * - Finite inputs: router logits must be finite (NaN/Inf are a precondition
+ *   violation).  The outputs of such a token are then unspecified, but every
+ *   index the router writes stays in [0, E): a NaN logit ranks below every
+ *   other logit.  moe_permute leaves a topk_idx entry outside [0, E)
+ *   unrouted (slot_row -1, in no count and not in the dropped-slot list);
+ *   such a permutation must not be passed to moe_backward.
  * - Routing semantics (the pages leave these open; this is the reading
  *   taken): selection on the float32 logits, ties to the lowest expert index
  *   (+0.0 == -0.0); gate weights are a softmax over the k selected logits;

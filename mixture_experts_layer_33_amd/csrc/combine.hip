@@ -111,11 +111,16 @@ __device__ __forceinline__ void gate_dropped_block(const ActT* __restrict__ x,
   const int32_t* list = row_token + kept;
   const int n = S - kept;
   // first j with expert(list[j]) >= v
+  // (an entry that is not a slot index sorts last and is skipped)
+  auto expert_of = [&](int j) {
+    const int s = list[j];
+    return (unsigned)s < (unsigned)S ? topk_idx[s] : E;
+  };
   auto lower = [&](int v) {
     int lo = 0, hi = n;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (topk_idx[list[mid]] < v) lo = mid + 1; else hi = mid;
+      if (expert_of(mid) < v) lo = mid + 1; else hi = mid;
     }
     return lo;
   };
@@ -124,6 +129,7 @@ __device__ __forceinline__ void gate_dropped_block(const ActT* __restrict__ x,
   float acc = 0.f, db = 0.f;
   for (int j = j0; j < j1; ++j) {
     const int s = list[j];
+    if ((unsigned)s >= (unsigned)S) continue;
     const float g = dsel[s];
     db += g;
     if (i < d) acc = fmaf(g, to_f32(x[(size_t)(s / k) * d + i]), acc);
@@ -305,7 +311,7 @@ dx_kernel(const ActT* __restrict__ dx_perm, const float* __restrict__ dsel,
     }
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      if (j < k) {
+      if (j < k && (unsigned)idx[j] < (unsigned)E) {
         const float* wr = wt + (size_t)idx[j] * d + c;
 #pragma unroll
         for (int i = 0; i < CK::N; ++i) acc[i] = fmaf(ds[j], wr[i], acc[i]);

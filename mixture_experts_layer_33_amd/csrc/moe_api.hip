@@ -409,7 +409,7 @@ moe_status moe_ep_plan(int32_t E, int32_t R, int32_t extra, const int32_t* offse
                        int32_t* replica_start, int32_t* replica_row0, int32_t* replica_rows,
                        int32_t* replica_rank, int32_t* rank_rows, void* stream) {
   if (E < 1 || E > MOE_MAX_EXPERTS || R < 1 || R > MOE_PLAN_MAX_RANKS || extra < 0 ||
-      E + extra > MOE_PLAN_MAX_COPIES)
+      extra > MOE_PLAN_MAX_COPIES - E)  // (no int overflow: E <= MOE_MAX_EXPERTS here)
     return MOE_ERR_INVALID_ARG;
   if (!ptrs_ok(offsets, replica_start, replica_row0, replica_rows, replica_rank, rank_rows))
     return MOE_ERR_INVALID_ARG;

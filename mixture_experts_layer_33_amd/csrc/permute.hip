@@ -58,7 +58,9 @@ rank_hist_kernel(const int32_t* __restrict__ topk_idx, int T, int k, bool choice
     const int q = tile * kRankTile + r * kRankThreads + tid;
     const bool valid = q < S;
     const int s = choice ? (q % T) * k + q / T : q;
-    const int e = valid ? topk_idx[s] : E;
+    // bucket E: past the end, or an expert id outside [0, E) (not counted)
+    int e = valid ? topk_idx[s] : E;
+    if ((unsigned)e > (unsigned)E) e = E;
     uint64_t m = ~0ull;
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -150,12 +152,14 @@ gather_kernel(const ActT* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const int s = t * k + lane;
     const int q = choice ? lane * T + t : s;  // position in the capacity walk
     const int e = topk_idx[s];
-    const int pos = tile_base[(size_t)e * n_tiles + q / kRankTile] + local_rank[q];
-    if (pos < C) {
-      my_row = off[e] + pos;
-      row_token[my_row] = t;
-    } else {
-      row_token[doff[e] + pos - C] = s;
+    if ((unsigned)e < (unsigned)E) {  // an id outside [0, E) stays unrouted
+      const int pos = tile_base[(size_t)e * n_tiles + q / kRankTile] + local_rank[q];
+      if (pos < C) {
+        my_row = off[e] + pos;
+        row_token[my_row] = t;
+      } else {
+        row_token[doff[e] + pos - C] = s;
+      }
     }
     slot_row[s] = my_row;
   }
@@ -222,14 +226,16 @@ index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ l
   const int t = (int)(s / k), j = (int)(s - (long long)t * k);
   const int q = choice ? j * T + t : (int)s;
   const int e = topk_idx[s];
-  const int pos = tile_base[(size_t)e * n_tiles + q / kRankTile] + local_rank[q];
   int row = -1;
-  if (pos < C) {
-    row = off[e] + pos;
-    row_token[row] = t;
-    row_slot[row] = (int)s;
-  } else {
-    row_token[doff[e] + pos - C] = (int)s;
+  if ((unsigned)e < (unsigned)E) {  // an id outside [0, E) stays unrouted
+    const int pos = tile_base[(size_t)e * n_tiles + q / kRankTile] + local_rank[q];
+    if (pos < C) {
+      row = off[e] + pos;
+      row_token[row] = t;
+      row_slot[row] = (int)s;
+    } else {
+      row_token[doff[e] + pos - C] = (int)s;
+    }
   }
   slot_row[s] = row;
 }

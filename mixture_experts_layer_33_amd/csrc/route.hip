@@ -110,6 +110,12 @@ route_kernel(const ActT* __restrict__ x, const float* __restrict__ w_gate,
     }
   }
 
+  // Selection keys: a NaN logit ranks as -inf, so every round finds a winner
+  // among the experts not yet taken and the indices stay in [0, E) whatever
+  // the logits hold (finite logits are the contract; this keeps a violation
+  // from producing indices that later kernels would use as addresses).
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) acc[j] = acc[j] != acc[j] ? -INFINITY : acc[j];
   // top-k: k rounds of a (value desc, index asc) max over the 16-lane group
   unsigned taken = 0;
   float sel_v[MOE_MAX_TOPK];
@@ -375,6 +381,9 @@ route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
           if (e < E) logits_out[(size_t)t * E + e] = v[j];
         }
       }
+      // a NaN logit ranks as -inf (selection stays total, indices in [0, E))
+#pragma unroll
+      for (int j = 0; j < FN; ++j) v[j] = v[j] != v[j] ? -INFINITY : v[j];
       unsigned taken = 0;
       float sv[MOE_MAX_TOPK];
       int si[MOE_MAX_TOPK];

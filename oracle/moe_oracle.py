@@ -67,18 +67,26 @@ F32 = np.float32
 # storage precision
 # --------------------------------------------------------------------------
 def _to_bf16(a: np.ndarray) -> np.ndarray:
-    """Round to the nearest bf16 value (ties to even) via float32.
+    """Round each float64 value to the nearest bf16 value, ties to even, in
+    ONE rounding step (no intermediate float32).
 
-    float64 -> float32 rounds to nearest even first; the second rounding can
-    differ from a direct float64 -> bf16 rounding only when the float32 value
-    lands exactly half-way between two bf16 values, i.e. by one bf16 ulp in
-    rare cases, far inside the bf16 tolerance.
+    bf16 keeps 8 significant bits over float32's exponent range.  A value
+    with 2**(e-1) <= |v| < 2**e is therefore rounded to a multiple of the
+    quantum 2**(e-8); below 2**-126 (bf16's subnormals) the quantum is fixed at
+    2**-133.  np.rint rounds half-way cases to the even multiple, which is the
+    even last significand bit.  Magnitudes that round to 2**128 or beyond are
+    infinite; NaN and infinities pass through.  Returned as float32 (exact).
     """
-    f = np.ascontiguousarray(a, dtype=F32)
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    u = (u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)
-    return u.astype(np.uint32).view(F32)
+    v = np.array(a, dtype=F64, copy=True)
+    fin = np.isfinite(v)
+    vf = v[fin]
+    _, e = np.frexp(vf)                       # vf = m * 2**e, 0.5 <= |m| < 1
+    q = np.maximum(e - 8, -133)
+    r = np.ldexp(np.rint(np.ldexp(vf, -q)), q)  # both scalings are exact
+    big = np.abs(r) >= 2.0 ** 128
+    r[big] = np.copysign(np.inf, r[big])
+    v[fin] = r
+    return v.astype(F32)
 
 
 def round_act(a: np.ndarray, act: str) -> np.ndarray:
@@ -133,7 +141,12 @@ def topk_gate(logits: np.ndarray, k: int):
 
 
 def capacity(T: int, k: int, E: int, capacity_factor: float) -> int:
-    """C = ceil(cf * T * k / E) in float64 (cf taken as a float32), clamped to
+    """C = ceil(cf * T * k / E), the capacity factor times an expert's even
+    share of the T*k slots, rounded UP to whole slots (GShard's expert
+    capacity, cited in A Survey on Mixture of Experts §5 and the PopFetcher
+    notes §2.2; the pages give no formula, so the plainest one is taken).  cf
+    is read as a float32 (the type the layer's shape carries it in) and the
+    product and quotient are evaluated left to right in float64.  Clamped to
     [1, T]; T when cf <= 0 (dropless: no expert can receive more than T)."""
     cf = float(np.float32(capacity_factor))
     if cf <= 0.0:

@@ -125,3 +125,40 @@ def test_identity_experts_reproduce_input_exactly():
     wsum = down(layer.topk_w).astype(np.float64).sum(1, keepdims=True)
     ref = wsum * inp["x"]
     assert np.all(np.abs(down(layer.y) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (32, 4), (128, 4)])
+def test_nonfinite_logits_keep_indices_in_range(E, k):
+    """Finite logits are a precondition, but a violation must not produce
+    expert ids that later kernels use as addresses: a NaN logit ranks below
+    every other value (as -inf, ties to the lowest index), so every index is
+    in [0, E) and distinct, and the permutation counts every slot."""
+    T = 700
+    rng = np.random.default_rng(E + k)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[::5] = np.nan                              # whole rows NaN
+    L[1::7, ::3] = np.nan                        # some entries NaN
+    L[2::9, 1] = np.inf
+    L[3::11, 0] = -np.inf
+    layer = MoeLayer(T, 64, 64, E, k, 0.0, act_code("bf16"), backward=False)
+    layer.route(None, None, None, logits_in=up(L))
+    torch.cuda.synchronize()
+    idx = down(layer.topk_idx)
+    key = np.where(np.isnan(L), -np.inf, L).astype(np.float64)
+    want = np.stack([np.lexsort((np.arange(E), -key[t]))[:k] for t in range(T)])
+    np.testing.assert_array_equal(idx, want)
+    # through x on the matrix-core router: NaN tokens give all-NaN logits
+    d = 128
+    x = workloads.round_to_bf16(rng.standard_normal((T, d)).astype(np.float32))
+    x[::13, 5] = np.nan
+    wg = (rng.standard_normal((d, E)) * 0.02).astype(np.float32)
+    layer.route(up(x, "bf16"), up(wg), up(np.zeros(E, np.float32)), logits_out=True)
+    torch.cuda.synchronize()
+    idx = down(layer.topk_idx)
+    assert ((idx >= 0) & (idx < E)).all()
+    assert all(len(set(r)) == k for r in idx.tolist())
+    np.testing.assert_array_equal(idx[::13], np.tile(np.arange(k), (idx[::13].shape[0], 1)))
+    layer.permute(up(x, "bf16"), topk_idx=layer.topk_idx)
+    torch.cuda.synchronize()
+    assert int(down(layer.counts_raw).sum()) == T * k
+    assert int(down(layer.offsets)[-1]) == T * k

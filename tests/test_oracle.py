@@ -294,6 +294,85 @@ def test_forward_equals_dense_per_token(cf):
     np.testing.assert_allclose(out["y"], ref, rtol=0, atol=2e-7 * np.abs(ref).max())
 
 
+def test_capacity_ceiling_hand_worked():
+    """Non-integer quotients where ceil, floor and nearest all differ
+    (golden/capacity_ceiling.json, worked by hand), plus a routing case in
+    which the ceiling decides which slot is dropped."""
+    g = load("capacity_ceiling.json")
+    for c in g["cases"]:
+        got = orc.capacity(c["T"], c["k"], c["E"], c["cf"])
+        assert got == c["C"], c
+        assert got != c["floor"] or c["floor"] < 1
+    d = g["drop_case"]
+    idx, _ = orc.topk_gate(np.array(d["logits"], np.float32), d["k"])
+    C = orc.capacity(d["T"], d["k"], d["E"], d["capacity_factor"])
+    assert C == d["C"]
+    s = orc.assign_slots(idx, d["E"], C)
+    for key in ("counts_raw", "counts_kept", "offsets", "slot_row", "row_token", "dropped"):
+        assert s[key].tolist() == d[key], key
+    assert s["drops"] == d["drops"]
+
+
+def test_capacity_is_the_least_sufficient_integer():
+    """Invariant of a ceiling: C - 1 < cf*T*k/E <= C (before the clamp), on
+    random shapes; exact rational arithmetic on the float32 capacity factor."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    for _ in range(500):
+        T, k = int(rng.integers(1, 5000)), int(rng.integers(1, 9))
+        E = int(rng.integers(k, 300))
+        cf = float(np.float32(rng.uniform(0.01, 3.0)))
+        q = Fraction(cf) * T * k / E
+        C = orc.capacity(T, k, E, cf)
+        if 1 < C < T:
+            assert C - 1 < q <= C, (T, k, E, cf, C, float(q))
+
+
+def test_bf16_single_rounding():
+    """float64 -> bf16 in one rounding: a value just above a bf16 half-way
+    point goes up (rounding through float32 first would land exactly on the
+    half-way point and then tie to even, down)."""
+    v = np.array([1 + 2 ** -8 + 2 ** -30, -(1 + 2 ** -8 + 2 ** -30), 1 + 2 ** -8 - 2 ** -30])
+    np.testing.assert_array_equal(orc.round_act(v, "bf16"),
+                                  [1 + 2 ** -7, -(1 + 2 ** -7), 1.0])
+
+
+def test_bf16_rounding_special_ranges():
+    """bf16 subnormals (quantum 2**-133, ties to even), the largest finite
+    value, overflow at the half-way point above it, signed zero, inf, NaN."""
+    v = np.array([1.5 * 2 ** -133, 2 ** -134, 3 * 2 ** -135, 2.5 * 2 ** -133,
+                  (2 - 2 ** -7) * 2 ** 127, (2 - 2 ** -8) * 2 ** 127, -0.0, -np.inf])
+    got = orc.round_act(v, "bf16")
+    np.testing.assert_array_equal(got[:6], [2 ** -132, 0.0, 2 ** -133, 2 ** -132,
+                                            (2 - 2 ** -7) * 2 ** 127, np.inf])
+    assert got[6] == 0.0 and np.signbit(got[6])
+    assert got[7] == -np.inf
+    assert np.isnan(orc.round_act(np.array([np.nan]), "bf16")[0])
+
+
+def test_bf16_rounding_against_brute_force():
+    """Every result is the nearest of all 65536 bf16 bit patterns (ties to
+    the pattern with an even last bit), by exhaustive search."""
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    ok = (pats & 0x7F80) != 0x7F80                     # finite patterns only
+    pats = pats[ok]
+    vals = (pats << 16).view(np.float32).astype(np.float64)
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-40, 39, 3000),
+                        vals[rng.integers(0, vals.size, 500)] * (1 + 2.0 ** -8)])
+    got = orc.round_act(v, "bf16")
+    for x, g in zip(v, got):
+        dist = np.abs(vals - x)
+        best = dist.min()
+        cand = pats[dist == best]
+        if cand.size > 1:
+            cand = cand[(cand & 1) == 0]
+        want = np.array([int(cand[0]) << 16], np.uint32).view(np.float32)[0]
+        if abs(x) >= (2 - 2 ** -8) * 2.0 ** 127:           # past the last half-way point
+            want = np.copysign(np.inf, x)
+        assert g == want, (x, g, want)
+
+
 def test_bf16_rounding_ties_to_even():
     vals = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -(1.0 + 2 ** -8)], np.float64)
     np.testing.assert_array_equal(orc.round_act(vals, "bf16"),
