@@ -220,6 +220,26 @@ moe_status moe_forward_fused(const moe_shape* shape, const void* x, const float*
                              uint32_t* relu_bits, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus the workspace),
+ * same kernels and the same results, bit for bit, as moe_forward.  The
+ * workspace is a library-owned static device array of 34 MiB, one per GPU,
+ * held until the process ends; no call allocates or frees anything.
+ * Limit: T*k <= MOE_NOALLOC_MAX_SLOTS (else MOE_ERR_UNSUPPORTED, nothing
+ * enqueued).  Every call on one GPU uses that GPU's one array, so calls that
+ * overlap on a GPU (other streams, other threads, a graph replay beside an
+ * eager call) race and corrupt each other; serialize them.  The array keeps
+ * the last call's contents; no call depends on them.  The first call on each
+ * device looks up the array's device address (host side, once). */
+#define MOE_NOALLOC_MAX_SLOTS 262144
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* w_gate,
+                               const float* b_gate, const void* w1, const void* w2, void* y,
+                               float* logits_out, int32_t* topk_idx, float* topk_w,
+                               int32_t* counts_raw, int32_t* counts_kept, int32_t* offsets,
+                               int32_t* slot_row, int32_t* row_token, void* x_perm, void* h,
+                               void* out_perm, uint32_t* relu_bits, void* stream);
+
 /* Backward of moe_forward for output gradient dy (PopFetcher notes §5.2.1:
  * one GEMM pass forward, two backward - gradients of the inputs and of the
  * expert parameters).  Reads the saved forward tensors and writes

@@ -17,7 +17,7 @@ __all__ = [
     "moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
-    "moe_predict_popularity", "OP", "PRIORITY",
+    "moe_predict_popularity", "moe_forward_noalloc", "OP", "PRIORITY", "NOALLOC_MAX_SLOTS",
 ]
 
 MOE_F32 = 0
@@ -28,7 +28,8 @@ OP = {"route": 0, "permute": 1, "expert_ffn": 2, "combine": 3, "forward": 4, "ba
 EXPORTS = ["moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
            "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
-           "moe_predict_popularity"]
+           "moe_predict_popularity", "moe_forward_noalloc"]
+NOALLOC_MAX_SLOTS = 262144  # MOE_NOALLOC_MAX_SLOTS
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -83,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [sp] + [_P] * 18 + [_P, ctypes.c_size_t, _P]
         L.moe_forward_fused.argtypes = [sp] + [_P] * 17 + [_P, ctypes.c_size_t, _P]
         L.moe_backward.argtypes = [sp] + [_P] * 20 + [_P, ctypes.c_size_t, _P]
+        L.moe_forward_noalloc.argtypes = [sp] + [_P] * 18 + [_P]
         L.moe_ep_plan.argtypes = [ctypes.c_int32] * 3 + [_P] * 6 + [_P]
         L.moe_cooccurrence_update.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_int64] + [_P] * 5
         L.moe_predict_popularity.argtypes = [ctypes.c_int32] * 2 + [_P] * 5
@@ -90,7 +92,7 @@ def lib() -> ctypes.CDLL:
                                             _P, _P, _P, _P]
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
                      "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan",
-                     "moe_cooccurrence_update", "moe_predict_popularity"):
+                     "moe_cooccurrence_update", "moe_predict_popularity", "moe_forward_noalloc"):
             getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -188,6 +190,17 @@ def moe_forward(shape, x, w_gate, b_gate, w1, w2, y, logits_out, topk_idx, topk_
                              _ptr(counts_raw), _ptr(counts_kept), _ptr(offsets), _ptr(slot_row),
                              _ptr(row_token), _ptr(x_perm), _ptr(h), _ptr(out_perm),
                              _ptr(relu_bits), ws, nb, _stream(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(shape, x, w_gate, b_gate, w1, w2, y, logits_out, topk_idx, topk_w,
+                        counts_raw, counts_kept, offsets, slot_row, row_token, x_perm, h, out_perm,
+                        relu_bits, stream=None):
+    _check(lib().moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(b_gate),
+                                     _ptr(w1), _ptr(w2), _ptr(y), _ptr(logits_out),
+                                     _ptr(topk_idx), _ptr(topk_w), _ptr(counts_raw),
+                                     _ptr(counts_kept), _ptr(offsets), _ptr(slot_row),
+                                     _ptr(row_token), _ptr(x_perm), _ptr(h), _ptr(out_perm),
+                                     _ptr(relu_bits), _stream(stream)), "moe_forward_noalloc")
 
 
 def moe_forward_fused(shape, x, w_gate, b_gate, w1, w2, y, logits_out, topk_idx, topk_w,

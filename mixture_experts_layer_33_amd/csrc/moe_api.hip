@@ -4,6 +4,8 @@
 // call only enqueues kernels on the caller's stream.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -175,6 +177,51 @@ moe_status do_route(const moe_shape* s, const void* x, const float* w_gate, cons
   MOE_HIP(launch_scan(pw.hist, nt, s->E, capacity_of(s), pw.tile_base, counts_raw, counts_kept,
                       st));
   return MOE_OK;
+}
+
+}  // namespace
+
+// Workspace of moe_forward_noalloc: a library-owned device array, one copy
+// per GPU (the loader places it with the code object on each device the
+// library runs on; it lives until the process ends).  Its size covers
+// moe_forward's workspace for every shape with T*k <= MOE_NOALLOC_MAX_SLOTS:
+// the per-slot ranks (4 bytes a slot), two per-(expert, 1024-slot tile)
+// tables, two per-expert count vectors, and the expert GEMMs' split-tail
+// partial tiles (32 MiB).  In host code `scratch` names a host-side stand-in,
+// not the device memory: only the address hipGetSymbolAddress returns for the
+// current device is ever passed to kernels.
+constexpr size_t kNoallocScratchBytes = 34u << 20;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+static_assert(((size_t)MOE_NOALLOC_MAX_SLOTS * 4 +
+               2 * (size_t)MOE_MAX_EXPERTS * (MOE_NOALLOC_MAX_SLOTS / kRankTile) * 4 +
+               2 * (size_t)MOE_MAX_EXPERTS * 4 + 5 * 256 + ((size_t)32 << 20)) <=
+                  kNoallocScratchBytes,
+              "the static workspace must hold the largest forward workspace");
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Device address of the current device's `scratch`, looked up once per
+// device (with that device current) and kept.
+hipError_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & (kAlign - 1)) != 0)
+      return hipErrorInvalidValue;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -440,6 +487,30 @@ moe_status moe_predict_popularity(int32_t E_a, int32_t E_b, const int32_t* count
   if (!ptrs_ok(counts_a, cooc, pred, order)) return MOE_ERR_INVALID_ARG;
   MOE_HIP(launch_predict(E_a, E_b, counts_a, cooc, pred, order, as_stream(stream)));
   return MOE_OK;
+}
+
+moe_status moe_forward_noalloc(const moe_shape* s, const void* x, const float* w_gate,
+                               const float* b_gate, const void* w1, const void* w2, void* y,
+                               float* logits_out, int32_t* topk_idx, float* topk_w,
+                               int32_t* counts_raw, int32_t* counts_kept, int32_t* offsets,
+                               int32_t* slot_row, int32_t* row_token, void* x_perm, void* h,
+                               void* out_perm, uint32_t* relu_bits, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (slots(s) > MOE_NOALLOC_MAX_SLOTS) return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe_workspace_bytes(s, MOE_OP_FORWARD);
+  if (need > kNoallocScratchBytes) return MOE_ERR_UNSUPPORTED;
+  if (!ptrs_ok(x, w_gate, b_gate, w1, w2, y, topk_idx, topk_w, counts_kept, offsets, slot_row,
+               row_token, x_perm, h, out_perm) ||
+      !opt_ok(logits_out) || !opt_ok(counts_raw) || !opt_ok(relu_bits))
+    return MOE_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  MOE_HIP(noalloc_scratch(&ws));
+  // The forward workspace holds nothing that must start at zero: every
+  // kernel writes its part before any kernel reads it.
+  return moe_forward(s, x, w_gate, b_gate, w1, w2, y, logits_out, topk_idx, topk_w, counts_raw,
+                     counts_kept, offsets, slot_row, row_token, x_perm, h, out_perm, relu_bits,
+                     ws, kNoallocScratchBytes, stream);
 }
 
 }  // extern "C"
