@@ -64,7 +64,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="uniform_cf125", choices=list(workloads.workloads()))
+    p.add_argument("--workload", default="mixtral_shaped", choices=list(workloads.workloads()))
     p.add_argument("--priority", default=None, choices=["slot", "choice"],
                    help="capacity priority (default: the workload's)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -82,7 +82,8 @@ def parse():
     return p.parse_args()
 
 
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_33_amd", "csrc", "gemm.hip")
+CSRC = os.path.join(ROOT, "mixture_experts_layer_33_amd", "csrc")
+GEMM_SRC = os.path.join(CSRC, "gemm.hip")
 GEMM_KERNEL = "rows_gemm_kernel"
 FIXUP_KERNEL = "rows_fixup_kernel"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -116,8 +117,16 @@ def summarize_traffic(args):
     w = workloads.workloads()[args.workload]
     out = {}
     lines = []
+    all_kib, all_n = {}, {}
     for counter, path in zip(("FETCH_SIZE", "WRITE_SIZE"), args.summarize_traffic):
         rows = _counter_rows(path, counter)
+        sums = {}
+        for r in rows:
+            acc = sums.setdefault(r["Kernel_Name"], [0.0, 0])
+            acc[0] += float(r["Counter_Value"])
+            acc[1] += 1
+        all_kib[counter] = {k: v[0] / v[1] for k, v in sums.items()}
+        all_n.update({k: v[1] for k, v in sums.items()})
         copies = [float(r["Counter_Value"]) for r in rows
                   if r["Kernel_Name"].startswith(COPY_KERNEL)
                   and float(r["Counter_Value"]) > COPY_BYTES / 1024 / 2]
@@ -188,6 +197,7 @@ def summarize_traffic(args):
     with open(traffic_path(w.name), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(traffic_path(w.name))
+    summarize_parts_traffic(args, all_kib, {c: out[c]["scale"] for c in out}, all_n)
 
 
 # the expert GEMM launches of one step: kernel-name pattern -> product
@@ -281,6 +291,113 @@ def summarize_mfma(args):
     with open(mfma_path(w.name), "w") as f:
         f.write("\n".join(L) + "\n")
     print(mfma_path(w.name))
+
+
+# the HBM-bound steps: kernels per call, and the sources they are built from
+PART_KERNELS = {
+    "route": ["route_mfma_kernel", "route_kernel"],
+    "permute": ["rank_hist_kernel", "scan_kernel", "gather_kernel"],
+    "combine": ["combine_kernel"],
+}
+PART_SOURCES = ["route.hip", "permute.hip", "combine.hip"]
+
+
+def parts_hbm_bytes(w, s_kept):
+    """Algorithmic bytes per call: route T*d*s + 4*d*E + 8*T*k (logits not
+    written); permute T*d*s + S_kept*d*s + 12*T*k; combine S_kept*d*s +
+    T*d*s + 8*T*k (s = bytes per activation element)."""
+    sx = 2 if w.dtype == "bf16" else 4
+    return {"route": w.T * w.d * sx + 4 * w.d * w.E + 8 * w.T * w.k,
+            "permute": w.T * w.d * sx + s_kept * w.d * sx + 12 * w.T * w.k,
+            "combine": s_kept * w.d * sx + w.T * w.d * sx + 8 * w.T * w.k}
+
+
+def parts_traffic_path(name):
+    return os.path.join(ROOT, "profiles", f"route_permute_combine_{name}_hbm_traffic.md")
+
+
+def parts_source_hashes():
+    import hashlib
+    out = {}
+    for f in PART_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            out[f] = hashlib.sha256(fh.read()).hexdigest()
+    return out
+
+
+def summarize_parts_traffic(args, per_kernel_kib, scales, dispatches):
+    """Counter bytes per call of route, permute and combine: for each step the
+    mean FETCH_SIZE and WRITE_SIZE of each of its kernels over that kernel's
+    dispatches, scaled by the calibration copy, summed over the step's
+    kernels; against the step's algorithmic bytes."""
+    w = workloads.workloads()[args.workload]
+    alg = parts_hbm_bytes(w, w.T * w.k)  # the measured workloads drop no slot
+    rows, rec = [], {}
+    for part, kernels in PART_KERNELS.items():
+        total, found = 0.0, []
+        for kn in kernels:
+            names = [n for n in per_kernel_kib["FETCH_SIZE"]
+                     if re.search(rf"\b{kn}\b", n) and n in per_kernel_kib["WRITE_SIZE"]]
+            for n in names:
+                fb = per_kernel_kib["FETCH_SIZE"][n] * 1024 * scales["FETCH_SIZE"]
+                wb = per_kernel_kib["WRITE_SIZE"][n] * 1024 * scales["WRITE_SIZE"]
+                found.append((n, dispatches[n], fb, wb))
+        if not found:
+            continue
+        # a kernel name can appear in several instantiations: weight them by
+        # their dispatch counts, then add the step's kernels up
+        by_kernel = {}
+        for n, nd, fb, wb in found:
+            base = next(kn for kn in kernels if re.search(rf"\b{kn}\b", n))
+            acc = by_kernel.setdefault(base, [0.0, 0.0, 0])
+            acc[0] += fb * nd
+            acc[1] += wb * nd
+            acc[2] += nd
+        for base, (fb, wb, nd) in by_kernel.items():
+            rows.append((part, base, nd, fb / nd, wb / nd))
+            total += (fb + wb) / nd
+        rec[part] = total
+    L = [f"# HBM traffic of route, permute and combine, {w.name}", "",
+         f"Workload: {w.description}.", "",
+         "Commands (run from the repository root on one MI355X):", "", "```",
+         args.command.strip() or "(not recorded)", "```", "",
+         "FETCH_SIZE and WRITE_SIZE per dispatch (KiB), averaged over each kernel's "
+         "dispatches in the run (warm and cold calls alike), scaled by 1 GiB / (the same "
+         f"counter's reading for the 1 GiB device copy `{COPY_KERNEL}`).  A step's bytes are "
+         "the sum over its kernels.  Algorithmic bytes: route T*d*s + 4*d*E + 8*T*k, permute "
+         "T*d*s + S*d*s + 12*T*k, combine S*d*s + T*d*s + 8*T*k (S = T*k slots, all kept "
+         "here), s = bytes per activation element.", "",
+         "| step | kernel | dispatches | fetch bytes | write bytes |", "|---|---|---|---|---|"]
+    for part, base, nd, fb, wb in rows:
+        L.append(f"| {part} | `{base}` | {nd} | {fb:.4g} | {wb:.4g} |")
+    L += ["", "| step | counter bytes per call | algorithmic bytes | ratio |", "|---|---|---|---|"]
+    for part, b in rec.items():
+        L.append(f"| {part} | {b:.4g} | {alg[part]:.4g} | {b / alg[part]:.3f} |")
+    L.append("")
+    L.append("parts-traffic-json: " + json.dumps({"workload": w.name,
+                                                  "sources_sha256": parts_source_hashes(),
+                                                  "bytes_per_call": rec,
+                                                  "algorithmic_bytes": alg}))
+    os.makedirs(os.path.dirname(parts_traffic_path(w.name)), exist_ok=True)
+    with open(parts_traffic_path(w.name), "w") as f:
+        f.write("\n".join(L) + "\n")
+    print(parts_traffic_path(w.name))
+
+
+def load_parts_traffic(name):
+    """Counter bytes per call of route/permute/combine from the committed
+    summary, or None when there is none or a source changed since."""
+    try:
+        with open(parts_traffic_path(name)) as f:
+            for line in f:
+                if line.startswith("parts-traffic-json: "):
+                    rec = json.loads(line[len("parts-traffic-json: "):])
+                    if rec["sources_sha256"] == parts_source_hashes():
+                        return rec["bytes_per_call"]
+                    log("route/permute/combine traffic summary is stale: counter_bytes = null")
+    except OSError:
+        pass
+    return None
 
 
 def load_traffic(name):
@@ -438,16 +555,55 @@ def main():
         return a.elapsed_time(b) / reps
 
     reps = args.kernel_reps
-    t_fwd = time_it(lambda: layer.forward(x, w_gate, b_gate, w1, w2, logits_out=False), reps)
-    t_bwd = time_it(lambda: layer.backward(dy, x, w_gate, w1, w2, dlogits=False), reps)
-    t_ffn = time_it(lambda: layer.expert_ffn(w1, w2), reps)
-    t_comb = time_it(lambda: layer.combine(), reps)
-    t_route = time_it(lambda: layer.route(x, w_gate, b_gate, logits_out=False, counts=False),
-                      reps)
-    t_perm = time_it(lambda: layer.permute(x), reps)
-    # the gather/scatter-fused forward (same y, no packed token copy)
-    t_fused = time_it(lambda: layer.forward_fused(x, w_gate, b_gate, w1, w2, logits_out=False),
-                      reps)
+    # cold cache: 512 MiB written before each repetition (evicts the 256 MB
+    # last-level cache and every L2); warm: calls back to back on the same
+    # inputs (working sets under 256 MB then come from the caches)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def pct(ts):
+        q = np.percentile(ts, [10, 50, 90])
+        return {"median": float(q[1]), "p10": float(q[0]), "p90": float(q[2])}
+
+    def warm(fn, reps=args.cold_reps):
+        """one call's time, calls back to back with caches warm"""
+        fn()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record(stream)
+        for r in range(reps):
+            fn()
+            evs[r + 1].record(stream)
+        torch.cuda.synchronize()
+        return pct([evs[r].elapsed_time(evs[r + 1]) for r in range(reps)])
+
+    def cold(fn, reps=args.cold_reps):
+        ts = []
+        for r in range(reps):
+            flush.fill_(r & 255)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return pct(ts)
+
+    # in the order of the layer, so each part reads what the one before wrote
+    part_fns = {
+        "route": lambda: layer.route(x, w_gate, b_gate, logits_out=False, counts=False),
+        "permute": lambda: layer.permute(x),
+        "expert_ffn": lambda: layer.expert_ffn(w1, w2),
+        "combine": lambda: layer.combine(),
+        "forward_fused": lambda: layer.forward_fused(x, w_gate, b_gate, w1, w2, logits_out=False),
+        "forward": lambda: layer.forward(x, w_gate, b_gate, w1, w2, logits_out=False),
+        "backward": lambda: layer.backward(dy, x, w_gate, w1, w2, dlogits=False),
+    }
+    parts = {}
+    for name, fn in part_fns.items():
+        parts[name] = {"warm": warm(fn), "cold": cold(fn)}
+        log(f"{name}: warm {parts[name]['warm']['median'] * 1e3:.1f} us, cold "
+            f"{parts[name]['cold']['median'] * 1e3:.1f} us (medians)")
+    t_ffn = parts["expert_ffn"]["warm"]["median"]
     # dispatch plan for 8 ranks with one extra copy per expert (not part of
     # the step: the planning that would feed an All-to-All)
     R_plan, extra_plan = 8, w.E
@@ -478,73 +634,36 @@ def main():
     flops_launch = 2.0 * w.d * w.F * s_kept
     achieved = flops_launch / (gemm_launch_ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    comb_bytes = s_kept * w.d * (2 if w.dtype == "bf16" else 4) + \
-        w.T * w.d * (2 if w.dtype == "bf16" else 4) + 8 * w.T * w.k
-    log(f"forward {t_fwd:.3f} ms (gather/scatter-fused {t_fused:.3f} ms), backward {t_bwd:.3f} ms, expert FFN {t_ffn:.3f} ms "
-        f"({achieved:.1f} TFLOP/s), combine {t_comb*1e3:.1f} us "
-        f"({comb_bytes / (t_comb / 1e3) / 1e9:.0f} GB/s)")
+    log(f"expert FFN {t_ffn:.3f} ms warm ({achieved:.1f} TFLOP/s per GEMM launch in the steps)")
 
-    # HBM-bound steps against their algorithmic bytes (route: E <= 16 only is
-    # HBM-bound; beyond, its MFMA work dominates)
-    sx = 2 if w.dtype == "bf16" else 4
-    hbm_bytes = {"route": w.T * w.d * sx + 4 * w.d * w.E + 8 * w.T * w.k,
-                 "permute": w.T * w.d * sx + s_kept * w.d * sx + 12 * w.T * w.k,
-                 "combine": s_kept * w.d * sx + w.T * w.d * sx + 8 * w.T * w.k}
+    # HBM-bound steps against their algorithmic bytes, from the cold-cache
+    # medians (HBM) and the warm ones (cache-resident working sets).  The
+    # router is also priced against its matrix-core work: three bf16 passes
+    # of 2*T*d*E flops each (W_gate split exactly into three bf16 parts).
+    hbm_bytes = parts_hbm_bytes(w, s_kept)
+    counters = load_parts_traffic(w.name)
     hbm = {}
-    for name, t in (("route", t_route), ("permute", t_perm), ("combine", t_comb)):
-        gbs = hbm_bytes[name] / (t / 1e3) / 1e9
-        hbm[name] = {"ms": t, "bytes": hbm_bytes[name], "GB/s": gbs,
-                     "frac": gbs / PEAK_HBM_GBS}
-
-    # cold cache: 512 MiB written before each repetition (evicts the 256 MB
-    # last-level cache), median / p10 / p90 of the forward and the backward
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-
-    def pct(ts):
-        q = np.percentile(ts, [10, 50, 90])
-        return {"median": float(q[1]), "p10": float(q[0]), "p90": float(q[2])}
-
-    def warm(fn, reps=args.cold_reps):
-        """one call's time, calls back to back with caches warm"""
-        fn()
-        torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        evs[0].record(stream)
-        for r in range(reps):
-            fn()
-            evs[r + 1].record(stream)
-        torch.cuda.synchronize()
-        return pct([evs[r].elapsed_time(evs[r + 1]) for r in range(reps)])
+    for name in ("route", "permute", "combine"):
+        tc, tw = parts[name]["cold"]["median"], parts[name]["warm"]["median"]
+        gbs = hbm_bytes[name] / (tc / 1e3) / 1e9
+        rec = {"bytes": hbm_bytes[name], "cold_ms": tc, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS,
+               "warm_ms": tw, "warm_GB/s (cache-resident)": hbm_bytes[name] / (tw / 1e3) / 1e9,
+               "counter_bytes": None if counters is None else counters.get(name)}
+        if name == "route":
+            bound_us = max(hbm_bytes[name] / PEAK_HBM_GBS / 1e3,
+                           3 * 2.0 * w.T * w.d * w.E / PEAK_BF16_TFLOPS / 1e6)
+            rec.update({"bound_us (max of HBM, 3-pass MFMA)": bound_us,
+                        "frac_of_bound": bound_us / (tc * 1e3)})
+        hbm[name] = rec
+    t_fwd_c, t_fwd_w = parts["forward"]["cold"]["median"], parts["forward"]["warm"]["median"]
+    fwd_tok = {"cold": w.T / (t_fwd_c / 1e3), "warm": w.T / (t_fwd_w / 1e3)}
+    log(f"forward: {fwd_tok['cold']:,.0f} tokens/s cold, {fwd_tok['warm']:,.0f} warm; "
+        + ", ".join(f"{k} {v['frac']:.0%} of HBM cold" for k, v in hbm.items()))
 
     step_ms = [(start if i == 0 else step_end[i - 1]).elapsed_time(step_end[i])
                for i in range(args.steps)]
-    warm_ms = {"step": pct(step_ms),
-               "forward": warm(lambda: layer.forward(x, w_gate, b_gate, w1, w2, logits_out=False)),
-               "forward_fused": warm(lambda: layer.forward_fused(x, w_gate, b_gate, w1, w2,
-                                                                 logits_out=False)),
-               "backward": warm(lambda: layer.backward(dy, x, w_gate, w1, w2, dlogits=False))}
-    log(f"warm: step {warm_ms['step']['median']:.3f} ms, forward "
-        f"{warm_ms['forward']['median']:.3f} ms, backward {warm_ms['backward']['median']:.3f} ms "
-        f"(medians)")
-
-    def cold(fn, reps=args.cold_reps):
-        ts = []
-        for r in range(reps):
-            flush.fill_(r & 255)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        return pct(ts)
-
-    cold_ms = {"forward": cold(lambda: layer.forward(x, w_gate, b_gate, w1, w2,
-                                                     logits_out=False)),
-               "backward": cold(lambda: layer.backward(dy, x, w_gate, w1, w2, dlogits=False))}
+    warm_ms = {"step": pct(step_ms)}
     del flush
-    log(f"cold cache: forward {cold_ms['forward']['median']:.3f} ms, backward "
-        f"{cold_ms['backward']['median']:.3f} ms (medians)")
 
     # Probes measured on the same GPU in the same run: a plain 1 GiB device
     # copy (read + write) and the vendor dense GEMM (torch.mm in bf16) with the
@@ -566,7 +685,7 @@ def main():
     copy_gbs = 2.0 * (1 << 30) / (probe_ms(lambda: dst.copy_(src)) * 1e-3) / 1e9
     del src, dst
     probes = {"copy_1GiB_GB/s": copy_gbs,
-              "hbm_parts_frac_of_copy": {k: v["GB/s"] / copy_gbs for k, v in hbm.items()}}
+              "hbm_parts_cold_frac_of_copy": {k: v["GB/s"] / copy_gbs for k, v in hbm.items()}}
     if w.dtype == "bf16":
         pa = torch.randn(s_kept, w.d, device="cuda").to(torch.bfloat16)
         pb = (torch.randn(w.d, w.F, device="cuda") * 0.02).to(torch.bfloat16)
@@ -602,14 +721,14 @@ def main():
                      "frac": achieved / peak, "traffic": load_traffic(w.name),
                      "flops_per_launch": flops_launch,
                      "launch_us": gemm_launch_ms * 1e3},
-        "parts_ms": {"forward": t_fwd, "forward_fused": t_fused, "backward": t_bwd, "expert_ffn": t_ffn,
-                     "combine": t_comb, "ep_plan_8_ranks": t_plan,
-                     "cooccurrence_update": t_co, "predict_popularity": t_pred},
+        "forward_tokens_per_s": fwd_tok,
+        "parts_ms": {**{k: {"warm": v["warm"], "cold": v["cold"]} for k, v in parts.items()},
+                     "ep_plan_8_ranks": t_plan, "cooccurrence_update": t_co,
+                     "predict_popularity": t_pred},
         "ep_plan": {"ranks": R_plan, "extra_copies": extra_plan,
                     "max_over_mean_rank_rows": plan_balance},
         "hbm_parts": hbm,
         "warm_ms": warm_ms,
-        "cold_ms": cold_ms,
         "probes": probes,
     }
     if not args.no_cpu_baseline:

@@ -114,6 +114,20 @@ def test_traffic_summary_scales_by_the_copy(tmp_path, out_root):
     fs = 1 / 0.6
     fpath = run("FETCH_SIZE", gib_kib * 0.6, 1000.0, 2000.0, 100.0)
     wpath = run("WRITE_SIZE", gib_kib, 300.0, 400.0, 50.0)
+    # route / permute / combine kernels in the same runs (two dispatches each,
+    # readings differing, so the per-call mean is checked)
+    part_kernels = {"void moe::route_mfma_kernel<16, 1, 4, 4, 1>(...)": (10.0, 1.0),
+                    "moe::rank_hist_kernel(...)": (2.0, 3.0),
+                    "moe::scan_kernel(...)": (0.5, 0.25),
+                    "void moe::gather_kernel<__bf16>(...)": (20.0, 30.0),
+                    "void moe::combine_kernel<__bf16>(...)": (40.0, 8.0)}
+    for counter, path, col in (("FETCH_SIZE", fpath, 0), ("WRITE_SIZE", wpath, 1)):
+        rows = list(csv.DictReader(open(path, newline="")))
+        extra = []
+        for name, vals in part_kernels.items():
+            extra += [(name, 10, {counter: vals[col]}), (name, 10, {counter: 3 * vals[col]})]
+        write_counters(path, [(r["Kernel_Name"], 10, {counter: float(r["Counter_Value"])})
+                              for r in rows] + extra)
     bench.summarize_traffic(types.SimpleNamespace(summarize_traffic=[fpath, wpath],
                                                   workload="uniform_cf125", command="cmd"))
     text = (out_root / "profiles" / "rows_gemm_uniform_cf125_hbm_traffic.md").read_text()
@@ -125,6 +139,15 @@ def test_traffic_summary_scales_by_the_copy(tmp_path, out_root):
     assert rec["traffic_bytes_per_launch"] == pytest.approx((b1 + b2) / 2)
     assert rec["gemm_source_sha256"] == bench.gemm_source_hash()
     assert bench.load_traffic("uniform_cf125") == pytest.approx((b1 + b2) / 2)
+    ptext = (out_root / "profiles" / "route_permute_combine_uniform_cf125_hbm_traffic.md").read_text()
+    prec = json.loads(ptext.split("parts-traffic-json: ")[1])
+    per = {n: 2 * (v[0] * fs + v[1]) * 1024 for n, v in part_kernels.items()}  # mean of 1x and 3x
+    keys = list(part_kernels)
+    want = {"route": per[keys[0]], "permute": per[keys[1]] + per[keys[2]] + per[keys[3]],
+            "combine": per[keys[4]]}
+    for k, v in want.items():
+        assert prec["bytes_per_call"][k] == pytest.approx(v), k
+    assert bench.load_parts_traffic("uniform_cf125") == pytest.approx(prec["bytes_per_call"])
 
 
 def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
