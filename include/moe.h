@@ -295,6 +295,25 @@ moe_status moe_ep_plan(int32_t E, int32_t R, int32_t extra, const int32_t* offse
                        int32_t* replica_start, int32_t* replica_row0, int32_t* replica_rows,
                        int32_t* replica_rank, int32_t* rank_rows, void* stream);
 
+/* All-to-All split sizes and send-buffer layout of an expert-parallel
+ * dispatch (A Survey on Mixture of Experts, §5 System Design, first
+ * paragraph: the per-expert packed rows are what the All-to-All sends).
+ * Segment i holds seg_rows[i] packed rows bound for rank seg_rank[i]: with an
+ * expert -> rank map, the segments are the experts (seg_rows = counts_kept,
+ * seg_rank = the map); with moe_ep_plan's copies, the copies (replica_rows,
+ * replica_rank).  The send buffer holds rank 0's rows, then rank 1's, ...,
+ * the segments of one rank in index order:
+ *   send_counts[r]      rows for rank r (the split sizes)        [R]
+ *   send_offsets[r]     exclusive prefix sum, send_offsets[R] = total  [R+1]
+ *   seg_send_offset[i]  first send-buffer row of segment i        [n]
+ * A segment whose rank is outside [0, R) is in no count and gets -1.  All
+ * int32 device memory; 1 <= n <= MOE_PLAN_MAX_COPIES, 1 <= R <=
+ * MOE_PLAN_MAX_RANKS, else MOE_ERR_INVALID_ARG.  One wavefront; enqueues
+ * only. */
+moe_status moe_dispatch_layout(int32_t n, int32_t R, const int32_t* seg_rows,
+                               const int32_t* seg_rank, int32_t* send_counts,
+                               int32_t* send_offsets, int32_t* seg_send_offset, void* stream);
+
 /* Cross-layer expert correlation (PopFetcher notes §4.1: a token choosing
  * expert x in layer j and x' in layer j+1 gives the tuple (x, x')).  Counts
  * this iteration's tuples of T tokens, idx_a [T, k_a] (layer j, experts

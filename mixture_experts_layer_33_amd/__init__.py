@@ -17,7 +17,8 @@ __all__ = [
     "moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
-    "moe_predict_popularity", "moe_forward_noalloc", "OP", "PRIORITY", "NOALLOC_MAX_SLOTS",
+    "moe_predict_popularity", "moe_forward_noalloc", "moe_dispatch_layout", "OP", "PRIORITY",
+    "NOALLOC_MAX_SLOTS",
 ]
 
 MOE_F32 = 0
@@ -28,7 +29,7 @@ OP = {"route": 0, "permute": 1, "expert_ffn": 2, "combine": 3, "forward": 4, "ba
 EXPORTS = ["moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
            "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
-           "moe_predict_popularity", "moe_forward_noalloc"]
+           "moe_predict_popularity", "moe_forward_noalloc", "moe_dispatch_layout"]
 NOALLOC_MAX_SLOTS = 262144  # MOE_NOALLOC_MAX_SLOTS
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -86,13 +87,15 @@ def lib() -> ctypes.CDLL:
         L.moe_backward.argtypes = [sp] + [_P] * 20 + [_P, ctypes.c_size_t, _P]
         L.moe_forward_noalloc.argtypes = [sp] + [_P] * 18 + [_P]
         L.moe_ep_plan.argtypes = [ctypes.c_int32] * 3 + [_P] * 6 + [_P]
+        L.moe_dispatch_layout.argtypes = [ctypes.c_int32] * 2 + [_P] * 5 + [_P]
         L.moe_cooccurrence_update.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_int64] + [_P] * 5
         L.moe_predict_popularity.argtypes = [ctypes.c_int32] * 2 + [_P] * 5
         L.moe_popularity_update.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                             _P, _P, _P, _P]
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
                      "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan",
-                     "moe_cooccurrence_update", "moe_predict_popularity", "moe_forward_noalloc"):
+                     "moe_cooccurrence_update", "moe_predict_popularity", "moe_forward_noalloc",
+                     "moe_dispatch_layout"):
             getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -238,6 +241,13 @@ def moe_ep_plan(E, R, extra, offsets, replica_start, replica_row0, replica_rows,
     _check(lib().moe_ep_plan(E, R, extra, _ptr(offsets), _ptr(replica_start), _ptr(replica_row0),
                              _ptr(replica_rows), _ptr(replica_rank), _ptr(rank_rows),
                              _stream(stream)), "moe_ep_plan")
+
+
+def moe_dispatch_layout(n, R, seg_rows, seg_rank, send_counts, send_offsets, seg_send_offset,
+                        stream=None):
+    _check(lib().moe_dispatch_layout(n, R, _ptr(seg_rows), _ptr(seg_rank), _ptr(send_counts),
+                                     _ptr(send_offsets), _ptr(seg_send_offset), _stream(stream)),
+           "moe_dispatch_layout")
 
 
 def moe_cooccurrence_update(E_a, E_b, k_a, k_b, T, window, it, idx_a, idx_b, ring, window_sum,

@@ -10,7 +10,7 @@ namespace moe {
 // logits = x * w_gate + b (float32); top-k with lowest-index ties; weights =
 // softmax over the selected logits.
 // bf16 without logits_in runs the router on MFMA (W_gate split into three
-// exact bf16 parts as it is staged).
+// exact bf16 parts in registers as its fragments are used).
 hipError_t launch_route(int act, const void* x, const float* w_gate, const float* b_gate,
                         const float* logits_in, float* logits_out, int32_t* topk_idx,
                         float* topk_w, int T, int d, int E, int k, hipStream_t s);
@@ -102,6 +102,9 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
 hipError_t launch_ep_plan(int E, int R, int extra, const int32_t* offsets,
                           int32_t* replica_start, int32_t* replica_row0, int32_t* replica_rows,
                           int32_t* replica_rank, int32_t* rank_rows, hipStream_t s);
+hipError_t launch_dispatch_layout(int n, int R, const int32_t* seg_rows, const int32_t* seg_rank,
+                                  int32_t* send_counts, int32_t* send_offsets,
+                                  int32_t* seg_send_offset, hipStream_t s);
 
 // ---- cross-layer correlation and popularity prediction (correl.hip)
 hipError_t launch_cooccurrence(int E_a, int E_b, int k_a, int k_b, int T, int window,

@@ -465,6 +465,18 @@ moe_status moe_ep_plan(int32_t E, int32_t R, int32_t extra, const int32_t* offse
   return MOE_OK;
 }
 
+moe_status moe_dispatch_layout(int32_t n, int32_t R, const int32_t* seg_rows,
+                               const int32_t* seg_rank, int32_t* send_counts,
+                               int32_t* send_offsets, int32_t* seg_send_offset, void* stream) {
+  if (n < 1 || n > MOE_PLAN_MAX_COPIES || R < 1 || R > MOE_PLAN_MAX_RANKS)
+    return MOE_ERR_INVALID_ARG;
+  if (!ptrs_ok(seg_rows, seg_rank, send_counts, send_offsets, seg_send_offset))
+    return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_dispatch_layout(n, R, seg_rows, seg_rank, send_counts, send_offsets,
+                                 seg_send_offset, as_stream(stream)));
+  return MOE_OK;
+}
+
 moe_status moe_cooccurrence_update(int32_t E_a, int32_t E_b, int32_t k_a, int32_t k_b,
                                    int32_t T, int32_t window, int64_t iter,
                                    const int32_t* idx_a, const int32_t* idx_b, int32_t* ring,

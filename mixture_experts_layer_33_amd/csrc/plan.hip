@@ -176,4 +176,64 @@ hipError_t launch_ep_plan(int E, int R, int extra, const int32_t* offsets,
   return hipGetLastError();
 }
 
+// All-to-All split sizes of a dispatch (A Survey on Mixture of Experts, §5
+// System Design, first paragraph: the packed per-expert rows are what the
+// All-to-All sends).  Segment i (an expert's packed rows, or a copy's share
+// of them) holds seg_rows[i] rows for rank seg_rank[i]; the send buffer holds
+// rank 0's rows, then rank 1's, ..., segments of one rank in index order.
+// One wavefront, lane r owning rank r: it walks the segments in order (their
+// rows and ranks staged in LDS) and gives each of its own the running row
+// count; a wavefront scan of the per-rank totals gives the rank offsets.  A
+// segment whose rank is outside [0, R) is in no count and gets offset -1.
+__global__ void __launch_bounds__(64)
+dispatch_layout_kernel(int n, int R, const int32_t* __restrict__ seg_rows,
+                       const int32_t* __restrict__ seg_rank, int32_t* __restrict__ send_counts,
+                       int32_t* __restrict__ send_offsets, int32_t* __restrict__ seg_send_offset) {
+  __shared__ int s_rows[MOE_PLAN_MAX_COPIES];
+  __shared__ int s_rank[MOE_PLAN_MAX_COPIES];
+  __shared__ int s_local[MOE_PLAN_MAX_COPIES];
+  __shared__ int s_base[MOE_PLAN_MAX_RANKS];
+  const int lane = threadIdx.x;
+  for (int i = lane; i < n; i += 64) {
+    s_rows[i] = seg_rows[i];
+    s_rank[i] = seg_rank[i];
+  }
+  __syncthreads();
+  int run = 0;
+  for (int i = 0; i < n; ++i) {
+    if (s_rank[i] == lane) {
+      s_local[i] = run;
+      run += s_rows[i];
+    }
+  }
+  // exclusive scan of the per-rank totals (lanes >= R hold nothing)
+  const int total_r = lane < R ? run : 0;
+  int incl = total_r;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  const int base = incl - total_r;
+  if (lane < R) {
+    send_counts[lane] = total_r;
+    send_offsets[lane] = base;
+    s_base[lane] = base;
+  }
+  if (lane == 63) send_offsets[R] = incl;
+  __syncthreads();
+  for (int i = lane; i < n; i += 64) {
+    const int r = s_rank[i];
+    seg_send_offset[i] = (r >= 0 && r < R) ? s_base[r] + s_local[i] : -1;
+  }
+}
+
+hipError_t launch_dispatch_layout(int n, int R, const int32_t* seg_rows, const int32_t* seg_rank,
+                                  int32_t* send_counts, int32_t* send_offsets,
+                                  int32_t* seg_send_offset, hipStream_t s) {
+  hipLaunchKernelGGL(dispatch_layout_kernel, dim3(1), dim3(64), 0, s, n, R, seg_rows, seg_rank,
+                     send_counts, send_offsets, seg_send_offset);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -11,6 +11,7 @@
 // by k rounds of a 16-lane (value, index) max reduction.
 #include <type_traits>
 
+#include "buffer.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -160,13 +161,15 @@ route_kernel(const ActT* __restrict__ x, const float* __restrict__ w_gate,
 }
 
 // ---------------------------------------------------------------------------
-// bf16 activations: the router product on MFMA.  W_gate (float32) is split
-// exactly into three bf16 parts, W = hi + mid + lo (each part takes the next
-// 8 bits of the 24-bit significand); bf16 x times each bf16 part is exact in
-// float32, so logits = sum over the three parts of x W_p with float32
-// accumulation: float32 accuracy at matrix-core rate.  The split happens
-// while W_gate is staged into LDS, as [3][EP][SW] (EP = E rounded up to 16,
-// extra rows zero), so there is no separate pass over W_gate.
+// bf16 activations: router logits as a tiled product on the matrix cores.
+//
+// Each float32 W_gate value is split exactly into three bf16 parts,
+// W = hi + mid + lo, each part taking the next 8 bits of the 24-bit
+// significand.  A bf16 x times a bf16 part is exact in float32, so summing
+// x*hi + x*mid + x*lo with float32 accumulation gives float32 accuracy at
+// matrix-core rate.  The split happens in registers, on the fragment a
+// wavefront is about to use, so every W_gate value is split once per
+// workgroup and W_gate is staged in its own float32 layout.
 __device__ __forceinline__ void split3(float v, bf16& hi, bf16& mid, bf16& lo) {
   hi = (bf16)v;
   const float r1 = v - (float)hi;
@@ -183,248 +186,330 @@ __device__ __forceinline__ void unroll_stages(F&& f) {
   }
 }
 
-// LDS row of SW bf16 (SW/8 16-byte chunks), chunks XOR-swizzled by the low
-// row bits so that the 16 rows of an MFMA operand read fall in different
-// banks.
-template <int SW>
-__device__ __forceinline__ int rswz(int row, int kc) {
-  constexpr int XM = (SW / 8 < 16 ? SW / 8 : 16) - 1;
-  return row * SW + ((kc ^ (row & XM)) * 8);
+// Router tile: one workgroup per BM tokens computes their logits against all
+// experts (v_mfma_f32_16x16x32_bf16, blocks of 16 tokens x 16 experts; EP =
+// E rounded up to a power of two >= 16), then selects each token's top k.
+//
+// The four wavefronts split the work WM x WN x WK ways: token blocks, expert
+// blocks, and the 32-deep k slices of each stage (their partial logits are
+// summed in a fixed order at the end).  Splitting k keeps the LDS reads per
+// MFMA lowest and has every W_gate value split by one wavefront only, so it
+// is preferred while the accumulators fit in registers.  A stage holds the x
+// tile [BM][KD] (bf16) and the KD rows of W_gate [KD][E] (float32, one
+// contiguous run of memory), copied global -> LDS by the buffer unit (16
+// bytes a lane, no registers; rows past the last token land as zeros; d is a
+// multiple of KD).  STAGES stages rotate, STAGES - 1 of them in flight, each
+// its own LDS object so that the compiler keeps the copies in flight past the
+// reads of other stages.  With few experts the kernel streams x from HBM; the
+// stage count sets how many bytes each CU keeps in flight.
+//
+// x rows in LDS are KD * 2 bytes.  Rows shorter than 256 bytes: chunk kc of
+// row r sits at kc ^ ((r / rows per 256 bytes) % chunks per row); longer
+// rows: at kc ^ (r % 16).  Either way the 16 rows of a fragment read (one
+// 16-byte chunk each) fall in 16 different 16-byte bank groups.
+template <int BM, int EP, int EW, int WM, int WN, int WK, int KD, int STAGES>
+struct RouteCfg {
+  static constexpr int FM = BM / 16 / WM;           // token blocks per wavefront
+  static constexpr int FN = EP / 16 / WN;           // expert blocks per wavefront
+  static constexpr int ROWB = KD * 2;               // bytes of an x row in LDS
+  static constexpr int CPR = KD / 8;                // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROWB;           // rows per wave copy instruction
+  static constexpr int XB = BM * ROWB;              // x tile bytes
+  static constexpr int WB = (KD * EW * 4 + 1023) / 1024 * 1024;  // W_gate rows (E <= EW)
+  static constexpr int STAGE = XB + WB;
+  static constexpr int NX = XB / 1024, NW = WB / 1024;  // copy instructions per stage (most)
+  static constexpr int NXW = (NX + 3) / 4, NWW = (NW + 3) / 4;  // per wavefront
+  static constexpr int NPW = NXW + NWW;             // copies per wavefront per stage
+  static constexpr int SL = KD / 32 / WK;           // MFMA k slices per wavefront per stage
+  static_assert(WM * WN * WK == 4, "four wavefronts");
+  static_assert(FM >= 1 && FN >= 1 && FM * 16 * WM == BM && FN * 16 * WN == EP, "blocks");
+  static_assert(EW == EP || (EW == 8 && EP == 16), "staged experts");
+  static_assert(SL >= 1 && SL * 32 * WK == KD, "whole slices per wavefront");
+  static_assert(XB % 1024 == 0 && ROWB <= 1024, "whole copy instructions");
+  static_assert(NPW * (STAGES - 2) <= 63, "s_waitcnt vmcnt counts at most 63");
+  static_assert(STAGES >= 2, "double buffering at least");
+};
+
+template <int KD>
+__device__ __forceinline__ int route_swz(int row) {
+  if constexpr (KD * 2 >= 256) return row & 15;
+  else return (row / (256 / (KD * 2))) & (KD / 8 - 1);
 }
 
-// Router logits on MFMA (v_mfma_f32_16x16x32_bf16, 16 tokens x 16 experts per
-// block).  Four wavefronts; KS of them share TG groups of 16 tokens and split
-// the k range of every LDS stage between them, their partial logits summed
-// in LDS in a fixed order, so a workgroup covers 64 TG / KS tokens (KS > 1
-// gives small batches enough workgroups; TG > 1 reuses each staged W_gate
-// slice for more tokens when experts are many).  Loads run D stages ahead, in
-// D register sets: W_gate through registers into LDS (split on the way, two
-// LDS buffers), x fragments straight into registers.  With few experts each
-// stage holds little work, so the kernel is bound by how many bytes each CU
-// keeps in flight: D sets the depth of that queue.
-template <int EP, int KS, int TG, int D, int UW>
+template <int BM, int EP, int EW, int WM, int WN, int WK, int KD, int STAGES>
 __global__ void __launch_bounds__(256)
-route_mfma_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
+route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
                   const float* __restrict__ b_gate, float* __restrict__ logits_out,
                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int d, int E,
                   int k) {
-  constexpr int BK = EP > 128 ? 32 : 64;          // k per wavefront per stage
-  constexpr int SW = KS * BK;                     // k per stage
-  constexpr int FN = EP / 16;
-  constexpr int ROWS = 3 * EP;                    // LDS rows per stage
-  constexpr int CPR = SW / 8;                     // 8-k chunks per row
-  constexpr int EU = EP / UW;                     // expert groups of a copy unit
-  constexpr int NU = EU * CPR;                    // (group, chunk) copy units per stage
-  constexpr int NCH = (NU + 255) / 256;           // copy units per thread
-  constexpr int TPW = 64 / KS * TG;               // tokens per workgroup
-  constexpr int NS = BK / 32;                     // MFMA k slices per wavefront per stage
-  __shared__ __attribute__((aligned(16))) bf16 lds[2][ROWS * SW];
-  __shared__ f32x4 red[KS > 1 ? 4 : 1][KS > 1 ? 64 * FN * TG : 1];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int grp = wid / KS, ks = wid % KS;
-  const int t0 = blockIdx.x * TPW + grp * 16 * TG;
-  const bf16* xrow[TG];
-#pragma unroll
-  for (int g = 0; g < TG; ++g) {
-    const int ta = min(t0 + g * 16 + (lane & 15), T - 1);  // A-fragment row (clamped)
-    xrow[g] = x + (size_t)ta * d + ks * BK + (lane >> 4) * 8;
-  }
-  f32x4 acc[TG][FN];
-#pragma unroll
-  for (int g = 0; g < TG; ++g)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the epilogue's gate bias (expert 16 j + lane % 16), loaded before the k
-  // loop so that its latency is hidden
-  float bias[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int e = j * 16 + (lane & 15);
-    bias[j] = (e < E) ? b_gate[e] : 0.f;
-  }
+  using Cf = RouteCfg<BM, EP, EW, WM, WN, WK, KD, STAGES>;
+  constexpr int FM = Cf::FM, FN = Cf::FN;
+  constexpr int S1 = STAGES > 1 ? Cf::STAGE : 16, S2 = STAGES > 2 ? Cf::STAGE : 16;
+  constexpr int S3 = STAGES > 3 ? Cf::STAGE : 16, S4 = STAGES > 4 ? Cf::STAGE : 16;
+  constexpr int S5 = STAGES > 5 ? Cf::STAGE : 16, S6 = STAGES > 6 ? Cf::STAGE : 16;
+  constexpr int S7 = STAGES > 7 ? Cf::STAGE : 16;
+  static_assert(STAGES <= 8, "at most eight stages");
+  __shared__ __attribute__((aligned(16))) char st0[Cf::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[S1];
+  __shared__ __attribute__((aligned(16))) char st2[S2];
+  __shared__ __attribute__((aligned(16))) char st3[S3];
+  __shared__ __attribute__((aligned(16))) char st4[S4];
+  __shared__ __attribute__((aligned(16))) char st5[S5];
+  __shared__ __attribute__((aligned(16))) char st6[S6];
+  __shared__ __attribute__((aligned(16))) char st7[S7];
+  __shared__ __attribute__((aligned(16))) char dummy[1024];  // target of padding copies
+  __shared__ float red[WK][16][EP + 1];                      // one token block's logits
+  char* const stage[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
 
-  // A copy unit is 8 consecutive k rows of W_gate (one LDS chunk) for UW
-  // consecutive experts: eight 16-byte loads when UW = 4 (E a multiple of 4,
-  // so with W_gate 16-byte aligned every row is), eight 4-byte ones when
-  // UW = 1.  Wide units pay
-  // off only when there are enough of them to occupy every thread.  Experts
-  // from E up to EP read a real expert's weights instead (clamped address,
-  // no branch): their logit columns are never read, and each output column
-  // of the product depends only on its own W_gate column.
-  static_assert(UW == 1 || UW == 4, "copy units are 1 or 4 experts wide");
-  static_assert(D >= 2 && D % 2 == 0, "register sets alternate over the two LDS buffers");
-  using WV = std::conditional_t<UW == 4, f32x4, float>;
-  WV wr[D][NCH][8];         // W_gate of the stages ahead (D register sets)
-  bf16x8 xr[D][TG][NS];     // x fragments of the stages ahead
-  int woff[NCH];            // element offset of each unit's first W_gate entry
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int q = tid + c * 256, eu = q % EU, kc = q / EU;
-    woff[c] = kc * 8 * E + min(UW * eu, E - UW);
-  }
-  auto load_w = [&](int kt, WV(&dst)[NCH][8]) {
-    const float* wk = w_gate + (size_t)kt * SW * E;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (NU % 256 != 0 && tid + c * 256 >= NU) continue;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dst[c][i] = *reinterpret_cast<const WV*>(wk + (size_t)i * E + woff[c]);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = (int)uniform((uint32_t)tid >> 6);
+  const int kw = wid % WK, wn = (wid / WK) % WN, wm = wid / (WK * WN);
+  const int t0 = blockIdx.x * BM;
+  const int rows_valid = min(BM, T - t0);
+  const int nst = d / KD;
+  // this stage's W_gate rows: KD * E floats, copied as whole 1 KiB pieces
+  const int nw = (KD * E * 4 + 1023) / 1024;
+
+  // Copy slots of this wavefront: NXW of x (instruction wid + 4 i of the
+  // stage's NX) then NWW of W_gate (wid + 4 i of nw).  A slot past its count
+  // is padding: no bytes, written to `dummy`.  Only the lane offsets are
+  // kept; the stage's k offset goes into the scalar offset.
+  uint32_t voff[Cf::NPW];
+  int ldst[Cf::NPW];  // LDS offset in the stage, or -1 (padding)
+  unroll_stages<0, Cf::NPW>([&](auto J_) __attribute__((always_inline)) {
+    constexpr int j = decltype(J_)::value;
+    constexpr bool isx = j < Cf::NXW;
+    const int q = wid + 4 * (isx ? j : j - Cf::NXW);
+    const bool pad = q >= (isx ? Cf::NX : nw);
+    if constexpr (isx) {
+      const int row = q * Cf::RPI + lane / Cf::CPR;
+      const int kc = (lane % Cf::CPR) ^ route_swz<KD>(row);
+      voff[j] = pad ? kPadOffset : (uint32_t)(row * d + kc * 8) * 2u;
+    } else {
+      voff[j] = pad ? kPadOffset : (uint32_t)(q * 1024 + lane * 16);
     }
+    ldst[j] = pad ? -1 : (isx ? 0 : Cf::XB) + q * 1024;
+  });
+  const bf16* xbase = x + (size_t)t0 * d;
+  const uint32_t xbytes = (uint32_t)rows_valid * (uint32_t)d * 2u;
+  const uint32_t wbytes = (uint32_t)d * (uint32_t)E * 4u;
+
+  auto issue = [&](int kt, char* dst) __attribute__((always_inline)) {
+    const bool live = kt < nst;
+    const Rsrc rx = make_rsrc(xbase, live ? xbytes : 0u);
+    const Rsrc rw = make_rsrc(w_gate, live ? wbytes : 0u);
+    unroll_stages<0, Cf::NPW>([&](auto J_) __attribute__((always_inline)) {
+      constexpr int j = decltype(J_)::value;
+      char* to = ldst[j] < 0 ? dummy : dst + ldst[j];
+      if constexpr (j < Cf::NXW)
+        copy16(rx, to, voff[j], (uint32_t)(kt * KD) * 2u);
+      else
+        copy16(rw, to, voff[j], (uint32_t)(kt * KD) * (uint32_t)E * 4u);
+    });
   };
-  auto store_w = [&](int buf, const WV(&src)[NCH][8]) {
+
+  f32x4 acc[FM][FN];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int q = tid + c * 256, eu = q % EU, kc = q / EU;
-      if (NU % 256 != 0 && q >= NU) continue;
+  for (int m = 0; m < FM; ++m)
 #pragma unroll
-      for (int u = 0; u < UW; ++u) {
-        bf16x8 hi, mid, lo;
+    for (int n = 0; n < FN; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int r16 = lane & 15, kq = lane >> 4;
+  // this lane's expert in each of the wavefront's expert blocks (experts past
+  // E read a real expert's weights; their logit columns are never used)
+  int ecol[FN];
+#pragma unroll
+  for (int n = 0; n < FN; ++n) ecol[n] = min((wn * FN + n) * 16 + r16, E - 1);
+  auto compute = [&](const char* st) __attribute__((always_inline)) {
+    const char* xs = st;
+    const float* ws = reinterpret_cast<const float*>(st + Cf::XB);
+#pragma unroll
+    for (int s = 0; s < Cf::SL; ++s) {
+      const int sl = kw * Cf::SL + s;  // slice of the stage
+      const int kc = sl * 4 + kq;
+      bf16x8 a[FM];
+#pragma unroll
+      for (int m = 0; m < FM; ++m) {
+        const int row = (wm * FM + m) * 16 + r16;
+        a[m] = *reinterpret_cast<const bf16x8*>(xs + row * Cf::ROWB +
+                                                ((kc ^ route_swz<KD>(row)) * 16));
+      }
+#pragma unroll
+      for (int n = 0; n < FN; ++n) {
+        // 8 consecutive k of this lane's expert, split into the 3 parts
+        bf16x8 pw[3];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float v;
-          if constexpr (UW == 4) v = src[c][i][u];
-          else v = src[c][i];
-          bf16 h, m, l;
-          split3(v, h, m, l);
-          hi[i] = h;
-          mid[i] = m;
-          lo[i] = l;
+          bf16 h, md, l;
+          split3(ws[(kc * 8 + i) * E + ecol[n]], h, md, l);
+          pw[0][i] = h;
+          pw[1][i] = md;
+          pw[2][i] = l;
         }
-        const int e = UW * eu + u;
-        *reinterpret_cast<bf16x8*>(&lds[buf][rswz<SW>(e, kc)]) = hi;
-        *reinterpret_cast<bf16x8*>(&lds[buf][rswz<SW>(EP + e, kc)]) = mid;
-        *reinterpret_cast<bf16x8*>(&lds[buf][rswz<SW>(2 * EP + e, kc)]) = lo;
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int m = 0; m < FM; ++m)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], pw[p], acc[m][n], 0, 0, 0);
       }
     }
   };
-  auto load_x = [&](int kt, bf16x8(&dst)[TG][NS]) {
-#pragma unroll
-    for (int g = 0; g < TG; ++g)
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        dst[g][s] = *reinterpret_cast<const bf16x8*>(xrow[g] + (size_t)kt * SW + s * 32);
+  // wait until this wavefront's copies of stage kt have landed (the later
+  // STAGES - 2 stages stay in flight) and its LDS reads are done, then meet
+  // the other wavefronts
+  auto sync = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(Cf::NPW * (STAGES - 2))
+                 : "memory");
   };
-  const int nk = d / SW;
-  // step kt: register set P = kt % D, LDS buffer kt % 2.  Stage kt's W_gate
-  // is already in LDS, so wr[P] takes the loads of stage kt + D; after the
-  // MFMAs, stage kt + 1 (loaded D - 1 steps earlier) goes into the other LDS
-  // buffer, and xr[P] takes the x fragments of stage kt + D
-  auto step = [&](auto P_, int kt) {
-    constexpr int P = decltype(P_)::value;
-    constexpr int L = P % 2;
-    if (kt + D < nk) load_w(kt + D, wr[P]);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int kc = ks * (BK / 8) + s * 4 + (lane >> 4);
-#pragma unroll
-      for (int p = 0; p < 3; ++p)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = p * EP + j * 16 + (lane & 15);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&lds[L][rswz<SW>(row, kc)]);
-#pragma unroll
-          for (int g = 0; g < TG; ++g)
-            acc[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[P][g][s], b, acc[g][j], 0, 0,
-                                                                0);
-        }
-    }
-    if (kt + 1 < nk) store_w(L ^ 1, wr[(P + 1) % D]);
-    if (kt + D < nk) load_x(kt + D, xr[P]);
-    __syncthreads();
+  // step kt on stage buffer S (= kt % STAGES): refill the buffer stage kt - 1
+  // used with stage kt + STAGES - 1, then compute on stage kt
+  auto step = [&](auto S_, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value;
+    sync();
+    issue(kt + STAGES - 1, stage[(S + STAGES - 1) % STAGES]);
+    compute(stage[S]);
   };
-  unroll_stages<0, D>([&](auto P_) {
-    constexpr int P = decltype(P_)::value;
-    if (P < nk) {
-      load_w(P, wr[P]);
-      load_x(P, xr[P]);
-    }
+  unroll_stages<0, STAGES - 1>([&](auto P_) __attribute__((always_inline)) {
+    issue(decltype(P_)::value, stage[decltype(P_)::value]);
   });
-  store_w(0, wr[0]);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += D)
-    unroll_stages<0, D>([&](auto P_) {
-      if (kt + decltype(P_)::value < nk) step(P_, kt + decltype(P_)::value);
+  for (int kt = 0; kt < nst; kt += STAGES)
+    unroll_stages<0, STAGES>([&](auto P_) __attribute__((always_inline)) {
+      if (kt + decltype(P_)::value < nst) step(P_, kt + decltype(P_)::value);
     });
-  if constexpr (KS > 1) {
+  // padding copies past the last stage are still in flight
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // epilogue, one block of 16 tokens at a time: the wavefronts holding the
+  // block's logits write them (partial sums per k-group) to LDS, then each
+  // 16-lane group takes one token: sum of the partials in k order, + bias,
+  // top-k, gate weights
+  constexpr int EPL = EP / 16;  // experts per lane of a 16-lane group
+  const int gl = lane & 15, grp = tid >> 4;
+  float bias[EPL];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) red[wid][lane * FN + j] = acc[0][j];
+  for (int q = 0; q < EPL; ++q) {
+    const int e = gl + 16 * q;
+    bias[q] = (e < E) ? b_gate[e] : 0.f;
+  }
+  for (int mb = 0; mb < BM / 16; ++mb) {
+    // (m compile-time: the accumulators stay in registers)
+#pragma unroll
+    for (int m = 0; m < FM; ++m) {
+      if (mb != wm * FM + m) continue;
+#pragma unroll
+      for (int n = 0; n < FN; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          red[kw][kq * 4 + i][(wn * FN + n) * 16 + r16] = acc[m][n][i];
+    }
     __syncthreads();
-    if (ks != 0) return;
+    const int t = t0 + mb * 16 + grp;
+    float v[EPL];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      f32x4 sum = red[wid][lane * FN + j];
+    for (int q = 0; q < EPL; ++q) {
+      float sum = red[0][grp][gl + 16 * q];
 #pragma unroll
-      for (int q = 1; q < KS; ++q) {
-        const f32x4 o = red[wid + q][lane * FN + j];
+      for (int w = 1; w < WK; ++w) sum += red[w][grp][gl + 16 * q];
+      v[q] = sum + bias[q];
+    }
+    __syncthreads();  // red is rewritten by the next block
+    if (t >= T) continue;
+    if (logits_out != nullptr) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sum[i] += o[i];
+      for (int q = 0; q < EPL; ++q) {
+        const int e = gl + 16 * q;
+        if (e < E) logits_out[(size_t)t * E + e] = v[q];
       }
-      acc[0][j] = sum;
+    }
+    // a NaN logit ranks as -inf (selection stays total, indices in [0, E))
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) v[q] = v[q] != v[q] ? -INFINITY : v[q];
+    // k rounds of a (value desc, index asc) maximum over the group; rounds
+    // unrolled to the largest k so the selections stay in registers
+    unsigned taken = 0;
+    float sv[MOE_MAX_TOPK];
+    int si[MOE_MAX_TOPK];
+#pragma unroll
+    for (int r = 0; r < MOE_MAX_TOPK; ++r) {
+      sv[r] = 0.f;
+      si[r] = 0;
+      if (r >= k) continue;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        const int e = gl + 16 * q;
+        if (e < E && !((taken >> q) & 1u) && better(v[q], e, bv, bi)) {
+          bv = v[q];
+          bi = e;
+        }
+      }
+      row16_best(bv, bi);
+      if ((bi & 15) == gl) taken |= 1u << (bi >> 4);
+      sv[r] = bv;
+      si[r] = bi;
+    }
+    // lane r of the group writes choice r
+    float sum = 0.f, mine = 0.f;
+    int mine_i = 0;
+#pragma unroll
+    for (int r = 0; r < MOE_MAX_TOPK; ++r) {
+      if (r >= k) continue;
+      const float p = expf(sv[r] - sv[0]);
+      sum += p;
+      if (r == gl) {
+        mine = p;
+        mine_i = si[r];
+      }
+    }
+    if (gl < k) {
+      topk_idx[(size_t)t * k + gl] = mine_i;
+      topk_w[(size_t)t * k + gl] = mine * (1.0f / sum);
     }
   }
-
-  // lane holds tokens t0 + 16 g + (lane/16)*4 + i (i < 4), experts j*16 + lane%16
-  const int gl = lane & 15;
-#pragma unroll
-  for (int g = 0; g < TG; ++g)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + g * 16 + (lane >> 4) * 4 + i;
-      float v[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) v[j] = acc[g][j][i] + bias[j];
-      if (logits_out != nullptr && t < T) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int e = j * 16 + gl;
-          if (e < E) logits_out[(size_t)t * E + e] = v[j];
-        }
-      }
-      // a NaN logit ranks as -inf (selection stays total, indices in [0, E))
-#pragma unroll
-      for (int j = 0; j < FN; ++j) v[j] = v[j] != v[j] ? -INFINITY : v[j];
-      unsigned taken = 0;
-      float sv[MOE_MAX_TOPK];
-      int si[MOE_MAX_TOPK];
-      for (int r = 0; r < k; ++r) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int e = j * 16 + gl;
-          if (e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
-            bv = v[j];
-            bi = e;
-          }
-        }
-        row16_best(bv, bi);
-        if ((bi & 15) == gl) taken |= 1u << (bi >> 4);
-        sv[r] = bv;
-        si[r] = bi;
-      }
-      if (gl == 0 && t < T) {
-        float pr[MOE_MAX_TOPK];
-        float sum = 0.f;
-        for (int r = 0; r < k; ++r) {
-          pr[r] = expf(sv[r] - sv[0]);
-          sum += pr[r];
-        }
-        const float inv = 1.0f / sum;
-        for (int r = 0; r < k; ++r) {
-          topk_idx[(size_t)t * k + r] = si[r];
-          topk_w[(size_t)t * k + r] = pr[r] * inv;
-        }
-      }
-    }
 }
 
-// Stages of loads in flight: deeper only where one wavefront covers a whole
-// stage's k range (the per-stage work is least there).
-constexpr int route_depth(int EP, int KS, int TG) { return KS == 1 && EP * TG < 128 ? 4 : 2; }
+// Launch shapes.  Tokens per workgroup BM: enough workgroups for every CU
+// (BM = T / 256 rounded down to a power of two, 16..128; 64 at most with 256
+// experts).  Wavefronts split k (four ways when a stage has four slices) as
+// far as the accumulators allow, then experts, then tokens.  Stage depth KD:
+// 128 where four wavefronts split it (d a multiple of 128), else 64 (32 with
+// 256 experts).  Stages: as many as fit in LDS, at most eight.
+struct RouteShape {
+  int bm, wm, wn, wk, kd;
+};
+static RouteShape route_shape(int T, int d, int EP) {
+  int bm = 16;
+  while (bm < 128 && T / (2 * bm) >= 256) bm *= 2;
+  if (EP == 256) return {bm > 64 ? 64 : bm, 1, 4, 1, 32};
+  if (EP >= 64) {
+    if (EP == 64 && bm == 128) return {128, 1, 4, 1, 64};
+    return {bm, 1, 2, 2, 64};
+  }
+  const bool k128 = d % 128 == 0;
+  if (EP == 32) {
+    if (bm == 128) return {128, 1, 2, 2, k128 ? 128 : 64};
+    return k128 ? RouteShape{bm, 1, 1, 4, 128} : RouteShape{bm, 1, 2, 2, 64};
+  }
+  // EP == 16
+  if (k128) return {bm, 1, 1, 4, 128};
+  return {bm < 32 ? 32 : bm, 2, 1, 2, 64};
+}
 
-// Experts per W_gate copy unit: 4 once that still leaves 256 units per stage.
-constexpr int route_unit(int EP, int KS) { return EP * KS * (EP > 128 ? 32 : 64) >= 8192 ? 4 : 1; }
+template <int BM, int EP, int EW, int WM, int WN, int WK, int KD>
+static void launch_route_tile(hipStream_t s, const bf16* x, const float* w_gate, const float* b,
+                              float* lo, int32_t* idx, float* w, int T, int d, int E, int k) {
+  using C2 = RouteCfg<BM, EP, EW, WM, WN, WK, KD, 2>;
+  // LDS: the stages, the epilogue's partial logits and the padding target
+  constexpr int RED = WK * 16 * (EP + 1) * 4;
+  constexpr int FIT = (160 * 1024 - RED - 1024 - 512) / C2::STAGE;
+  constexpr int VM = 63 / C2::NPW + 2;
+  constexpr int MAXS = FIT < VM ? FIT : VM;
+  constexpr int STAGES = MAXS < 2 ? 2 : (MAXS > 8 ? 8 : MAXS);
+  hipLaunchKernelGGL((route_tile_kernel<BM, EP, EW, WM, WN, WK, KD, STAGES>),
+                     dim3((T + BM - 1) / BM), dim3(256), 0, s, x, w_gate, b, lo, idx, w, T, d, E,
+                     k);
+}
 
 int route_padded_experts(int E) {
   int ep = 16;
@@ -436,59 +521,50 @@ hipError_t launch_route(int act, const void* x, const float* w_gate, const float
                         const float* logits_in, float* logits_out, int32_t* topk_idx,
                         float* topk_w, int T, int d, int E, int k, hipStream_t s) {
   if (act == MOE_BF16 && logits_in == nullptr) {
-    const int EP = route_padded_experts(E);
-    // Token groups per wavefront (TG): as many as keep one workgroup per CU
-    // (and the registers unspilled); then, for batches too
-    // small for that, split each stage's k range over KS wavefronts (LDS
-    // and d permitting).
-    const int bk = EP > 128 ? 32 : 64;
-    const int max_tg = EP <= 64 ? 4 : EP == 128 ? 2 : 1;  // more would spill
-    const int max_ks = EP <= 32 ? 4 : EP == 64 ? 2 : 1;
-    int tg = 1, ks = 1;
-    while (tg < max_tg && (T + 64 * 2 * tg - 1) / (64 * 2 * tg) >= 256) tg *= 2;
-    if (tg == 1)
-      while (ks < max_ks && (T + 64 / ks - 1) / (64 / ks) < 256 && d % (2 * ks * bk) == 0)
-        ks *= 2;
-    const int tpw = 64 / ks * tg;
-    dim3 grid((T + tpw - 1) / tpw), block(256);
-    const bf16* xs = (const bf16*)x;
-#define MOE_ROUTE_U(EPV, KSV, TGV, UWV)                                                      \
-  hipLaunchKernelGGL((route_mfma_kernel<EPV, KSV, TGV, route_depth(EPV, KSV, TGV), UWV>), grid, \
-                     block, 0, s, xs, w_gate, b_gate, logits_out, topk_idx, topk_w, T, d, E, k)
-#define MOE_ROUTE(EPV, KSV, TGV) MOE_ROUTE_U(EPV, KSV, TGV, route_unit(EPV, KSV))
-    if (route_unit(EP, ks) == 4 && E % 4 != 0) {
-      // rows of W_gate not 16-byte aligned: copied one expert at a time, one
-      // token group per wavefront
-      grid = dim3((T + 63) / 64);
-      switch (EP) {  // four-expert units never run at EP = 16
-        case 32: MOE_ROUTE_U(32, 1, 1, 1); break;
-        case 64: MOE_ROUTE_U(64, 1, 1, 1); break;
-        case 128: MOE_ROUTE_U(128, 1, 1, 1); break;
-        default: MOE_ROUTE_U(256, 1, 1, 1); break;
-      }
-      return hipGetLastError();
+    const int EP = route_padded_experts(E), EW = E <= 8 ? 8 : EP;
+    const RouteShape r = route_shape(T, d, EP);
+    const bf16* xs = static_cast<const bf16*>(x);
+    const int key = EW * 1000000 + r.bm * 1000 + r.wm * 100 + r.wn * 10 + r.kd / 32;
+#define MOE_RT(BM, EPV, EWV, WM, WN, WK, KD)                                                    \
+  case EWV * 1000000 + BM * 1000 + WM * 100 + WN * 10 + KD / 32:                                \
+    launch_route_tile<BM, EPV, EWV, WM, WN, WK, KD>(s, xs, w_gate, b_gate, logits_out,          \
+                                                    topk_idx, topk_w, T, d, E, k);              \
+    break;
+#define MOE_RT16(EWV)                       \
+  MOE_RT(16, 16, EWV, 1, 1, 4, 128)         \
+  MOE_RT(32, 16, EWV, 1, 1, 4, 128)         \
+  MOE_RT(64, 16, EWV, 1, 1, 4, 128)         \
+  MOE_RT(128, 16, EWV, 1, 1, 4, 128)        \
+  MOE_RT(32, 16, EWV, 2, 1, 2, 64)          \
+  MOE_RT(64, 16, EWV, 2, 1, 2, 64)          \
+  MOE_RT(128, 16, EWV, 2, 1, 2, 64)
+    switch (key) {
+      MOE_RT16(8)
+      MOE_RT16(16)
+      MOE_RT(16, 32, 32, 1, 1, 4, 128)
+      MOE_RT(32, 32, 32, 1, 1, 4, 128)
+      MOE_RT(64, 32, 32, 1, 1, 4, 128)
+      MOE_RT(128, 32, 32, 1, 2, 2, 128)
+      MOE_RT(16, 32, 32, 1, 2, 2, 64)
+      MOE_RT(32, 32, 32, 1, 2, 2, 64)
+      MOE_RT(64, 32, 32, 1, 2, 2, 64)
+      MOE_RT(128, 32, 32, 1, 2, 2, 64)
+      MOE_RT(16, 64, 64, 1, 2, 2, 64)
+      MOE_RT(32, 64, 64, 1, 2, 2, 64)
+      MOE_RT(64, 64, 64, 1, 2, 2, 64)
+      MOE_RT(128, 64, 64, 1, 4, 1, 64)
+      MOE_RT(16, 128, 128, 1, 2, 2, 64)
+      MOE_RT(32, 128, 128, 1, 2, 2, 64)
+      MOE_RT(64, 128, 128, 1, 2, 2, 64)
+      MOE_RT(128, 128, 128, 1, 2, 2, 64)
+      MOE_RT(16, 256, 256, 1, 4, 1, 32)
+      MOE_RT(32, 256, 256, 1, 4, 1, 32)
+      MOE_RT(64, 256, 256, 1, 4, 1, 32)
+      default:
+        return hipErrorInvalidValue;
     }
-    switch ((EP * 8 + ks) * 8 + tg) {
-      case (16 * 8 + 4) * 8 + 1: MOE_ROUTE(16, 4, 1); break;
-      case (16 * 8 + 2) * 8 + 1: MOE_ROUTE(16, 2, 1); break;
-      case (16 * 8 + 1) * 8 + 1: MOE_ROUTE(16, 1, 1); break;
-      case (16 * 8 + 1) * 8 + 2: MOE_ROUTE(16, 1, 2); break;
-      case (16 * 8 + 1) * 8 + 4: MOE_ROUTE(16, 1, 4); break;
-      case (32 * 8 + 4) * 8 + 1: MOE_ROUTE(32, 4, 1); break;
-      case (32 * 8 + 2) * 8 + 1: MOE_ROUTE(32, 2, 1); break;
-      case (32 * 8 + 1) * 8 + 1: MOE_ROUTE(32, 1, 1); break;
-      case (32 * 8 + 1) * 8 + 2: MOE_ROUTE(32, 1, 2); break;
-      case (32 * 8 + 1) * 8 + 4: MOE_ROUTE(32, 1, 4); break;
-      case (64 * 8 + 2) * 8 + 1: MOE_ROUTE(64, 2, 1); break;
-      case (64 * 8 + 1) * 8 + 1: MOE_ROUTE(64, 1, 1); break;
-      case (64 * 8 + 1) * 8 + 2: MOE_ROUTE(64, 1, 2); break;
-      case (64 * 8 + 1) * 8 + 4: MOE_ROUTE(64, 1, 4); break;
-      case (128 * 8 + 1) * 8 + 1: MOE_ROUTE(128, 1, 1); break;
-      case (128 * 8 + 1) * 8 + 2: MOE_ROUTE(128, 1, 2); break;
-      default: MOE_ROUTE(256, 1, 1); break;
-    }
-#undef MOE_ROUTE_U
-#undef MOE_ROUTE
+#undef MOE_RT16
+#undef MOE_RT
     return hipGetLastError();
   }
   dim3 grid((T + kRouteTok - 1) / kRouteTok), block(kRouteThreads);

@@ -35,7 +35,8 @@ only where the layer stores a tensor):
   and Expert Replication, main contributions 2 and 3: physical copies of
   experts by token demand, their number limited by GPU memory) and
   least-loaded placement of the copies on ranks (LLEP notes, §2.1: work goes
-  to the least-loaded GPU);
+  to the least-loaded GPU); the All-to-All split sizes and send-buffer
+  offsets of an expert -> rank map or of such a plan;
 * cross-layer expert correlation and popularity prediction (PopFetcher notes
   §4.1: tuples of a token's selections in consecutive layers; §4.2, Eq. 2
   and Eq. 3, bodies missing: conditional probabilities from the windowed
@@ -504,6 +505,33 @@ def ep_plan(offsets, extra: int, R: int) -> Dict[str, np.ndarray]:
     i32 = lambda v: np.array(v, dtype=np.int32)  # noqa: E731
     return {"replica_start": i32(start), "replica_row0": i32(row0), "replica_rows": i32(rows),
             "replica_rank": i32(rank), "rank_rows": i32(load)}
+
+
+def dispatch_layout(seg_rows, seg_rank, R: int) -> Dict[str, np.ndarray]:
+    """All-to-All split sizes of a dispatch (A Survey on Mixture of Experts,
+    §5 System Design, first paragraph: the per-expert packed rows are what
+    the All-to-All sends).  Segment i - one expert's packed rows, or one
+    copy's share of them from ep_plan - holds seg_rows[i] rows bound for rank
+    seg_rank[i].  The send buffer holds rank 0's rows, then rank 1's, ...;
+    within a rank the segments keep their index order.  Returns send_counts
+    [R] (rows per rank: the split sizes), send_offsets [R + 1] (exclusive
+    prefix sum) and seg_send_offset [n] (where segment i starts)."""
+    rows = [int(v) for v in seg_rows]
+    rank = [int(v) for v in seg_rank]
+    counts = [0] * R
+    for n_i, r in zip(rows, rank):
+        counts[r] += n_i
+    offsets = [0] * (R + 1)
+    for r in range(R):
+        offsets[r + 1] = offsets[r] + counts[r]
+    filled = list(offsets[:R])
+    start = [0] * len(rows)
+    for i, (n_i, r) in enumerate(zip(rows, rank)):
+        start[i] = filled[r]
+        filled[r] += n_i
+    i32 = lambda v: np.array(v, dtype=np.int32)  # noqa: E731
+    return {"send_counts": i32(counts), "send_offsets": i32(offsets),
+            "seg_send_offset": i32(start)}
 
 
 # --------------------------------------------------------------------------

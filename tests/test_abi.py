@@ -148,6 +148,11 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.moe_ep_plan(16, 65, 0, P, P, P, P, P, P, None) == -1
     assert L.moe_ep_plan(16, 8, -1, P, P, P, P, P, P, None) == -1
     assert L.moe_ep_plan(256, 8, 769, P, P, P, P, P, P, None) == -1
+    assert L.moe_dispatch_layout(0, 8, P, P, P, P, P, None) == -1
+    assert L.moe_dispatch_layout(1025, 8, P, P, P, P, P, None) == -1
+    assert L.moe_dispatch_layout(16, 0, P, P, P, P, P, None) == -1
+    assert L.moe_dispatch_layout(16, 65, P, P, P, P, P, None) == -1
+    assert L.moe_dispatch_layout(16, 8, P, None, P, P, P, None) == -1
     # E + extra would overflow int32: rejected before any launch
     assert L.moe_ep_plan(16, 8, 2 ** 31 - 1, P, P, P, P, P, P, None) == -1
     assert L.moe_ep_plan(256, 8, 2 ** 31 - 200, P, P, P, P, P, P, None) == -1

@@ -94,24 +94,38 @@ def test_router_logits(name):
     assert_close(down(layer.logits), ref, 1e-5, "logits")
 
 
-# (T, d, E, k) reaching each MFMA router launch shape (padded E, k-split over
-# wavefronts, 16-token groups per wavefront) that the scaled workloads do not
-ROUTER_SHAPES = {
-    "E16_tg2": (32768, 64, 16, 2),
-    "E16_tg4": (65536, 64, 16, 2),
-    "E32_ks1": (20000, 64, 32, 2),
-    "E32_tg2": (32768, 64, 32, 2),
-    "E32_tg4": (65536, 64, 32, 4),
-    "E64_ks2": (4000, 128, 64, 2),
-    "E64_ks1": (20000, 64, 64, 1),
-    "E64_tg2": (32768, 64, 64, 2),
-    "E48_tg4": (65536, 64, 48, 3),
-    # W_gate copied one expert at a time where four-expert copies would
-    # otherwise run: E not a multiple of 4
-    "E33_ks2_single_copies": (4000, 256, 33, 2),
-    "E126_single_copies": (1000, 128, 126, 4),
-    "E250_single_copies": (700, 64, 250, 8),
-}
+# (T, d, E, k) reaching each launch shape of the matrix-core router: staged
+# experts per part (8 for E <= 8, else E rounded up to a power of two >= 16)
+# x tokens per workgroup BM in {16, 32, 64, 128} (BM grows with T: 16 below
+# 8192 tokens, 32, 64 from 16384, 128 from 32768; at most 64 with 256
+# experts), each with its preferred stage depth (d a multiple of 128) and the
+# 64-deep fallback, with ragged token tails and E below its padded size
+ROUTER_SHAPES = {}
+for _ew, _es in (("EW8", (8, 7, 8, 5, 8, 8, 6, 8)), ("EW16", (16, 13, 16, 13, 16, 16, 9, 12))):
+    for _i, (_T, _d) in enumerate(((3001, 512), (3001, 320), (9000, 256), (9000, 64),
+                                   (20000, 128), (20000, 192), (40000, 128), (40000, 64))):
+        ROUTER_SHAPES[f"{_ew}_T{_T}_d{_d}"] = (_T, _d, _es[_i], 2 if _es[_i] > 1 else 1)
+ROUTER_SHAPES.update({
+    "EP32_BM16_KD128": (1000, 128, 32, 2),
+    "EP32_BM16_KD64": (1000, 192, 32, 2),
+    "EP32_BM32_KD128_padded": (9001, 128, 20, 3),
+    "EP32_BM32_KD64_padded": (9001, 64, 20, 3),
+    "EP32_BM64_KD128": (17000, 128, 32, 2),
+    "EP32_BM64_KD64": (17000, 64, 32, 2),
+    "EP32_BM128_KD128_padded": (33000, 128, 31, 4),
+    "EP32_BM128_KD64_padded": (33000, 64, 31, 4),
+    "EP64_BM16": (2000, 128, 64, 2),
+    "EP64_BM32_padded": (8192, 64, 48, 3),
+    "EP64_BM64": (16384, 64, 64, 2),
+    "EP64_BM128_top1": (32768, 64, 40, 1),
+    "EP128_BM16_padded": (1000, 128, 126, 4),
+    "EP128_BM32": (9000, 64, 128, 4),
+    "EP128_BM64_padded": (16500, 64, 100, 2),
+    "EP128_BM128": (32768, 128, 128, 4),
+    "EP256_BM16_padded": (700, 64, 250, 8),
+    "EP256_BM32": (8200, 64, 256, 2),
+    "EP256_BM64_padded": (16384, 64, 200, 8),
+})
 
 
 def _router_case(T, d, E, k):

@@ -73,3 +73,59 @@ def test_ep_plan_on_the_layers_routing(name, extra, R):
     flat = run_plan(offsets, 0, R)["rank_rows"].max()
     repl = run_plan(offsets, extra, R)["rank_rows"].max()
     assert repl <= flat
+
+
+def run_layout(seg_rows, seg_rank, R):
+    n = len(seg_rows)
+    z = lambda m: torch.full((m,), -7, dtype=torch.int32, device="cuda")  # noqa: E731
+    out = {"send_counts": z(R), "send_offsets": z(R + 1), "seg_send_offset": z(n)}
+    moe.moe_dispatch_layout(n, R, up_i32(np.asarray(seg_rows, np.int32)),
+                            up_i32(np.asarray(seg_rank, np.int32)), out["send_counts"],
+                            out["send_offsets"], out["seg_send_offset"])
+    torch.cuda.synchronize()
+    return {k: down(v) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("n,R,seed", [(1, 1, 0), (5, 3, 1), (8, 8, 2), (128, 8, 3), (300, 64, 4),
+                                      (1024, 64, 5), (1024, 1, 6), (777, 13, 7)])
+def test_dispatch_layout_matches_reference(n, R, seed):
+    """Split sizes and send-buffer offsets of random segments, bit for bit."""
+    rng = np.random.default_rng(seed)
+    rows = (rng.integers(0, 5000, n) * (rng.random(n) > 0.15)).astype(np.int32)
+    rank = rng.integers(0, R, n).astype(np.int32)
+    got = run_layout(rows, rank, R)
+    want = orc.dispatch_layout(rows, rank, R)
+    for key, v in want.items():
+        np.testing.assert_array_equal(got[key], v, err_msg=key)
+
+
+@pytest.mark.parametrize("name,extra,R", [("skewed_zipf12", 32, 8), ("fine_grained", 128, 8)])
+def test_dispatch_layout_of_expert_map_and_plan(name, extra, R):
+    """The layer's own packed rows of a skewed workload (scaled): split sizes
+    of a round-robin expert -> rank map (segments = experts, rows =
+    counts_kept) and of the dispatch plan's copies (segments = copies), both
+    against the reference; the plan's per-rank totals are its rank_rows."""
+    w = workloads.scaled(workloads.workloads()[name], T=4096, d=128, F=128)
+    inp = workloads.make_inputs(w, 0, with_weights=False)
+    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, 0.0, act_code(w.dtype), backward=False)
+    layer.route(up(inp["x"], w.dtype), up(inp["w_gate"]), up(inp["b_gate"]))
+    layer.permute(up(inp["x"], w.dtype))
+    torch.cuda.synchronize()
+    counts = down(layer.counts_kept)
+    emap = (np.arange(w.E) % R).astype(np.int32)
+    got = run_layout(counts, emap, R)
+    want = orc.dispatch_layout(counts, emap, R)
+    for key, v in want.items():
+        np.testing.assert_array_equal(got[key], v, err_msg=key)
+    plan = run_plan(down(layer.offsets), extra, R)
+    got = run_layout(plan["replica_rows"], plan["replica_rank"], R)
+    want = orc.dispatch_layout(plan["replica_rows"], plan["replica_rank"], R)
+    for key, v in want.items():
+        np.testing.assert_array_equal(got[key], v, err_msg=key)
+    np.testing.assert_array_equal(got["send_counts"], plan["rank_rows"])
+
+
+def test_dispatch_layout_out_of_range_rank():
+    got = run_layout([3, 4, 5], [0, 9, 1], 2)
+    assert got["seg_send_offset"].tolist() == [0, -1, 3]
+    assert got["send_counts"].tolist() == [3, 5]

@@ -711,3 +711,41 @@ def test_prediction_special_cases():
     np.testing.assert_allclose(pred, (10 + 20 + 40 + 50) * q / q.sum(), rtol=1e-15)
     assert orc.top_hit_rate(pred, q, n=2) == 1.0
     assert orc.top_hit_rate(pred, q[::-1], n=2) == 0.0
+
+
+# ---------------------------------------------------------------- dispatch layout
+def test_hand_worked_dispatch_layout():
+    g = load("dispatch_layout.json")
+    for c in g["cases"]:
+        out = orc.dispatch_layout(c["seg_rows"], c["seg_rank"], c["R"])
+        for key in ("send_counts", "send_offsets", "seg_send_offset"):
+            assert out[key].tolist() == c[key], (c["what"], key)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dispatch_layout_invariants(seed):
+    """Split sizes are the per-rank row sums (np.bincount); the send buffer
+    is the segments in a stable sort by rank (np.argsort kind="stable"), so
+    each segment starts at the running sum of the rows before it in that
+    order; the non-empty segments tile [0, total) exactly once; with ranks
+    non-decreasing in segment order the layout is the plain prefix sum."""
+    rng = np.random.default_rng(seed)
+    n, R = int(rng.integers(1, 300)), int(rng.integers(1, 65))
+    rows = rng.integers(0, 50, n) * (rng.random(n) > 0.2)
+    rank = rng.integers(0, R, n)
+    out = orc.dispatch_layout(rows, rank, R)
+    np.testing.assert_array_equal(out["send_counts"], np.bincount(rank, weights=rows, minlength=R))
+    order = np.argsort(rank, kind="stable")
+    start = np.zeros(n, np.int64)
+    start[order] = np.concatenate([[0], np.cumsum(rows[order])[:-1]])
+    np.testing.assert_array_equal(out["seg_send_offset"], start)
+    np.testing.assert_array_equal(out["send_offsets"],
+                                  np.concatenate([[0], np.cumsum(out["send_counts"])]))
+    cover = np.zeros(int(rows.sum()), np.int32)
+    for i in range(n):
+        cover[start[i]:start[i] + rows[i]] += 1
+    assert (cover == 1).all()
+    srt = np.sort(rank)
+    mono = orc.dispatch_layout(rows, srt, R)
+    np.testing.assert_array_equal(mono["seg_send_offset"],
+                                  np.concatenate([[0], np.cumsum(rows)[:-1]]))
