@@ -186,8 +186,13 @@ combine_bwd_kernel(const ActT* __restrict__ dy, const ActT* __restrict__ out_per
                    const int32_t* __restrict__ slot_row, ActT* __restrict__ d_out,
                    float* __restrict__ dsel, float* __restrict__ dsel_perm,
                    float* __restrict__ dlogits, const float* __restrict__ w_gate,
-                   float* __restrict__ w_gate_t, int T, int d, int E, int k) {
+                   float* __restrict__ w_gate_t, int32_t* __restrict__ counters, int T, int d,
+                   int E, int k) {
   using CK = Chunk<ActT>;
+  // the weight-gradient GEMMs later on this stream take their tiles from
+  // these counters: they start at zero
+  if (counters != nullptr && blockIdx.x == 0 && threadIdx.x < kBwdCounters)
+    counters[threadIdx.x] = 0;
   const int tok_blocks = (T + kRowThreads / 64 - 1) / (kRowThreads / 64);
   if ((int)blockIdx.x >= tok_blocks) {  // the blocks past the tokens transpose W_gate
     transpose_gate_tile(w_gate, w_gate_t, d, E, blockIdx.x - tok_blocks);
@@ -376,18 +381,19 @@ hipError_t launch_combine_bwd(int act, const void* dy, const void* out_perm,
                               const float* topk_w, const int32_t* topk_idx,
                               const int32_t* slot_row, void* d_out, float* dsel,
                               float* dsel_perm, float* dlogits, const float* w_gate,
-                              float* w_gate_t, int T, int d, int E, int k, hipStream_t s) {
+                              float* w_gate_t, int32_t* counters, int T, int d, int E, int k,
+                              hipStream_t s) {
   const int tok_blocks = (T + 3) / 4;
   const int tr_blocks = ((d + 31) / 32) * ((E + 31) / 32);
   dim3 grid(tok_blocks + tr_blocks), block(kRowThreads);
   if (act == MOE_BF16)
     hipLaunchKernelGGL(combine_bwd_kernel<bf16>, grid, block, 0, s, (const bf16*)dy,
                        (const bf16*)out_perm, topk_w, topk_idx, slot_row, (bf16*)d_out, dsel,
-                       dsel_perm, dlogits, w_gate, w_gate_t, T, d, E, k);
+                       dsel_perm, dlogits, w_gate, w_gate_t, counters, T, d, E, k);
   else
     hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, block, 0, s, (const float*)dy,
                        (const float*)out_perm, topk_w, topk_idx, slot_row, (float*)d_out, dsel,
-                       dsel_perm, dlogits, w_gate, w_gate_t, T, d, E, k);
+                       dsel_perm, dlogits, w_gate, w_gate_t, counters, T, d, E, k);
   return hipGetLastError();
 }
 

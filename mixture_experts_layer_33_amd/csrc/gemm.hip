@@ -926,10 +926,21 @@ struct WgradArgs {
   const float* gsel;
   float* dw_gate;
   float* db_gate;
+  int32_t* next_tile;  // tile queue: zero at launch
   int N1, N2, E;
 };
 
-// With GATE, the workgroups of the first N1 tile also produce the gate's
+// Persistent: one workgroup per CU takes tiles from a queue (an atomic
+// counter) in longest-processing-time order - the experts by decreasing row
+// count (ties by index), each expert's tiles row by row - so the long K loops
+// of popular experts start first and the short ones fill in behind them.  A
+// tile's float32 dW leaves through non-temporal stores that stay in flight
+// while the next tile's k loop runs (only LDS is fenced between tiles).
+// Which workgroup takes which tile varies; each tile is computed the same
+// way, so the results are bitwise reproducible.  Experts with no rows store
+// zeros.
+//
+// With GATE, the tiles of the first N1 tile row also produce the gate's
 // weight gradient over the same rows, dW_gate[:, e] = X2_e^T gsel_e and
 // db[e] = sum(gsel_e), from the X2 tiles they already stream (for FC1's
 // weight gradient X2 is x_perm and gsel the gate-softmax gradient per row).
@@ -938,6 +949,7 @@ __global__ void __launch_bounds__(kGemmThreads)
 wgrad_kernel(WgradArgs p) {
   __shared__ int s_perm[MOE_MAX_EXPERTS];
   __shared__ int s_cnt[MOE_MAX_EXPERTS];
+  __shared__ int s_tile;
   const int tid = threadIdx.x;
   if (tid < p.E) s_cnt[tid] = p.offsets[tid + 1] - p.offsets[tid];
   __syncthreads();
@@ -950,42 +962,38 @@ wgrad_kernel(WgradArgs p) {
     }
     s_perm[r] = tid;
   }
-  __syncthreads();
   const int T1 = (p.N1 + BM - 1) / BM, T2 = (p.N2 + BN - 1) / BN;
   const int per = T1 * T2;
-  // Workgroup bid runs on XCD bid % 8.  Tiles are handed out in chunks of 8
-  // consecutive tiles (one expert, neighbouring output columns, sharing the
-  // X1 tile), chunk c to XCD c % 8, so the hottest-first order holds across
-  // the XCDs and each XCD's L2 serves a chunk's shared operand once.  The
-  // tail past the last whole round of chunks keeps bid order.
-  constexpr int CH = 8;
-  const int total = gridDim.x;
-  const int full = total / (kXcds * CH) * (kXcds * CH);
-  int bid = blockIdx.x;
-  if (bid < full) {
-    const int x = bid % kXcds, i = bid / kXcds;
-    bid = ((i / CH) * kXcds + x) * CH + i % CH;
-  }
-  const int rank = bid / per, in = bid % per;
-  const int e = s_perm[rank];
-  const int t1 = in / T2, t2 = in % T2;
-  const int n1 = t1 * BM, n2 = t2 * BN;
-  const int r0 = p.offsets[e], K = s_cnt[e];
-  const int rows = min(BM, p.N1 - n1), cols = min(BN, p.N2 - n2);
+  const int total = p.E * per;
   using TG = TileGemm<BM, BN, false, false, GATE>;
-  TG tg;
   const StageBufs L = tile_lds<TG>();
-  const bool gate_here = GATE && t1 == 0;
-  tg.run(p.X1 + (size_t)r0 * p.N1 + n1, p.N1, rows, p.X2 + (size_t)r0 * p.N2 + n2, p.N2, cols, K,
-         L, gate_here ? p.gsel + r0 : nullptr);
-  store_tile<EPI_F32>(tg, L, p.C + (size_t)e * p.N1 * p.N2 + (size_t)n1 * p.N2 + n2, p.N2, rows,
-                      cols, nullptr, 0);
-  if constexpr (GATE) {
-    if (gate_here) {
-      __syncthreads();
-      tg.gate_reduce(reinterpret_cast<float*>(L.a[0]), cols, p.dw_gate + (size_t)n2 * p.E + e, p.E,
-                     t2 == 0 ? p.db_gate + e : nullptr);
+  for (;;) {
+    if (tid == 0) s_tile = atomicAdd(p.next_tile, 1);
+    __syncthreads();  // s_perm written; s_tile visible
+    const int tile = s_tile;
+    if (tile >= total) break;
+    const int e = s_perm[tile / per], in = tile % per;
+    const int t1 = in / T2, t2 = in % T2;
+    const int n1 = t1 * BM, n2 = t2 * BN;
+    const int r0 = p.offsets[e], K = s_cnt[e];
+    const int rows = min(BM, p.N1 - n1), cols = min(BN, p.N2 - n2);
+    TG tg;
+    const bool gate_here = GATE && t1 == 0;
+    tg.run(p.X1 + (size_t)r0 * p.N1 + n1, p.N1, rows, p.X2 + (size_t)r0 * p.N2 + n2, p.N2, cols,
+           K, L, gate_here ? p.gsel + r0 : nullptr);
+    store_tile<EPI_F32>(tg, L, p.C + (size_t)e * p.N1 * p.N2 + (size_t)n1 * p.N2 + n2, p.N2, rows,
+                        cols, nullptr, 0);
+    if constexpr (GATE) {
+      if (gate_here) {
+        __syncthreads();
+        tg.gate_reduce(reinterpret_cast<float*>(L.a[0]), cols, p.dw_gate + (size_t)n2 * p.E + e,
+                       p.E, t2 == 0 ? p.db_gate + e : nullptr);
+      }
     }
+    // every wave has read its epilogue strip (and the gate sums) before the
+    // next tile's copies reuse the stage buffers, and thread 0 has read
+    // s_tile before the next take rewrites it; the dW stores stay in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
 
@@ -1219,7 +1227,8 @@ static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const uint3
 
 template <int BM, int BN, bool GATE>
 static hipError_t launch_wgrad_t(const WgradArgs& p, hipStream_t s) {
-  const long long grid = (long long)p.E * ((p.N1 + BM - 1) / BM) * ((p.N2 + BN - 1) / BN);
+  const long long tiles = (long long)p.E * ((p.N1 + BM - 1) / BM) * ((p.N2 + BN - 1) / BN);
+  const long long grid = std::min<long long>(tiles, device_cus());  // one workgroup per CU
   hipLaunchKernelGGL((wgrad_kernel<BM, BN, GATE>), dim3((unsigned)grid), dim3(kGemmThreads), 0,
                      s, p);
   return hipGetLastError();
@@ -1227,9 +1236,9 @@ static hipError_t launch_wgrad_t(const WgradArgs& p, hipStream_t s) {
 
 template <bool GATE>
 static hipError_t launch_wgrad(const bf16* X1, const bf16* X2, float* C, const int32_t* offsets,
-                               const float* gsel, float* dw_gate, float* db_gate, int N1, int N2,
-                               int E, hipStream_t s) {
-  WgradArgs p{X1, X2, C, offsets, gsel, dw_gate, db_gate, N1, N2, E};
+                               const float* gsel, float* dw_gate, float* db_gate,
+                               int32_t* next_tile, int N1, int N2, int E, hipStream_t s) {
+  WgradArgs p{X1, X2, C, offsets, gsel, dw_gate, db_gate, next_tile, N1, N2, E};
   auto mt = [&](int bm) { return (long long)E * ((N1 + bm - 1) / bm); };
   const Shape2 t = pick_tile(mt, N2);
   if (t.bm == 256 && t.bn == 256) return launch_wgrad_t<256, 256, GATE>(p, s);
@@ -1302,8 +1311,8 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
                              const int32_t* offsets, const void* w1, const void* w2, void* dz,
                              void* dx_perm, float* dw1, float* dw2, const float* dsel_perm,
                              float* dw_gate, float* db_gate, const uint32_t* relu_bits_in,
-                             uint32_t* relu_bits_ws, float* partial, int S_max, int max_rows,
-                             int d, int F, int E, hipStream_t s) {
+                             uint32_t* relu_bits_ws, float* partial, int32_t* counters,
+                             int S_max, int max_rows, int d, int F, int E, hipStream_t s) {
   if (act == MOE_BF16) {
     // keep bits of the ReLU (unless the forward kept them), then
     // dz = (dO W2[e]) * [h > 0]: A = dO [rows][d], B = W2[e] as [K=d][N=F]
@@ -1321,10 +1330,10 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
                                           max_rows, partial, s)));
     // dW2[e] = dO^T h  ([d][F])
     MOE_TRY((launch_wgrad<false>((const bf16*)d_out, (const bf16*)h, dw2, offsets, nullptr,
-                                 nullptr, nullptr, d, F, E, s)));
+                                 nullptr, nullptr, counters, d, F, E, s)));
     // dW1[e] = dz^T x_perm  ([F][d]), with the gate's dW_gate / db over the kept rows
     MOE_TRY((launch_wgrad<true>((const bf16*)dz, (const bf16*)x_perm, dw1, offsets, dsel_perm,
-                                dw_gate, db_gate, F, d, E, s)));
+                                dw_gate, db_gate, counters + 1, F, d, E, s)));
     // dx_perm = dz W1[e]: A = dz [rows][F], B = W1[e] as [K=F][N=d]  (may reuse dO's
     // memory: it runs after the last reader of dO).  Last of the four, so the
     // decode of dX that follows reads dx_perm while it is still cached.

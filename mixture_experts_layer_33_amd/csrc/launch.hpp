@@ -46,12 +46,16 @@ hipError_t launch_index(const int32_t* topk_idx, const int32_t* local_rank,
 hipError_t launch_combine(int act, const void* out_perm, const float* topk_w,
                           const int32_t* slot_row, void* y, int T, int d, int k, hipStream_t s,
                           bool slot_order = false);
-// Decode backward; its extra workgroups also write w_gate_t = W_gate^T.
+// Decode backward; its extra workgroups also write w_gate_t = W_gate^T, and
+// it zeroes the kBwdCounters tile counters of the weight-gradient GEMMs that
+// follow on the stream (counters may be null).
+constexpr int kBwdCounters = 2;
 hipError_t launch_combine_bwd(int act, const void* dy, const void* out_perm,
                               const float* topk_w, const int32_t* topk_idx,
                               const int32_t* slot_row, void* d_out, float* dsel,
                               float* dsel_perm, float* dlogits, const float* w_gate,
-                              float* w_gate_t, int T, int d, int E, int k, hipStream_t s);
+                              float* w_gate_t, int32_t* counters, int T, int d, int E, int k,
+                              hipStream_t s);
 // dW_gate / db over each expert's packed rows (float32 path; bf16 folds it
 // into the FC1 weight gradient) ...
 hipError_t launch_gate_rows(int act, const void* x_perm, const float* dsel_perm,
@@ -89,13 +93,15 @@ hipError_t launch_expert_fwd_fused(int act, const void* x, const int32_t* row_to
 // dx_perm = dz W1[e]; dW1[e] = dz^T x_perm.
 // bf16 also folds dW_gate / db over the kept rows into the FC1 wgrad and
 // takes the ReLU mask from relu_bits_in if non-null, else derives it from h
-// into relu_bits_ws ([S_max][F/32] words of scratch).
+// into relu_bits_ws ([S_max][F/32] words of scratch).  The two bf16 weight
+// gradients take their tiles from counters[0] and counters[1], which must be
+// zero at launch (launch_combine_bwd zeroes them).
 hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, const void* h,
                              const int32_t* offsets, const void* w1, const void* w2,
                              void* dz, void* dx_perm, float* dw1, float* dw2,
                              const float* dsel_perm, float* dw_gate, float* db_gate,
                              const uint32_t* relu_bits_in, uint32_t* relu_bits_ws,
-                             float* partial, int S_max, int max_rows,
+                             float* partial, int32_t* counters, int S_max, int max_rows,
                              int d, int F, int E, hipStream_t s);
 
 // ---- expert-parallel dispatch plan (plan.hip)

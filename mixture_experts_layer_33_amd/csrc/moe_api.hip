@@ -97,6 +97,7 @@ struct BwdWs {
   float* dsel_perm; // [S]     the same per packed row
   float* w_gate_t;  // [E][d]
   uint32_t* relu_bits;  // [S][F/32] keep bits of the ReLU (bf16 path)
+  int32_t* counters;    // tile queues of the two weight-gradient GEMMs
   float* partial;       // split-tail partial tiles of the row-grouped GEMMs
 };
 
@@ -104,7 +105,7 @@ size_t bwd_ws_bytes(const moe_shape* s) {
   const size_t S = (size_t)slots(s), a = act_bytes(s);
   return align_up(S * s->d_model * a) + align_up(S * s->d_ff * a) + 2 * align_up(S * 4) +
          align_up((size_t)s->E * s->d_model * 4) + align_up(S * (size_t)s->d_ff / 8) +
-         rows_partial_bytes(s->act_dtype);
+         align_up(kBwdCounters * 4) + rows_partial_bytes(s->act_dtype);
 }
 
 BwdWs carve_bwd(const moe_shape* s, void* ws) {
@@ -123,6 +124,8 @@ BwdWs carve_bwd(const moe_shape* s, void* ws) {
   p += align_up((size_t)s->E * s->d_model * 4);
   w.relu_bits = reinterpret_cast<uint32_t*>(p);
   p += align_up(S * (size_t)s->d_ff / 8);
+  w.counters = reinterpret_cast<int32_t*>(p);
+  p += align_up(kBwdCounters * 4);
   w.partial = rows_partial_bytes(s->act_dtype) ? reinterpret_cast<float*>(p) : nullptr;
   return w;
 }
@@ -425,14 +428,15 @@ moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const
   hipStream_t stream_ = as_stream(stream);
   const int act = s->act_dtype;
   MOE_HIP(launch_combine_bwd(act, dy, out_perm, topk_w, topk_idx, slot_row, bw.d_out, bw.dsel,
-                             bw.dsel_perm, dlogits, w_gate, bw.w_gate_t, s->T, s->d_model, s->E,
-                             s->k, stream_));
+                             bw.dsel_perm, dlogits, w_gate, bw.w_gate_t, bw.counters, s->T,
+                             s->d_model, s->E, s->k, stream_));
   // dx_perm reuses d_out's memory: the FC1 dgrad runs after the FC2 wgrad,
   // the last reader of d_out.  For bf16 the FC1 wgrad also writes dW_gate and
   // db over the kept rows.
   MOE_HIP(launch_expert_bwd(act, bw.d_out, x_perm, h, offsets, w1, w2, bw.dz, bw.d_out, dw1, dw2,
                             bw.dsel_perm, dw_gate, db_gate, relu_bits, bw.relu_bits, bw.partial,
-                            (int)slots(s), capacity_of(s), s->d_model, s->d_ff, s->E, stream_));
+                            bw.counters, (int)slots(s), capacity_of(s), s->d_model, s->d_ff, s->E,
+                            stream_));
   if (act != MOE_BF16)
     MOE_HIP(launch_gate_rows(act, x_perm, bw.dsel_perm, offsets, dw_gate, db_gate, s->d_model,
                              s->E, stream_));
