@@ -613,6 +613,33 @@ def main():
     t_plan = time_it(lambda: moe.moe_ep_plan(w.E, R_plan, extra_plan, layer.offsets, *plan), reps)
     rank_rows = plan[4].cpu().numpy()
     plan_balance = float(rank_rows.max() / max(rank_rows.mean(), 1e-9))
+    # All-to-All split sizes of that plan's copies
+    lay_out = [zi(R_plan), zi(R_plan + 1), zi(w.E + extra_plan)]
+    t_layout = time_it(lambda: moe.moe_dispatch_layout(w.E + extra_plan, R_plan, plan[2], plan[3],
+                                                       *lay_out), reps)
+    # the backward with each expert's weight gradients split over that plan's
+    # copies (bf16 only), after a forward that leaves its saved tensors
+    rep_ms = None
+    if w.dtype == "bf16":
+        P_plan = w.E + extra_plan
+        rep_ws = torch.empty(moe.moe_backward_replicated_workspace_bytes(layer.shape, P_plan),
+                             dtype=torch.uint8, device="cuda")
+        layer.forward(x, w_gate, b_gate, w1, w2, logits_out=False)
+        moe.moe_ep_plan(w.E, R_plan, extra_plan, layer.offsets, *plan)
+
+        def bwd_rep():
+            moe.moe_backward_replicated(layer.shape, dy, x, w_gate, w1, w2, layer.topk_idx,
+                                        layer.topk_w, layer.slot_row, layer.row_token,
+                                        layer.offsets, layer.x_perm, layer.h, layer.out_perm,
+                                        layer.relu_bits, P_plan, plan[0], plan[1], plan[2],
+                                        layer.dx, layer.dw1, layer.dw2, layer.dw_gate,
+                                        layer.db_gate, None, rep_ws)
+        rep_ms = {"warm": warm(bwd_rep), "cold": cold(bwd_rep),
+                  "copies": P_plan, "experts_with_copies": int(
+                      (plan[0][1:] - plan[0][:-1] > 1).sum().item())}
+        log(f"backward over the plan's copies: warm {rep_ms['warm']['median'] * 1e3:.1f} us, "
+            f"cold {rep_ms['cold']['median'] * 1e3:.1f} us")
+        del rep_ws
     # cross-layer co-occurrence window and next-layer popularity prediction,
     # with this layer's routing as layer j and seeded successor choices as j+1
     idx_b = torch.from_numpy(workloads.next_layer_choices(layer.topk_idx.cpu().numpy(), w.E,
@@ -723,8 +750,9 @@ def main():
                      "launch_us": gemm_launch_ms * 1e3},
         "forward_tokens_per_s": fwd_tok,
         "parts_ms": {**{k: {"warm": v["warm"], "cold": v["cold"]} for k, v in parts.items()},
-                     "ep_plan_8_ranks": t_plan, "cooccurrence_update": t_co,
-                     "predict_popularity": t_pred},
+                     "ep_plan_8_ranks": t_plan, "dispatch_layout_8_ranks": t_layout,
+                     "backward_replicated_8_ranks": rep_ms,
+                     "cooccurrence_update": t_co, "predict_popularity": t_pred},
         "ep_plan": {"ranks": R_plan, "extra_copies": extra_plan,
                     "max_over_mean_rank_rows": plan_balance},
         "hbm_parts": hbm,

@@ -262,6 +262,37 @@ moe_status moe_backward(const moe_shape* shape, const void* dy, const void* x,
                         float* dlogits, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* moe_backward with each expert's weight gradients split over its replicas
+ * (Fast MoE Inference via Predictive Prefetching and Expert Replication,
+ * main contributions 2 and 3: hot experts get physical copies, each serving
+ * a share of their tokens; A Survey on Mixture of Experts, §5.1
+ * Computation: the layer waits for the most loaded expert).  Copy p =
+ * replica_start[e] + c of expert e takes the packed rows
+ * [replica_row0[p], replica_row0[p] + replica_rows[p]) - moe_ep_plan's
+ * outputs, n_copies = replica_start[E] = E + extra.  The weight-gradient
+ * GEMMs schedule every copy as a K range of its own (what that copy's rank
+ * would compute), and an expert with several copies gets dW1[e], dW2[e],
+ * dW_gate[:, e] and db[e] as the sum of its copies' float32 partial
+ * gradients in copy order (the fixed-order reduction of the copies'
+ * gradients); an expert with one copy gets exactly moe_backward's values, as
+ * do dx and dlogits.  bf16 only (MOE_ERR_UNSUPPORTED otherwise); E <=
+ * n_copies <= MOE_PLAN_MAX_COPIES.  Copies that do not tile their expert's
+ * rows give unspecified weight gradients (never an access outside the
+ * operands).  Workspace: moe_backward_replicated_workspace_bytes(shape,
+ * n_copies) (moe_backward's plus 2 (n_copies - E) partial gradients). */
+size_t moe_backward_replicated_workspace_bytes(const moe_shape* shape, int32_t n_copies);
+moe_status moe_backward_replicated(const moe_shape* shape, const void* dy, const void* x,
+                                   const float* w_gate, const void* w1, const void* w2,
+                                   const int32_t* topk_idx, const float* topk_w,
+                                   const int32_t* slot_row, const int32_t* row_token,
+                                   const int32_t* offsets, const void* x_perm, const void* h,
+                                   const void* out_perm, const uint32_t* relu_bits,
+                                   int32_t n_copies, const int32_t* replica_start,
+                                   const int32_t* replica_row0, const int32_t* replica_rows,
+                                   void* dx, float* dw1, float* dw2, float* dw_gate,
+                                   float* db_gate, float* dlogits, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* Per-expert popularity over a sliding window of iterations (PopFetcher
  * notes §3.1, routing-information collector; §4.2, Eq. 1: token
  * distribution over the last s iterations).  Writes counts_raw into row

@@ -17,7 +17,8 @@ __all__ = [
     "moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
-    "moe_predict_popularity", "moe_forward_noalloc", "moe_dispatch_layout", "OP", "PRIORITY",
+    "moe_predict_popularity", "moe_forward_noalloc", "moe_dispatch_layout",
+    "moe_backward_replicated", "moe_backward_replicated_workspace_bytes", "OP", "PRIORITY",
     "NOALLOC_MAX_SLOTS",
 ]
 
@@ -29,7 +30,8 @@ OP = {"route": 0, "permute": 1, "expert_ffn": 2, "combine": 3, "forward": 4, "ba
 EXPORTS = ["moe_workspace_bytes", "moe_check_shape", "moe_capacity", "moe_status_string",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
            "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan", "moe_cooccurrence_update",
-           "moe_predict_popularity", "moe_forward_noalloc", "moe_dispatch_layout"]
+           "moe_predict_popularity", "moe_forward_noalloc", "moe_dispatch_layout",
+           "moe_backward_replicated", "moe_backward_replicated_workspace_bytes"]
 NOALLOC_MAX_SLOTS = 262144  # MOE_NOALLOC_MAX_SLOTS
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +90,10 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_noalloc.argtypes = [sp] + [_P] * 18 + [_P]
         L.moe_ep_plan.argtypes = [ctypes.c_int32] * 3 + [_P] * 6 + [_P]
         L.moe_dispatch_layout.argtypes = [ctypes.c_int32] * 2 + [_P] * 5 + [_P]
+        L.moe_backward_replicated_workspace_bytes.argtypes = [sp, ctypes.c_int32]
+        L.moe_backward_replicated_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_backward_replicated.argtypes = ([sp] + [_P] * 14 + [ctypes.c_int32] + [_P] * 3 +
+                                              [_P] * 6 + [_P, ctypes.c_size_t, _P])
         L.moe_cooccurrence_update.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_int64] + [_P] * 5
         L.moe_predict_popularity.argtypes = [ctypes.c_int32] * 2 + [_P] * 5
         L.moe_popularity_update.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
@@ -95,7 +101,7 @@ def lib() -> ctypes.CDLL:
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
                      "moe_forward_fused", "moe_backward", "moe_popularity_update", "moe_ep_plan",
                      "moe_cooccurrence_update", "moe_predict_popularity", "moe_forward_noalloc",
-                     "moe_dispatch_layout"):
+                     "moe_dispatch_layout", "moe_backward_replicated"):
             getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -228,6 +234,23 @@ def moe_backward(shape, dy, x, w_gate, w1, w2, topk_idx, topk_w, slot_row, row_t
                               _ptr(out_perm), _ptr(relu_bits), _ptr(dx), _ptr(dw1), _ptr(dw2),
                               _ptr(dw_gate), _ptr(db_gate), _ptr(dlogits), ws, nb,
                               _stream(stream)), "moe_backward")
+
+
+def moe_backward_replicated_workspace_bytes(shape: MoeShape, n_copies: int) -> int:
+    return int(lib().moe_backward_replicated_workspace_bytes(ctypes.byref(shape), n_copies))
+
+
+def moe_backward_replicated(shape, dy, x, w_gate, w1, w2, topk_idx, topk_w, slot_row, row_token,
+                            offsets, x_perm, h, out_perm, relu_bits, n_copies, replica_start,
+                            replica_row0, replica_rows, dx, dw1, dw2, dw_gate, db_gate, dlogits,
+                            workspace, stream=None):
+    ws, nb = _ws(workspace)
+    _check(lib().moe_backward_replicated(
+        ctypes.byref(shape), _ptr(dy), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w2), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(slot_row), _ptr(row_token), _ptr(offsets), _ptr(x_perm), _ptr(h),
+        _ptr(out_perm), _ptr(relu_bits), n_copies, _ptr(replica_start), _ptr(replica_row0),
+        _ptr(replica_rows), _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(dw_gate), _ptr(db_gate),
+        _ptr(dlogits), ws, nb, _stream(stream)), "moe_backward_replicated")
 
 
 def moe_popularity_update(E, window, it, counts_raw, ring, window_sum, stream=None):

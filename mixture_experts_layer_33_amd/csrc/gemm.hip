@@ -927,18 +927,47 @@ struct WgradArgs {
   float* dw_gate;
   float* db_gate;
   int32_t* next_tile;  // tile queue: zero at launch
+  // Replicas (null rep_start: none).  Copy p = rep_start[e] + c of expert e
+  // takes the packed rows [rep_row0[p], rep_row0[p] + rep_rows[p]); an
+  // expert with several copies gets one float32 partial dW per copy
+  // (part [slot][N1][N2], gate partials gpart [slot][N2], dbpart [slot]),
+  // summed in copy order by wgrad_reduce_kernel.
+  const int32_t* rep_start;
+  const int32_t* rep_row0;
+  const int32_t* rep_rows;
+  float* part;
+  float* gpart;
+  float* dbpart;
+  int n_copies, max_slots;  // sizes of rep_row0 / rep_rows and of part
   int N1, N2, E;
 };
 
+// Per-expert copy counts and the partial slots of experts with several
+// copies (LDS, whole block): s_nc[e] copies, s_slot[e] first slot or -1.
+__device__ __forceinline__ void wgrad_copies(const WgradArgs& p, int* s_nc, int* s_slot,
+                                             int* s_scratch) {
+  const int tid = threadIdx.x;
+  int nc = 1;
+  if (tid < p.E && p.rep_start != nullptr) nc = p.rep_start[tid + 1] - p.rep_start[tid];
+  const int multi = (tid < p.E && nc > 1) ? nc : 0;
+  int total;
+  const int ex = block_exclusive_scan(multi, s_scratch, &total);
+  if (tid < p.E) {
+    s_nc[tid] = nc;
+    s_slot[tid] = multi > 0 ? ex : -1;
+  }
+}
+
 // Persistent: one workgroup per CU takes tiles from a queue (an atomic
 // counter) in longest-processing-time order - the experts by decreasing row
-// count (ties by index), each expert's tiles row by row - so the long K loops
-// of popular experts start first and the short ones fill in behind them.  A
-// tile's float32 dW leaves through non-temporal stores that stay in flight
-// while the next tile's k loop runs (only LDS is fenced between tiles).
-// Which workgroup takes which tile varies; each tile is computed the same
-// way, so the results are bitwise reproducible.  Experts with no rows store
-// zeros.
+// count (ties by index), each expert's copies in order, each copy's tiles row
+// by row - so the long K loops of popular experts start first and the short
+// ones fill in behind them.  A tile's float32 dW leaves through non-temporal
+// stores that stay in flight while the next tile's k loop runs (only LDS is
+// fenced between tiles).  Which workgroup takes which tile varies; each tile
+// is computed the same way, so the results are bitwise reproducible.
+// Experts with no rows store zeros.  An expert with one copy (always, without
+// replicas) computes exactly the unreplicated tiles.
 //
 // With GATE, the tiles of the first N1 tile row also produce the gate's
 // weight gradient over the same rows, dW_gate[:, e] = X2_e^T gsel_e and
@@ -949,10 +978,14 @@ __global__ void __launch_bounds__(kGemmThreads)
 wgrad_kernel(WgradArgs p) {
   __shared__ int s_perm[MOE_MAX_EXPERTS];
   __shared__ int s_cnt[MOE_MAX_EXPERTS];
+  __shared__ int s_nc[MOE_MAX_EXPERTS];
+  __shared__ int s_slot[MOE_MAX_EXPERTS];
+  __shared__ int s_tpre[MOE_MAX_EXPERTS + 1];  // first tile of each expert rank
+  __shared__ int s_scratch[kGemmThreads / 64 + 1];
   __shared__ int s_tile;
   const int tid = threadIdx.x;
   if (tid < p.E) s_cnt[tid] = p.offsets[tid + 1] - p.offsets[tid];
-  __syncthreads();
+  wgrad_copies(p, s_nc, s_slot, s_scratch);  // (ends with a barrier)
   if (tid < p.E) {  // rank experts by row count, most rows first, ties by index
     const int c = s_cnt[tid];
     int r = 0;
@@ -962,38 +995,128 @@ wgrad_kernel(WgradArgs p) {
     }
     s_perm[r] = tid;
   }
+  __syncthreads();
   const int T1 = (p.N1 + BM - 1) / BM, T2 = (p.N2 + BN - 1) / BN;
   const int per = T1 * T2;
-  const int total = p.E * per;
+  {
+    const int nt = tid < p.E ? s_nc[s_perm[tid]] * per : 0;
+    int total;
+    const int ex = block_exclusive_scan(nt, s_scratch, &total);
+    if (tid < p.E) s_tpre[tid] = ex;
+    if (tid == 0) s_tpre[p.E] = total;
+  }
   using TG = TileGemm<BM, BN, false, false, GATE>;
   const StageBufs L = tile_lds<TG>();
   for (;;) {
     if (tid == 0) s_tile = atomicAdd(p.next_tile, 1);
-    __syncthreads();  // s_perm written; s_tile visible
+    __syncthreads();  // s_tpre written; s_tile visible
     const int tile = s_tile;
-    if (tile >= total) break;
-    const int e = s_perm[tile / per], in = tile % per;
+    if (tile >= s_tpre[p.E]) break;
+    int lo = 0, hi = p.E - 1;  // expert rank holding this tile
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tpre[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    const int e = s_perm[lo], j = tile - s_tpre[lo];
+    const int c = j / per, in = j % per;
     const int t1 = in / T2, t2 = in % T2;
     const int n1 = t1 * BM, n2 = t2 * BN;
-    const int r0 = p.offsets[e], K = s_cnt[e];
+    int r0 = p.offsets[e], K = s_cnt[e];
+    if (p.rep_start != nullptr) {
+      // a copy's rows, kept inside the expert's own rows whatever the plan
+      // holds (copies that do not tile the rows give unspecified results,
+      // never an access outside the operands)
+      const int cp = p.rep_start[e] + c;
+      const bool ok = cp >= 0 && cp < p.n_copies;
+      const int a = ok ? p.rep_row0[cp] : r0;
+      const int n = ok ? p.rep_rows[cp] : 0;
+      const int lo_r = r0, hi_r = r0 + K;
+      r0 = min(max(a, lo_r), hi_r);
+      K = max(0, min(n, hi_r - r0));
+    }
+    const int slot = s_slot[e] < 0 ? -1 : s_slot[e] + c;
+    if (slot >= p.max_slots) {  // more copies than the plan's size: skipped
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      continue;
+    }
     const int rows = min(BM, p.N1 - n1), cols = min(BN, p.N2 - n2);
     TG tg;
     const bool gate_here = GATE && t1 == 0;
     tg.run(p.X1 + (size_t)r0 * p.N1 + n1, p.N1, rows, p.X2 + (size_t)r0 * p.N2 + n2, p.N2, cols,
            K, L, gate_here ? p.gsel + r0 : nullptr);
-    store_tile<EPI_F32>(tg, L, p.C + (size_t)e * p.N1 * p.N2 + (size_t)n1 * p.N2 + n2, p.N2, rows,
-                        cols, nullptr, 0);
+    float* dst = slot < 0 ? p.C + (size_t)e * p.N1 * p.N2 : p.part + (size_t)slot * p.N1 * p.N2;
+    store_tile<EPI_F32>(tg, L, dst + (size_t)n1 * p.N2 + n2, p.N2, rows, cols, nullptr, 0);
     if constexpr (GATE) {
       if (gate_here) {
         __syncthreads();
-        tg.gate_reduce(reinterpret_cast<float*>(L.a[0]), cols, p.dw_gate + (size_t)n2 * p.E + e,
-                       p.E, t2 == 0 ? p.db_gate + e : nullptr);
+        if (slot < 0)
+          tg.gate_reduce(reinterpret_cast<float*>(L.a[0]), cols,
+                         p.dw_gate + (size_t)n2 * p.E + e, p.E,
+                         t2 == 0 ? p.db_gate + e : nullptr);
+        else
+          tg.gate_reduce(reinterpret_cast<float*>(L.a[0]), cols,
+                         p.gpart + (size_t)slot * p.N2 + n2, 1,
+                         t2 == 0 ? p.dbpart + slot : nullptr);
       }
     }
     // every wave has read its epilogue strip (and the gate sums) before the
     // next tile's copies reuse the stage buffers, and thread 0 has read
     // s_tile before the next take rewrites it; the dW stores stay in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
+// Weight gradients of experts with several copies: the sum of the copies'
+// partial dW in copy order (the fixed-order reduction a replicated expert's
+// gradient needs), plus, with gate partials, dW_gate[:, e] and db[e].
+// Workgroup row y handles the y-th such expert (in index order); its columns
+// stride over the N1 x N2 elements, 4 per thread.
+__global__ void __launch_bounds__(256)
+wgrad_reduce_kernel(WgradArgs p) {
+  __shared__ int s_nc[MOE_MAX_EXPERTS];
+  __shared__ int s_slot[MOE_MAX_EXPERTS];
+  __shared__ int s_scratch[256 / 64 + 1];
+  __shared__ int s_e;
+  wgrad_copies(p, s_nc, s_slot, s_scratch);
+  if (threadIdx.x < p.E) {  // the y-th expert with several copies, if any
+    const int e = threadIdx.x;
+    int before = 0;
+    for (int o = 0; o < e; ++o) before += s_nc[o] > 1;
+    if (s_nc[e] > 1 && before == (int)blockIdx.y) s_e = e;
+  }
+  if (threadIdx.x == 0) {
+    int m = 0;
+    for (int o = 0; o < p.E; ++o) m += s_nc[o] > 1;
+    if ((int)blockIdx.y >= m) s_e = -1;
+  }
+  __syncthreads();
+  const int e = s_e;
+  if (e < 0) return;
+  const int nc = s_nc[e], slot0 = s_slot[e];
+  if (slot0 + nc > p.max_slots) return;  // beyond the plan's size (precondition)
+  const size_t n = (size_t)p.N1 * p.N2;  // a multiple of 4 (N2 is)
+  float* dst = p.C + (size_t)e * n;
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n;
+       i += (size_t)gridDim.x * 256 * 4) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(p.part + (size_t)slot0 * n + i);
+    for (int c = 1; c < nc; ++c) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p.part + (size_t)(slot0 + c) * n + i);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += v[q];
+    }
+    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(dst + i));
+  }
+  if (p.gpart != nullptr && blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < p.N2; i += 256) {
+      float acc = p.gpart[(size_t)slot0 * p.N2 + i];
+      for (int c = 1; c < nc; ++c) acc += p.gpart[(size_t)(slot0 + c) * p.N2 + i];
+      p.dw_gate[(size_t)i * p.E + e] = acc;
+    }
+    if (threadIdx.x == 0) {
+      float acc = p.dbpart[slot0];
+      for (int c = 1; c < nc; ++c) acc += p.dbpart[slot0 + c];
+      p.db_gate[e] = acc;
+    }
   }
 }
 
@@ -1226,29 +1349,58 @@ static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const uint3
 }
 
 template <int BM, int BN, bool GATE>
-static hipError_t launch_wgrad_t(const WgradArgs& p, hipStream_t s) {
-  const long long tiles = (long long)p.E * ((p.N1 + BM - 1) / BM) * ((p.N2 + BN - 1) / BN);
+static hipError_t launch_wgrad_t(const WgradArgs& p, int n_copies, hipStream_t s) {
+  const long long tiles =
+      (long long)n_copies * ((p.N1 + BM - 1) / BM) * ((p.N2 + BN - 1) / BN);
   const long long grid = std::min<long long>(tiles, device_cus());  // one workgroup per CU
   hipLaunchKernelGGL((wgrad_kernel<BM, BN, GATE>), dim3((unsigned)grid), dim3(kGemmThreads), 0,
                      s, p);
+  MOE_TRY(hipGetLastError());
+  if (p.rep_start != nullptr && n_copies > p.E) {
+    // at most n_copies - E experts have several copies
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(512, n_copies - p.E), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
+
+// Replicas of the weight-gradient GEMMs (see WgradArgs); null = none.
+struct WgradReplicas {
+  const int32_t* start;
+  const int32_t* row0;
+  const int32_t* rows;
+  int n_copies;
+  float* part;
+  float* gpart;
+  float* dbpart;
+};
 
 template <bool GATE>
 static hipError_t launch_wgrad(const bf16* X1, const bf16* X2, float* C, const int32_t* offsets,
                                const float* gsel, float* dw_gate, float* db_gate,
-                               int32_t* next_tile, int N1, int N2, int E, hipStream_t s) {
-  WgradArgs p{X1, X2, C, offsets, gsel, dw_gate, db_gate, next_tile, N1, N2, E};
+                               int32_t* next_tile, int N1, int N2, int E,
+                               const WgradReplicas* rep, hipStream_t s) {
+  const int max_slots = rep && rep->n_copies > E ? 2 * (rep->n_copies - E) : 0;
+  WgradArgs p{X1, X2, C, offsets, gsel, dw_gate, db_gate, next_tile,
+              rep ? rep->start : nullptr, rep ? rep->row0 : nullptr, rep ? rep->rows : nullptr,
+              rep ? rep->part : nullptr, rep && GATE ? rep->gpart : nullptr,
+              rep && GATE ? rep->dbpart : nullptr, rep ? rep->n_copies : 0, max_slots,
+              N1, N2, E};
+  const int n_copies = rep ? rep->n_copies : E;
   auto mt = [&](int bm) { return (long long)E * ((N1 + bm - 1) / bm); };
   const Shape2 t = pick_tile(mt, N2);
-  if (t.bm == 256 && t.bn == 256) return launch_wgrad_t<256, 256, GATE>(p, s);
-  if (t.bm == 256 && t.bn == 128) return launch_wgrad_t<256, 128, GATE>(p, s);
-  if (t.bm == 128 && t.bn == 256) return launch_wgrad_t<128, 256, GATE>(p, s);
-  return launch_wgrad_t<128, 128, GATE>(p, s);
+  if (t.bm == 256 && t.bn == 256) return launch_wgrad_t<256, 256, GATE>(p, n_copies, s);
+  if (t.bm == 256 && t.bn == 128) return launch_wgrad_t<256, 128, GATE>(p, n_copies, s);
+  if (t.bm == 128 && t.bn == 256) return launch_wgrad_t<128, 256, GATE>(p, n_copies, s);
+  return launch_wgrad_t<128, 128, GATE>(p, n_copies, s);
 }
 
 // Bytes of float32 partial tiles a row-grouped launch may use: the split
 // tail never holds more than kMaxSplitUnits tiles of the largest row tile.
+size_t wgrad_replica_bytes(int n_copies, int E, int d, int F) {
+  const size_t slots = n_copies > E ? 2 * (size_t)(n_copies - E) : 0;
+  return slots * ((size_t)d * F + d + 1) * sizeof(float);
+}
+
 size_t rows_partial_bytes(int act) {
   return act == MOE_BF16 ? (size_t)kMaxSplitUnits * kMaxRowTileArea * sizeof(float) : 0;
 }
@@ -1312,7 +1464,14 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
                              void* dx_perm, float* dw1, float* dw2, const float* dsel_perm,
                              float* dw_gate, float* db_gate, const uint32_t* relu_bits_in,
                              uint32_t* relu_bits_ws, float* partial, int32_t* counters,
-                             int S_max, int max_rows, int d, int F, int E, hipStream_t s) {
+                             int S_max, int max_rows, int d, int F, int E, hipStream_t s,
+                             const int32_t* rep_start, const int32_t* rep_row0,
+                             const int32_t* rep_rows, int n_copies, float* rep_part) {
+  const size_t rep_slots = n_copies > E ? 2 * (size_t)(n_copies - E) : 0;
+  const WgradReplicas rep{rep_start, rep_row0, rep_rows, n_copies, rep_part,
+                          rep_part + rep_slots * (size_t)d * F,
+                          rep_part + rep_slots * (size_t)d * F + rep_slots * (size_t)d};
+  const WgradReplicas* repp = rep_start != nullptr ? &rep : nullptr;
   if (act == MOE_BF16) {
     // keep bits of the ReLU (unless the forward kept them), then
     // dz = (dO W2[e]) * [h > 0]: A = dO [rows][d], B = W2[e] as [K=d][N=F]
@@ -1330,10 +1489,10 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
                                           max_rows, partial, s)));
     // dW2[e] = dO^T h  ([d][F])
     MOE_TRY((launch_wgrad<false>((const bf16*)d_out, (const bf16*)h, dw2, offsets, nullptr,
-                                 nullptr, nullptr, counters, d, F, E, s)));
+                                 nullptr, nullptr, counters, d, F, E, repp, s)));
     // dW1[e] = dz^T x_perm  ([F][d]), with the gate's dW_gate / db over the kept rows
     MOE_TRY((launch_wgrad<true>((const bf16*)dz, (const bf16*)x_perm, dw1, offsets, dsel_perm,
-                                dw_gate, db_gate, counters + 1, F, d, E, s)));
+                                dw_gate, db_gate, counters + 1, F, d, E, repp, s)));
     // dx_perm = dz W1[e]: A = dz [rows][F], B = W1[e] as [K=F][N=d]  (may reuse dO's
     // memory: it runs after the last reader of dO).  Last of the four, so the
     // decode of dX that follows reads dx_perm while it is still cached.
@@ -1342,6 +1501,7 @@ hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, con
                                            max_rows, partial, s)));
     return hipSuccess;
   }
+  if (rep_start != nullptr) return hipErrorInvalidValue;  // replicas: bf16 only
   dim3 b(256);
   const int rt = (S_max + kF32Rows - 1) / kF32Rows;
   hipLaunchKernelGGL((f32_rows_kernel<false, EPI_MASK>), dim3(rt, (F + 63) / 64), b, 0, s,

@@ -95,14 +95,25 @@ hipError_t launch_expert_fwd_fused(int act, const void* x, const int32_t* row_to
 // takes the ReLU mask from relu_bits_in if non-null, else derives it from h
 // into relu_bits_ws ([S_max][F/32] words of scratch).  The two bf16 weight
 // gradients take their tiles from counters[0] and counters[1], which must be
-// zero at launch (launch_combine_bwd zeroes them).
+// zero at launch (launch_combine_bwd zeroes them).  With replicas (bf16
+// only; rep_start [E+1], rep_row0 / rep_rows [n_copies] as moe_ep_plan writes
+// them), each copy of an expert is a K range of its own and an expert with
+// several copies gets the sum of the copies' partial weight gradients in copy
+// order (rep_part: wgrad_replica_bytes of scratch).
 hipError_t launch_expert_bwd(int act, const void* d_out, const void* x_perm, const void* h,
                              const int32_t* offsets, const void* w1, const void* w2,
                              void* dz, void* dx_perm, float* dw1, float* dw2,
                              const float* dsel_perm, float* dw_gate, float* db_gate,
                              const uint32_t* relu_bits_in, uint32_t* relu_bits_ws,
                              float* partial, int32_t* counters, int S_max, int max_rows,
-                             int d, int F, int E, hipStream_t s);
+                             int d, int F, int E, hipStream_t s,
+                             const int32_t* rep_start = nullptr,
+                             const int32_t* rep_row0 = nullptr,
+                             const int32_t* rep_rows = nullptr, int n_copies = 0,
+                             float* rep_part = nullptr);
+// Scratch of the replicated weight gradients (bf16): per partial slot a dW,
+// a gate column and a db value; at most 2 (n_copies - E) slots.
+size_t wgrad_replica_bytes(int n_copies, int E, int d, int F);
 
 // ---- expert-parallel dispatch plan (plan.hip)
 hipError_t launch_ep_plan(int E, int R, int extra, const int32_t* offsets,

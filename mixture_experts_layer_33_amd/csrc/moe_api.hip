@@ -410,6 +410,48 @@ moe_status moe_forward_fused(const moe_shape* s, const void* x, const float* w_g
   return MOE_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// moe_backward, with the weight gradients optionally split over replicas
+moe_status backward_impl(const moe_shape* s, const void* dy, const void* x, const float* w_gate,
+                         const void* w1, const void* w2, const int32_t* topk_idx,
+                         const float* topk_w, const int32_t* slot_row, const int32_t* row_token,
+                         const int32_t* offsets, const void* x_perm, const void* h,
+                         const void* out_perm, const uint32_t* relu_bits, void* dx, float* dw1,
+                         float* dw2, float* dw_gate, float* db_gate, float* dlogits, void* ws,
+                         const int32_t* rep_start, const int32_t* rep_row0,
+                         const int32_t* rep_rows, int n_copies, hipStream_t stream_) {
+  BwdWs bw = carve_bwd(s, ws);
+  float* rep_part = rep_start != nullptr
+                        ? reinterpret_cast<float*>(static_cast<char*>(ws) + bwd_ws_bytes(s))
+                        : nullptr;
+  const int act = s->act_dtype;
+  MOE_HIP(launch_combine_bwd(act, dy, out_perm, topk_w, topk_idx, slot_row, bw.d_out, bw.dsel,
+                             bw.dsel_perm, dlogits, w_gate, bw.w_gate_t, bw.counters, s->T,
+                             s->d_model, s->E, s->k, stream_));
+  // dx_perm reuses d_out's memory: the FC1 dgrad runs after the FC2 wgrad,
+  // the last reader of d_out.  For bf16 the FC1 wgrad also writes dW_gate and
+  // db over the kept rows.
+  MOE_HIP(launch_expert_bwd(act, bw.d_out, x_perm, h, offsets, w1, w2, bw.dz, bw.d_out, dw1, dw2,
+                            bw.dsel_perm, dw_gate, db_gate, relu_bits, bw.relu_bits, bw.partial,
+                            bw.counters, (int)slots(s), capacity_of(s), s->d_model, s->d_ff, s->E,
+                            stream_, rep_start, rep_row0, rep_rows, n_copies, rep_part));
+  if (act != MOE_BF16)
+    MOE_HIP(launch_gate_rows(act, x_perm, bw.dsel_perm, offsets, dw_gate, db_gate, s->d_model,
+                             s->E, stream_));
+  // with a capacity below T slots can be dropped: dx also adds their gate gradient
+  MOE_HIP(launch_dx(act, bw.d_out, bw.dsel, topk_idx, slot_row, bw.w_gate_t, dx, s->T,
+                    s->d_model, s->k, capacity_of(s) < s->T, x, offsets, row_token, dw_gate,
+                    db_gate, s->E, stream_));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const float* w_gate,
                         const void* w1, const void* w2, const int32_t* topk_idx,
                         const float* topk_w, const int32_t* slot_row, const int32_t* row_token,
@@ -424,27 +466,45 @@ moe_status moe_backward(const moe_shape* s, const void* dy, const void* x, const
       !opt_ok(dlogits) || !opt_ok(relu_bits))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, MOE_OP_BACKWARD, ws, ws_bytes)) != MOE_OK) return st;
-  BwdWs bw = carve_bwd(s, ws);
-  hipStream_t stream_ = as_stream(stream);
-  const int act = s->act_dtype;
-  MOE_HIP(launch_combine_bwd(act, dy, out_perm, topk_w, topk_idx, slot_row, bw.d_out, bw.dsel,
-                             bw.dsel_perm, dlogits, w_gate, bw.w_gate_t, bw.counters, s->T,
-                             s->d_model, s->E, s->k, stream_));
-  // dx_perm reuses d_out's memory: the FC1 dgrad runs after the FC2 wgrad,
-  // the last reader of d_out.  For bf16 the FC1 wgrad also writes dW_gate and
-  // db over the kept rows.
-  MOE_HIP(launch_expert_bwd(act, bw.d_out, x_perm, h, offsets, w1, w2, bw.dz, bw.d_out, dw1, dw2,
-                            bw.dsel_perm, dw_gate, db_gate, relu_bits, bw.relu_bits, bw.partial,
-                            bw.counters, (int)slots(s), capacity_of(s), s->d_model, s->d_ff, s->E,
-                            stream_));
-  if (act != MOE_BF16)
-    MOE_HIP(launch_gate_rows(act, x_perm, bw.dsel_perm, offsets, dw_gate, db_gate, s->d_model,
-                             s->E, stream_));
-  // with a capacity below T slots can be dropped: dx also adds their gate gradient
-  MOE_HIP(launch_dx(act, bw.d_out, bw.dsel, topk_idx, slot_row, bw.w_gate_t, dx, s->T,
-                    s->d_model, s->k, capacity_of(s) < s->T, x, offsets, row_token, dw_gate,
-                    db_gate, s->E, stream_));
-  return MOE_OK;
+  return backward_impl(s, dy, x, w_gate, w1, w2, topk_idx, topk_w, slot_row, row_token, offsets,
+                       x_perm, h, out_perm, relu_bits, dx, dw1, dw2, dw_gate, db_gate, dlogits,
+                       ws, nullptr, nullptr, nullptr, 0, as_stream(stream));
+}
+
+size_t moe_backward_replicated_workspace_bytes(const moe_shape* s, int32_t n_copies) {
+  if (check_shape(s) != MOE_OK || s->act_dtype != MOE_BF16 || n_copies < s->E ||
+      n_copies > MOE_PLAN_MAX_COPIES)
+    return 0;
+  return bwd_ws_bytes(s) + align_up(wgrad_replica_bytes(n_copies, s->E, s->d_model, s->d_ff));
+}
+
+moe_status moe_backward_replicated(const moe_shape* s, const void* dy, const void* x,
+                                   const float* w_gate, const void* w1, const void* w2,
+                                   const int32_t* topk_idx, const float* topk_w,
+                                   const int32_t* slot_row, const int32_t* row_token,
+                                   const int32_t* offsets, const void* x_perm, const void* h,
+                                   const void* out_perm, const uint32_t* relu_bits,
+                                   int32_t n_copies, const int32_t* replica_start,
+                                   const int32_t* replica_row0, const int32_t* replica_rows,
+                                   void* dx, float* dw1, float* dw2, float* dw_gate,
+                                   float* db_gate, float* dlogits, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (n_copies < s->E || n_copies > MOE_PLAN_MAX_COPIES) return MOE_ERR_INVALID_ARG;
+  if (!ptrs_ok(dy, x, w_gate, w1, w2, topk_idx, topk_w, slot_row, row_token, offsets, x_perm, h,
+               out_perm, dx, dw1, dw2, dw_gate, db_gate, replica_start, replica_row0,
+               replica_rows) ||
+      !opt_ok(dlogits) || !opt_ok(relu_bits))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_backward_replicated_workspace_bytes(s, n_copies);
+  if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+    return MOE_ERR_WORKSPACE;
+  return backward_impl(s, dy, x, w_gate, w1, w2, topk_idx, topk_w, slot_row, row_token, offsets,
+                       x_perm, h, out_perm, relu_bits, dx, dw1, dw2, dw_gate, db_gate, dlogits,
+                       ws, replica_start, replica_row0, replica_rows, n_copies,
+                       as_stream(stream));
 }
 
 moe_status moe_popularity_update(int32_t E, int32_t window, int64_t iter,

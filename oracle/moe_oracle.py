@@ -306,9 +306,38 @@ def popularity_update(ring: np.ndarray, it: int, counts_raw: np.ndarray):
 # --------------------------------------------------------------------------
 # backward
 # --------------------------------------------------------------------------
-def backward(dy, fwd: Dict[str, np.ndarray], x, w_gate, w1, w2, act: str):
+def _copy_ranges(copies, offsets, E):
+    """The packed-row ranges of each expert's copies, checked to tile the
+    expert's rows in order: [[(row0, rows), ...] per expert]."""
+    start = [int(v) for v in copies["replica_start"]]
+    row0 = [int(v) for v in copies["replica_row0"]]
+    rows = [int(v) for v in copies["replica_rows"]]
+    if len(start) != E + 1:
+        raise ValueError("replica_start needs E + 1 entries")
+    out = []
+    for e in range(E):
+        cur, ranges = int(offsets[e]), []
+        for p in range(start[e], start[e + 1]):
+            if row0[p] != cur or rows[p] < 0:
+                raise ValueError(f"copies of expert {e} do not tile its rows in order")
+            ranges.append((row0[p], rows[p]))
+            cur += rows[p]
+        if cur != int(offsets[e + 1]) or not ranges:
+            raise ValueError(f"copies of expert {e} do not cover its rows")
+        out.append(ranges)
+    return out
+
+
+def backward(dy, fwd: Dict[str, np.ndarray], x, w_gate, w1, w2, act: str, copies=None):
     """Gradients of the layer for output gradient dy, given this module's own
     forward results ``fwd``.
+
+    ``copies`` (optional; ep_plan's replica_start / replica_row0 /
+    replica_rows) splits each expert's rows over its copies: the expert's
+    weight gradients are then the sum, in copy order, of each copy's
+    gradient over its own rows - what the copies' ranks compute and a
+    reduction adds up when hot experts are replicated (Fast MoE Inference via
+    Predictive Prefetching and Expert Replication, main contributions 2-3).
 
     Output decode: dO[r] = w[t, j] dy[t] for the kept slot (t, j) held by row
     r, and dg[t, j] = <dy[t], O[r]> (0 for a dropped slot).
@@ -343,6 +372,7 @@ def backward(dy, fwd: Dict[str, np.ndarray], x, w_gate, w1, w2, act: str):
     dw1 = np.zeros((E, F, d), dtype=F64)
     dw2 = np.zeros((E, d, F), dtype=F64)
     dx_perm = np.zeros((R, d), dtype=F64)
+    ranges = _copy_ranges(copies, offsets, E) if copies is not None else None
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if a == b:
@@ -351,9 +381,15 @@ def backward(dy, fwd: Dict[str, np.ndarray], x, w_gate, w1, w2, act: str):
         he = h[a:b]
         dh = dO @ np.asarray(w2[e], F64)
         dz = dh * (he > 0.0)
-        dw2[e] = dO.T @ he
         dx_perm[a:b] = dz @ np.asarray(w1[e], F64)
-        dw1[e] = dz.T @ x_perm[a:b]
+        if ranges is None:
+            dw2[e] = dO.T @ he
+            dw1[e] = dz.T @ x_perm[a:b]
+        else:
+            for r0, n in ranges[e]:  # each copy over its own rows, in copy order
+                i, j = r0 - a, r0 - a + n
+                dw2[e] += dO[i:j].T @ he[i:j]
+                dw1[e] += dz[i:j].T @ x_perm[r0:r0 + n]
 
     # input encode backward (sum over the token's kept rows, in j order)
     dx_exp = np.zeros((T, d), dtype=F64)

@@ -1,0 +1,102 @@
+"""moe_backward_replicated on the GPU: each expert's weight gradients split
+over the copies of the dispatch plan (moe_ep_plan, run on the GPU from the
+layer's own packed rows), summed in copy order.  Against the reference's
+backward with the same copies (oracle.backward(copies=...)) through the
+end-to-end comparison, and against moe_backward on the same saved tensors:
+dx and dlogits bit for bit, single-copy experts' weight and gate gradients
+bit for bit, multi-copy experts within tolerance."""
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import moe_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+from gpu_helpers import TOL, assert_close_per_expert, down, upload_case  # noqa: E402
+from test_gpu_parity import SMALL, _setup, compare_end_to_end  # noqa: E402
+
+if torch.cuda.is_available():
+    import mixture_experts_layer_33_amd as moe
+
+CASES = [
+    ("skewed_zipf12", 32, 8),           # E = 32: the hot experts get several copies
+    ("fine_grained", 128, 8),           # E = 128, top-4
+    ("mixtral_shaped", 8, 4),           # E = 8
+    ("uniform_cf050", 16, 4),           # drops: the dropped slots' gate gradient on top
+    ("skewed_split_tail", 32, 8),       # K = F = 2048, split-tail row GEMMs
+    ("skewed_zipf12", 0, 8),            # no extra copies: all bit for bit
+]
+
+
+def _plan(layer, E, extra, R):
+    P = E + extra
+    z = lambda n: torch.empty(n, dtype=torch.int32, device="cuda")  # noqa: E731
+    out = {"replica_start": z(E + 1), "replica_row0": z(P), "replica_rows": z(P),
+           "replica_rank": z(P), "rank_rows": z(R)}
+    moe.moe_ep_plan(E, R, extra, layer.offsets, out["replica_start"], out["replica_row0"],
+                    out["replica_rows"], out["replica_rank"], out["rank_rows"])
+    return out, P
+
+
+@pytest.mark.parametrize("name,extra,R", CASES)
+def test_backward_replicated(name, extra, R):
+    w, inp, dev, layer = _setup(name)
+    layer.forward(dev["x"], dev["w_gate"], dev["b_gate"], dev["w1"], dev["w2"])
+    layer.backward(dev["dy"], dev["x"], dev["w_gate"], dev["w1"], dev["w2"])
+    plan, P = _plan(layer, w.E, extra, R)
+    g = {k: torch.full_like(getattr(layer, k), 7.0) for k in
+         ("dx", "dw1", "dw2", "dw_gate", "db_gate", "dlogits")}
+    nb = moe.moe_backward_replicated_workspace_bytes(layer.shape, P)
+    assert nb >= moe.moe_workspace_bytes(layer.shape, "backward")
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    moe.moe_backward_replicated(layer.shape, dev["dy"], dev["x"], dev["w_gate"], dev["w1"],
+                                dev["w2"], layer.topk_idx, layer.topk_w, layer.slot_row,
+                                layer.row_token, layer.offsets, layer.x_perm, layer.h,
+                                layer.out_perm, layer.relu_bits, P, plan["replica_start"],
+                                plan["replica_row0"], plan["replica_rows"], g["dx"], g["dw1"],
+                                g["dw2"], g["dw_gate"], g["db_gate"], g["dlogits"], ws)
+    torch.cuda.synchronize()
+    ncopy = np.diff(down(plan["replica_start"]))
+    multi = ncopy > 1
+    if extra:
+        assert multi.any(), "the plan should replicate at least one expert"
+    # against moe_backward on the same saved tensors
+    for key in ("dx", "dlogits"):
+        assert torch.equal(g[key], getattr(layer, key)), key
+    single = ~multi
+    for key in ("dw1", "dw2"):
+        a, b = down(g[key]), down(getattr(layer, key))
+        np.testing.assert_array_equal(a[single], b[single], err_msg=key)
+        if multi.any():
+            assert_close_per_expert(a[multi], b[multi], TOL[w.dtype], key)
+    np.testing.assert_array_equal(down(g["dw_gate"])[:, single], down(layer.dw_gate)[:, single])
+    np.testing.assert_array_equal(down(g["db_gate"])[single], down(layer.db_gate)[single])
+    # against the reference's backward with the same copies
+    fwd = orc.forward(inp["x"], inp["w_gate"], inp["b_gate"], inp["w1"], inp["w2"], w.k,
+                      w.capacity_factor, w.dtype, priority=w.priority)
+    if not np.array_equal(fwd["offsets"], down(layer.offsets)):
+        pytest.skip("routing differs on a near-tie: the plan is not the reference's")
+    copies = {k: down(v) for k, v in plan.items()}
+    bwd = orc.backward(inp["dy"], fwd, inp["x"], inp["w_gate"], inp["w1"], inp["w2"], w.dtype,
+                       copies=copies)
+    view = types.SimpleNamespace(**{k: getattr(layer, k) for k in (
+        "logits", "topk_idx", "counts_raw", "counts_kept", "offsets", "slot_row", "y", "h")},
+        **g)
+    mism = compare_end_to_end(w, view, fwd, bwd, inp["w1"])
+    assert mism.size == 0
+
+
+def test_backward_replicated_rejects():
+    w = SMALL["skewed_zipf12"]
+    sh = moe.MoeShape.make(w.T, w.d, w.F, w.E, w.k, 0.0, moe.MOE_BF16)
+    assert moe.moe_backward_replicated_workspace_bytes(sh, w.E - 1) == 0
+    f32 = moe.MoeShape.make(w.T, w.d, w.F, w.E, w.k, 0.0, moe.MOE_F32)
+    assert moe.moe_backward_replicated_workspace_bytes(f32, w.E) == 0
+    P = 0x1000
+    with pytest.raises(moe.MoeError) as err:
+        moe.moe_backward_replicated(f32, *([P] * 14), w.E, P, P, P, *([P] * 6), None)
+    assert err.value.status == -2

@@ -749,3 +749,66 @@ def test_dispatch_layout_invariants(seed):
     mono = orc.dispatch_layout(rows, srt, R)
     np.testing.assert_array_equal(mono["seg_send_offset"],
                                   np.concatenate([[0], np.cumsum(rows)[:-1]]))
+
+
+# ---------------------------------------------------------------- replicated weight gradients
+def _small_layer(seed=0, T=40, d=8, F=16, E=4, k=2, cf=0.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((d, E)) * 0.3
+    b = np.array([0.8, 0.2, 0.0, -0.5][:E])
+    w1 = rng.standard_normal((E, F, d)) * 0.3
+    w2 = rng.standard_normal((E, d, F)) * 0.3
+    dy = rng.standard_normal((T, d))
+    fwd = orc.forward(x, wg, b, w1, w2, k, cf, "f64")
+    return x, wg, w1, w2, dy, fwd
+
+
+@pytest.mark.parametrize("extra,R", [(0, 2), (3, 2), (6, 3)])
+def test_replicated_weight_gradients(extra, R):
+    """Splitting an expert's rows over copies changes nothing but the order
+    of the row sum: one copy per expert gives the unsplit gradients bit for
+    bit; the dispatch plan's copies give them within float64 rounding; every
+    other gradient is untouched."""
+    x, wg, w1, w2, dy, fwd = _small_layer(seed=extra)
+    plain = orc.backward(dy, fwd, x, wg, w1, w2, "f64")
+    copies = orc.ep_plan(fwd["offsets"], extra, R)
+    if extra:
+        assert (np.diff(copies["replica_start"]) > 1).any()
+    rep = orc.backward(dy, fwd, x, wg, w1, w2, "f64", copies=copies)
+    for key in ("dw1_f64", "dw2_f64"):
+        np.testing.assert_allclose(rep[key], plain[key], rtol=0,
+                                   atol=1e-12 * np.abs(plain[key]).max())
+        if extra == 0:
+            np.testing.assert_array_equal(rep[key], plain[key])
+    for key in ("dx", "dw_gate", "db_gate", "dlogits"):
+        np.testing.assert_array_equal(rep[key], plain[key])
+
+
+def test_replicated_weight_gradients_hand_worked():
+    """One expert, three rows split 2 + 1: dW2 = dO[0:2]^T h[0:2] + dO[2:3]^T
+    h[2:3], the copy partials worked by hand on integer-valued operands."""
+    fwd = {"idx": np.zeros((3, 1), np.int32), "w": np.ones((3, 1), np.float32),
+           "slot_row": np.array([0, 1, 2], np.int32), "offsets": np.array([0, 3], np.int32),
+           "h": np.array([[1.0, 2.0], [0.0, 1.0], [3.0, 0.0]]),
+           "o": np.zeros((3, 1)), "x_perm": np.array([[1.0], [2.0], [-1.0]])}
+    dy = np.array([[1.0], [2.0], [-1.0]])
+    w1 = np.ones((1, 2, 1))
+    w2 = np.array([[[1.0, 1.0]]])
+    copies = {"replica_start": [0, 2], "replica_row0": [0, 2], "replica_rows": [2, 1]}
+    rep = orc.backward(dy, fwd, np.zeros((3, 1)), np.zeros((1, 1)), w1, w2, "f64", copies=copies)
+    # dO = w * dy = dy; copy 0: [1*1 + 2*0, 1*2 + 2*1] = [1, 4]; copy 1: [-3, 0]
+    np.testing.assert_array_equal(rep["dw2_f64"][0], [[-2.0, 4.0]])
+    # dz = (dO @ W2) * [h > 0]: rows [1,1], [0,2], [-1,0]; dW1 = dz^T x_perm:
+    # copy 0: [1*1 + 0*2, 1*1 + 2*2] = [1, 5]; copy 1: [(-1)(-1), 0] = [1, 0]
+    np.testing.assert_array_equal(rep["dw1_f64"][0], [[2.0], [5.0]])
+
+
+def test_replicated_copies_must_tile_the_rows():
+    x, wg, w1, w2, dy, fwd = _small_layer()
+    good = orc.ep_plan(fwd["offsets"], 2, 2)
+    bad = {k: np.array(v, copy=True) for k, v in good.items()}
+    p = int(np.argmax(bad["replica_rows"]))
+    bad["replica_rows"][p] -= 1
+    with pytest.raises(ValueError):
+        orc.backward(dy, fwd, x, wg, w1, w2, "f64", copies=bad)
