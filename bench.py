@@ -77,6 +77,9 @@ def parse():
                    help="write the HBM traffic summary from two counter runs (no GPU)")
     p.add_argument("--summarize-mfma", nargs=3, metavar=("COUNTER_CSV", "AGENT_CSV", "BENCH_JSON"),
                    help="write the MFMA utilization summary from one counter run (no GPU)")
+    p.add_argument("--summarize-kernels", metavar="KERNEL_STATS_CSV",
+                   help="write the per-kernel time summary of one rocprofv3 --kernel-trace "
+                        "--stats run of bench.py (no GPU)")
     p.add_argument("--command", default="",
                    help="the command lines that produced the counter files (recorded)")
     return p.parse_args()
@@ -295,7 +298,7 @@ def summarize_mfma(args):
 
 # the HBM-bound steps: kernels per call, and the sources they are built from
 PART_KERNELS = {
-    "route": ["route_mfma_kernel", "route_kernel"],
+    "route": ["route_tile_kernel", "route_kernel"],
     "permute": ["rank_hist_kernel", "scan_kernel", "gather_kernel"],
     "combine": ["combine_kernel"],
 }
@@ -336,8 +339,10 @@ def summarize_parts_traffic(args, per_kernel_kib, scales, dispatches):
     for part, kernels in PART_KERNELS.items():
         total, found = 0.0, []
         for kn in kernels:
+            # (names may be mangled: "13gather_kernelIDF16b..."; no listed name is
+            # a substring of another kernel's)
             names = [n for n in per_kernel_kib["FETCH_SIZE"]
-                     if re.search(rf"\b{kn}\b", n) and n in per_kernel_kib["WRITE_SIZE"]]
+                     if kn in n and n in per_kernel_kib["WRITE_SIZE"]]
             for n in names:
                 fb = per_kernel_kib["FETCH_SIZE"][n] * 1024 * scales["FETCH_SIZE"]
                 wb = per_kernel_kib["WRITE_SIZE"][n] * 1024 * scales["WRITE_SIZE"]
@@ -348,7 +353,7 @@ def summarize_parts_traffic(args, per_kernel_kib, scales, dispatches):
         # their dispatch counts, then add the step's kernels up
         by_kernel = {}
         for n, nd, fb, wb in found:
-            base = next(kn for kn in kernels if re.search(rf"\b{kn}\b", n))
+            base = next(kn for kn in kernels if kn in n)
             acc = by_kernel.setdefault(base, [0.0, 0.0, 0])
             acc[0] += fb * nd
             acc[1] += wb * nd
@@ -398,6 +403,47 @@ def load_parts_traffic(name):
     except OSError:
         pass
     return None
+
+
+def kernels_path(name):
+    return os.path.join(ROOT, "profiles", f"kernels_{name}_kernel_stats.md")
+
+
+def summarize_kernels(args):
+    """Per-kernel averages of a rocprofv3 --kernel-trace --stats run of
+    bench.py: every kernel of the run (timed steps, part timings, probes),
+    sorted by total time, with the expert GEMM launches' TFLOP/s."""
+    import csv
+    w = workloads.workloads()[args.workload]
+    with open(args.summarize_kernels, newline="") as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    alg = 2.0 * w.d * w.F * w.T * w.k  # every slot kept in the measured workloads
+    L = [f"# Kernel times, {w.name} (rocprofv3 --kernel-trace --stats)", "",
+         f"Workload: {w.description}.", "",
+         "Command (run from the repository root on one MI355X):", "", "```",
+         args.command.strip() or "(not recorded)", "```", "",
+         "All kernels of the run: the timed steps plus the per-part warm and cold timings "
+         "(cold ones after a 512 MiB fill kernel) and the probes; averages over each "
+         f"kernel's dispatches.  Expert GEMM TFLOP/s: 2 d F S = {alg / 1e9:.1f} GFLOP per "
+         "product over the kernel's average duration.", "",
+         "| kernel | calls | average µs | total ms | share | GEMM TFLOP/s |",
+         "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        avg = float(r["AverageNs"]) / 1e3
+        tf = ""
+        if re.search(r"rows_gemm_kernel|wgrad_kernel<", name):
+            tf = f"{alg / (avg * 1e-6) / 1e12:.0f}"
+        short = name if len(name) <= 90 else name[:87] + "..."
+        L.append(f"| `{short}` | {r['Calls']} | {avg:.1f} | "
+                 f"{float(r['TotalDurationNs']) / 1e6:.2f} | "
+                 f"{float(r['TotalDurationNs']) / total:.1%} | {tf} |")
+    os.makedirs(os.path.dirname(kernels_path(w.name)), exist_ok=True)
+    with open(kernels_path(w.name), "w") as f:
+        f.write("\n".join(L) + "\n")
+    print(kernels_path(w.name))
 
 
 def load_traffic(name):
@@ -459,6 +505,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args)
+        return
+    if args.summarize_kernels:
+        summarize_kernels(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",

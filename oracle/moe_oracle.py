@@ -361,12 +361,10 @@ def backward(dy, fwd: Dict[str, np.ndarray], x, w_gate, w1, w2, act: str, copies
 
     # output decode backward
     d_o = np.zeros((R, d), dtype=F64)
-    dg = np.zeros((T, k), dtype=F64)
     for j in range(k):
         r = slot_row[:, j]
         kept = r >= 0
         d_o[r[kept]] = w[kept, j][:, None] * dy[kept]
-        dg[kept, j] = np.einsum("td,td->t", dy[kept], o[r[kept]])
 
     # expert backward
     dw1 = np.zeros((E, F, d), dtype=F64)
@@ -399,6 +397,33 @@ def backward(dy, fwd: Dict[str, np.ndarray], x, w_gate, w1, w2, act: str, copies
         dx_exp[kept] += dx_perm[r[kept]]
 
     # gate backward
+    g = gate_backward(dy, fwd, x, w_gate, E)
+    dlogits = g["dlogits_f64"]
+    dx = dx_exp + dlogits @ np.asarray(w_gate, F64).T
+    return {"dx": round_act(dx, act), "dw1": dw1.astype(F32), "dw2": dw2.astype(F32),
+            "dw_gate": g["dw_gate"], "db_gate": g["db_gate"],
+            "dlogits": g["dlogits"], "dg": g["dg"], "d_o": d_o, "dx_exp": dx_exp,
+            "dw1_f64": dw1, "dw2_f64": dw2, "dx_f64": dx}
+
+
+def gate_backward(dy, fwd: Dict[str, np.ndarray], x, w_gate, E: int):
+    """The gate's part of the backward, from the forward's expert outputs:
+    dg[t, j] = <dy[t], O[row of slot (t, j)]> (0 for a dropped slot); the
+    softmax over the chosen logits gives dsel_j = w_j (dg_j - sum_i w_i dg_i)
+    and dlogits[t, idx_j] = dsel_j (0 elsewhere); dW_gate = x^T dlogits and
+    db = sum_t dlogits.  float64 throughout; dlogits, dW_gate and db are also
+    returned rounded to float32."""
+    dy = np.asarray(dy, F64)
+    T = dy.shape[0]
+    idx, w = fwd["idx"], np.asarray(fwd["w"], F64)
+    k = idx.shape[1]
+    slot_row = fwd["slot_row"].reshape(T, k)
+    o = fwd["o"]
+    dg = np.zeros((T, k), dtype=F64)
+    for j in range(k):
+        r = slot_row[:, j]
+        kept = r >= 0
+        dg[kept, j] = np.einsum("td,td->t", dy[kept], o[r[kept]])
     s = (w * dg).sum(axis=1, keepdims=True)
     dsel = w * (dg - s)
     dlogits = np.zeros((T, E), dtype=F64)
@@ -407,11 +432,8 @@ def backward(dy, fwd: Dict[str, np.ndarray], x, w_gate, w1, w2, act: str, copies
         dlogits[rows, idx[:, j]] += dsel[:, j]
     dw_gate = np.asarray(x, F64).T @ dlogits
     db = dlogits.sum(axis=0)
-    dx = dx_exp + dlogits @ np.asarray(w_gate, F64).T
-    return {"dx": round_act(dx, act), "dw1": dw1.astype(F32), "dw2": dw2.astype(F32),
-            "dw_gate": dw_gate.astype(F32), "db_gate": db.astype(F32),
-            "dlogits": dlogits.astype(F32), "dg": dg, "d_o": d_o, "dx_exp": dx_exp,
-            "dw1_f64": dw1, "dw2_f64": dw2, "dx_f64": dx}
+    return {"dg": dg, "dlogits_f64": dlogits, "dlogits": dlogits.astype(F32),
+            "dw_gate": dw_gate.astype(F32), "db_gate": db.astype(F32)}
 
 
 # --------------------------------------------------------------------------

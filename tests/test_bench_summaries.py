@@ -116,11 +116,11 @@ def test_traffic_summary_scales_by_the_copy(tmp_path, out_root):
     wpath = run("WRITE_SIZE", gib_kib, 300.0, 400.0, 50.0)
     # route / permute / combine kernels in the same runs (two dispatches each,
     # readings differing, so the per-call mean is checked)
-    part_kernels = {"void moe::route_mfma_kernel<16, 1, 4, 4, 1>(...)": (10.0, 1.0),
+    part_kernels = {"void moe::route_tile_kernel<64, 16, 8, 1, 1, 4, 128, 7>(...)": (10.0, 1.0),
                     "moe::rank_hist_kernel(...)": (2.0, 3.0),
                     "moe::scan_kernel(...)": (0.5, 0.25),
-                    "void moe::gather_kernel<__bf16>(...)": (20.0, 30.0),
-                    "void moe::combine_kernel<__bf16>(...)": (40.0, 8.0)}
+                    "_ZN3moe13gather_kernelIDF16bEEvPKT_PKi": (20.0, 30.0),
+                    "_ZN3moe14combine_kernelIDF16bEEvPKT_PKfPKiPS1_iiib": (40.0, 8.0)}
     for counter, path, col in (("FETCH_SIZE", fpath, 0), ("WRITE_SIZE", wpath, 1)):
         rows = list(csv.DictReader(open(path, newline="")))
         extra = []

@@ -11,6 +11,8 @@ against the CPU reference on what it can compute at that size:
   the expert's rows;
 * dW_gate = x^T dlogits and db = sum_t dlogits (properties at any size,
   evaluated on the GPU's own dlogits) and dlogits on the sampled tokens;
+  on the skewed workload, dW_gate, db and every token's dlogits against the
+  reference's full forward and gate backward;
 * the popularity window over the fine-grained workload's 8 drifting
   iterations (exact integers).
 """
@@ -152,3 +154,32 @@ def test_fine_grained_popularity_over_drifting_iterations():
         touched = set().union(*touched_hist[-w.window:])
         keep = np.array([e not in touched for e in range(w.E)])
         np.testing.assert_array_equal(ws_gpu[keep], ws_ref[keep])
+
+
+def test_skewed_full_size_gate_gradients_against_reference():
+    """The skewed workload at full size (T=8192, d=2048, F=8192, E=32):
+    dW_gate and db against the reference's own full forward and gate
+    backward (dg from every expert output), on every expert that no
+    near-tie routing disagreement touches."""
+    w = WL["skewed_zipf12"]
+    print(f"full-size gate gradients {w.name}: {w.description}", flush=True)
+    inp, dev = _setup(w)
+    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, w.capacity_factor, act_code(w.dtype))
+    layer.forward(dev["x"], dev["w_gate"], dev["b_gate"], dev["w1"], dev["w2"])
+    layer.backward(dev["dy"], dev["x"], dev["w_gate"], dev["w1"], dev["w2"])
+    torch.cuda.synchronize()
+    fwd = orc.forward(inp["x"], inp["w_gate"], inp["b_gate"], inp["w1"], inp["w2"], w.k,
+                      w.capacity_factor, w.dtype)
+    g = orc.gate_backward(inp["dy"], fwd, inp["x"], inp["w_gate"], w.E)
+    gidx = down(layer.topk_idx)
+    mism = np.where((gidx != fwd["idx"]).any(axis=1))[0]
+    assert set(mism.tolist()) <= set(ambiguous_tokens(fwd["logits"], w.k).tolist())
+    touched = set(fwd["idx"][mism].reshape(-1).tolist()) | set(gidx[mism].reshape(-1).tolist())
+    keep = np.array([e not in touched for e in range(w.E)])
+    assert keep.sum() >= w.E - 4
+    tol = TOL[w.dtype]
+    assert_close(down(layer.dw_gate)[:, keep], g["dw_gate"][:, keep], tol, "dw_gate")
+    assert_close(down(layer.db_gate)[keep], g["db_gate"][keep], tol, "db_gate")
+    keep_t = np.ones(w.T, bool)
+    keep_t[mism] = False
+    assert_close(down(layer.dlogits)[keep_t], g["dlogits"][keep_t], tol, "dlogits")
