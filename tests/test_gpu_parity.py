@@ -247,7 +247,10 @@ def compare_end_to_end(w, layer, fwd, bwd, w1=None):
     (float32 rounding of a pre-activation at zero), and the FC1 weight-
     gradient rows and the tokens they touch are left out of those two
     comparisons.  Everything else must match: integers bit-exact, floats
-    within tolerance."""
+    within tolerance.  The numbers set aside are printed (run with -s to see
+    them) and bounded: a near-kink flip needs a pre-activation within float32
+    rounding of zero, so at most 0.1% of the dW1 rows and of the tokens (and
+    a handful in tiny cases) may be set aside for it."""
     tol = TOL[w.dtype]
     assert_close(down(layer.logits), fwd["logits"], 1e-5, "logits")
     gidx = down(layer.topk_idx)
@@ -266,6 +269,7 @@ def compare_end_to_end(w, layer, fwd, bwd, w1=None):
     assert_close(down(layer.y)[keep_t], fwd["y"][keep_t], tol, "y")
     dw1_g, dw1_r = down(layer.dw1), np.array(bwd["dw1"])
     keep_dx = keep_t.copy()
+    pairs = []
     if w1 is not None and w.dtype == "bf16":
         og, orf = down(layer.offsets), fwd["offsets"]
         rows_g = {e: (int(og[e]), int(og[e + 1])) for e in range(w.E)}
@@ -275,6 +279,12 @@ def compare_end_to_end(w, layer, fwd, bwd, w1=None):
         for e, c in pairs:
             dw1_g[e, c] = dw1_r[e, c] = 0.0
         keep_dx[fwd["row_token"][rows]] = False
+    kink_tokens = int(keep_t.sum() - keep_dx.sum())
+    print(f"set aside T={w.T} E={w.E} F={w.F}: {mism.size} near-tie tokens "
+          f"({int((~keep_e).sum())} experts), {len(pairs)} near-kink dW1 rows, "
+          f"{kink_tokens} near-kink dX tokens", flush=True)
+    assert len(pairs) <= max(4, w.E * w.F // 1000), f"{len(pairs)} dW1 rows set aside"
+    assert kink_tokens <= max(4, w.T // 1000), f"{kink_tokens} dX tokens set aside"
     assert_close(down(layer.dx)[keep_dx], bwd["dx"][keep_dx], tol, "dx")
     assert_close(down(layer.dlogits)[keep_t], bwd["dlogits"][keep_t], tol, "dlogits")
     assert_close_per_expert(dw1_g[keep_e], dw1_r[keep_e], tol, "dw1")
