@@ -16,9 +16,13 @@ traffic      = HBM bytes per launch of that kernel from the FETCH_SIZE and
                WRITE_SIZE counters (profiles/rows_gemm_<workload>_hbm_traffic.md),
                or null when the GEMM source changed since they were taken
 cpu_baseline = the CPU reference on a bounded sample of the same workload
-warm_ms      = median, p10 and p90 of the timed steps and of single forward,
-               fused-forward and backward calls back to back; cold_ms the same
-               for forward and backward after writing 512 MiB (caches flushed)
+warm_ms      = median, p10 and p90 of the timed steps
+parts_ms     = each entry point and next-row step, warm (calls back to back)
+               and cold (after writing 512 MiB and then reading another
+               512 MiB, so the caches hold clean lines of other data)
+hbm_parts    = route, permute and combine, cold, against their algorithmic
+               bytes; also timed after the write alone, whose dirty lines'
+               write-back then lands inside the timed call
 probes       = a 1 GiB device copy and the vendor dense GEMM of the same flops,
                measured in the same run, with the run's fractions of them
 
@@ -604,10 +608,14 @@ def main():
         return a.elapsed_time(b) / reps
 
     reps = args.kernel_reps
-    # cold cache: 512 MiB written before each repetition (evicts the 256 MB
-    # last-level cache and every L2); warm: calls back to back on the same
-    # inputs (working sets under 256 MB then come from the caches)
+    # cold cache: 512 MiB written, then 512 MiB of another buffer read before
+    # each repetition (evicts the 256 MB last-level cache and every L2 and
+    # leaves them holding clean lines: after the write alone, up to 256 MB of
+    # dirty lines would be written back during the timed call); warm: calls
+    # back to back on the same inputs (working sets under 256 MB then come
+    # from the caches)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush_rd = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
 
     def pct(ts):
         q = np.percentile(ts, [10, 50, 90])
@@ -625,10 +633,12 @@ def main():
         torch.cuda.synchronize()
         return pct([evs[r].elapsed_time(evs[r + 1]) for r in range(reps)])
 
-    def cold(fn, reps=args.cold_reps):
+    def cold(fn, reps=args.cold_reps, clean=True):
         ts = []
         for r in range(reps):
             flush.fill_(r & 255)
+            if clean:
+                flush_rd.sum()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             fn()
@@ -650,6 +660,8 @@ def main():
     parts = {}
     for name, fn in part_fns.items():
         parts[name] = {"warm": warm(fn), "cold": cold(fn)}
+        if name in ("route", "permute", "combine"):
+            parts[name]["cold_after_write_only"] = cold(fn, clean=False)
         log(f"{name}: warm {parts[name]['warm']['median'] * 1e3:.1f} us, cold "
             f"{parts[name]['cold']['median'] * 1e3:.1f} us (medians)")
     t_ffn = parts["expert_ffn"]["warm"]["median"]
@@ -724,7 +736,8 @@ def main():
         gbs = hbm_bytes[name] / (tc / 1e3) / 1e9
         rec = {"bytes": hbm_bytes[name], "cold_ms": tc, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS,
                "warm_ms": tw, "warm_GB/s (cache-resident)": hbm_bytes[name] / (tw / 1e3) / 1e9,
-               "counter_bytes": None if counters is None else counters.get(name)}
+               "counter_bytes": None if counters is None else counters.get(name),
+               "cold_after_write_only_ms": parts[name]["cold_after_write_only"]["median"]}
         if name == "route":
             bound_us = max(hbm_bytes[name] / PEAK_HBM_GBS / 1e3,
                            3 * 2.0 * w.T * w.d * w.E / PEAK_BF16_TFLOPS / 1e6)
@@ -739,7 +752,6 @@ def main():
     step_ms = [(start if i == 0 else step_end[i - 1]).elapsed_time(step_end[i])
                for i in range(args.steps)]
     warm_ms = {"step": pct(step_ms)}
-    del flush
 
     # Probes measured on the same GPU in the same run: a plain 1 GiB device
     # copy (read + write) and the vendor dense GEMM (torch.mm in bf16) with the
@@ -759,9 +771,13 @@ def main():
     src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)
     copy_gbs = 2.0 * (1 << 30) / (probe_ms(lambda: dst.copy_(src)) * 1e-3) / 1e9
-    del src, dst
-    probes = {"copy_1GiB_GB/s": copy_gbs,
-              "hbm_parts_cold_frac_of_copy": {k: v["GB/s"] / copy_gbs for k, v in hbm.items()}}
+    # the same copy once, after the cold-cache flush the parts are timed after
+    copy_cold_gbs = 2.0 * (1 << 30) / (cold(lambda: dst.copy_(src))["median"] * 1e-3) / 1e9
+    del src, dst, flush, flush_rd
+    probes = {"copy_1GiB_GB/s": copy_gbs, "copy_1GiB_cold_GB/s": copy_cold_gbs,
+              "hbm_parts_cold_frac_of_copy": {k: v["GB/s"] / copy_gbs for k, v in hbm.items()},
+              "hbm_parts_cold_frac_of_cold_copy": {k: v["GB/s"] / copy_cold_gbs
+                                                   for k, v in hbm.items()}}
     if w.dtype == "bf16":
         pa = torch.randn(s_kept, w.d, device="cuda").to(torch.bfloat16)
         pb = (torch.randn(w.d, w.F, device="cuda") * 0.02).to(torch.bfloat16)
@@ -769,7 +785,7 @@ def main():
         probes.update({"dense_gemm_shape": [s_kept, w.d, w.F], "dense_gemm_TFLOP/s": mm_tflops,
                        "roofline_frac_of_dense_gemm": achieved / mm_tflops})
         del pa, pb
-    log(f"probes: copy {copy_gbs:.0f} GB/s, dense GEMM "
+    log(f"probes: copy {copy_gbs:.0f} GB/s ({copy_cold_gbs:.0f} cold), dense GEMM "
         f"{probes.get('dense_gemm_TFLOP/s', float('nan')):.0f} TFLOP/s")
 
     if args.copy_calibration:

@@ -270,12 +270,15 @@ moe_status moe_backward(const moe_shape* shape, const void* dy, const void* x,
  * replica_start[e] + c of expert e takes the packed rows
  * [replica_row0[p], replica_row0[p] + replica_rows[p]) - moe_ep_plan's
  * outputs, n_copies = replica_start[E] = E + extra.  The weight-gradient
- * GEMMs schedule every copy as a K range of its own (what that copy's rank
- * would compute), and an expert with several copies gets dW1[e], dW2[e],
- * dW_gate[:, e] and db[e] as the sum of its copies' float32 partial
- * gradients in copy order (the fixed-order reduction of the copies'
- * gradients); an expert with one copy gets exactly moe_backward's values, as
- * do dx and dlogits.  bf16 only (MOE_ERR_UNSUPPORTED otherwise); E <=
+ * tile scheduler splits an expert with several copies over them when one of
+ * its unsplit output tiles would outlast a workgroup's mean share of the
+ * launch (rows_e * workgroups > output tiles per expert * all rows; the
+ * workgroups are min(the device's CUs, n_copies * output tiles per expert)):
+ * each copy is then a K range of its own (what that copy's rank would
+ * compute), and dW1[e], dW2[e], dW_gate[:, e] and db[e] are the sum of its
+ * copies' float32 partial gradients in copy order (the fixed-order reduction
+ * of the copies' gradients).  Every other expert, whatever its copies, gets
+ * exactly moe_backward's values, as do dx and dlogits.  bf16 only (MOE_ERR_UNSUPPORTED otherwise); E <=
  * n_copies <= MOE_PLAN_MAX_COPIES.  Copies that do not tile their expert's
  * rows give unspecified weight gradients (never an access outside the
  * operands).  Workspace: moe_backward_replicated_workspace_bytes(shape,

@@ -928,8 +928,8 @@ struct WgradArgs {
   float* db_gate;
   int32_t* next_tile;  // tile queue: zero at launch
   // Replicas (null rep_start: none).  Copy p = rep_start[e] + c of expert e
-  // takes the packed rows [rep_row0[p], rep_row0[p] + rep_rows[p]); an
-  // expert with several copies gets one float32 partial dW per copy
+  // takes the packed rows [rep_row0[p], rep_row0[p] + rep_rows[p]).  An
+  // expert split over its copies gets one float32 partial dW per copy
   // (part [slot][N1][N2], gate partials gpart [slot][N2], dbpart [slot]),
   // summed in copy order by wgrad_reduce_kernel.
   const int32_t* rep_start;
@@ -939,16 +939,32 @@ struct WgradArgs {
   float* gpart;
   float* dbpart;
   int n_copies, max_slots;  // sizes of rep_row0 / rep_rows and of part
+  int tiles_per_copy, grid;  // output tiles of one expert; workgroups launched
   int N1, N2, E;
 };
 
-// Per-expert copy counts and the partial slots of experts with several
-// copies (LDS, whole block): s_nc[e] copies, s_slot[e] first slot or -1.
+// Per-expert copy counts in the schedule and the partial slots of the
+// experts split over their copies (LDS, whole block): s_nc[e] copies (1 when
+// not split), s_slot[e] first slot or -1.
+//
+// An expert with several copies is split over them only where that can
+// shorten the schedule: when one of its unsplit tiles (a K loop over all its
+// rows) would take longer than a workgroup's mean share of the whole launch,
+// rows_e * grid > tiles_per_copy * rows of all experts.  Otherwise its tiles
+// run over all its rows, exactly as without copies, and the tile queue
+// balances the load by itself.  The rule reads only the offsets and the
+// launch shape, so both kernels of a launch (and every call with the same
+// inputs) take the same decision.
 __device__ __forceinline__ void wgrad_copies(const WgradArgs& p, int* s_nc, int* s_slot,
                                              int* s_scratch) {
   const int tid = threadIdx.x;
   int nc = 1;
-  if (tid < p.E && p.rep_start != nullptr) nc = p.rep_start[tid + 1] - p.rep_start[tid];
+  if (tid < p.E && p.rep_start != nullptr) {
+    nc = p.rep_start[tid + 1] - p.rep_start[tid];
+    const long long rows = p.offsets[tid + 1] - p.offsets[tid];
+    const long long all_rows = p.offsets[p.E];
+    if (nc > 1 && rows * p.grid <= (long long)p.tiles_per_copy * all_rows) nc = 1;
+  }
   const int multi = (tid < p.E && nc > 1) ? nc : 0;
   int total;
   const int ex = block_exclusive_scan(multi, s_scratch, &total);
@@ -960,14 +976,14 @@ __device__ __forceinline__ void wgrad_copies(const WgradArgs& p, int* s_nc, int*
 
 // Persistent: one workgroup per CU takes tiles from a queue (an atomic
 // counter) in longest-processing-time order - the experts by decreasing row
-// count (ties by index), each expert's copies in order, each copy's tiles row
-// by row - so the long K loops of popular experts start first and the short
-// ones fill in behind them.  A tile's float32 dW leaves through non-temporal
+// count (ties by index), a split expert's copies in order, each copy's tiles
+// row by row - so the long K loops of popular experts start first and the
+// short ones fill in behind them.  A tile's float32 dW leaves through non-temporal
 // stores that stay in flight while the next tile's k loop runs (only LDS is
 // fenced between tiles).  Which workgroup takes which tile varies; each tile
 // is computed the same way, so the results are bitwise reproducible.
-// Experts with no rows store zeros.  An expert with one copy (always, without
-// replicas) computes exactly the unreplicated tiles.
+// Experts with no rows store zeros.  An expert that is not split (always,
+// without replicas) computes exactly the unreplicated tiles.
 //
 // With GATE, the tiles of the first N1 tile row also produce the gate's
 // weight gradient over the same rows, dW_gate[:, e] = X2_e^T gsel_e and
@@ -1022,7 +1038,7 @@ wgrad_kernel(WgradArgs p) {
     const int t1 = in / T2, t2 = in % T2;
     const int n1 = t1 * BM, n2 = t2 * BN;
     int r0 = p.offsets[e], K = s_cnt[e];
-    if (p.rep_start != nullptr) {
+    if (p.rep_start != nullptr && s_nc[e] > 1) {
       // a copy's rows, kept inside the expert's own rows whatever the plan
       // holds (copies that do not tile the rows give unspecified results,
       // never an access outside the operands)
@@ -1066,7 +1082,7 @@ wgrad_kernel(WgradArgs p) {
   }
 }
 
-// Weight gradients of experts with several copies: the sum of the copies'
+// Weight gradients of the experts split over their copies: the sum of the copies'
 // partial dW in copy order (the fixed-order reduction a replicated expert's
 // gradient needs), plus, with gate partials, dW_gate[:, e] and db[e].
 // Workgroup row y handles the y-th such expert (in index order); its columns
@@ -1349,15 +1365,17 @@ static hipError_t launch_rows(const bf16* A, const bf16* B, bf16* C, const uint3
 }
 
 template <int BM, int BN, bool GATE>
-static hipError_t launch_wgrad_t(const WgradArgs& p, int n_copies, hipStream_t s) {
-  const long long tiles =
-      (long long)n_copies * ((p.N1 + BM - 1) / BM) * ((p.N2 + BN - 1) / BN);
-  const long long grid = std::min<long long>(tiles, device_cus());  // one workgroup per CU
-  hipLaunchKernelGGL((wgrad_kernel<BM, BN, GATE>), dim3((unsigned)grid), dim3(kGemmThreads), 0,
-                     s, p);
+static hipError_t launch_wgrad_t(WgradArgs p, int n_copies, hipStream_t s) {
+  p.tiles_per_copy = ((p.N1 + BM - 1) / BM) * ((p.N2 + BN - 1) / BN);
+  const long long tiles = (long long)n_copies * p.tiles_per_copy;
+  // one workgroup per CU (at most as many as the tiles of a schedule that
+  // splits every expert over all its copies)
+  p.grid = (int)std::min<long long>(tiles, device_cus());
+  hipLaunchKernelGGL((wgrad_kernel<BM, BN, GATE>), dim3((unsigned)p.grid), dim3(kGemmThreads),
+                     0, s, p);
   MOE_TRY(hipGetLastError());
   if (p.rep_start != nullptr && n_copies > p.E) {
-    // at most n_copies - E experts have several copies
+    // at most n_copies - E experts are split
     hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(512, n_copies - p.E), dim3(256), 0, s, p);
   }
   return hipGetLastError();
@@ -1384,7 +1402,7 @@ static hipError_t launch_wgrad(const bf16* X1, const bf16* X2, float* C, const i
               rep ? rep->start : nullptr, rep ? rep->row0 : nullptr, rep ? rep->rows : nullptr,
               rep ? rep->part : nullptr, rep && GATE ? rep->gpart : nullptr,
               rep && GATE ? rep->dbpart : nullptr, rep ? rep->n_copies : 0, max_slots,
-              N1, N2, E};
+              0, 0, N1, N2, E};
   const int n_copies = rep ? rep->n_copies : E;
   auto mt = [&](int bm) { return (long long)E * ((N1 + bm - 1) / bm); };
   const Shape2 t = pick_tile(mt, N2);

@@ -73,6 +73,9 @@ SMALL = {
     # K = d = 2048: FC1 (ReLU and keep bits) and the masked input gradient
     # split their last round along K, so their fixups apply those epilogues
     "skewed_split_fc1": workloads.scaled(WL["skewed_zipf12"], T=700, d=2048, F=512),
+    # 32 weight-gradient tiles per expert (256 x 128) and even experts: with
+    # copies, no expert's rows are worth splitting over them
+    "uniform_walk_k512": workloads.scaled(WL["uniform_cf125"], T=4096, d=512, F=2048),
 }
 
 

@@ -1,10 +1,11 @@
-"""moe_backward_replicated on the GPU: each expert's weight gradients split
-over the copies of the dispatch plan (moe_ep_plan, run on the GPU from the
-layer's own packed rows), summed in copy order.  Against the reference's
-backward with the same copies (oracle.backward(copies=...)) through the
-end-to-end comparison, and against moe_backward on the same saved tensors:
-dx and dlogits bit for bit, single-copy experts' weight and gate gradients
-bit for bit, multi-copy experts within tolerance."""
+"""moe_backward_replicated on the GPU: the weight gradients of experts with
+copies in the dispatch plan (moe_ep_plan, run on the GPU from the layer's own
+packed rows) split over those copies where the tile schedule gains from it,
+summed in copy order.  Against the reference's backward with the same copies
+(oracle.backward(copies=...)) through the end-to-end comparison, and against
+moe_backward on the same saved tensors: dx and dlogits bit for bit, every
+expert's weight and gate gradients either bit for bit (not split) or, for an
+expert with copies, within tolerance (split)."""
 import types
 
 import numpy as np
@@ -29,7 +30,15 @@ CASES = [
     ("uniform_cf050", 16, 4),           # drops: the dropped slots' gate gradient on top
     ("skewed_split_tail", 32, 8),       # K = F = 2048, split-tail row GEMMs
     ("skewed_zipf12", 0, 8),            # no extra copies: all bit for bit
+    ("uniform_walk_k512", 16, 8),       # copies, but no split pays: all bit for bit
 ]
+
+# Cases where the split must run (a small per-expert tile count and a hot
+# expert: one of its unsplit tiles would outlast a workgroup's mean share)
+# and where it must not (each expert's share of the rows, 1/16 on average,
+# under 32 tiles per expert / 256 CUs = 1/8).
+MUST_SPLIT = {"skewed_zipf12", "mixtral_shaped"}
+NO_SPLIT = {"uniform_walk_k512"}
 
 
 def _plan(layer, E, extra, R):
@@ -67,14 +76,20 @@ def test_backward_replicated(name, extra, R):
     # against moe_backward on the same saved tensors
     for key in ("dx", "dlogits"):
         assert torch.equal(g[key], getattr(layer, key)), key
-    single = ~multi
+    same = np.ones(w.E, bool)
     for key in ("dw1", "dw2"):
         a, b = down(g[key]), down(getattr(layer, key))
-        np.testing.assert_array_equal(a[single], b[single], err_msg=key)
+        same &= np.array([np.array_equal(a[e], b[e]) for e in range(w.E)])
         if multi.any():
             assert_close_per_expert(a[multi], b[multi], TOL[w.dtype], key)
-    np.testing.assert_array_equal(down(g["dw_gate"])[:, single], down(layer.dw_gate)[:, single])
-    np.testing.assert_array_equal(down(g["db_gate"])[single], down(layer.db_gate)[single])
+    assert same[~multi].all(), "an expert without copies must match moe_backward bit for bit"
+    split = ~same
+    np.testing.assert_array_equal(down(g["dw_gate"])[:, ~split], down(layer.dw_gate)[:, ~split])
+    np.testing.assert_array_equal(down(g["db_gate"])[~split], down(layer.db_gate)[~split])
+    if extra and name in MUST_SPLIT:
+        assert split.any(), "a hot expert with copies should have been split"
+    if name in NO_SPLIT:
+        assert not split.any(), "no expert should have been split"
     # against the reference's backward with the same copies
     fwd = orc.forward(inp["x"], inp["w_gate"], inp["b_gate"], inp["w1"], inp["w2"], w.k,
                       w.capacity_factor, w.dtype, priority=w.priority)
