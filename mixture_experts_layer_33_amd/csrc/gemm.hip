@@ -1082,56 +1082,44 @@ wgrad_kernel(WgradArgs p) {
   }
 }
 
-// Weight gradients of the experts split over their copies: the sum of the copies'
-// partial dW in copy order (the fixed-order reduction a replicated expert's
-// gradient needs), plus, with gate partials, dW_gate[:, e] and db[e].
-// Workgroup row y handles the y-th such expert (in index order); its columns
-// stride over the N1 x N2 elements, 4 per thread.
+// Weight gradients of the experts split over their copies: the sum of the
+// copies' partial dW in copy order (the fixed-order reduction a replicated
+// expert's gradient needs), plus, with gate partials, dW_gate[:, e] and db[e].
+// Every workgroup walks the split experts in index order (none: it exits at
+// once), its threads striding over each one's N1 x N2 elements, 4 per thread.
 __global__ void __launch_bounds__(256)
 wgrad_reduce_kernel(WgradArgs p) {
   __shared__ int s_nc[MOE_MAX_EXPERTS];
   __shared__ int s_slot[MOE_MAX_EXPERTS];
   __shared__ int s_scratch[256 / 64 + 1];
-  __shared__ int s_e;
   wgrad_copies(p, s_nc, s_slot, s_scratch);
-  if (threadIdx.x < p.E) {  // the y-th expert with several copies, if any
-    const int e = threadIdx.x;
-    int before = 0;
-    for (int o = 0; o < e; ++o) before += s_nc[o] > 1;
-    if (s_nc[e] > 1 && before == (int)blockIdx.y) s_e = e;
-  }
-  if (threadIdx.x == 0) {
-    int m = 0;
-    for (int o = 0; o < p.E; ++o) m += s_nc[o] > 1;
-    if ((int)blockIdx.y >= m) s_e = -1;
-  }
   __syncthreads();
-  const int e = s_e;
-  if (e < 0) return;
-  const int nc = s_nc[e], slot0 = s_slot[e];
-  if (slot0 + nc > p.max_slots) return;  // beyond the plan's size (precondition)
   const size_t n = (size_t)p.N1 * p.N2;  // a multiple of 4 (N2 is)
-  float* dst = p.C + (size_t)e * n;
-  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n;
-       i += (size_t)gridDim.x * 256 * 4) {
-    f32x4 acc = *reinterpret_cast<const f32x4*>(p.part + (size_t)slot0 * n + i);
-    for (int c = 1; c < nc; ++c) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.part + (size_t)(slot0 + c) * n + i);
+  for (int e = 0; e < p.E; ++e) {
+    const int nc = s_nc[e], slot0 = s_slot[e];
+    if (nc <= 1 || slot0 + nc > p.max_slots) continue;  // not split / beyond the plan's size
+    float* dst = p.C + (size_t)e * n;
+    for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n;
+         i += (size_t)gridDim.x * 256 * 4) {
+      f32x4 acc = *reinterpret_cast<const f32x4*>(p.part + (size_t)slot0 * n + i);
+      for (int c = 1; c < nc; ++c) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(p.part + (size_t)(slot0 + c) * n + i);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += v[q];
+        for (int q = 0; q < 4; ++q) acc[q] += v[q];
+      }
+      __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(dst + i));
     }
-    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(dst + i));
-  }
-  if (p.gpart != nullptr && blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < p.N2; i += 256) {
-      float acc = p.gpart[(size_t)slot0 * p.N2 + i];
-      for (int c = 1; c < nc; ++c) acc += p.gpart[(size_t)(slot0 + c) * p.N2 + i];
-      p.dw_gate[(size_t)i * p.E + e] = acc;
-    }
-    if (threadIdx.x == 0) {
-      float acc = p.dbpart[slot0];
-      for (int c = 1; c < nc; ++c) acc += p.dbpart[slot0 + c];
-      p.db_gate[e] = acc;
+    if (p.gpart != nullptr && (int)blockIdx.x == e % (int)gridDim.x) {
+      for (int i = threadIdx.x; i < p.N2; i += 256) {
+        float acc = p.gpart[(size_t)slot0 * p.N2 + i];
+        for (int c = 1; c < nc; ++c) acc += p.gpart[(size_t)(slot0 + c) * p.N2 + i];
+        p.dw_gate[(size_t)i * p.E + e] = acc;
+      }
+      if (threadIdx.x == 0) {
+        float acc = p.dbpart[slot0];
+        for (int c = 1; c < nc; ++c) acc += p.dbpart[slot0 + c];
+        p.db_gate[e] = acc;
+      }
     }
   }
 }
@@ -1375,8 +1363,7 @@ static hipError_t launch_wgrad_t(WgradArgs p, int n_copies, hipStream_t s) {
                      0, s, p);
   MOE_TRY(hipGetLastError());
   if (p.rep_start != nullptr && n_copies > p.E) {
-    // at most n_copies - E experts are split
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(512, n_copies - p.E), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(2 * device_cus()), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -164,17 +164,43 @@ route_kernel(const ActT* __restrict__ x, const float* __restrict__ w_gate,
 // bf16 activations: router logits as a tiled product on the matrix cores.
 //
 // Each float32 W_gate value is split exactly into three bf16 parts,
-// W = hi + mid + lo, each part taking the next 8 bits of the 24-bit
-// significand.  A bf16 x times a bf16 part is exact in float32, so summing
-// x*hi + x*mid + x*lo with float32 accumulation gives float32 accuracy at
-// matrix-core rate.  The split happens in registers, on the fragment a
-// wavefront is about to use, so every W_gate value is split once per
-// workgroup and W_gate is staged in its own float32 layout.
-__device__ __forceinline__ void split3(float v, bf16& hi, bf16& mid, bf16& lo) {
-  hi = (bf16)v;
-  const float r1 = v - (float)hi;
-  mid = (bf16)r1;
-  lo = (bf16)(r1 - (float)mid);
+// W = hi + mid + lo: hi keeps the top 8 significant bits (the float's upper
+// half), mid the top 8 of the remainder, lo what is left, at most 8 bits
+// (exact while |W| >= 2^-103; below, lo's bits under float32's normal range
+// are dropped).  Both subtractions are exact.  A bf16 x times a bf16 part is
+// exact in float32, so summing x*hi + x*mid + x*lo with float32 accumulation
+// gives float32 accuracy at matrix-core rate.  The split happens in
+// registers, on the fragment a wavefront is about to use, so every W_gate
+// value is split once per workgroup and W_gate is staged in its own float32
+// layout.  Two values at a time: each part of the pair is the upper halves
+// of the two floats, packed by one byte permute (11 operations per pair).
+__device__ __forceinline__ void split3_pair(float w0, float w1, uint32_t& hi, uint32_t& mid,
+                                            uint32_t& lo) {
+  constexpr uint32_t kUpper = 0xffff0000u;  // upper half of a float: its bf16 truncation
+  constexpr uint32_t kPackUpper = 0x07060302u;  // perm: upper half of S1, then of S0
+  const uint32_t b0 = __builtin_bit_cast(uint32_t, w0), b1 = __builtin_bit_cast(uint32_t, w1);
+  const float r0 = w0 - __builtin_bit_cast(float, b0 & kUpper);
+  const float r1 = w1 - __builtin_bit_cast(float, b1 & kUpper);
+  const uint32_t c0 = __builtin_bit_cast(uint32_t, r0), c1 = __builtin_bit_cast(uint32_t, r1);
+  const float q0 = r0 - __builtin_bit_cast(float, c0 & kUpper);
+  const float q1 = r1 - __builtin_bit_cast(float, c1 & kUpper);
+  hi = __builtin_amdgcn_perm(b1, b0, kPackUpper);
+  mid = __builtin_amdgcn_perm(c1, c0, kPackUpper);
+  lo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, q1), __builtin_bit_cast(uint32_t, q0),
+                             kPackUpper);
+}
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// s_waitcnt vmcnt(VM) lgkmcnt(LGKM) (expcnt not waited), then s_barrier.  As
+// builtins rather than inline assembly, so that the compiler's own wait
+// counting sees them and adds no waits for loads already known complete;
+// s_barrier alone, without __syncthreads()' fence, which would wait for
+// every copy in flight.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(VM >= 0 && VM <= 63 && LGKM >= 0 && LGKM <= 15, "wait counts");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (LGKM << 8) | ((VM >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
 }
 
 // f(Ic<P>{}) for P = P0 .. N - 1, unrolled at compile time
@@ -190,9 +216,10 @@ __device__ __forceinline__ void unroll_stages(F&& f) {
 // experts (v_mfma_f32_16x16x32_bf16, blocks of 16 tokens x 16 experts; EP =
 // E rounded up to a power of two >= 16), then selects each token's top k.
 //
-// The four wavefronts split the work WM x WN x WK ways: token blocks, expert
-// blocks, and the 32-deep k slices of each stage (their partial logits are
-// summed in a fixed order at the end).  Splitting k keeps the LDS reads per
+// The four or eight wavefronts split the work WM x WN x WK ways: token
+// blocks, expert blocks, and the 32-deep k slices of each stage (their
+// partial logits are summed in a fixed order at the end).  Eight wavefronts
+// (two per SIMD) let one wavefront's split run beside another's MFMAs.  Splitting k keeps the LDS reads per
 // MFMA lowest and has every W_gate value split by one wavefront only, so it
 // is preferred while the accumulators fit in registers.  A stage holds the x
 // tile [BM][KD] (bf16) and the KD rows of W_gate [KD][E] (float32, one
@@ -200,34 +227,43 @@ __device__ __forceinline__ void unroll_stages(F&& f) {
 // bytes a lane, no registers; rows past the last token land as zeros; d is a
 // multiple of KD).  STAGES stages rotate, STAGES - 1 of them in flight, each
 // its own LDS object so that the compiler keeps the copies in flight past the
-// reads of other stages.  With few experts the kernel streams x from HBM; the
-// stage count sets how many bytes each CU keeps in flight.
+// reads of other stages; the epilogue's partial logits reuse the first.
+// With few experts the kernel streams x from HBM; the stage count sets how
+// many bytes each CU keeps in flight.
 //
 // x rows in LDS are KD * 2 bytes.  Rows shorter than 256 bytes: chunk kc of
 // row r sits at kc ^ ((r / rows per 256 bytes) % chunks per row); longer
 // rows: at kc ^ (r % 16).  Either way the 16 rows of a fragment read (one
 // 16-byte chunk each) fall in 16 different 16-byte bank groups.
-template <int BM, int EP, int EW, int WM, int WN, int WK, int KD, int STAGES>
+// Padding after each 1 KiB of staged W_gate (WP, only when E = EW, a power
+// of two from 32 to 128): the four k groups of a fragment read (rows 8 apart)
+// then start 16 banks apart instead of on the same banks.
+constexpr int route_wpad(int EW) { return EW == 32 ? 64 : EW == 64 ? 32 : EW == 128 ? 16 : 0; }
+
+template <int BM, int EP, int EW, int WM, int WN, int WK, int KD, int STAGES, bool WP>
 struct RouteCfg {
+  static constexpr int NWV = WM * WN * WK;          // wavefronts per workgroup
   static constexpr int FM = BM / 16 / WM;           // token blocks per wavefront
   static constexpr int FN = EP / 16 / WN;           // expert blocks per wavefront
   static constexpr int ROWB = KD * 2;               // bytes of an x row in LDS
   static constexpr int CPR = KD / 8;                // 16-byte chunks per row
   static constexpr int RPI = 1024 / ROWB;           // rows per wave copy instruction
   static constexpr int XB = BM * ROWB;              // x tile bytes
-  static constexpr int WB = (KD * EW * 4 + 1023) / 1024 * 1024;  // W_gate rows (E <= EW)
+  static constexpr int WCH = WP ? 1024 + route_wpad(EW) : 1024;  // LDS pitch of 1 KiB of W
+  static constexpr int WB = (KD * EW * 4 + 1023) / 1024 * WCH;  // W_gate rows (E <= EW)
   static constexpr int STAGE = XB + WB;
-  static constexpr int NX = XB / 1024, NW = WB / 1024;  // copy instructions per stage (most)
-  static constexpr int NXW = (NX + 3) / 4, NWW = (NW + 3) / 4;  // per wavefront
+  static constexpr int NX = XB / 1024, NW = WB / WCH;  // copy instructions per stage (most)
+  static constexpr int NXW = (NX + NWV - 1) / NWV, NWW = (NW + NWV - 1) / NWV;  // per wavefront
   static constexpr int NPW = NXW + NWW;             // copies per wavefront per stage
   static constexpr int SL = KD / 32 / WK;           // MFMA k slices per wavefront per stage
-  static_assert(WM * WN * WK == 4, "four wavefronts");
+  static_assert(NWV == 4 || NWV == 8, "four or eight wavefronts");
   static_assert(FM >= 1 && FN >= 1 && FM * 16 * WM == BM && FN * 16 * WN == EP, "blocks");
   static_assert(EW == EP || (EW == 8 && EP == 16), "staged experts");
   static_assert(SL >= 1 && SL * 32 * WK == KD, "whole slices per wavefront");
   static_assert(XB % 1024 == 0 && ROWB <= 1024, "whole copy instructions");
   static_assert(NPW * (STAGES - 2) <= 63, "s_waitcnt vmcnt counts at most 63");
   static_assert(STAGES >= 2, "double buffering at least");
+  static_assert(!WP || (route_wpad(EW) > 0 && EW == EP), "padded W_gate rows");
 };
 
 template <int KD>
@@ -236,14 +272,14 @@ __device__ __forceinline__ int route_swz(int row) {
   else return (row / (256 / (KD * 2))) & (KD / 8 - 1);
 }
 
-template <int BM, int EP, int EW, int WM, int WN, int WK, int KD, int STAGES>
-__global__ void __launch_bounds__(256)
+template <int BM, int EP, int EW, int WM, int WN, int WK, int KD, int STAGES, bool WP>
+__global__ void __launch_bounds__(64 * WM * WN * WK)
 route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
                   const float* __restrict__ b_gate, float* __restrict__ logits_out,
                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int d, int E,
                   int k) {
-  using Cf = RouteCfg<BM, EP, EW, WM, WN, WK, KD, STAGES>;
-  constexpr int FM = Cf::FM, FN = Cf::FN;
+  using Cf = RouteCfg<BM, EP, EW, WM, WN, WK, KD, STAGES, WP>;
+  constexpr int FM = Cf::FM, FN = Cf::FN, NWV = Cf::NWV;
   constexpr int S1 = STAGES > 1 ? Cf::STAGE : 16, S2 = STAGES > 2 ? Cf::STAGE : 16;
   constexpr int S3 = STAGES > 3 ? Cf::STAGE : 16, S4 = STAGES > 4 ? Cf::STAGE : 16;
   constexpr int S5 = STAGES > 5 ? Cf::STAGE : 16, S6 = STAGES > 6 ? Cf::STAGE : 16;
@@ -258,7 +294,10 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
   __shared__ __attribute__((aligned(16))) char st6[S6];
   __shared__ __attribute__((aligned(16))) char st7[S7];
   __shared__ __attribute__((aligned(16))) char dummy[1024];  // target of padding copies
-  __shared__ float red[WK][16][EP + 1];                      // one token block's logits
+  // one token block's logits, after the main loop: in stage 0's memory
+  typedef float RedRow[16][EP + 1];
+  static_assert(sizeof(RedRow) * WK <= Cf::STAGE, "the epilogue fits in a stage buffer");
+  RedRow* const red = reinterpret_cast<RedRow*>(st0);
   char* const stage[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -270,8 +309,8 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
   // this stage's W_gate rows: KD * E floats, copied as whole 1 KiB pieces
   const int nw = (KD * E * 4 + 1023) / 1024;
 
-  // Copy slots of this wavefront: NXW of x (instruction wid + 4 i of the
-  // stage's NX) then NWW of W_gate (wid + 4 i of nw).  A slot past its count
+  // Copy slots of this wavefront: NXW of x (instruction wid + NWV i of the
+  // stage's NX) then NWW of W_gate (wid + NWV i of nw).  A slot past its count
   // is padding: no bytes, written to `dummy`.  Only the lane offsets are
   // kept; the stage's k offset goes into the scalar offset.
   uint32_t voff[Cf::NPW];
@@ -279,7 +318,7 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
   unroll_stages<0, Cf::NPW>([&](auto J_) __attribute__((always_inline)) {
     constexpr int j = decltype(J_)::value;
     constexpr bool isx = j < Cf::NXW;
-    const int q = wid + 4 * (isx ? j : j - Cf::NXW);
+    const int q = wid + NWV * (isx ? j : j - Cf::NXW);
     const bool pad = q >= (isx ? Cf::NX : nw);
     if constexpr (isx) {
       const int row = q * Cf::RPI + lane / Cf::CPR;
@@ -288,7 +327,7 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
     } else {
       voff[j] = pad ? kPadOffset : (uint32_t)(q * 1024 + lane * 16);
     }
-    ldst[j] = pad ? -1 : (isx ? 0 : Cf::XB) + q * 1024;
+    ldst[j] = pad ? -1 : (isx ? q * 1024 : Cf::XB + q * Cf::WCH);
   });
   const bf16* xbase = x + (size_t)t0 * d;
   const uint32_t xbytes = (uint32_t)rows_valid * (uint32_t)d * 2u;
@@ -320,64 +359,88 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
   int ecol[FN];
 #pragma unroll
   for (int n = 0; n < FN; ++n) ecol[n] = min((wn * FN + n) * 16 + r16, E - 1);
-  auto compute = [&](const char* st) __attribute__((always_inline)) {
+  // One stage's operands in registers: this wavefront's x fragments and, per
+  // expert block, the 8 W_gate values of each lane, for each of its slices.
+  struct Frag {
+    bf16x8 a[Cf::SL][FM];
+    float w[Cf::SL][FN][8];
+  };
+  auto load = [&](const char* st, Frag& f) __attribute__((always_inline)) {
     const char* xs = st;
     const float* ws = reinterpret_cast<const float*>(st + Cf::XB);
 #pragma unroll
     for (int s = 0; s < Cf::SL; ++s) {
-      const int sl = kw * Cf::SL + s;  // slice of the stage
-      const int kc = sl * 4 + kq;
-      bf16x8 a[FM];
+      const int kc = (kw * Cf::SL + s) * 4 + kq;  // this lane's 8-deep k chunk
 #pragma unroll
       for (int m = 0; m < FM; ++m) {
         const int row = (wm * FM + m) * 16 + r16;
-        a[m] = *reinterpret_cast<const bf16x8*>(xs + row * Cf::ROWB +
-                                                ((kc ^ route_swz<KD>(row)) * 16));
+        f.a[s][m] = *reinterpret_cast<const bf16x8*>(xs + row * Cf::ROWB +
+                                                     ((kc ^ route_swz<KD>(row)) * 16));
       }
 #pragma unroll
       for (int n = 0; n < FN; ++n) {
-        // 8 consecutive k of this lane's expert, split into the 3 parts
-        bf16x8 pw[3];
+        // WP: row kc * 8 starts kc * EW / 32 padded KiB in; row kc * 8 + i
+        // at a compile-time offset from it
+        const char* wrow = reinterpret_cast<const char*>(ws) + kc * (EW / 32) * Cf::WCH +
+                           ecol[n] * 4;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          bf16 h, md, l;
-          split3(ws[(kc * 8 + i) * E + ecol[n]], h, md, l);
-          pw[0][i] = h;
-          pw[1][i] = md;
-          pw[2][i] = l;
+          if constexpr (WP)
+            f.w[s][n][i] = *reinterpret_cast<const float*>(
+                wrow + ((i * EW * 4) >> 10) * Cf::WCH + ((i * EW * 4) & 1023));
+          else
+            f.w[s][n][i] = ws[(kc * 8 + i) * E + ecol[n]];
         }
+      }
+    }
+  };
+  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < Cf::SL; ++s)
+#pragma unroll
+      for (int n = 0; n < FN; ++n) {
+        // 8 consecutive k of this lane's expert, split into the 3 parts
+        u32x4 ph, pm, pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t h, md, l;
+          split3_pair(f.w[s][n][2 * i], f.w[s][n][2 * i + 1], h, md, l);
+          ph[i] = h;
+          pm[i] = md;
+          pl[i] = l;
+        }
+        const bf16x8 pw[3] = {__builtin_bit_cast(bf16x8, ph), __builtin_bit_cast(bf16x8, pm),
+                              __builtin_bit_cast(bf16x8, pl)};
 #pragma unroll
         for (int p = 0; p < 3; ++p)
 #pragma unroll
           for (int m = 0; m < FM; ++m)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], pw[p], acc[m][n], 0, 0, 0);
+            acc[m][n] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[s][m], pw[p], acc[m][n], 0, 0, 0);
       }
-    }
-  };
-  // wait until this wavefront's copies of stage kt have landed (the later
-  // STAGES - 2 stages stay in flight) and its LDS reads are done, then meet
-  // the other wavefronts
-  auto sync = [&]() __attribute__((always_inline)) {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(Cf::NPW * (STAGES - 2))
-                 : "memory");
-  };
-  // step kt on stage buffer S (= kt % STAGES): refill the buffer stage kt - 1
-  // used with stage kt + STAGES - 1, then compute on stage kt
-  auto step = [&](auto S_, int kt) __attribute__((always_inline)) {
-    constexpr int S = decltype(S_)::value;
-    sync();
-    issue(kt + STAGES - 1, stage[(S + STAGES - 1) % STAGES]);
-    compute(stage[S]);
   };
   unroll_stages<0, STAGES - 1>([&](auto P_) __attribute__((always_inline)) {
     issue(decltype(P_)::value, stage[decltype(P_)::value]);
   });
+  // Step kt on stage buffer P = kt % STAGES: wait until this wavefront's
+  // copies of stage kt have landed (the later STAGES - 2 stay in flight) and
+  // its LDS reads are done, meet the other wavefronts, refill the buffer
+  // stage kt - 1 used with stage kt + STAGES - 1, then read and compute stage
+  // kt.  (Reading the next stage into registers during this one's MFMAs was
+  // measured: no faster.)
   for (int kt = 0; kt < nst; kt += STAGES)
     unroll_stages<0, STAGES>([&](auto P_) __attribute__((always_inline)) {
-      if (kt + decltype(P_)::value < nst) step(P_, kt + decltype(P_)::value);
+      constexpr int P = decltype(P_)::value;
+      if (kt + P < nst) {
+        wait_barrier<Cf::NPW * (STAGES - 2), 0>();
+        issue(kt + P + STAGES - 1, stage[(P + STAGES - 1) % STAGES]);
+        Frag f;
+        load(stage[P], f);
+        mma(f);
+      }
     });
   // padding copies past the last stage are still in flight
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  wait_barrier<0, 15>();
 
   // epilogue, one block of 16 tokens at a time: the wavefronts holding the
   // block's logits write them (partial sums per k-group) to LDS, then each
@@ -403,17 +466,18 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
           red[kw][kq * 4 + i][(wn * FN + n) * 16 + r16] = acc[m][n][i];
     }
     __syncthreads();
-    const int t = t0 + mb * 16 + grp;
+    // (eight wavefronts: groups 16..31 idle here)
+    const int g16 = grp & 15, t = t0 + mb * 16 + g16;
     float v[EPL];
 #pragma unroll
     for (int q = 0; q < EPL; ++q) {
-      float sum = red[0][grp][gl + 16 * q];
+      float sum = red[0][g16][gl + 16 * q];
 #pragma unroll
-      for (int w = 1; w < WK; ++w) sum += red[w][grp][gl + 16 * q];
+      for (int w = 1; w < WK; ++w) sum += red[w][g16][gl + 16 * q];
       v[q] = sum + bias[q];
     }
     __syncthreads();  // red is rewritten by the next block
-    if (t >= T) continue;
+    if (grp >= 16 || t >= T) continue;
     if (logits_out != nullptr) {
 #pragma unroll
       for (int q = 0; q < EPL; ++q) {
@@ -469,12 +533,17 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
   }
 }
 
-// Launch shapes.  Tokens per workgroup BM: enough workgroups for every CU
-// (BM = T / 256 rounded down to a power of two, 16..128; 64 at most with 256
-// experts).  Wavefronts split k (four ways when a stage has four slices) as
-// far as the accumulators allow, then experts, then tokens.  Stage depth KD:
-// 128 where four wavefronts split it (d a multiple of 128), else 64 (32 with
-// 256 experts).  Stages: as many as fit in LDS, at most eight.
+// Launch shapes, from timings on the four workloads' sizes (cold and warm).
+// Tokens per workgroup BM: enough workgroups for every CU (BM = T / 256
+// rounded down to a power of two, 16..128; 64 at most with 256 experts).
+// Wavefronts split k as far as the accumulators allow, then experts, then
+// tokens; eight wavefronts (two per SIMD) where the split's VALU work is
+// large against the MFMAs and the accumulators fit in half the registers:
+// with 16 padded experts (k eight ways, 256-deep stages, BM <= 64, d a
+// multiple of 256), 32 (experts two ways, k four ways) and 128 at BM = 128
+// (experts four ways, k two ways).  Stage depth KD: 128 where four
+// wavefronts split it (d a multiple of 128), else 64 (32 with 256 experts).
+// Stages: as many as fit in LDS, at most eight.
 struct RouteShape {
   int bm, wm, wn, wk, kd;
 };
@@ -482,33 +551,31 @@ static RouteShape route_shape(int T, int d, int EP) {
   int bm = 16;
   while (bm < 128 && T / (2 * bm) >= 256) bm *= 2;
   if (EP == 256) return {bm > 64 ? 64 : bm, 1, 4, 1, 32};
-  if (EP >= 64) {
-    if (EP == 64 && bm == 128) return {128, 1, 4, 1, 64};
-    return {bm, 1, 2, 2, 64};
-  }
+  if (EP == 128) return bm == 128 ? RouteShape{128, 1, 4, 2, 64} : RouteShape{bm, 1, 2, 2, 64};
+  if (EP == 64) return bm == 128 ? RouteShape{128, 1, 4, 1, 64} : RouteShape{bm, 1, 2, 2, 64};
   const bool k128 = d % 128 == 0;
   if (EP == 32) {
     if (bm == 128) return {128, 1, 2, 2, k128 ? 128 : 64};
-    return k128 ? RouteShape{bm, 1, 1, 4, 128} : RouteShape{bm, 1, 2, 2, 64};
+    return k128 ? RouteShape{bm, 1, 2, 4, 128} : RouteShape{bm, 1, 2, 2, 64};
   }
   // EP == 16
+  if (d % 256 == 0 && bm <= 64) return {bm, 1, 1, 8, 256};
   if (k128) return {bm, 1, 1, 4, 128};
   return {bm < 32 ? 32 : bm, 2, 1, 2, 64};
 }
 
-template <int BM, int EP, int EW, int WM, int WN, int WK, int KD>
+template <int BM, int EP, int EW, int WM, int WN, int WK, int KD, bool WP>
 static void launch_route_tile(hipStream_t s, const bf16* x, const float* w_gate, const float* b,
                               float* lo, int32_t* idx, float* w, int T, int d, int E, int k) {
-  using C2 = RouteCfg<BM, EP, EW, WM, WN, WK, KD, 2>;
-  // LDS: the stages, the epilogue's partial logits and the padding target
-  constexpr int RED = WK * 16 * (EP + 1) * 4;
-  constexpr int FIT = (160 * 1024 - RED - 1024 - 512) / C2::STAGE;
+  using C2 = RouteCfg<BM, EP, EW, WM, WN, WK, KD, 2, WP>;
+  // LDS: the stages (the epilogue reuses the first) and the padding target
+  constexpr int FIT = (160 * 1024 - 1024 - 512) / C2::STAGE;
   constexpr int VM = 63 / C2::NPW + 2;
   constexpr int MAXS = FIT < VM ? FIT : VM;
   constexpr int STAGES = MAXS < 2 ? 2 : (MAXS > 8 ? 8 : MAXS);
-  hipLaunchKernelGGL((route_tile_kernel<BM, EP, EW, WM, WN, WK, KD, STAGES>),
-                     dim3((T + BM - 1) / BM), dim3(256), 0, s, x, w_gate, b, lo, idx, w, T, d, E,
-                     k);
+  hipLaunchKernelGGL((route_tile_kernel<BM, EP, EW, WM, WN, WK, KD, STAGES, WP>),
+                     dim3((T + BM - 1) / BM), dim3(64 * C2::NWV), 0, s, x, w_gate, b, lo, idx, w,
+                     T, d, E, k);
 }
 
 int route_padded_experts(int E) {
@@ -524,13 +591,22 @@ hipError_t launch_route(int act, const void* x, const float* w_gate, const float
     const int EP = route_padded_experts(E), EW = E <= 8 ? 8 : EP;
     const RouteShape r = route_shape(T, d, EP);
     const bf16* xs = static_cast<const bf16*>(x);
-    const int key = EW * 1000000 + r.bm * 1000 + r.wm * 100 + r.wn * 10 + r.kd / 32;
+    const long long key =
+        (((((long long)EW * 1000 + r.bm) * 10 + r.wm) * 10 + r.wn) * 10 + r.wk) * 10 + r.kd / 32;
+    const bool wp = E == EW && route_wpad(EW) > 0;
 #define MOE_RT(BM, EPV, EWV, WM, WN, WK, KD)                                                    \
-  case EWV * 1000000 + BM * 1000 + WM * 100 + WN * 10 + KD / 32:                                \
-    launch_route_tile<BM, EPV, EWV, WM, WN, WK, KD>(s, xs, w_gate, b_gate, logits_out,          \
-                                                    topk_idx, topk_w, T, d, E, k);              \
+  case ((((EWV * 1000LL + BM) * 10 + WM) * 10 + WN) * 10 + WK) * 10 + KD / 32:                  \
+    if (wp)                                                                                     \
+      launch_route_tile<BM, EPV, EWV, WM, WN, WK, KD, (route_wpad(EWV) > 0)>(                   \
+          s, xs, w_gate, b_gate, logits_out, topk_idx, topk_w, T, d, E, k);                     \
+    else                                                                                        \
+      launch_route_tile<BM, EPV, EWV, WM, WN, WK, KD, false>(s, xs, w_gate, b_gate, logits_out, \
+                                                             topk_idx, topk_w, T, d, E, k);     \
     break;
 #define MOE_RT16(EWV)                       \
+  MOE_RT(16, 16, EWV, 1, 1, 8, 256)         \
+  MOE_RT(32, 16, EWV, 1, 1, 8, 256)         \
+  MOE_RT(64, 16, EWV, 1, 1, 8, 256)         \
   MOE_RT(16, 16, EWV, 1, 1, 4, 128)         \
   MOE_RT(32, 16, EWV, 1, 1, 4, 128)         \
   MOE_RT(64, 16, EWV, 1, 1, 4, 128)         \
@@ -538,31 +614,26 @@ hipError_t launch_route(int act, const void* x, const float* w_gate, const float
   MOE_RT(32, 16, EWV, 2, 1, 2, 64)          \
   MOE_RT(64, 16, EWV, 2, 1, 2, 64)          \
   MOE_RT(128, 16, EWV, 2, 1, 2, 64)
+#define MOE_RT_BM(EPV, WM, WN, WK, KD) \
+  MOE_RT(16, EPV, EPV, WM, WN, WK, KD)  \
+  MOE_RT(32, EPV, EPV, WM, WN, WK, KD)  \
+  MOE_RT(64, EPV, EPV, WM, WN, WK, KD)
     switch (key) {
       MOE_RT16(8)
       MOE_RT16(16)
-      MOE_RT(16, 32, 32, 1, 1, 4, 128)
-      MOE_RT(32, 32, 32, 1, 1, 4, 128)
-      MOE_RT(64, 32, 32, 1, 1, 4, 128)
+      MOE_RT_BM(32, 1, 2, 4, 128)
+      MOE_RT_BM(32, 1, 2, 2, 64)
       MOE_RT(128, 32, 32, 1, 2, 2, 128)
-      MOE_RT(16, 32, 32, 1, 2, 2, 64)
-      MOE_RT(32, 32, 32, 1, 2, 2, 64)
-      MOE_RT(64, 32, 32, 1, 2, 2, 64)
       MOE_RT(128, 32, 32, 1, 2, 2, 64)
-      MOE_RT(16, 64, 64, 1, 2, 2, 64)
-      MOE_RT(32, 64, 64, 1, 2, 2, 64)
-      MOE_RT(64, 64, 64, 1, 2, 2, 64)
+      MOE_RT_BM(64, 1, 2, 2, 64)
       MOE_RT(128, 64, 64, 1, 4, 1, 64)
-      MOE_RT(16, 128, 128, 1, 2, 2, 64)
-      MOE_RT(32, 128, 128, 1, 2, 2, 64)
-      MOE_RT(64, 128, 128, 1, 2, 2, 64)
-      MOE_RT(128, 128, 128, 1, 2, 2, 64)
-      MOE_RT(16, 256, 256, 1, 4, 1, 32)
-      MOE_RT(32, 256, 256, 1, 4, 1, 32)
-      MOE_RT(64, 256, 256, 1, 4, 1, 32)
+      MOE_RT_BM(128, 1, 2, 2, 64)
+      MOE_RT(128, 128, 128, 1, 4, 2, 64)
+      MOE_RT_BM(256, 1, 4, 1, 32)
       default:
         return hipErrorInvalidValue;
     }
+#undef MOE_RT_BM
 #undef MOE_RT16
 #undef MOE_RT
     return hipGetLastError();

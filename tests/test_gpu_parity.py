@@ -101,30 +101,51 @@ def test_router_logits(name):
 # experts per part (8 for E <= 8, else E rounded up to a power of two >= 16)
 # x tokens per workgroup BM in {16, 32, 64, 128} (BM grows with T: 16 below
 # 8192 tokens, 32, 64 from 16384, 128 from 32768; at most 64 with 256
-# experts), each with its preferred stage depth (d a multiple of 128) and the
-# 64-deep fallback, with ragged token tails and E below its padded size
+# experts), each with the stage depths its table offers (16 experts: 256
+# deep with eight wavefronts where d is a multiple of 256 and BM <= 64, else
+# 128, else 64; 32: 128, else 64), with ragged token tails; for 32, 64 and
+# 128 experts both the padded W_gate layout (E a power of two) and the plain
+# one (E below its padded size)
 ROUTER_SHAPES = {}
-for _ew, _es in (("EW8", (8, 7, 8, 5, 8, 8, 6, 8)), ("EW16", (16, 13, 16, 13, 16, 16, 9, 12))):
+for _ew, _es in (("EW8", (8, 7, 8, 5, 8, 8, 6, 8, 8, 7, 5)),
+                 ("EW16", (16, 13, 16, 13, 16, 16, 9, 12, 16, 15, 11))):
     for _i, (_T, _d) in enumerate(((3001, 512), (3001, 320), (9000, 256), (9000, 64),
-                                   (20000, 128), (20000, 192), (40000, 128), (40000, 64))):
+                                   (20000, 128), (20000, 192), (40000, 128), (40000, 64),
+                                   (20000, 256), (3001, 384), (9000, 384))):
         ROUTER_SHAPES[f"{_ew}_T{_T}_d{_d}"] = (_T, _d, _es[_i], 2 if _es[_i] > 1 else 1)
 ROUTER_SHAPES.update({
     "EP32_BM16_KD128": (1000, 128, 32, 2),
+    "EP32_BM16_KD128_padded": (1000, 128, 24, 2),
     "EP32_BM16_KD64": (1000, 192, 32, 2),
+    "EP32_BM16_KD64_padded": (1000, 192, 17, 2),
+    "EP32_BM32_KD64": (9001, 64, 32, 2),
+    "EP32_BM32_KD128": (9001, 128, 32, 2),
     "EP32_BM32_KD128_padded": (9001, 128, 20, 3),
     "EP32_BM32_KD64_padded": (9001, 64, 20, 3),
     "EP32_BM64_KD128": (17000, 128, 32, 2),
+    "EP32_BM64_KD128_padded": (17000, 128, 30, 2),
     "EP32_BM64_KD64": (17000, 64, 32, 2),
+    "EP32_BM64_KD64_padded": (17000, 64, 27, 2),
+    "EP32_BM128_KD128": (33000, 128, 32, 2),
     "EP32_BM128_KD128_padded": (33000, 128, 31, 4),
+    "EP32_BM128_KD64": (33000, 64, 32, 4),
     "EP32_BM128_KD64_padded": (33000, 64, 31, 4),
     "EP64_BM16": (2000, 128, 64, 2),
+    "EP64_BM16_padded": (2000, 128, 33, 2),
+    "EP64_BM32": (8192, 64, 64, 3),
     "EP64_BM32_padded": (8192, 64, 48, 3),
     "EP64_BM64": (16384, 64, 64, 2),
-    "EP64_BM128_top1": (32768, 64, 40, 1),
+    "EP64_BM64_padded": (16384, 64, 57, 2),
+    "EP64_BM128": (32768, 64, 64, 2),
+    "EP64_BM128_top1_padded": (32768, 64, 40, 1),
+    "EP128_BM16": (1000, 128, 128, 4),
     "EP128_BM16_padded": (1000, 128, 126, 4),
     "EP128_BM32": (9000, 64, 128, 4),
+    "EP128_BM32_padded": (9000, 64, 65, 4),
+    "EP128_BM64": (16500, 64, 128, 2),
     "EP128_BM64_padded": (16500, 64, 100, 2),
     "EP128_BM128": (32768, 128, 128, 4),
+    "EP128_BM128_padded": (32768, 64, 120, 4),
     "EP256_BM16_padded": (700, 64, 250, 8),
     "EP256_BM32": (8200, 64, 256, 2),
     "EP256_BM64_padded": (16384, 64, 200, 8),
