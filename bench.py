@@ -429,7 +429,7 @@ def summarize_kernels(args):
          "Command (run from the repository root on one MI355X):", "", "```",
          args.command.strip() or "(not recorded)", "```", "",
          "All kernels of the run: the timed steps plus the per-part warm and cold timings "
-         "(cold ones after a 512 MiB fill kernel) and the probes; averages over each "
+         "(cold ones after a 512 MiB fill and a 512 MiB sum) and the probes; averages over each "
          f"kernel's dispatches.  Expert GEMM TFLOP/s: 2 d F S = {alg / 1e9:.1f} GFLOP per "
          "product over the kernel's average duration.", "",
          "| kernel | calls | average µs | total ms | share | GEMM TFLOP/s |",
