@@ -13,7 +13,8 @@ tokens, so it is checked two ways on the same seeded inputs:
 
 Cases: scaled copies of the workloads that span several GEMM tiles with
 ragged tails (drops under both capacity priorities, top-1, float32, E = 128
-with k = 4), and the headline and fine-grained shapes at full size."""
+with k = 4), and the four bf16 workloads at full size (there against the
+reference on every token's logits and routing and on sampled tokens' y)."""
 import numpy as np
 import pytest
 import torch
@@ -117,14 +118,39 @@ def test_fused_forward_edge_cases(name):
     _check_against_reference(w, inp, layer)
 
 
-@pytest.mark.parametrize("name", ["uniform_cf125", "fine_grained"])
-def test_fused_forward_full_size_matches_forward(name):
-    """At full size (the launch shapes bench.py times), bit for bit against
-    moe_forward, whose full-size results are sampled against the reference
-    in the full-size parity file."""
+def _check_sampled_against_reference(w, inp, layer, n_tokens=12):
+    """Full size: logits and routing of every token, and y of sampled tokens,
+    each from that token alone (the reference's per-token forward)."""
+    L = orc.router_logits(inp["x"], inp["w_gate"], inp["b_gate"])
+    assert_close(down(layer.logits), L, 1e-5, "logits")
+    idx, wt = orc.topk_gate(L, w.k)
+    gidx = down(layer.topk_idx)
+    mism = np.where((gidx != idx).any(axis=1))[0]
+    assert set(mism.tolist()) <= set(ambiguous_tokens(L, w.k).tolist())
+    s = orc.assign_slots(idx, w.E, orc.capacity(w.T, w.k, w.E, w.capacity_factor),
+                         priority=w.priority)
+    if mism.size == 0:
+        np.testing.assert_array_equal(down(layer.slot_row), s["slot_row"])
+    rng = np.random.default_rng(1)
+    toks = [int(t) for t in rng.choice(w.T, size=2 * n_tokens, replace=False)
+            if t not in mism][:n_tokens]
+    y_g = down(layer.y)
+    for t in toks:
+        y_ref = orc.token_output(t, inp["x"], wt, idx, s["slot_row"], inp["w1"], inp["w2"],
+                                 w.dtype)
+        assert_close(y_g[t], y_ref, TOL[w.dtype], f"y[{t}]")
+
+
+@pytest.mark.parametrize("name", ["uniform_cf125", "skewed_zipf12", "mixtral_shaped",
+                                  "fine_grained"])
+def test_fused_forward_full_size(name):
+    """At full size (the launch shapes bench.py times): bit for bit against
+    moe_forward, and logits, routing and sampled tokens' y against the
+    reference."""
     w = WL[name]
     inp, layer, ref, out_perm = _run(w)
     _check_against_unfused(w, layer, ref, out_perm)
+    _check_sampled_against_reference(w, inp, layer)
 
 
 def test_fused_forward_repeated_calls_and_smaller_shape():
