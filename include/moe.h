@@ -224,7 +224,7 @@ moe_status moe_forward_fused(const moe_shape* shape, const void* x, const float*
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation.  Same arguments (minus the workspace),
  * same kernels and the same results, bit for bit, as moe_forward.  The
- * workspace is a library-owned static device array of 34 MiB, one per GPU,
+ * workspace is a library-owned static device array of 36 MiB, one per GPU,
  * held until the process ends; no call allocates or frees anything.
  * Limit: T*k <= MOE_NOALLOC_MAX_SLOTS (else MOE_ERR_UNSUPPORTED, nothing
  * enqueued).  Every call on one GPU uses that GPU's one array, so calls that

@@ -17,7 +17,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 constexpr int kWave = 64;
 
 // Slots per tile of the permutation's per-tile histograms.
-constexpr int kRankTile = 1024;
+constexpr int kRankTile = 256;
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }

@@ -188,12 +188,12 @@ moe_status do_route(const moe_shape* s, const void* x, const float* w_gate, cons
 // per GPU (the loader places it with the code object on each device the
 // library runs on; it lives until the process ends).  Its size covers
 // moe_forward's workspace for every shape with T*k <= MOE_NOALLOC_MAX_SLOTS:
-// the per-slot ranks (4 bytes a slot), two per-(expert, 1024-slot tile)
+// the per-slot ranks (4 bytes a slot), two per-(expert, 256-slot tile)
 // tables, two per-expert count vectors, and the expert GEMMs' split-tail
 // partial tiles (32 MiB).  In host code `scratch` names a host-side stand-in,
 // not the device memory: only the address hipGetSymbolAddress returns for the
 // current device is ever passed to kernels.
-constexpr size_t kNoallocScratchBytes = 34u << 20;
+constexpr size_t kNoallocScratchBytes = 36u << 20;
 static __device__ __align__(256) char scratch[kNoallocScratchBytes];
 static_assert(((size_t)MOE_NOALLOC_MAX_SLOTS * 4 +
                2 * (size_t)MOE_MAX_EXPERTS * (MOE_NOALLOC_MAX_SLOTS / kRankTile) * 4 +

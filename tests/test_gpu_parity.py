@@ -27,7 +27,7 @@ if torch.cuda.is_available():
 
 WL = workloads.workloads()
 
-# scaled copies: T not a multiple of the 1024-slot tiles or the 128-row GEMM
+# scaled copies: T not a multiple of the 256-slot tiles or the 128-row GEMM
 # tiles, F not a multiple of the 128-column GEMM tiles
 SMALL = {
     "tiny_fp32": WL["tiny_fp32"],
