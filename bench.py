@@ -720,6 +720,8 @@ def main():
     t_pred = time_it(lambda: moe.moe_predict_popularity(w.E, w.E, layer.counts_raw, co_sum, pred,
                                                         order), reps)
     flops_launch = 2.0 * w.d * w.F * s_kept
+    # FC1 and FC2 move the same bytes: E*d*F weights, S_kept rows of d and F
+    gemm_bytes = float((2 if w.dtype == "bf16" else 4) * (w.E * w.d * w.F + s_kept * (w.d + w.F)))
     achieved = flops_launch / (gemm_launch_ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     log(f"expert FFN {t_ffn:.3f} ms warm ({achieved:.1f} TFLOP/s per GEMM launch in the steps)")
@@ -812,7 +814,14 @@ def main():
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": load_traffic(w.name),
                      "flops_per_launch": flops_launch,
-                     "launch_us": gemm_launch_ms * 1e3},
+                     "launch_us": gemm_launch_ms * 1e3,
+                     # attainable roofline of one launch: max(flops / peak,
+                     # algorithmic bytes / 8 TB/s); bytes = one expert weight
+                     # tensor + the packed rows in (d or F wide) and out
+                     "bytes_per_launch": gemm_bytes,
+                     "attainable_frac": max(flops_launch / (peak * 1e12),
+                                            gemm_bytes / (PEAK_HBM_GBS * 1e9))
+                                        / (gemm_launch_ms / 1e3)},
         "forward_tokens_per_s": fwd_tok,
         "parts_ms": {**{k: {"warm": v["warm"], "cold": v["cold"]} for k, v in parts.items()},
                      "ep_plan_8_ranks": t_plan, "dispatch_layout_8_ranks": t_layout,
