@@ -1148,50 +1148,122 @@ relu_bits_kernel(const bf16* __restrict__ h, const int32_t* __restrict__ offsets
 }
 
 // ---------------------------------------------------------------------------
-// float32 path (act = MOE_F32): plain FMA kernels, no reduced precision.
+// float32 path (act = MOE_F32): FMA kernels, no reduced precision.  Operands
+// are staged through LDS in k chunks; every output still accumulates its k
+// terms in increasing k order, one fmaf each, as a plain loop would.
 constexpr int kF32Rows = 16;
+constexpr int kF32Chunk = 32;  // k (rows of the expert for dW) per LDS chunk
 
 // C[r][n] = epi(sum_k A[r][k] B_e(n, k)); B_e(n,k) = B[e][n][k] (B_K) or B[e][k][n].
+// A workgroup takes 16 consecutive packed rows and 64 columns; its rows lie
+// in a contiguous range of experts (rows are packed by expert), and each
+// expert of that range gets its own pass over B_e.  Thread (row r, lane g)
+// computes columns g, g + 16, g + 32, g + 48.
+// Optional maps as in RowsArgs: A row a_map[r], C row c_map[r] (null: r).
 template <bool B_K, int EPI>
 __global__ void __launch_bounds__(256)
-// Optional maps as in RowsArgs: A row a_map[r], C row c_map[r] (null: r).
 f32_rows_kernel(const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C,
                 const float* __restrict__ aux, const int32_t* __restrict__ offsets, int K, int N,
                 int E, int S_max, const int32_t* __restrict__ a_map,
                 const int32_t* __restrict__ c_map) {
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
-  for (int i = threadIdx.x; i <= E; i += 256) s_off[i] = offsets[i];
+  __shared__ float sa[kF32Rows][kF32Chunk + 1];
+  __shared__ float sb[64][kF32Chunk + 1];
+  const int tid = threadIdx.x;
+  for (int i = tid; i <= E; i += 256) s_off[i] = offsets[i];
   __syncthreads();
-  const int r = blockIdx.x * kF32Rows + (threadIdx.x >> 4);
-  const int g = threadIdx.x & 15;
-  if (r >= s_off[E] || r >= S_max) return;
-  int e = 0;
-  while (!(s_off[e] <= r && r < s_off[e + 1])) ++e;
-  const float* a = A + (size_t)(a_map ? a_map[r] : r) * K;
-  const float* b = B + (size_t)e * N * K;
+  const int rows = min(s_off[E], S_max);
+  const int rb = blockIdx.x * kF32Rows;
+  if (rb >= rows) return;  // (the whole workgroup)
+  const int rl = min(rb + kF32Rows, rows) - 1;  // last live row of the workgroup
+  auto expert_of = [&](int row) {
+    int e = 0;
+    while (!(s_off[e] <= row && row < s_off[e + 1])) ++e;
+    return e;
+  };
+  const int lr = tid >> 4, g = tid & 15;
+  const int r = rb + lr;
+  const bool live = r <= rl;
+  const int e = live ? expert_of(r) : -1;
+  const int e_first = expert_of(rb), e_last = expert_of(rl);
+  const int n0 = blockIdx.y * 64;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int ee = e_first; ee <= e_last; ++ee) {
+    if (s_off[ee] == s_off[ee + 1]) continue;  // no rows (same for the whole workgroup)
+    const float* b = B + (size_t)ee * N * K;
+    for (int k0 = 0; k0 < K; k0 += kF32Chunk) {
+      __syncthreads();  // the previous chunk has been used
+      for (int i = tid; i < kF32Rows * kF32Chunk; i += 256) {
+        const int rr = i / kF32Chunk, kk = i % kF32Chunk, row = rb + rr, k = k0 + kk;
+        sa[rr][kk] = (row <= rl && k < K) ? A[(size_t)(a_map ? a_map[row] : row) * K + k] : 0.f;
+      }
+      for (int i = tid; i < 64 * kF32Chunk; i += 256) {
+        // B_K: consecutive threads along k, else along n (both read memory in order)
+        const int nn = B_K ? i / kF32Chunk : i % 64, kk = B_K ? i % kF32Chunk : i / 64;
+        const int n = n0 + nn, k = k0 + kk;
+        sb[nn][kk] = (n < N && k < K) ? (B_K ? b[(size_t)n * K + k] : b[(size_t)k * N + n]) : 0.f;
+      }
+      __syncthreads();
+      if (e == ee) {
+        const int kn = min(kF32Chunk, K - k0);
+        for (int kk = 0; kk < kn; ++kk) {
+          const float av = sa[lr][kk];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] = fmaf(av, sb[g + 16 * q][kk], acc[q]);
+        }
+      }
+    }
+  }
+  if (!live) return;
   const size_t cr = (size_t)(c_map ? c_map[r] : r);
-  for (int n = blockIdx.y * 64 + g; n < min(N, blockIdx.y * 64 + 64); n += 16) {
-    float acc = 0.f;
-    for (int k = 0; k < K; ++k) acc = fmaf(a[k], B_K ? b[(size_t)n * K + k] : b[(size_t)k * N + n], acc);
-    if (EPI == EPI_RELU) acc = fmaxf(acc, 0.f);
-    if (EPI == EPI_MASK && !(aux[(size_t)r * N + n] > 0.f)) acc = 0.f;
-    C[cr * N + n] = acc;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int n = n0 + g + 16 * q;
+    if (n >= N) continue;
+    float v = acc[q];
+    if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+    if (EPI == EPI_MASK && !(aux[(size_t)r * N + n] > 0.f)) v = 0.f;
+    C[cr * N + n] = v;
   }
 }
 
-// dW[e][n1][n2] = sum over e's rows m of X1[m][n1] X2[m][n2]
+// dW[e][n1][n2] = sum over e's rows m of X1[m][n1] X2[m][n2]: a workgroup
+// takes 16 n1 x 64 n2 of one expert and stages chunks of its rows; thread
+// (n1, lane g) computes n2 = g, g + 16, g + 32, g + 48.
 __global__ void __launch_bounds__(256)
 f32_wgrad_kernel(const float* __restrict__ X1, const float* __restrict__ X2, float* __restrict__ C,
                  const int32_t* __restrict__ offsets, int N1, int N2) {
-  const int e = blockIdx.x;
-  const int n1 = blockIdx.y * 16 + (threadIdx.x >> 4);
-  const int g = threadIdx.x & 15;
-  if (n1 >= N1) return;
+  __shared__ float s1[kF32Chunk][16 + 1];
+  __shared__ float s2[kF32Chunk][64 + 1];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int n1b = blockIdx.y * 16, n2b = blockIdx.z * 64;
+  const int l1 = tid >> 4, g = tid & 15;
   const int r0 = offsets[e], r1 = offsets[e + 1];
-  for (int n2 = blockIdx.z * 64 + g; n2 < min(N2, blockIdx.z * 64 + 64); n2 += 16) {
-    float acc = 0.f;
-    for (int m = r0; m < r1; ++m) acc = fmaf(X1[(size_t)m * N1 + n1], X2[(size_t)m * N2 + n2], acc);
-    C[((size_t)e * N1 + n1) * N2 + n2] = acc;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int m0 = r0; m0 < r1; m0 += kF32Chunk) {
+    __syncthreads();  // the previous chunk has been used
+    for (int i = tid; i < kF32Chunk * 16; i += 256) {
+      const int mm = i / 16, c = i % 16, m = m0 + mm;
+      s1[mm][c] = (m < r1 && n1b + c < N1) ? X1[(size_t)m * N1 + n1b + c] : 0.f;
+    }
+    for (int i = tid; i < kF32Chunk * 64; i += 256) {
+      const int mm = i / 64, c = i % 64, m = m0 + mm;
+      s2[mm][c] = (m < r1 && n2b + c < N2) ? X2[(size_t)m * N2 + n2b + c] : 0.f;
+    }
+    __syncthreads();
+    const int mn = min(kF32Chunk, r1 - m0);
+    for (int mm = 0; mm < mn; ++mm) {
+      const float x1 = s1[mm][l1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(x1, s2[mm][g + 16 * q], acc[q]);
+    }
+  }
+  const int n1 = n1b + l1;
+  if (n1 >= N1) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int n2 = n2b + g + 16 * q;
+    if (n2 < N2) C[((size_t)e * N1 + n1) * N2 + n2] = acc[q];
   }
 }
 
