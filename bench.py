@@ -291,9 +291,35 @@ def summarize_mfma(args):
         L.append(f"| {r['role']} | `{r['kernel'][:70]}` | {r['dispatches']} | {r['us']:.1f} | "
                  f"{r['busy']:.1%} | {r['ghz']:.2f} | {r['flops'] / r['alg']:.3f} | "
                  f"{r['alg'] / (r['us'] * 1e-6) / 1e12:.0f} |")
+    # the router's dispatches (matrix-core kernel), if the run has them
+    rds = [d for d in disp.values() if "route_tile_kernel" in d["name"]
+           and all(c in d["c"] for c in need)]
+    router = None
+    if rds:
+        n = len(rds)
+        us = sum(d["ns"] for d in rds) / n / 1e3
+        cyc = sum(d["c"][need[2]] for d in rds) / n / xcds
+        ep = 16
+        while ep < cfg["E"]:
+            ep *= 2
+        method = 2.0 * cfg["T"] * cfg["d_model"] * cfg["E"]
+        router = {"kernel": rds[0]["name"], "dispatches": n, "us": us,
+                  "busy": sum(d["c"][need[0]] for d in rds) / n / (simds * cyc),
+                  "ghz": cyc / (us * 1e3),
+                  "flops": sum(d["c"][need[1]] for d in rds) / n * 512,
+                  "three_pass": 3.0 * 2.0 * cfg["T"] * cfg["d_model"] * ep, "method": method}
+        L += ["", "Router (`route_tile_kernel`, warm and cold calls alike): executed flops "
+              "against three bf16 passes over E rounded up to a power of two >= 16 "
+              f"({router['three_pass'] / 1e9:.1f} GFLOP) and against the method's 2 T d E "
+              f"({method / 1e9:.2f} GFLOP).", "",
+              "| kernel | dispatches | µs | MFMA busy | clock GHz | executed / three-pass | "
+              "executed / method |", "|---|---|---|---|---|---|---|",
+              f"| `{router['kernel'][:70]}` | {n} | {us:.1f} | {router['busy']:.1%} | "
+              f"{router['ghz']:.2f} | {router['flops'] / router['three_pass']:.3f} | "
+              f"{router['flops'] / method:.2f} |"]
     L.append("")
     L.append("mfma-json: " + json.dumps({"workload": w.name, "gemm_source_sha256":
-                                         gemm_source_hash(), "rows": rows}))
+                                         gemm_source_hash(), "rows": rows, "router": router}))
     os.makedirs(os.path.dirname(mfma_path(w.name)), exist_ok=True)
     with open(mfma_path(w.name), "w") as f:
         f.write("\n".join(L) + "\n")
