@@ -106,10 +106,18 @@ def traffic_path(name):
     return os.path.join(ROOT, "profiles", f"rows_gemm_{name}_hbm_traffic.md")
 
 
+# headers the kernels include: a change there changes the kernels too
+SHARED_HEADERS = ["common.hpp", "buffer.hpp"]
+
+
 def gemm_source_hash():
+    """sha256 over gemm.hip and the headers it shares with the other kernels"""
     import hashlib
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in [GEMM_SRC] + [os.path.join(CSRC, f) for f in SHARED_HEADERS]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _counter_rows(path, counter):
@@ -332,7 +340,7 @@ PART_KERNELS = {
     "permute": ["rank_hist_kernel", "scan_kernel", "gather_kernel"],
     "combine": ["combine_kernel"],
 }
-PART_SOURCES = ["route.hip", "permute.hip", "combine.hip"]
+PART_SOURCES = ["route.hip", "permute.hip", "combine.hip", "common.hpp", "buffer.hpp"]
 
 
 def parts_hbm_bytes(w, s_kept):
