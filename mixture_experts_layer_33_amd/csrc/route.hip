@@ -5,10 +5,11 @@
 // notes §2.1.2: each token goes to its top-k experts, k usually 1 or 2.
 //
 // Two router kernels: for bf16 activations an MFMA kernel (three exact bf16
-// parts of W_gate, below); for float32 activations, or when the caller
-// passes the logits, a float32 FMA kernel with W_gate staged through LDS.  In
-// both, each token's logits sit in one 16-lane group, which selects the top k
-// by k rounds of a 16-lane (value, index) max reduction.
+// parts of W_gate, below), which selects the top k by merging sorted lists;
+// for float32 activations, or when the caller passes the logits, a float32
+// FMA kernel with W_gate staged through LDS, where each token's logits sit
+// in one 16-lane group that selects the top k by k rounds of a (value,
+// index) max reduction.
 #include <type_traits>
 
 #include "buffer.hpp"
@@ -24,32 +25,6 @@ constexpr int kRouteThreads = 256; // 16 tokens x 16 lanes
 // a ranks before b: larger value, or equal value and smaller index.
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
-}
-
-// Keep the better of (bv, bi) and the pair that DPP control CTRL brings from
-// another lane of the same 16-lane row.
-template <int CTRL>
-__device__ __forceinline__ void dpp_better(float& bv, int& bi) {
-  const int vb = __builtin_bit_cast(int, bv);
-  const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(vb, vb, CTRL, 0xF, 0xF, false));
-  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, 0xF, 0xF, false);
-  if (better(ov, oi, bv, bi)) {
-    bv = ov;
-    bi = oi;
-  }
-}
-
-// The best (value, index) pair of each row of 16 lanes, left in every lane of
-// the row, by register moves between lanes (no LDS): after the mirror
-// (lane i with 15 - i) and the half-row mirror (i with 7 - i in each half) the
-// four lanes of every quad hold four disjoint quarters of the row, which the
-// two quad swaps combine.  The order is total, so any pairing gives the same
-// winner.
-__device__ __forceinline__ void row16_best(float& bv, int& bi) {
-  dpp_better<0x140>(bv, bi);  // row_mirror
-  dpp_better<0x141>(bv, bi);  // row_half_mirror
-  dpp_better<0x4E>(bv, bi);   // quad_perm [2, 3, 0, 1]
-  dpp_better<0xB1>(bv, bi);   // quad_perm [1, 0, 3, 2]
 }
 
 template <typename ActT>
@@ -266,6 +241,119 @@ struct RouteCfg {
   static_assert(!WP || (route_wpad(EW) > 0 && EW == EP), "padded W_gate rows");
 };
 
+// Top-k by sorted lists (route_tile_kernel's epilogue).  A list holds the
+// best KL (value, expert) pairs seen so far, best first in the order of
+// better(); empty slots are (-inf, INT_MAX), which every real pair beats.
+template <int KL>
+struct TopList {
+  float v[KL];
+  int i[KL];
+};
+
+// Merge with the list of the partner lane that DPP control CTRL names (an
+// involution within 16-lane rows): the better of each slot and the partner's
+// slot KL - 1 - j keeps the best KL of the two lists (they form a bitonic
+// sequence), then half-cleaners sort them.  Both partners end with the same
+// list: better() is a total order on distinct experts.
+template <int CTRL, int KL>
+__device__ __forceinline__ void merge_partner(TopList<KL>& L) {
+  float ov[KL];
+  int oi[KL];
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    const int vb = __builtin_bit_cast(int, L.v[j]);
+    ov[j] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(vb, vb, CTRL, 0xF, 0xF, false));
+    oi[j] = __builtin_amdgcn_update_dpp(L.i[j], L.i[j], CTRL, 0xF, 0xF, false);
+  }
+  float mv[KL];
+  int mi[KL];
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    const bool t = better(ov[KL - 1 - j], oi[KL - 1 - j], L.v[j], L.i[j]);
+    mv[j] = t ? ov[KL - 1 - j] : L.v[j];
+    mi[j] = t ? oi[KL - 1 - j] : L.i[j];
+  }
+#pragma unroll
+  for (int h = KL / 2; h >= 1; h >>= 1)
+#pragma unroll
+    for (int j = 0; j < KL; ++j)
+      if ((j & h) == 0) {
+        const bool sw = better(mv[j + h], mi[j + h], mv[j], mi[j]);
+        const float a = mv[j], b = mv[j + h];
+        const int ia = mi[j], ib = mi[j + h];
+        mv[j] = sw ? b : a;
+        mv[j + h] = sw ? a : b;
+        mi[j] = sw ? ib : ia;
+        mi[j + h] = sw ? ia : ib;
+      }
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    L.v[j] = mv[j];
+    L.i[j] = mi[j];
+  }
+}
+
+// One token's top k from its row of logits in LDS, by TPT consecutive lanes
+// (s = this lane's place): lane s takes experts s, s + TPT, ...  Inserting
+// in increasing index order, a new pair beats a filled slot only with a
+// strictly larger value (ties go to the smaller index already there), and
+// the first j pairs fill slots 0..j-1.  A NaN logit ranks as -inf, so the
+// selection is total and every index written is in [0, E).  Lane s writes
+// choices s, s + TPT, ... < k: the expert, and its gate weight
+// exp(v_r - v_0) / sum_{r' < k} exp(v_r' - v_0).
+template <int KL, int TPT, int EPT>
+__device__ __forceinline__ void route_select(const float* row, int s, int E, int k, int t, int T,
+                                             int32_t* __restrict__ topk_idx,
+                                             float* __restrict__ topk_w) {
+  TopList<KL> L;
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    L.v[j] = -INFINITY;
+    L.i[j] = 0x7fffffff;
+  }
+#pragma unroll
+  for (int jj = 0; jj < EPT; ++jj) {
+    const int e = s + TPT * jj;
+    float x = row[e];
+    x = x != x ? -INFINITY : x;
+    const bool valid = e < E;
+    bool c[KL];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) c[j] = valid && (j >= jj || x > L.v[j]);
+#pragma unroll
+    for (int j = KL - 1; j >= 1; --j) {
+      L.v[j] = c[j - 1] ? L.v[j - 1] : (c[j] ? x : L.v[j]);
+      L.i[j] = c[j - 1] ? L.i[j - 1] : (c[j] ? e : L.i[j]);
+    }
+    L.v[0] = c[0] ? x : L.v[0];
+    L.i[0] = c[0] ? e : L.i[0];
+  }
+  // partners: lane ^ 1, lane ^ 2 (quads now agree), then lane i of each 8
+  // with 7 - i (one in each quad), then i of each 16 with 15 - i
+  if constexpr (TPT >= 2) merge_partner<0xB1>(L);   // quad_perm [1, 0, 3, 2]
+  if constexpr (TPT >= 4) merge_partner<0x4E>(L);   // quad_perm [2, 3, 0, 1]
+  if constexpr (TPT >= 8) merge_partner<0x141>(L);  // row_half_mirror
+  if constexpr (TPT >= 16) merge_partner<0x140>(L); // row_mirror
+  if (t >= T) return;
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < KL; ++r)
+    if (r < k) sum += expf(L.v[r] - L.v[0]);
+#pragma unroll
+  for (int r = 0; r < KL; ++r)
+    if (r < k && r % TPT == s) {
+      topk_idx[(size_t)t * k + r] = L.i[r];
+      topk_w[(size_t)t * k + r] = expf(L.v[r] - L.v[0]) * (1.0f / sum);
+    }
+}
+
+constexpr int pow2_floor(int v) { return v >= 2 ? 2 * pow2_floor(v / 2) : 1; }
+// threads per token when nt threads select for `tokens` tokens: a power of two,
+// 1 to 16 (a DPP row)
+constexpr int route_tpt(int nt, int tokens) {
+  return nt / tokens >= 16 ? 16 : (nt / tokens >= 1 ? pow2_floor(nt / tokens) : 1);
+}
+
 template <int KD>
 __device__ __forceinline__ int route_swz(int row) {
   if constexpr (KD * 2 >= 256) return row & 15;
@@ -442,94 +530,87 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
   // padding copies past the last stage are still in flight
   wait_barrier<0, 15>();
 
-  // epilogue, one block of 16 tokens at a time: the wavefronts holding the
-  // block's logits write them (partial sums per k-group) to LDS, then each
-  // 16-lane group takes one token: sum of the partials in k order, + bias,
-  // top-k, gate weights
-  constexpr int EPL = EP / 16;  // experts per lane of a 16-lane group
-  const int gl = lane & 15, grp = tid >> 4;
-  float bias[EPL];
+  // Epilogue.  Per block of 16 tokens, the wavefronts holding its logits
+  // write their partial sums (one per k group) to `red`; after a barrier
+  // every thread sums some of them in k order, adds the bias, and stores the
+  // logit in the token-major table `fl` in the other stage buffers.  Once a
+  // chunk of blocks is in `fl`, TPT threads per token select its top k:
+  // each inserts its experts, in increasing index order, into a sorted list
+  // of the best KL (KL = k rounded up to 2, 4 or 8), then partner lanes merge
+  // their lists by register moves until all TPT hold the token's best KL.
+  constexpr int NT = 64 * NWV;
+  constexpr int RBUF = (2 * WK * (int)sizeof(RedRow) <= Cf::STAGE) ? 2 : 1;  // red copies
+  // fl: 16-token blocks of rows of RS floats; RS = EP + TPT keeps the TPT
+  // threads of the 64 / TPT tokens a wavefront reads on distinct banks
+  constexpr int RS = EP + route_tpt(NT, BM);
+  constexpr int FLB = 16 * RS * 4;                 // bytes of one block in fl
+  constexpr int BPB = Cf::STAGE / FLB;             // blocks per stage buffer
+  static_assert(STAGES >= 2 && BPB >= 1, "the logits table fits in the stage buffers");
+  constexpr int NB = BM / 16;
+  constexpr int CHB = (STAGES - 1) * BPB < NB ? (STAGES - 1) * BPB : NB;  // blocks per chunk
+  constexpr int CT = CHB * 16;                     // tokens per chunk
+  constexpr int TPT = route_tpt(NT, CT);           // threads per token
+  constexpr int EPT = EP / TPT;                    // experts per thread
+  constexpr int TPP = NT / TPT;                    // tokens per pass
+  static_assert(NT % EP == 0, "a thread sums one expert column of each block");
+  auto fl_row = [&](int tc) __attribute__((always_inline)) -> float* {
+    const int b = tc >> 4, sb = b / BPB;  // block within the chunk, its buffer
+    char* const base = sb == 0   ? st1
+                       : sb == 1 ? st2
+                       : sb == 2 ? st3
+                       : sb == 3 ? st4
+                       : sb == 4 ? st5
+                       : sb == 5 ? st6
+                                 : st7;
+    return reinterpret_cast<float*>(base) + (b % BPB) * 16 * RS + (tc & 15) * RS;
+  };
+  const int ecl = tid % EP;  // this thread's expert column when summing
+  const float bias_e = ecl < E ? b_gate[ecl] : 0.f;
+  for (int cb = 0; cb < NB; cb += CHB) {
+    for (int mb = cb; mb < cb + CHB && mb < NB; ++mb) {
+      RedRow* const rb = red + (mb % RBUF) * WK;
+      // (m compile-time: the accumulators stay in registers)
 #pragma unroll
-  for (int q = 0; q < EPL; ++q) {
-    const int e = gl + 16 * q;
-    bias[q] = (e < E) ? b_gate[e] : 0.f;
-  }
-  for (int mb = 0; mb < BM / 16; ++mb) {
-    // (m compile-time: the accumulators stay in registers)
+      for (int m = 0; m < FM; ++m) {
+        if (mb != wm * FM + m) continue;
 #pragma unroll
-    for (int m = 0; m < FM; ++m) {
-      if (mb != wm * FM + m) continue;
+        for (int n = 0; n < FN; ++n)
 #pragma unroll
-      for (int n = 0; n < FN; ++n)
+          for (int i = 0; i < 4; ++i)
+            rb[kw][kq * 4 + i][(wn * FN + n) * 16 + r16] = acc[m][n][i];
+      }
+      __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          red[kw][kq * 4 + i][(wn * FN + n) * 16 + r16] = acc[m][n][i];
+      for (int qq = 0; qq < (16 * EP + NT - 1) / NT; ++qq) {
+        const int q = tid / EP + qq * (NT / EP);  // token of the block
+        if (q >= 16) break;
+        float sum = rb[0][q][ecl];
+#pragma unroll
+        for (int w = 1; w < WK; ++w) sum += rb[w][q][ecl];
+        const float v = sum + bias_e;
+        fl_row((mb - cb) * 16 + q)[ecl] = v;
+        const int t = t0 + mb * 16 + q;
+        if (logits_out != nullptr && ecl < E && t < T) logits_out[(size_t)t * E + ecl] = v;
+      }
+      // the next block's partial sums go to the other copy of red, or wait
+      if constexpr (RBUF == 1) __syncthreads();
     }
-    __syncthreads();
-    // (eight wavefronts: groups 16..31 idle here)
-    const int g16 = grp & 15, t = t0 + mb * 16 + g16;
-    float v[EPL];
-#pragma unroll
-    for (int q = 0; q < EPL; ++q) {
-      float sum = red[0][g16][gl + 16 * q];
-#pragma unroll
-      for (int w = 1; w < WK; ++w) sum += red[w][g16][gl + 16 * q];
-      v[q] = sum + bias[q];
-    }
-    __syncthreads();  // red is rewritten by the next block
-    if (grp >= 16 || t >= T) continue;
-    if (logits_out != nullptr) {
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) {
-        const int e = gl + 16 * q;
-        if (e < E) logits_out[(size_t)t * E + e] = v[q];
+    if constexpr (RBUF == 2) __syncthreads();
+    const int nct = min(CT, BM - cb * 16);
+    for (int tc0 = 0; tc0 < nct; tc0 += TPP) {
+      const int tc = tc0 + tid / TPT;  // whole TPT-lane groups share a token
+      if (tc < nct) {
+        const float* row = fl_row(tc);
+        const int t = t0 + cb * 16 + tc, s = tid % TPT;
+        if (k <= 2)
+          route_select<2, TPT, EPT>(row, s, E, k, t, T, topk_idx, topk_w);
+        else if (k <= 4)
+          route_select<4, TPT, EPT>(row, s, E, k, t, T, topk_idx, topk_w);
+        else
+          route_select<8, TPT, EPT>(row, s, E, k, t, T, topk_idx, topk_w);
       }
     }
-    // a NaN logit ranks as -inf (selection stays total, indices in [0, E))
-#pragma unroll
-    for (int q = 0; q < EPL; ++q) v[q] = v[q] != v[q] ? -INFINITY : v[q];
-    // k rounds of a (value desc, index asc) maximum over the group; rounds
-    // unrolled to the largest k so the selections stay in registers
-    unsigned taken = 0;
-    float sv[MOE_MAX_TOPK];
-    int si[MOE_MAX_TOPK];
-#pragma unroll
-    for (int r = 0; r < MOE_MAX_TOPK; ++r) {
-      sv[r] = 0.f;
-      si[r] = 0;
-      if (r >= k) continue;
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) {
-        const int e = gl + 16 * q;
-        if (e < E && !((taken >> q) & 1u) && better(v[q], e, bv, bi)) {
-          bv = v[q];
-          bi = e;
-        }
-      }
-      row16_best(bv, bi);
-      if ((bi & 15) == gl) taken |= 1u << (bi >> 4);
-      sv[r] = bv;
-      si[r] = bi;
-    }
-    // lane r of the group writes choice r
-    float sum = 0.f, mine = 0.f;
-    int mine_i = 0;
-#pragma unroll
-    for (int r = 0; r < MOE_MAX_TOPK; ++r) {
-      if (r >= k) continue;
-      const float p = expf(sv[r] - sv[0]);
-      sum += p;
-      if (r == gl) {
-        mine = p;
-        mine_i = si[r];
-      }
-    }
-    if (gl < k) {
-      topk_idx[(size_t)t * k + gl] = mine_i;
-      topk_w[(size_t)t * k + gl] = mine * (1.0f / sum);
-    }
+    __syncthreads();  // fl (and red) are rewritten by the next chunk
   }
 }
 
