@@ -236,7 +236,12 @@ struct RouteCfg {
   static_assert(EW == EP || (EW == 8 && EP == 16), "staged experts");
   static_assert(SL >= 1 && SL * 32 * WK == KD, "whole slices per wavefront");
   static_assert(XB % 1024 == 0 && ROWB <= 1024, "whole copy instructions");
-  static_assert(NPW * (STAGES - 2) <= 63, "s_waitcnt vmcnt counts at most 63");
+  // Software-pipelined main loop (split of the next stage under this one's
+  // MFMAs) where a wavefront has 8 or more token blocks: enough MFMAs per
+  // W_gate fragment to hide its split.  Its prologue waits with one more
+  // stage in flight.
+  static constexpr bool PIPE = FM >= 8 && STAGES >= 3;
+  static_assert(NPW * (STAGES - (PIPE ? 1 : 2)) <= 63, "s_waitcnt vmcnt counts at most 63");
   static_assert(STAGES >= 2, "double buffering at least");
   static_assert(!WP || (route_wpad(EW) > 0 && EW == EP), "padded W_gate rows");
 };
@@ -368,6 +373,7 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
                   int k) {
   using Cf = RouteCfg<BM, EP, EW, WM, WN, WK, KD, STAGES, WP>;
   constexpr int FM = Cf::FM, FN = Cf::FN, NWV = Cf::NWV;
+  constexpr bool PIPE = Cf::PIPE;
   constexpr int S1 = STAGES > 1 ? Cf::STAGE : 16, S2 = STAGES > 2 ? Cf::STAGE : 16;
   constexpr int S3 = STAGES > 3 ? Cf::STAGE : 16, S4 = STAGES > 4 ? Cf::STAGE : 16;
   constexpr int S5 = STAGES > 5 ? Cf::STAGE : 16, S6 = STAGES > 6 ? Cf::STAGE : 16;
@@ -453,36 +459,47 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
     bf16x8 a[Cf::SL][FM];
     float w[Cf::SL][FN][8];
   };
-  auto load = [&](const char* st, Frag& f) __attribute__((always_inline)) {
-    const char* xs = st;
+  auto load_x = [&](const char* st, Frag& f, int s, int kc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < FM; ++m) {
+      const int row = (wm * FM + m) * 16 + r16;
+      f.a[s][m] = *reinterpret_cast<const bf16x8*>(st + row * Cf::ROWB +
+                                                   ((kc ^ route_swz<KD>(row)) * 16));
+    }
+  };
+  auto load_w = [&](const char* st, Frag& f, int s, int kc) __attribute__((always_inline)) {
     const float* ws = reinterpret_cast<const float*>(st + Cf::XB);
 #pragma unroll
-    for (int s = 0; s < Cf::SL; ++s) {
-      const int kc = (kw * Cf::SL + s) * 4 + kq;  // this lane's 8-deep k chunk
+    for (int n = 0; n < FN; ++n) {
+      // WP: row kc * 8 starts kc * EW / 32 padded KiB in; row kc * 8 + i
+      // at a compile-time offset from it
+      const char* wrow = reinterpret_cast<const char*>(ws) + kc * (EW / 32) * Cf::WCH +
+                         ecol[n] * 4;
 #pragma unroll
-      for (int m = 0; m < FM; ++m) {
-        const int row = (wm * FM + m) * 16 + r16;
-        f.a[s][m] = *reinterpret_cast<const bf16x8*>(xs + row * Cf::ROWB +
-                                                     ((kc ^ route_swz<KD>(row)) * 16));
-      }
-#pragma unroll
-      for (int n = 0; n < FN; ++n) {
-        // WP: row kc * 8 starts kc * EW / 32 padded KiB in; row kc * 8 + i
-        // at a compile-time offset from it
-        const char* wrow = reinterpret_cast<const char*>(ws) + kc * (EW / 32) * Cf::WCH +
-                           ecol[n] * 4;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if constexpr (WP)
-            f.w[s][n][i] = *reinterpret_cast<const float*>(
-                wrow + ((i * EW * 4) >> 10) * Cf::WCH + ((i * EW * 4) & 1023));
-          else
-            f.w[s][n][i] = ws[(kc * 8 + i) * E + ecol[n]];
-        }
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (WP)
+          f.w[s][n][i] = *reinterpret_cast<const float*>(
+              wrow + ((i * EW * 4) >> 10) * Cf::WCH + ((i * EW * 4) & 1023));
+        else
+          f.w[s][n][i] = ws[(kc * 8 + i) * E + ecol[n]];
       }
     }
   };
-  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
+  // (pipelined: W_gate's values first, which the split waits for)
+  auto load = [&](const char* st, Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < Cf::SL; ++s) {
+      const int kc = (kw * Cf::SL + s) * 4 + kq;  // this lane's 8-deep k chunk
+      if constexpr (PIPE) {
+        load_w(st, f, s, kc);
+        load_x(st, f, s, kc);
+      } else {
+        load_x(st, f, s, kc);
+        load_w(st, f, s, kc);
+      }
+    }
+  };
+  auto split_mma = [&](const Frag& f) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < Cf::SL; ++s)
 #pragma unroll
@@ -507,26 +524,105 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[s][m], pw[p], acc[m][n], 0, 0, 0);
       }
   };
-  unroll_stages<0, STAGES - 1>([&](auto P_) __attribute__((always_inline)) {
-    issue(decltype(P_)::value, stage[decltype(P_)::value]);
-  });
-  // Step kt on stage buffer P = kt % STAGES: wait until this wavefront's
-  // copies of stage kt have landed (the later STAGES - 2 stay in flight) and
-  // its LDS reads are done, meet the other wavefronts, refill the buffer
-  // stage kt - 1 used with stage kt + STAGES - 1, then read and compute stage
-  // kt.  (Reading the next stage into registers during this one's MFMAs was
-  // measured: no faster.)
-  for (int kt = 0; kt < nst; kt += STAGES)
-    unroll_stages<0, STAGES>([&](auto P_) __attribute__((always_inline)) {
-      constexpr int P = decltype(P_)::value;
-      if (kt + P < nst) {
-        wait_barrier<Cf::NPW * (STAGES - 2), 0>();
-        issue(kt + P + STAGES - 1, stage[(P + STAGES - 1) % STAGES]);
-        Frag f;
-        load(stage[P], f);
-        mma(f);
+  // The three bf16 parts of a stage's W_gate fragments.
+  struct Parts {
+    bf16x8 p[Cf::SL][FN][3];
+  };
+  auto split = [&](const Frag& f, Parts& q) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < Cf::SL; ++s)
+#pragma unroll
+      for (int n = 0; n < FN; ++n) {
+        // 8 consecutive k of this lane's expert, split into the 3 parts
+        u32x4 ph, pm, pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t h, md, l;
+          split3_pair(f.w[s][n][2 * i], f.w[s][n][2 * i + 1], h, md, l);
+          ph[i] = h;
+          pm[i] = md;
+          pl[i] = l;
+        }
+        q.p[s][n][0] = __builtin_bit_cast(bf16x8, ph);
+        q.p[s][n][1] = __builtin_bit_cast(bf16x8, pm);
+        q.p[s][n][2] = __builtin_bit_cast(bf16x8, pl);
       }
+  };
+  auto mma = [&](const Frag& f, const Parts& q) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < Cf::SL; ++s)
+#pragma unroll
+      for (int n = 0; n < FN; ++n)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int m = 0; m < FM; ++m)
+            acc[m][n] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[s][m], q.p[s][n][p], acc[m][n], 0, 0, 0);
+  };
+  if constexpr (!PIPE) {
+    unroll_stages<0, STAGES - 1>([&](auto P_) __attribute__((always_inline)) {
+      issue(decltype(P_)::value, stage[decltype(P_)::value]);
     });
+    // Step kt on stage buffer P = kt % STAGES: wait until this wavefront's
+    // copies of stage kt have landed (the later STAGES - 2 stay in flight) and
+    // its LDS reads are done, meet the other wavefronts, refill the buffer
+    // stage kt - 1 used with stage kt + STAGES - 1, then read and compute stage
+    // kt, each fragment's split just before its MFMAs.
+    for (int kt = 0; kt < nst; kt += STAGES)
+      unroll_stages<0, STAGES>([&](auto P_) __attribute__((always_inline)) {
+        constexpr int P = decltype(P_)::value;
+        if (kt + P < nst) {
+          wait_barrier<Cf::NPW * (STAGES - 2), 0>();
+          issue(kt + P + STAGES - 1, stage[(P + STAGES - 1) % STAGES]);
+          Frag f;
+          load(stage[P], f);
+          split_mma(f);
+        }
+      });
+  } else {
+    // Three or more stages, software-pipelined: while the MFMAs of stage kt
+    // run on operands already in registers, the wavefront reads stage kt + 1
+    // from LDS and splits its W_gate fragments.  Step kt waits until its
+    // copies of stage kt + 1 have landed (the later STAGES - 2 stay in flight)
+    // and its reads of stage kt are done, meets the other wavefronts (so
+    // every read of stage kt is done), and refills that buffer with stage
+    // kt + STAGES.  Register sets alternate, so the loop is unrolled over a
+    // multiple of 2 and of STAGES.
+    unroll_stages<0, STAGES>([&](auto P_) __attribute__((always_inline)) {
+      issue(decltype(P_)::value, stage[decltype(P_)::value]);
+    });
+    Frag f[2];
+    Parts q[2];
+    wait_barrier<Cf::NPW * (STAGES - 1), 15>();
+    load(stage[0], f[0]);
+    split(f[0], q[0]);
+    constexpr int L = STAGES % 2 == 0 ? STAGES : 2 * STAGES;
+    for (int kt = 0; kt < nst; kt += L)
+      unroll_stages<0, L>([&](auto P_) __attribute__((always_inline)) {
+        constexpr int P = decltype(P_)::value;
+        const int kk = kt + P;
+        if (kk < nst) {
+          wait_barrier<Cf::NPW * (STAGES - 2), 0>();
+          issue(kk + STAGES, stage[P % STAGES]);
+          // (after the last stage this reads the zeros of a copy past the
+          // end: in bounds, and unused)
+          load(stage[(P + 1) % STAGES], f[(P + 1) % 2]);
+          split(f[(P + 1) % 2], q[(P + 1) % 2]);
+          mma(f[P % 2], q[P % 2]);
+          // the LDS reads first, then the split's VALU work spread over the
+          // MFMAs (without this the compiler runs the split as one block)
+          constexpr int NMF = Cf::SL * FN * 3 * FM, NDS = Cf::SL * (FM + 4 * FN);
+          constexpr int NV = (Cf::SL * FN * 48 + NMF - 1) / NMF;
+          __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);  // LDS reads
+          unroll_stages<0, NMF>([&](auto) __attribute__((always_inline)) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // NV VALU
+          });
+        }
+      });
+  }
+
   // padding copies past the last stage are still in flight
   wait_barrier<0, 15>();
 
@@ -651,7 +747,7 @@ static void launch_route_tile(hipStream_t s, const bf16* x, const float* w_gate,
   using C2 = RouteCfg<BM, EP, EW, WM, WN, WK, KD, 2, WP>;
   // LDS: the stages (the epilogue reuses the first) and the padding target
   constexpr int FIT = (160 * 1024 - 1024 - 512) / C2::STAGE;
-  constexpr int VM = 63 / C2::NPW + 2;
+  constexpr int VM = 63 / C2::NPW + (C2::FM >= 8 ? 1 : 2);  // vmcnt limit (see PIPE)
   constexpr int MAXS = FIT < VM ? FIT : VM;
   constexpr int STAGES = MAXS < 2 ? 2 : (MAXS > 8 ? 8 : MAXS);
   hipLaunchKernelGGL((route_tile_kernel<BM, EP, EW, WM, WN, WK, KD, STAGES, WP>),
