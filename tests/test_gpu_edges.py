@@ -127,6 +127,41 @@ def test_identity_experts_reproduce_input_exactly():
     assert np.all(np.abs(down(layer.y) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
 
 
+# (T, d, E, k): every padded expert count of the matrix-core router, with
+# small and large token counts (16 and 128 tokens per workgroup; the large
+# ones take the software-pipelined loop where a wavefront holds 8 token
+# blocks), and k up to 8 so that each selection list length (2, 4, 8) is used
+TILE_TIES = [(3001, 256, 8, 8), (3001, 128, 16, 8), (40000, 128, 16, 5), (3001, 128, 32, 8),
+             (33000, 128, 32, 5), (2000, 128, 64, 8), (32768, 64, 64, 3), (1000, 128, 128, 8),
+             (32768, 64, 128, 7), (700, 64, 256, 8), (16384, 64, 256, 3)]
+
+
+@pytest.mark.parametrize("T,d,E,k", TILE_TIES)
+def test_tile_router_exact_ties(T, d, E, k):
+    """x in {-1, 0, 1} and W_gate, b_gate on a 0.5 grid: every product and
+    partial sum is exact, so the matrix-core router's logits equal the
+    reference's exactly and ties are everywhere; its top k must break them
+    as the reference does (lowest index first) with any k up to 8."""
+    rng = np.random.default_rng(T + d + E + k)
+    x = rng.integers(-1, 2, (T, d)).astype(np.float32)
+    x[::9] = 0.0  # whole rows of ties at the bias
+    wg = (rng.integers(-2, 3, (d, E)) * 0.5).astype(np.float32)
+    bg = (rng.integers(-1, 2, E) * 0.5).astype(np.float32)
+    layer = MoeLayer(T, d, 64, E, k, 0.0, act_code("bf16"), backward=False)
+    layer.route(up(x, "bf16"), up(wg), up(bg), logits_out=True)
+    torch.cuda.synchronize()
+    L = down(layer.logits)
+    ref = orc.router_logits(x, wg, bg)
+    np.testing.assert_array_equal(L, ref.astype(np.float32))
+    idx, wt = orc.topk_gate(ref, k)
+    np.testing.assert_array_equal(down(layer.topk_idx), idx)
+    assert_close(down(layer.topk_w), wt, 1e-5, "topk_w")
+    # the ties are real: equal logits among the top k + 1 of many tokens
+    # (every zero row of x, whose logits are the bias on three levels)
+    srt = -np.sort(-ref, axis=1)[:, :min(k + 1, E)]
+    assert (np.diff(srt, axis=1) == 0).any(axis=1).mean() > 0.1
+
+
 @pytest.mark.parametrize("E,k", [(8, 2), (32, 4), (128, 4)])
 def test_nonfinite_logits_keep_indices_in_range(E, k):
     """Finite logits are a precondition, but a violation must not produce
