@@ -194,15 +194,17 @@ __device__ __forceinline__ void unroll_stages(F&& f) {
 // The four or eight wavefronts split the work WM x WN x WK ways: token
 // blocks, expert blocks, and the 32-deep k slices of each stage (their
 // partial logits are summed in a fixed order at the end).  Eight wavefronts
-// (two per SIMD) let one wavefront's split run beside another's MFMAs.  Splitting k keeps the LDS reads per
-// MFMA lowest and has every W_gate value split by one wavefront only, so it
-// is preferred while the accumulators fit in registers.  A stage holds the x
-// tile [BM][KD] (bf16) and the KD rows of W_gate [KD][E] (float32, one
-// contiguous run of memory), copied global -> LDS by the buffer unit (16
-// bytes a lane, no registers; rows past the last token land as zeros; d is a
-// multiple of KD).  STAGES stages rotate, STAGES - 1 of them in flight, each
-// its own LDS object so that the compiler keeps the copies in flight past the
-// reads of other stages; the epilogue's partial logits reuse the first.
+// (two per SIMD) let one wavefront's split run beside another's MFMAs.
+// Splitting k keeps the LDS reads per MFMA lowest and has every W_gate value
+// split by one wavefront only, so it is preferred while the accumulators fit
+// in registers.  A stage holds the x tile [BM][KD] (bf16) and the KD rows of
+// W_gate [KD][E] (float32, one contiguous run of memory), copied global ->
+// LDS by the buffer unit (16 bytes a lane, no registers; rows past the last
+// token land as zeros; d is a multiple of KD).  STAGES stages rotate, up to
+// STAGES - 1 of them in flight, each its own LDS object so that the compiler
+// keeps the copies in flight past the reads of other stages; the epilogue
+// reuses them (partial logits in the first, the summed logits in the
+// others).
 // With few experts the kernel streams x from HBM; the stage count sets how
 // many bytes each CU keeps in flight.
 //
@@ -636,8 +638,9 @@ route_tile_kernel(const bf16* __restrict__ x, const float* __restrict__ w_gate,
   // their lists by register moves until all TPT hold the token's best KL.
   constexpr int NT = 64 * NWV;
   constexpr int RBUF = (2 * WK * (int)sizeof(RedRow) <= Cf::STAGE) ? 2 : 1;  // red copies
-  // fl: 16-token blocks of rows of RS floats; RS = EP + TPT keeps the TPT
-  // threads of the 64 / TPT tokens a wavefront reads on distinct banks
+  // fl: 16-token blocks of rows of RS floats; RS = EP + (threads per token
+  // when the tile is one chunk) keeps the threads of the tokens a wavefront
+  // reads on distinct banks
   constexpr int RS = EP + route_tpt(NT, BM);
   constexpr int FLB = 16 * RS * 4;                 // bytes of one block in fl
   constexpr int BPB = Cf::STAGE / FLB;             // blocks per stage buffer
