@@ -90,14 +90,17 @@ typedef int32_t moe_status;
 #define MOE_PRIORITY_SLOT 0
 #define MOE_PRIORITY_CHOICE 1
 
-/* Limits of the compiled kernels (MOE_ERR_UNSUPPORTED beyond them). */
+/* Limits of the compiled kernels (MOE_ERR_UNSUPPORTED beyond them).  Besides
+ * these, every operand a kernel addresses through one buffer resource stays
+ * under 2 GiB: T*k*max(d, F)*2, d*F*2 and d*E*4 bytes (an unsupported shape
+ * returns the error; it is never run with wrapped offsets). */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 8
 #define MOE_PLAN_MAX_RANKS 64
 #define MOE_PLAN_MAX_COPIES 1024 /* E + extra copies in moe_ep_plan */
 
 typedef struct moe_shape {
-  int32_t T;               /* tokens */
+  int32_t T;               /* tokens, >= 1 (an empty batch is MOE_ERR_INVALID_ARG) */
   int32_t d_model;         /* d: multiple of 64 */
   int32_t d_ff;            /* F: multiple of 64 */
   int32_t E;               /* experts, 1..MOE_MAX_EXPERTS */

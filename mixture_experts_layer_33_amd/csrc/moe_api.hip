@@ -42,7 +42,8 @@ moe_status check_shape(const moe_shape* s) {
   // the GEMM's buffer resources address an operand tile in 31-bit offsets
   const int64_t wide = s->d_model > s->d_ff ? s->d_model : s->d_ff;
   const int64_t limit = 0x7ffffff0;  // bytes addressable from one resource
-  if (S * wide * 2 >= limit || (int64_t)s->d_model * s->d_ff * 2 >= limit)
+  if (S * wide * 2 >= limit || (int64_t)s->d_model * s->d_ff * 2 >= limit ||
+      (int64_t)s->d_model * s->E * 4 >= limit)  // the router's float32 W_gate
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

@@ -55,6 +55,8 @@ def shape(**kw):
     ({"priority": "choice"}, 0), ({"prio_code": 2}, -1), ({"prio_code": -1}, -1),
     # one GEMM operand would exceed the 2 GiB a buffer resource addresses
     ({"T": 1 << 17, "k": 4, "d": 4096}, -2), ({"d": 32768, "F": 32768}, -2),
+    # the router's float32 W_gate (d x E) likewise
+    ({"T": 4, "d": 1 << 21, "F": 64, "E": 256}, -2), ({"T": 4, "d": 1 << 20, "F": 64, "E": 256}, 0),
 ])
 def test_shape_validation(kw, status):
     assert moe.moe_check_shape(shape(**kw)) == status
