@@ -183,3 +183,81 @@ def test_skewed_full_size_gate_gradients_against_reference():
     keep_t = np.ones(w.T, bool)
     keep_t[mism] = False
     assert_close(down(layer.dlogits)[keep_t], g["dlogits"][keep_t], tol, "dlogits")
+
+
+def test_largest_supported_shape():
+    """The largest shape the header accepts for one of its bounds: h
+    ([T*k, F] bf16) 32 KiB short of 2 GiB, with T = 65535 (odd, so every
+    tile count is ragged), E = 64, top-8, dropless, a Zipf(1.0) router bias.
+    One token more is rejected.  Checked against the reference: every token's
+    logits and routing, the counts, offsets and slot rows bit-exact, y, dX and
+    dlogits of the tokens whose rows are the last and first packed rows (the
+    largest offsets into x_perm, h and the backward's buffers) and of random
+    ones, and dW1 / dW2 entries of the last expert (the last packed rows) and
+    the hottest one."""
+    import mixture_experts_layer_33_amd as moe
+    w = workloads.scaled(WL["fine_grained"], name="largest", T=65535, d=1024, F=2048, E=64, k=8,
+                         iters=1, drift_swaps=0)
+    over = moe.MoeShape.make(w.T + 1, w.d, w.F, w.E, w.k, 0.0, moe.MOE_BF16)
+    assert moe.moe_check_shape(over) == -2  # MOE_ERR_UNSUPPORTED
+    assert w.T * w.k * w.F * 2 == (1 << 31) - (1 << 15)
+    print(f"largest supported shape: {w.description}", flush=True)
+    inp, dev = _setup(w)
+    layer = MoeLayer(w.T, w.d, w.F, w.E, w.k, 0.0, act_code(w.dtype))
+    layer.forward(dev["x"], dev["w_gate"], dev["b_gate"], dev["w1"], dev["w2"])
+    layer.backward(dev["dy"], dev["x"], dev["w_gate"], dev["w1"], dev["w2"])
+    torch.cuda.synchronize()
+    tol = TOL[w.dtype]
+
+    L = orc.router_logits(inp["x"], inp["w_gate"], inp["b_gate"])
+    assert_close(down(layer.logits), L, 1e-5, "logits")
+    idx, wt = orc.topk_gate(L, w.k)
+    gidx = down(layer.topk_idx)
+    mism = np.where((gidx != idx).any(axis=1))[0]
+    assert set(mism.tolist()) <= set(ambiguous_tokens(L, w.k).tolist())
+    assert mism.size <= max(3, w.T // 2000), mism.size
+    s = orc.assign_slots(gidx, w.E, w.T)  # the GPU's own routing, laid out by the reference
+    for key in ("counts_raw", "counts_kept", "offsets", "slot_row"):
+        np.testing.assert_array_equal(down(getattr(layer, key)), s[key], err_msg=key)
+    S = w.T * w.k
+    assert int(s["offsets"][-1]) == S
+    np.testing.assert_array_equal(down(layer.row_token), s["row_token"])
+
+    rt = s["row_token"]
+    rng = np.random.default_rng(1)
+    cand = [int(rt[S - 1]), int(rt[S - 2]), int(rt[S // 2]), int(rt[0])]
+    cand += [int(t) for t in rng.choice(w.T, size=8, replace=False)]
+    toks = [t for t in dict.fromkeys(cand) if t not in mism][:8]
+    assert int(rt[S - 1]) in toks
+    gw = down(layer.topk_w).astype(np.float64)
+    y_g, dx_g, dl_g = down(layer.y), down(layer.dx), down(layer.dlogits)
+    for t in toks:
+        y_ref = orc.token_output(t, inp["x"], gw, gidx, s["slot_row"], inp["w1"], inp["w2"],
+                                 w.dtype)
+        assert_close(y_g[t], y_ref, tol, f"y[{t}]")
+        dx_ref, dl_ref = orc.token_backward(t, inp["dy"][t], inp["x"], inp["w_gate"], inp["w1"],
+                                            inp["w2"], gidx, gw, s["slot_row"], w.dtype)
+        assert_close(dx_g[t], dx_ref, tol, f"dx[{t}]")
+        assert_close(dl_g[t], dl_ref, tol, f"dlogits[{t}]")
+
+    counts = s["counts_kept"]
+    dw1_g, dw2_g = down(layer.dw1), down(layer.dw2)
+    last = max(e for e in range(w.E) if counts[e] > 0)
+    hot = int(np.argmax(counts))
+    sr = s["slot_row"]
+    for e in dict.fromkeys((last, hot)):
+        a, b = int(s["offsets"][e]), int(s["offsets"][e + 1])
+        slot_of_row = np.empty(b - a, np.int64)
+        kept = np.where((sr >= a) & (sr < b))[0]
+        slot_of_row[sr[kept] - a] = kept
+        w_rows = gw.reshape(-1)[slot_of_row]
+        rows_tok = rt[a:b]
+        fs = sorted(rng.choice(w.F, size=3, replace=False).tolist()) + [w.F - 1]
+        is_ = sorted(rng.choice(w.d, size=3, replace=False).tolist()) + [w.d - 1]
+        dw1_ref, dw2_ref = orc.expert_weight_grad_entries(
+            e, fs, is_, inp["x"][rows_tok], inp["dy"][rows_tok], w_rows, inp["w1"][e],
+            inp["w2"][e], w.dtype)
+        assert np.abs(dw1_g[e][np.ix_(fs, is_)] - dw1_ref).max() <= tol * np.abs(dw1_ref).max(), \
+            f"dw1[{e}]"
+        assert np.abs(dw2_g[e][np.ix_(is_, fs)] - dw2_ref).max() <= tol * np.abs(dw2_ref).max(), \
+            f"dw2[{e}]"
