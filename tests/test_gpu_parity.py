@@ -431,3 +431,66 @@ def test_side_stream_gives_the_same_bits(name):
         if n in ("h", "out_perm"):  # rows past the kept ones are not written
             a, b = a[:n_kept], b[:n_kept]
         assert torch.equal(a, b), n
+
+
+# Experts whose last row tile is short: a few rows up to a whole tile.
+# Shapes whose two products take 256 x 128 tiles (both), 128 x 256 then
+# 128 x 128, and 128 x 128 then 128 x 256 (the tile picker's choices for at
+# most T*k rows; K < 2048, so every tile is whole and no K split changes the
+# summation), with expert row counts around a quarter, a half and all of a
+# tile's rows.
+SHORT_TILE_CASES = {
+    "tiles_256x128": (16384, 128, 128, [1, 31, 33, 64, 65, 127, 129, 200]),
+    "tiles_128x256_128x128": (4096, 128, 512,
+                              [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 160, 0, 5, 96, 97, 250]),
+    "tiles_128x128_128x256": (8192, 256, 512, [2, 30, 40, 64, 100, 128, 130, 255]),
+}
+
+
+@pytest.mark.parametrize("case", list(SHORT_TILE_CASES))
+def test_expert_ffn_short_last_tiles(case):
+    """h, O and the ReLU keep bits against the reference per expert, and bit
+    for bit against the same rows computed inside whole tiles (each expert's
+    rows padded with other rows to a multiple of 256)."""
+    T, d, F, counts = SHORT_TILE_CASES[case]
+    E, k = len(counts), 2
+    rng = np.random.default_rng(7)
+    S = sum(counts)
+    x = workloads.round_to_bf16(rng.standard_normal((S, d), dtype=np.float32))
+    w1 = workloads.round_to_bf16(0.05 * rng.standard_normal((E, F, d), dtype=np.float32))
+    w2 = workloads.round_to_bf16(0.05 * rng.standard_normal((E, d, F), dtype=np.float32))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    dw1, dw2 = up(w1, "bf16"), up(w2, "bf16")
+
+    def run(xp_np, offs):
+        layer = MoeLayer(T, d, F, E, k, 0.0, act_code("bf16"), backward=False)
+        xp = torch.zeros(T * k, d, dtype=layer.dtype, device="cuda")
+        xp[:xp_np.shape[0]] = up(xp_np, "bf16")
+        layer.expert_ffn(dw1, dw2, x_perm=xp, offsets=up_i32(offs))
+        torch.cuda.synchronize()
+        n = int(offs[-1])
+        return (down(layer.h)[:n], down(layer.out_perm)[:n],
+                layer.relu_bits[:n].cpu().numpy().view(np.uint32))
+
+    h_g, o_g, bits_g = run(x, offsets)
+    h_r, o_r = orc.expert_ffn(x, offsets, w1, w2, "bf16")
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if a == b:
+            continue
+        assert_close(h_g[a:b], h_r[a:b], TOL["bf16"], f"h[{e}]")
+        assert_close(o_g[a:b], o_r[a:b], TOL["bf16"], f"O[{e}]")
+    keep = (h_g > 0).reshape(S, F // 32, 32)
+    np.testing.assert_array_equal(bits_g, (keep * (1 << np.arange(32, dtype=np.uint64))).sum(-1))
+
+    # the same rows inside whole tiles: expert e's rows, then filler rows
+    pad = [-(-c // 256) * 256 for c in counts]
+    assert sum(pad) <= T * k
+    offs2 = np.concatenate([[0], np.cumsum(pad)]).astype(np.int32)
+    x2 = workloads.round_to_bf16(rng.standard_normal((sum(pad), d), dtype=np.float32))
+    src = np.concatenate([np.arange(offs2[e], offs2[e] + counts[e]) for e in range(E)])
+    x2[src] = x
+    h2, o2, bits2 = run(x2, offs2)
+    np.testing.assert_array_equal(workloads.bf16_bits(h_g), workloads.bf16_bits(h2[src]))
+    np.testing.assert_array_equal(workloads.bf16_bits(o_g), workloads.bf16_bits(o2[src]))
+    np.testing.assert_array_equal(bits_g, bits2[src])
